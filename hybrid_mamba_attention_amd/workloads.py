@@ -1,0 +1,286 @@
+"""Seeded synthetic workloads for the H-Spec drafter layer.
+
+This module only draws random inputs and lays them out; it holds none of the
+method's arithmetic (no projection, no scan, no softmax).  Both the CPU oracle
+(through the tests and the bench's CPU leg) and the HIP path receive the very
+same host arrays produced here.
+
+Shapes follow the five workloads of the drafter layer (the tiny fp32 case, the
+Llama-3-8B-shaped cases at concurrency 1 / 32 / 128, and the wider 64-head
+case).  The method itself comes from "H-Spec: Parallel Speculative Decoding
+Without a Drafter-Side KV Cache" (Abstract): the Mamba state is initialised
+from a projection of the target's last-token hidden state, and attention reads
+the target's paged KV cache in place.  The pages print no shapes or value
+distributions; those below are the stated synthetic recipe.
+
+Value recipe (every workload):
+  * u, x, B, Cm, q, k_blk, v_blk and both KV pools: N(0, 1)
+  * W_init: N(0, 0.02^2)  (0.02 read as a standard deviation)
+  * delta = softplus(N(0,1) - 4)  (already positive; the kernel takes it as is)
+  * A = -exp(U(0, 1))
+  * bf16 tensors are drawn in fp32 and rounded once to bf16 (round to
+    nearest even); delta and A stay fp32.
+Paged KV recipe:
+  * page size 16; pool = sum_b ceil(ctx_b/16) pages + 64 spare pages
+  * a seeded permutation of the pool hands pages to requests, so pages of
+    different requests interleave in the one shared pool
+  * spare pages and the tail slots past ctx_b of each last page hold NaN
+  * page-table entries past a request's last page are -1
+"""
+from __future__ import annotations
+
+import math
+import os
+from concurrent.futures import ThreadPoolExecutor
+from dataclasses import dataclass, field, replace
+
+import numpy as np
+
+PAGE = 16
+SPARE_PAGES = 64
+BF16_NAN = np.uint16(0x7FC0)
+F32_NAN = np.float32("nan")
+
+# Fixed order of the per-tensor random streams (SeedSequence(seed).spawn).
+STREAMS = ("ctx", "perm", "u", "w_init", "x", "delta", "A", "B", "Cm",
+           "q", "k_blk", "v_blk", "k_cache", "v_cache", "Dskip")
+CHUNK = 1 << 22  # elements per independently seeded chunk of a big tensor
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    dtype: str            # "f32" or "bf16": element type of the activation tensors
+    C: int                # concurrent requests
+    ctx: tuple            # ("fixed", n) | ("uniform", lo, hi) | ("loguniform", lo, hi)
+    K: int                # draft block length
+    d_model: int
+    Hq: int
+    Hkv: int
+    D: int                # attention head dim
+    H: int                # Mamba-2 heads
+    P: int                # Mamba-2 head dim
+    N: int                # Mamba-2 state size
+    chunk: int            # SSD chunk length
+    seed: int
+    ng: int = 1           # B/C groups
+
+    @property
+    def S(self) -> int:
+        return self.H * self.P * self.N
+
+    @property
+    def G(self) -> int:
+        return self.Hq // self.Hkv
+
+
+WORKLOADS = {
+    0: Workload("tiny-f32-c1-ctx64", "f32", 1, ("fixed", 64), 4, 256, 4, 2, 64,
+                4, 64, 16, 4, 1000),
+    1: Workload("llama8b-bf16-c1-ctx2048", "bf16", 1, ("fixed", 2048), 16, 4096,
+                32, 8, 128, 16, 64, 32, 16, 1001),
+    2: Workload("llama8b-bf16-c32-ctx512to4096", "bf16", 32, ("uniform", 512, 4096),
+                16, 4096, 32, 8, 128, 16, 64, 32, 16, 1002),
+    3: Workload("llama8b-bf16-c128-ctx8192", "bf16", 128, ("fixed", 8192), 16, 4096,
+                32, 8, 128, 16, 64, 32, 16, 1003),
+    4: Workload("wide64h-bf16-c64-ctx1024to16384", "bf16", 64,
+                ("loguniform", 1024, 16384), 16, 5120, 64, 8, 128, 32, 64, 64, 16, 1004),
+}
+
+
+def sweep_workload(C: int) -> Workload:
+    """Concurrency sweep point: the C=128 workload's shapes at another C."""
+    base = WORKLOADS[3]
+    return replace(base, name=f"llama8b-bf16-c{C}-ctx8192", C=C, seed=2000 + C)
+
+
+# ----------------------------------------------------------------------------
+# helpers (format conversion only)
+# ----------------------------------------------------------------------------
+
+def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """Round fp32 to bf16 (nearest, ties to even); returns the uint16 bit patterns."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    u = a.view(np.uint32)
+    out = ((u + (((u >> 16) & np.uint32(1)) + np.uint32(0x7FFF))) >> 16).astype(np.uint16)
+    nan = np.isnan(a)
+    if nan.any():
+        out[nan] = BF16_NAN
+    return out
+
+
+def _threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def _normal_chunked(ss: np.random.SeedSequence, n: int, std: float, bf16: bool,
+                    out: np.ndarray | None = None) -> np.ndarray:
+    """n draws of N(0, std^2), produced in CHUNK-sized independently seeded pieces.
+
+    The result does not depend on the thread count.  Returns fp32 or bf16 bits.
+    """
+    if out is None:
+        out = np.empty(n, dtype=np.uint16 if bf16 else np.float32)
+    nchunks = max(1, -(-n // CHUNK))
+    kids = ss.spawn(nchunks)
+
+    def work(i):
+        lo, hi = i * CHUNK, min(n, (i + 1) * CHUNK)
+        g = np.random.default_rng(kids[i])
+        v = g.standard_normal(hi - lo, dtype=np.float32)
+        if std != 1.0:
+            v *= np.float32(std)
+        out[lo:hi] = f32_to_bf16_bits(v) if bf16 else v
+
+    if nchunks == 1:
+        work(0)
+    else:
+        with ThreadPoolExecutor(_threads()) as ex:
+            list(ex.map(work, range(nchunks)))
+    return out
+
+
+# ----------------------------------------------------------------------------
+# context lengths, page pool and page table
+# ----------------------------------------------------------------------------
+
+def draw_ctx_lens(w: Workload, ss: np.random.SeedSequence) -> np.ndarray:
+    g = np.random.default_rng(ss)
+    kind = w.ctx[0]
+    if kind == "fixed":
+        return np.full(w.C, w.ctx[1], dtype=np.int32)
+    if kind == "uniform":
+        lo, hi = w.ctx[1], w.ctx[2]
+        return g.integers(lo, hi, endpoint=True, size=w.C).astype(np.int32)
+    if kind == "loguniform":
+        lo, hi = w.ctx[1], w.ctx[2]
+        v = np.floor(np.exp(g.uniform(math.log(lo), math.log(hi), size=w.C)))
+        return np.clip(v, lo, hi).astype(np.int32)
+    raise ValueError(kind)
+
+
+def build_page_table(ctx_lens: np.ndarray, ss: np.random.SeedSequence,
+                     spare: int = SPARE_PAGES, identity: bool = False):
+    """Shared page pool with interleaved pages.
+
+    Returns (page_table int32 [C, max_pages] with -1 padding, num_pages, pages_of
+    list of int arrays).  identity=True hands out pages in order (no shuffle).
+    """
+    ctx_lens = np.asarray(ctx_lens, dtype=np.int64)
+    n_pages = (ctx_lens + PAGE - 1) // PAGE
+    total = int(n_pages.sum())
+    pool = total + spare
+    if identity:
+        perm = np.arange(pool, dtype=np.int64)
+    else:
+        perm = np.random.default_rng(ss).permutation(pool)
+    max_pages = max(1, int(n_pages.max()) if len(n_pages) else 1)
+    pt = np.full((len(ctx_lens), max_pages), -1, dtype=np.int32)
+    off = 0
+    pages_of = []
+    for b, n in enumerate(n_pages):
+        p = perm[off:off + n]
+        pt[b, :n] = p
+        pages_of.append(p.astype(np.int64))
+        off += n
+    return pt, pool, pages_of
+
+
+def _poison_kv(pool_arr: np.ndarray, ctx_lens, pages_of, used_pages, nan_value):
+    """NaN into spare pages and into the tail slots past ctx of each last page."""
+    spare = np.ones(pool_arr.shape[0], dtype=bool)
+    spare[used_pages] = False
+    pool_arr[spare] = nan_value
+    for L, pages in zip(ctx_lens, pages_of):
+        r = int(L) % PAGE
+        if r:
+            pool_arr[pages[-1], r:] = nan_value
+
+
+# ----------------------------------------------------------------------------
+# full input set
+# ----------------------------------------------------------------------------
+
+@dataclass
+class Inputs:
+    w: Workload
+    ctx_lens: np.ndarray          # int32 [C]
+    page_table: np.ndarray        # int32 [C, max_pages]
+    num_pages: int
+    arrays: dict = field(default_factory=dict)
+    # arrays: u [C,d], w_init [d,S], x [C,K,H,P], B/Cm [C,K,ng,N] (act dtype: fp32 or
+    # bf16 bits as uint16); delta f32 [C,K,H]; A f32 [H]; q [C,K,Hq,D];
+    # k_blk/v_blk [C,K,Hkv,D]; k_cache/v_cache [num_pages,16,Hkv,D] (act dtype)
+
+    @property
+    def max_pages(self) -> int:
+        return int(self.page_table.shape[1])
+
+    @property
+    def max_ctx(self) -> int:
+        return int(self.ctx_lens.max()) if len(self.ctx_lens) else 0
+
+
+def make_inputs(w: Workload, *, ctx_lens=None, identity_pages: bool = False,
+                with_dskip: bool = False, parts=("mamba", "attn")) -> Inputs:
+    """Draw every input of workload `w` from its seed.
+
+    ctx_lens overrides the drawn context lengths (edge-case tests).  parts
+    selects which halves to draw ("mamba": u, W_init, x, delta, A, B, Cm;
+    "attn": q, block K/V, KV pools); the streams stay the same either way.
+    """
+    root = np.random.SeedSequence(w.seed)
+    ss = dict(zip(STREAMS, root.spawn(len(STREAMS))))
+    bf16 = w.dtype == "bf16"
+    act = np.uint16 if bf16 else np.float32
+
+    if ctx_lens is None:
+        ctx_lens = draw_ctx_lens(w, ss["ctx"])
+    ctx_lens = np.asarray(ctx_lens, dtype=np.int32)
+    pt, pool, pages_of = build_page_table(ctx_lens, ss["perm"], identity=identity_pages)
+    inp = Inputs(w, ctx_lens, pt, pool)
+    a = inp.arrays
+
+    def normal(name, shape, std=1.0):
+        n = int(np.prod(shape))
+        return _normal_chunked(ss[name], n, std, bf16).reshape(shape)
+
+    if "mamba" in parts:
+        a["u"] = normal("u", (w.C, w.d_model))
+        a["w_init"] = normal("w_init", (w.d_model, w.S), 0.02)
+        a["x"] = normal("x", (w.C, w.K, w.H, w.P))
+        z = np.random.default_rng(ss["delta"]).standard_normal((w.C, w.K, w.H)) - 4.0
+        a["delta"] = np.logaddexp(0.0, z).astype(np.float32)          # softplus
+        a["A"] = (-np.exp(np.random.default_rng(ss["A"]).uniform(0.0, 1.0, w.H))).astype(np.float32)
+        a["B"] = normal("B", (w.C, w.K, w.ng, w.N))
+        a["Cm"] = normal("Cm", (w.C, w.K, w.ng, w.N))
+        if with_dskip:
+            a["Dskip"] = np.random.default_rng(ss["Dskip"]).standard_normal(w.H).astype(np.float32)
+    if "attn" in parts:
+        a["q"] = normal("q", (w.C, w.K, w.Hq, w.D))
+        a["k_blk"] = normal("k_blk", (w.C, w.K, w.Hkv, w.D))
+        a["v_blk"] = normal("v_blk", (w.C, w.K, w.Hkv, w.D))
+        shape = (pool, PAGE, w.Hkv, w.D)
+        used = np.concatenate(pages_of) if pages_of else np.zeros(0, np.int64)
+        nan = BF16_NAN if bf16 else F32_NAN
+        for name in ("k_cache", "v_cache"):
+            arr = normal(name, shape)
+            _poison_kv(arr, ctx_lens, pages_of, used, nan)
+            a[name] = arr
+    assert all(v.dtype in (act, np.float32) for v in a.values())
+    return inp
+
+
+def kv_bytes(w: Workload, ctx_lens) -> int:
+    """Bytes of target KV a layer call must read in place (K and V, valid tokens)."""
+    e = 2 if w.dtype == "bf16" else 4
+    return int(np.sum(np.asarray(ctx_lens, np.int64))) * w.Hkv * w.D * 2 * e
+
+
+def w_init_bytes(w: Workload) -> int:
+    e = 2 if w.dtype == "bf16" else 4
+    return w.d_model * w.S * e

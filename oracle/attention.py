@@ -1,0 +1,142 @@
+"""E4 / E5: block-query attention over the target's paged KV, read in place.
+
+H-Spec (Abstract; review page, Summary): the drafter's attention modules use
+the target model's own KV cache where it lies, so no drafter-side KV cache is
+ever built.  The K queries of the draft block attend to the request's whole
+target context plus the block's own K keys (read here as no mask inside the
+block: every block query sees every context key and every block key).
+
+Definition, per request b and query head i (kv head j = i // G, G = Hq/Hkv):
+
+    Kall = concat(Kctx_b,j, k_blk[b, :, j]),  Vall likewise
+    Kctx_b,j[n] = Kc[PT[b, n // 16], n % 16, j]     for n < ctx_b
+    o[b, :, i] = softmax(scale * q[b, :, i] @ Kall^T) @ Vall,   scale = 1/sqrt(D)
+
+Page reads here are strict: a page-table entry outside the pool, or a NaN in
+a token that should be valid, raises PoisonedRead.  The workloads fill spare
+pages and the tail slots past ctx_b with NaN, so reading the wrong page or the
+wrong slot cannot go unnoticed.
+
+block_attention is the definition.  block_attention_splits restates it as
+split-KV: each split of the plan yields a partial (running max m, sum l,
+unnormalised output); partials merge as
+    M = max_s m_s,   o = sum_s e^(m_s - M) O_s / sum_s e^(m_s - M) l_s,
+with an empty split contributing m = -inf, l = 0, O = 0.
+"""
+import numpy as np
+
+from .numerics import decode
+
+PAGE = 16
+
+
+class PoisonedRead(RuntimeError):
+    """The oracle was asked to read a page or slot that holds no valid token."""
+
+
+def gather_context(cache, page_row, ctx_len: int, j: int, dtype: str) -> np.ndarray:
+    """Target keys (or values) of one request and kv head as [ctx_len, D] float64.
+
+    cache: stored pool [num_pages, 16, Hkv, D]; page_row: that request's page
+    table row.  Reads only the pages and slots that hold valid tokens.
+    """
+    ctx_len = int(ctx_len)
+    D = cache.shape[-1]
+    if ctx_len == 0:
+        return np.zeros((0, D))
+    n_pages = -(-ctx_len // PAGE)
+    pages = np.asarray(page_row[:n_pages], dtype=np.int64)
+    if len(pages) < n_pages or (pages < 0).any() or (pages >= cache.shape[0]).any():
+        raise PoisonedRead(f"page table entry out of range: {pages}")
+    rows = np.asarray(cache[pages, :, j, :]).reshape(n_pages * PAGE, D)[:ctx_len]
+    rows = decode(rows, dtype)
+    if np.isnan(rows).any():
+        raise PoisonedRead("read a NaN-poisoned token")
+    return rows
+
+
+def _scale(D, scale):
+    return 1.0 / np.sqrt(D) if not scale else float(scale)
+
+
+def block_attention(q, k_blk, v_blk, k_cache, v_cache, page_table, ctx_lens, *,
+                    dtype: str, scale=None, requests=None) -> np.ndarray:
+    """Brute-force attention over (context read through the page table) + block.
+
+    q [C,K,Hq,D], k_blk/v_blk [C,K,Hkv,D] and the caches in stored form.
+    Returns o [C,K,Hq,D] float64 (rows of requests not in `requests` stay 0).
+    """
+    C, K, Hq, D = q.shape
+    Hkv = k_blk.shape[2]
+    G = Hq // Hkv
+    sc = _scale(D, scale)
+    out = np.zeros((C, K, Hq, D))
+    reqs = range(C) if requests is None else requests
+    for b in reqs:
+        qb = decode(q[b], dtype)                                       # [K,Hq,D]
+        kb = decode(k_blk[b], dtype)
+        vb = decode(v_blk[b], dtype)
+        for j in range(Hkv):
+            kall = np.concatenate([gather_context(k_cache, page_table[b], ctx_lens[b], j, dtype), kb[:, j]])
+            vall = np.concatenate([gather_context(v_cache, page_table[b], ctx_lens[b], j, dtype), vb[:, j]])
+            qj = qb[:, j * G:(j + 1) * G, :].reshape(K * G, D)
+            s = sc * (qj @ kall.T)                                     # [K*G, ctx+K]
+            s = s - s.max(axis=1, keepdims=True)
+            p = np.exp(s)
+            p /= p.sum(axis=1, keepdims=True)
+            out[b, :, j * G:(j + 1) * G, :] = (p @ vall).reshape(K, G, D)
+    return out
+
+
+def split_partials(qj, kall, vall, sc, bounds):
+    """Partials (m [R], l [R], O [R,D]) of query rows qj over key ranges `bounds`."""
+    parts = []
+    for lo, hi in bounds:
+        R = qj.shape[0]
+        if hi <= lo:
+            parts.append((np.full(R, -np.inf), np.zeros(R), np.zeros((R, vall.shape[1]))))
+            continue
+        s = sc * (qj @ kall[lo:hi].T)
+        m = s.max(axis=1)
+        p = np.exp(s - m[:, None])
+        parts.append((m, p.sum(axis=1), p @ vall[lo:hi]))
+    return parts
+
+
+def merge_partials(parts):
+    """Combine split partials into the normalised output [R, D]."""
+    ms = np.stack([p[0] for p in parts])                               # [S,R]
+    M = ms.max(axis=0)
+    w = np.where(np.isneginf(ms), 0.0, np.exp(ms - np.where(np.isneginf(M), 0.0, M)[None]))
+    num = sum(w[k][:, None] * parts[k][2] for k in range(len(parts)))
+    den = sum(w[k] * parts[k][1] for k in range(len(parts)))
+    return num / den[:, None]
+
+
+def block_attention_splits(q, k_blk, v_blk, k_cache, v_cache, page_table, ctx_lens, pps, *,
+                           dtype: str, scale=None, requests=None) -> np.ndarray:
+    """Split-KV restatement of block_attention: pps context pages per split,
+    block keys in the last split, partials merged as in the module docstring."""
+    C, K, Hq, D = q.shape
+    Hkv = k_blk.shape[2]
+    G = Hq // Hkv
+    sc = _scale(D, scale)
+    out = np.zeros((C, K, Hq, D))
+    reqs = range(C) if requests is None else requests
+    for b in reqs:
+        ctx = int(ctx_lens[b])
+        n_pages = -(-ctx // PAGE)
+        n_splits = max(1, -(-n_pages // pps))
+        bounds = [(s * pps * PAGE, min(ctx, (s + 1) * pps * PAGE)) for s in range(n_splits)]
+        lo_last = bounds[-1][0]
+        bounds[-1] = (lo_last, ctx + K)                                 # block keys join the last split
+        qb = decode(q[b], dtype)
+        kb = decode(k_blk[b], dtype)
+        vb = decode(v_blk[b], dtype)
+        for j in range(Hkv):
+            kall = np.concatenate([gather_context(k_cache, page_table[b], ctx, j, dtype), kb[:, j]])
+            vall = np.concatenate([gather_context(v_cache, page_table[b], ctx, j, dtype), vb[:, j]])
+            qj = qb[:, j * G:(j + 1) * G, :].reshape(K * G, D)
+            o = merge_partials(split_partials(qj, kall, vall, sc, bounds))
+            out[b, :, j * G:(j + 1) * G, :] = o.reshape(K, G, D)
+    return out
