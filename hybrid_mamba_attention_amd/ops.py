@@ -1,0 +1,291 @@
+"""Thin ctypes binding over libhspec.so (include/hspec.h).
+
+Argument marshalling only: tensors are passed by data pointer together with
+torch's current HIP stream; every step of the layer runs in the library's
+kernels.  There is no fallback of any kind -- if the library is missing or
+refuses the arguments, the call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libhspec.so")
+
+F32, BF16 = 0, 1
+_STATUS = {0: "HSPEC_OK", -1: "HSPEC_ERR_INVALID_ARG", -2: "HSPEC_ERR_UNSUPPORTED",
+           -3: "HSPEC_ERR_WORKSPACE", -4: "HSPEC_ERR_HIP"}
+
+_vp, _i, _i64, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+
+
+class LayerArgs(ctypes.Structure):
+    """Mirror of hspec_layer_args (field order and types as in include/hspec.h)."""
+    _fields_ = [
+        ("dtype", _i), ("C", _i), ("K", _i),
+        ("d_model", _i), ("H", _i), ("P", _i), ("ng", _i), ("N", _i), ("chunk", _i),
+        ("u", _vp), ("w_init", _vp), ("h0", _vp),
+        ("x", _vp), ("delta", _vp), ("A", _vp), ("B", _vp), ("Cm", _vp),
+        ("Dskip", _vp), ("y", _vp), ("h_final", _vp),
+        ("Hq", _i), ("Hkv", _i), ("D", _i),
+        ("q", _vp), ("k_blk", _vp), ("v_blk", _vp),
+        ("k_cache", _vp), ("v_cache", _vp),
+        ("page_stride", _i64), ("token_stride", _i64), ("head_stride", _i64),
+        ("num_pages", _i), ("page_table", _vp), ("max_pages", _i),
+        ("ctx_lens", _vp), ("max_ctx", _i),
+        ("kv_split_pages", _i), ("scale", _f), ("out", _vp),
+        ("workspace", _vp), ("workspace_bytes", _sz),
+    ]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libhspec.so (once) and declare its signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing; build it with "
+                           "`python -m hybrid_mamba_attention_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    L.hspec_status_string.restype = ctypes.c_char_p
+    L.hspec_status_string.argtypes = [_i]
+    L.hspec_abi_version.restype = _i
+    L.hspec_layer_args_size.restype = _sz
+    L.hspec_init_state.restype = _i
+    L.hspec_init_state.argtypes = [_vp, _i, _i, _i, _i, _vp, _vp, _vp]
+    L.hspec_ssd_scan.restype = _i
+    L.hspec_ssd_scan.argtypes = [_vp, _i] + [_i] * 7 + [_vp] * 9
+    L.hspec_block_attn_inplace.restype = _i
+    L.hspec_block_attn_inplace.argtypes = ([_vp, _i, _i, _i, _i, _i, _i] + [_vp] * 5 +
+                                           [_i64, _i64, _i64, _i, _vp, _i, _vp, _i, _i, _f, _vp,
+                                            _vp, ctypes.POINTER(_sz)])
+    L.hspec_draft_layer.restype = _i
+    L.hspec_draft_layer.argtypes = [_vp, ctypes.POINTER(LayerArgs), ctypes.POINTER(_sz)]
+    if L.hspec_abi_version() != 1:
+        raise RuntimeError("libhspec.so ABI version mismatch")
+    if L.hspec_layer_args_size() != ctypes.sizeof(LayerArgs):
+        raise RuntimeError("hspec_layer_args layout mismatch between library and binding")
+    _lib = L
+    return L
+
+
+def status_string(code: int) -> str:
+    return _STATUS.get(code, f"status {code}")
+
+
+class HspecError(RuntimeError):
+    def __init__(self, fn: str, code: int):
+        super().__init__(f"{fn} failed: {status_string(code)}")
+        self.code = code
+
+
+def _check(fn: str, code: int):
+    if code != 0:
+        raise HspecError(fn, code)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"activation tensors must be float32 or bfloat16, got {t.dtype}")
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _contig(*ts):
+    for t in ts:
+        if t is not None and not t.is_contiguous():
+            raise ValueError("tensor must be contiguous")
+
+
+# ---------------------------------------------------------------------------
+# a1
+# ---------------------------------------------------------------------------
+
+def init_state(u: torch.Tensor, w_init: torch.Tensor, h0: torch.Tensor | None = None,
+               stream=None) -> torch.Tensor:
+    """h0[C, S] (fp32) = u[C, d] . w_init[d, S]."""
+    _contig(u, w_init, h0)
+    C, d = u.shape
+    S = w_init.shape[1]
+    if h0 is None:
+        h0 = torch.empty((C, S), dtype=torch.float32, device=u.device)
+    _check("hspec_init_state", lib().hspec_init_state(
+        _stream(stream), _dtype_code(u), C, d, S, _ptr(u), _ptr(w_init), _ptr(h0)))
+    return h0
+
+
+# ---------------------------------------------------------------------------
+# a2
+# ---------------------------------------------------------------------------
+
+def ssd_scan(x, delta, A, B, Cm, *, chunk: int, h0=None, Dskip=None, y=None, h_final=None,
+             want_final: bool = False, stream=None):
+    """y[C,K,H,P] (fp32) and optionally h_final[C,H,P,N] of the chunked SSD scan."""
+    _contig(x, delta, A, B, Cm, h0, Dskip, y, h_final)
+    C, K, H, P = x.shape
+    ng, N = B.shape[2], B.shape[3]
+    if y is None:
+        y = torch.empty((C, K, H, P), dtype=torch.float32, device=x.device)
+    if h_final is None and want_final:
+        h_final = torch.empty((C, H, P, N), dtype=torch.float32, device=x.device)
+    _check("hspec_ssd_scan", lib().hspec_ssd_scan(
+        _stream(stream), _dtype_code(x), C, K, H, P, ng, N, chunk,
+        _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(Cm), _ptr(Dskip), _ptr(h0), _ptr(y),
+        _ptr(h_final)))
+    return y, h_final
+
+
+# ---------------------------------------------------------------------------
+# a0 + a3 + a4
+# ---------------------------------------------------------------------------
+
+def kv_strides(k_cache: torch.Tensor, layout: str = "NHD"):
+    """(page, token, head) strides in elements of a pool tensor.
+
+    NHD pools are [pages, 16, Hkv, D]; HND pools are [pages, Hkv, 16, D]."""
+    s = k_cache.stride()
+    if k_cache.stride(-1) != 1:
+        raise ValueError("the head dimension of the KV pool must be contiguous")
+    if layout == "NHD":
+        return s[0], s[1], s[2]
+    if layout == "HND":
+        return s[0], s[2], s[1]
+    raise ValueError(layout)
+
+
+def _attn_call(L, stream, q, k_blk, v_blk, k_cache, v_cache, page_table, ctx_lens, max_ctx,
+               kv_split_pages, scale, out, ws, ws_bytes, layout):
+    C, K, Hq, D = q.shape
+    Hkv = k_blk.shape[2]
+    ps, ts, hs = kv_strides(k_cache, layout)
+    if kv_strides(v_cache, layout) != (ps, ts, hs):
+        raise ValueError("K and V pools must share strides")
+    return L.hspec_block_attn_inplace(
+        stream, _dtype_code(q), C, K, Hq, Hkv, D, _ptr(q), _ptr(k_blk), _ptr(v_blk),
+        _ptr(k_cache), _ptr(v_cache), ps, ts, hs, k_cache.shape[0], _ptr(page_table),
+        page_table.shape[1], _ptr(ctx_lens), int(max_ctx), int(kv_split_pages), float(scale),
+        _ptr(out), ws, ctypes.byref(ws_bytes))
+
+
+def attn_workspace_bytes(q, k_blk, v_blk, k_cache, v_cache, page_table, ctx_lens, *, max_ctx,
+                         kv_split_pages=0, scale=0.0, layout="NHD") -> int:
+    n = _sz(0)
+    out = torch.empty(1, dtype=q.dtype, device=q.device)  # never written by a size query
+    _check("hspec_block_attn_inplace", _attn_call(
+        lib(), _stream(None), q, k_blk, v_blk, k_cache, v_cache, page_table, ctx_lens, max_ctx,
+        kv_split_pages, scale, out, None, n, layout))
+    return n.value
+
+
+def block_attn_inplace(q, k_blk, v_blk, k_cache, v_cache, page_table, ctx_lens, *, max_ctx,
+                       kv_split_pages=0, scale=0.0, out=None, workspace=None, layout="NHD",
+                       stream=None):
+    """out[C,K,Hq,D] = attention of the block queries over paged target KV + block KV.
+
+    workspace: a uint8 CUDA tensor of at least attn_workspace_bytes(...) bytes
+    (allocated here if None).  Returns (out, workspace)."""
+    _contig(q, k_blk, v_blk, page_table, ctx_lens, out)
+    if page_table.dtype != torch.int32 or ctx_lens.dtype != torch.int32:
+        raise TypeError("page_table and ctx_lens must be int32")
+    L = lib()
+    if out is None:
+        out = torch.empty_like(q)
+    if workspace is None:
+        nbytes = attn_workspace_bytes(q, k_blk, v_blk, k_cache, v_cache, page_table, ctx_lens,
+                                      max_ctx=max_ctx, kv_split_pages=kv_split_pages, scale=scale,
+                                      layout=layout)
+        workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q.device)
+    n = _sz(workspace.numel())
+    _check("hspec_block_attn_inplace", _attn_call(
+        L, _stream(stream), q, k_blk, v_blk, k_cache, v_cache, page_table, ctx_lens, max_ctx,
+        kv_split_pages, scale, out, _ptr(workspace), n, layout))
+    return out, workspace
+
+
+# ---------------------------------------------------------------------------
+# a5
+# ---------------------------------------------------------------------------
+
+class DraftLayer:
+    """Holds the marshalled argument block of one drafter-layer configuration so
+    that repeated calls (benchmarks, serving loops) only re-issue the C call."""
+
+    def __init__(self, *, u, w_init, x, delta, A, B, Cm, chunk, q, k_blk, v_blk, k_cache, v_cache,
+                 page_table, ctx_lens, max_ctx, kv_split_pages=0, scale=0.0, Dskip=None,
+                 want_final=False, layout="NHD"):
+        _contig(u, w_init, x, delta, A, B, Cm, q, k_blk, v_blk, page_table, ctx_lens, Dskip)
+        dev = u.device
+        C, d = u.shape
+        _, K, H, P = x.shape
+        ng, N = B.shape[2], B.shape[3]
+        _, _, Hq, D = q.shape
+        Hkv = k_blk.shape[2]
+        self.h0 = torch.empty((C, H * P * N), dtype=torch.float32, device=dev)
+        self.y = torch.empty((C, K, H, P), dtype=torch.float32, device=dev)
+        self.h_final = (torch.empty((C, H, P, N), dtype=torch.float32, device=dev)
+                        if want_final else None)
+        self.out = torch.empty_like(q)
+        ps, ts, hs = kv_strides(k_cache, layout)
+        a = LayerArgs()
+        a.dtype = _dtype_code(u)
+        a.C, a.K = C, K
+        a.d_model, a.H, a.P, a.ng, a.N, a.chunk = d, H, P, ng, N, chunk
+        a.u, a.w_init, a.h0 = u.data_ptr(), w_init.data_ptr(), self.h0.data_ptr()
+        a.x, a.delta, a.A = x.data_ptr(), delta.data_ptr(), A.data_ptr()
+        a.B, a.Cm = B.data_ptr(), Cm.data_ptr()
+        a.Dskip = Dskip.data_ptr() if Dskip is not None else None
+        a.y = self.y.data_ptr()
+        a.h_final = self.h_final.data_ptr() if self.h_final is not None else None
+        a.Hq, a.Hkv, a.D = Hq, Hkv, D
+        a.q, a.k_blk, a.v_blk = q.data_ptr(), k_blk.data_ptr(), v_blk.data_ptr()
+        a.k_cache, a.v_cache = k_cache.data_ptr(), v_cache.data_ptr()
+        a.page_stride, a.token_stride, a.head_stride = ps, ts, hs
+        a.num_pages = k_cache.shape[0]
+        a.page_table, a.max_pages = page_table.data_ptr(), page_table.shape[1]
+        a.ctx_lens, a.max_ctx = ctx_lens.data_ptr(), int(max_ctx)
+        a.kv_split_pages, a.scale = int(kv_split_pages), float(scale)
+        a.out = self.out.data_ptr()
+        a.workspace, a.workspace_bytes = None, 0
+        need = _sz(0)
+        _check("hspec_draft_layer", lib().hspec_draft_layer(None, ctypes.byref(a), ctypes.byref(need)))
+        self.workspace = torch.empty(max(need.value, 256), dtype=torch.uint8, device=dev)
+        a.workspace, a.workspace_bytes = self.workspace.data_ptr(), self.workspace.numel()
+        self._args = a
+        self._keep = (u, w_init, x, delta, A, B, Cm, Dskip, q, k_blk, v_blk, k_cache, v_cache,
+                      page_table, ctx_lens)
+
+    def __call__(self, stream=None):
+        _check("hspec_draft_layer", lib().hspec_draft_layer(_stream(stream), ctypes.byref(self._args), None))
+        return self
+
+    def plan(self) -> torch.Tensor:
+        """The int32 split plan at the head of the workspace (see include/hspec.h)."""
+        w = self.workspace
+        C = self._args.C
+        M = int(w[12:16].view(torch.int32).item())
+        return w[:4 * (4 + 2 * C + 2 * M)].view(torch.int32)
+
+
+def draft_layer(**kw):
+    """One drafter-layer call; returns the DraftLayer holding h0, y, h_final, out."""
+    return DraftLayer(**kw)()

@@ -1,0 +1,187 @@
+/*
+ * hspec.h -- C ABI of libhspec.so, the MI355X (gfx950) drafter-layer library.
+ *
+ * The layer is the block-parallel drafter layer of "H-Spec: Parallel
+ * Speculative Decoding Without a Drafter-Side KV Cache" (Abstract; review
+ * page, Summary): a Mamba-2 module whose state starts from a projection of the
+ * target's last-token hidden state and scans the K-token draft block in
+ * parallel, and an attention module whose K block queries read the target's
+ * paged KV cache in place -- the library has no argument through which it
+ * could write a drafter-side KV cache.
+ *
+ * Conventions shared by every entry point
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Every call only
+ *     enqueues work on it and returns; nothing synchronises.  Host-side
+ *     argument errors are returned before anything is enqueued; launch errors
+ *     come back as HSPEC_ERR_HIP; faults inside kernels surface at the
+ *     caller's next synchronisation.
+ *   - All pointers except the integer metadata noted below are device
+ *     pointers.  The caller owns every buffer; the library allocates nothing
+ *     and keeps no state between calls, so calls on different streams may run
+ *     concurrently as long as their output and workspace buffers differ.
+ *   - `dtype` selects the element type of the "act" tensors: HSPEC_F32
+ *     (float) or HSPEC_BF16 (bfloat16 bits).  Accumulation is always fp32.
+ *   - Shapes are row-major, last index fastest; "act" tensors are contiguous
+ *     unless strides are given; every device pointer must be 16-byte aligned.
+ */
+#ifndef HSPEC_H
+#define HSPEC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { HSPEC_F32 = 0, HSPEC_BF16 = 1 } hspec_dtype;
+
+typedef enum {
+  HSPEC_OK = 0,
+  HSPEC_ERR_INVALID_ARG = -1,   /* a size, pointer or stride breaks the contract      */
+  HSPEC_ERR_UNSUPPORTED = -2,   /* legal but outside the shapes these kernels handle  */
+  HSPEC_ERR_WORKSPACE = -3,     /* workspace pointer missing or smaller than required */
+  HSPEC_ERR_HIP = -4            /* the HIP runtime refused a launch                   */
+} hspec_status;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* hspec_status_string(int status);
+
+/* ABI version of this header; bumped on any incompatible change. */
+#define HSPEC_ABI_VERSION 1
+int hspec_abi_version(void);
+
+/*
+ * a1 -- initial Mamba-2 state from the target's last-token hidden state.
+ * H-Spec, Abstract and review Summary: the Mamba module is initialised from
+ * a projection of the last-token target hidden state.  Linear, no bias:
+ *
+ *   h0[b, s] = sum_i u[b, i] * w_init[i, s],   s = (h*P + p)*N + n
+ *
+ *   u       act  [C, d_model]      last-token hidden state per request
+ *   w_init  act  [d_model, S]      projection weight, S = H*P*N
+ *   h0      fp32 [C, S]            output (overwritten)
+ * Limits: C >= 1, d_model % 32 == 0, S % 64 == 0 (else UNSUPPORTED).
+ * Runs on bf16 (or fp32) matrix cores with fp32 accumulation.
+ */
+int hspec_init_state(void* stream, int dtype, int C, int d_model, int S,
+                     const void* u, const void* w_init, float* h0);
+
+/*
+ * a2 -- Mamba-2 (SSD) chunked parallel scan over the draft block.
+ * H-Spec, Abstract: the Mamba module keeps drafting block-parallel through
+ * its parallel scan.  Per request b and head h (group g = h / (H/ng)):
+ *
+ *   H_t = exp(delta[b,t,h] * A[h]) * H_{t-1} + delta[b,t,h] * x[b,t,h,:] (outer) B[b,t,g,:]
+ *   y[b,t,h,:] = H_t @ Cm[b,t,g,:] + Dskip[h] * x[b,t,h,:],     H_{-1} = h0[b,h]
+ *
+ * evaluated chunk by chunk (intra-chunk decay matrix + inter-chunk state
+ * passing, Mamba-2's SSD form), which equals the recurrence exactly in real
+ * arithmetic.
+ *   x       act  [C, K, H, P]
+ *   delta   fp32 [C, K, H]        step sizes, already positive
+ *   A       fp32 [H]              per-head decay rate (negative)
+ *   B, Cm   act  [C, K, ng, N]
+ *   Dskip   fp32 [H] or NULL      NULL = no skip term
+ *   h0      fp32 [C, H, P, N] or NULL (NULL = zero state); the layout of a1's h0
+ *   y       fp32 [C, K, H, P]     output
+ *   h_final fp32 [C, H, P, N] or NULL: the state after the last block position
+ * Limits: chunk in {1,2,4,8,16,32,64}; P <= 128; N <= 128; P*N <= 8192;
+ * ng divides H (else INVALID_ARG / UNSUPPORTED).
+ */
+int hspec_ssd_scan(void* stream, int dtype, int C, int K, int H, int P, int ng, int N, int chunk,
+                   const void* x, const float* delta, const float* A,
+                   const void* B, const void* Cm, const float* Dskip,
+                   const float* h0, float* y, float* h_final);
+
+/*
+ * a0 + a3 + a4 -- block-query attention over the target's paged KV, in place.
+ * H-Spec, Abstract and review Summary: attention reuses the target's KV
+ * where it lies; no drafter-side KV cache exists.  Per request b and query
+ * head i (kv head j = i / (Hq/Hkv)), the K block queries attend, with no mask
+ * inside the block, to the ctx_lens[b] context tokens read through the page
+ * table plus the K block keys:
+ *
+ *   keys   = Kc[page_table[b][n/16], n%16, j] (n < ctx_lens[b])  ++  k_blk[b, :, j]
+ *   out[b, :, i] = softmax(scale * q[b, :, i] @ keys^T) @ values
+ *
+ *   q            act [C, K, Hq, D]
+ *   k_blk, v_blk act [C, K, Hkv, D]   the block's own keys / values (transient)
+ *   k_cache,     act pools, read only; element (page, slot, j, d) sits at
+ *   v_cache          page*page_stride + slot*token_stride + j*head_stride + d
+ *                    (strides in elements, multiples of 8; d contiguous;
+ *                    16 slots per page).  NHD [pages,16,Hkv,D] and HND
+ *                    [pages,Hkv,16,D] pools are both just strides.
+ *   num_pages    pages in each pool (entries must lie in [0, num_pages))
+ *   page_table   int32 [C, max_pages] device; row b lists request b's pages
+ *                in context order; entries past ceil(ctx_lens[b]/16) are unused
+ *   ctx_lens     int32 [C] device; 0 <= ctx_lens[b] <= max_ctx
+ *   max_ctx      host upper bound of ctx_lens (sizes the grid and workspace);
+ *                max_pages >= ceil(max_ctx/16)
+ *   kv_split_pages  context pages per split-KV work item (0 = pick
+ *                automatically); results do not depend on it beyond fp32
+ *                rounding, and are bitwise repeatable for a fixed value
+ *   scale        softmax scale; 0.f means 1/sqrt(D)
+ *   out          act [C, K, Hq, D]
+ *   workspace / workspace_bytes:
+ *       workspace == NULL: size query -- *workspace_bytes receives the bytes
+ *       this call needs; nothing is launched.  Otherwise *workspace_bytes is
+ *       the capacity of `workspace` (device, 256-byte aligned), which must be
+ *       at least the queried size.  The workspace starts with the int32 split
+ *       plan:
+ *         [0] items  [1] pages per split  [2] C  [3] capacity M
+ *         [4, 4+C) splits of request b    [4+C, 4+2C) first item of request b
+ *         [4+2C, 4+2C+M) request of item i (-1 unused)
+ *         [4+2C+M, 4+2C+2M) split of item i (-1 unused)
+ *       with splits_b = max(1, ceil(ceil(ctx_b/16) / pages_per_split)) and
+ *       M = C * max(1, ceil(ceil(max_ctx/16) / pages_per_split)); the rest
+ *       holds fp32 split partials.
+ * Limits: D in {64, 128}; 1 <= K <= 64; Hq % Hkv == 0; (Hq/Hkv)*K <= 256.
+ */
+int hspec_block_attn_inplace(void* stream, int dtype, int C, int K, int Hq, int Hkv, int D,
+                             const void* q, const void* k_blk, const void* v_blk,
+                             const void* k_cache, const void* v_cache,
+                             int64_t page_stride, int64_t token_stride, int64_t head_stride,
+                             int num_pages, const int32_t* page_table, int max_pages,
+                             const int32_t* ctx_lens, int max_ctx,
+                             int kv_split_pages, float scale, void* out,
+                             void* workspace, size_t* workspace_bytes);
+
+/*
+ * a5 -- the whole drafter layer: a1 -> a2 (Mamba half) and a0 -> a3 -> a4
+ * (attention half) on one stream, with the arguments of the calls above.
+ * H-Spec, Abstract: the two kinds of target context (last-token hidden
+ * state, in-place target KV) enter through the two complementary modules.
+ * `h0` is written by a1 and read by a2; `h_final` and `Dskip` may be NULL.
+ * `workspace` == NULL is a size query exactly as for a3.
+ */
+typedef struct hspec_layer_args {
+  int dtype;
+  int C, K;
+  /* Mamba half */
+  int d_model, H, P, ng, N, chunk;
+  const void* u; const void* w_init; float* h0;
+  const void* x; const float* delta; const float* A; const void* B; const void* Cm;
+  const float* Dskip; float* y; float* h_final;
+  /* attention half */
+  int Hq, Hkv, D;
+  const void* q; const void* k_blk; const void* v_blk;
+  const void* k_cache; const void* v_cache;
+  int64_t page_stride, token_stride, head_stride;
+  int num_pages; const int32_t* page_table; int max_pages;
+  const int32_t* ctx_lens; int max_ctx;
+  int kv_split_pages; float scale; void* out;
+  void* workspace; size_t workspace_bytes;
+} hspec_layer_args;
+
+/* sizeof(hspec_layer_args) as compiled into the library (binding check). */
+size_t hspec_layer_args_size(void);
+
+/* `required_bytes` receives the workspace size a5 needs (may be NULL when
+ * a->workspace is set). */
+int hspec_draft_layer(void* stream, const hspec_layer_args* a, size_t* required_bytes);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* HSPEC_H */

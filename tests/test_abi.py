@@ -1,0 +1,99 @@
+"""The C ABI on the host (no GPU work): the library loads, exports every entry
+point include/hspec.h declares, and rejects bad arguments with the documented
+status before touching the HIP runtime."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from hybrid_mamba_attention_amd import ops
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hspec.h")
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, -1, -2, -3
+FAKE = 1 << 20   # aligned, never dereferenced on the host (validation fails or size query)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(hspec_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_loads_and_exports_every_declared_symbol():
+    L = ops.lib()
+    names = declared_functions()
+    assert {"hspec_init_state", "hspec_ssd_scan", "hspec_block_attn_inplace",
+            "hspec_draft_layer"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in hspec.h but not exported"
+    assert L.hspec_abi_version() == 1
+    assert L.hspec_layer_args_size() == ctypes.sizeof(ops.LayerArgs)
+    assert L.hspec_status_string(-2) == b"HSPEC_ERR_UNSUPPORTED"
+
+
+def _init(**kw):
+    a = dict(stream=None, dtype=1, C=4, d=4096, S=32768, u=FAKE, w=FAKE, h0=FAKE)
+    a.update(kw)
+    return ops.lib().hspec_init_state(a["stream"], a["dtype"], a["C"], a["d"], a["S"], a["u"], a["w"], a["h0"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=7), INVALID), (dict(C=0), INVALID), (dict(u=None), INVALID),
+    (dict(h0=FAKE + 4), INVALID), (dict(d=100), UNSUPPORTED), (dict(S=100), UNSUPPORTED),
+])
+def test_init_state_validation(kw, code):
+    assert _init(**kw) == code
+
+
+def _ssd(no_y=False, **kw):
+    a = dict(dtype=1, C=2, K=16, H=16, P=64, ng=1, N=32, chunk=16)
+    a.update(kw)
+    # x, delta, A, B, Cm, Dskip, h0, y, h_final
+    ptrs = [FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None if no_y else FAKE, None]
+    return ops.lib().hspec_ssd_scan(None, a["dtype"], a["C"], a["K"], a["H"], a["P"], a["ng"],
+                                    a["N"], a["chunk"], *ptrs)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(K=0), INVALID), (dict(ng=3), INVALID), (dict(no_y=True), INVALID),
+    (dict(chunk=12), UNSUPPORTED), (dict(chunk=128), UNSUPPORTED), (dict(P=256), UNSUPPORTED),
+])
+def test_ssd_validation(kw, code):
+    assert _ssd(**kw) == code
+
+
+def _attn(ws=None, nbytes=0, **kw):
+    a = dict(dtype=1, C=4, K=16, Hq=32, Hkv=8, D=128, ps=16 * 8 * 128, ts=8 * 128, hs=128,
+             num_pages=100, max_pages=64, max_ctx=1000, split=0, scale=0.0)
+    a.update(kw)
+    n = ctypes.c_size_t(nbytes)
+    code = ops.lib().hspec_block_attn_inplace(
+        None, a["dtype"], a["C"], a["K"], a["Hq"], a["Hkv"], a["D"], FAKE, FAKE, FAKE, FAKE, FAKE,
+        a["ps"], a["ts"], a["hs"], a["num_pages"], FAKE, a["max_pages"], FAKE, a["max_ctx"],
+        a["split"], a["scale"], FAKE, ws, ctypes.byref(n))
+    return code, n.value
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Hq=30), INVALID), (dict(ts=100), INVALID), (dict(max_pages=10), INVALID),
+    (dict(scale=-1.0), INVALID), (dict(split=-1), INVALID), (dict(K=0), INVALID),
+    (dict(D=96), UNSUPPORTED), (dict(K=65), UNSUPPORTED), (dict(Hq=64, Hkv=2, K=16), UNSUPPORTED),
+])
+def test_attention_validation(kw, code):
+    assert _attn(**kw)[0] == code
+
+
+def test_attention_workspace_query():
+    code, n = _attn(split=32)
+    assert code == OK
+    C, M = 4, 4 * 2                                  # ceil(ceil(1000/16)/32) = 2 splits max
+    plan = (4 + 2 * C + 2 * M) * 4
+    rows = 4 * 16
+    expect = -(-plan // 256) * 256 + -(-(M * 8 * rows * 128 * 4) // 256) * 256 + -(-(M * 8 * rows * 2 * 4) // 256) * 256
+    assert n == expect
+    code1, n1 = _attn(split=1000)                      # one split per request: no partials
+    assert code1 == OK and n1 == 256
+    # a real (non-NULL) workspace that is too small is refused before any launch
+    assert _attn(ws=FAKE, nbytes=n - 1, split=32)[0] == WORKSPACE

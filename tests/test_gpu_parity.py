@@ -1,0 +1,61 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 oracle on
+the same seeded inputs, for all five drafter-layer workloads.
+
+Workloads 0-2 are compared element by element on every output.  Workloads 3
+and 4 (full size, launch configuration as benchmarked) are compared in full on
+the projection and the scan, and on a seeded sample of requests for the
+attention output, which the oracle computes one request at a time.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from hybrid_mamba_attention_amd import workloads as wl
+
+from helpers import (assert_close, flush, layer_from_inputs, oracle_attn, oracle_h0, oracle_scan,
+                     to_host64)
+
+pytestmark = pytest.mark.gpu
+
+
+def _check_layer(idx, sample_requests=None):
+    w = wl.WORKLOADS[idx]
+    flush(f"[parity] workload {idx} {w.name}: drawing inputs")
+    inp = wl.make_inputs(w)
+    flush(f"[parity] workload {idx}: running the layer on the GPU (max_ctx={inp.max_ctx})")
+    layer = layer_from_inputs(inp)
+    h0 = oracle_h0(inp)
+    assert_close(to_host64(layer.h0), h0, w.dtype, f"w{idx} h0")
+    y, hf = oracle_scan(inp, h0)
+    assert_close(to_host64(layer.y), y, w.dtype, f"w{idx} y")
+    assert_close(to_host64(layer.h_final), hf, w.dtype, f"w{idx} h_final")
+    reqs = sample_requests(inp) if sample_requests else None
+    o = oracle_attn(inp, requests=reqs)
+    got = to_host64(layer.out)
+    if reqs is not None:
+        got, o = got[reqs], o[reqs]
+    assert_close(got, o, w.dtype, f"w{idx} attention out")
+    # the int32 split plan at the head of the workspace, bit for bit
+    plan = layer.plan().cpu().numpy()
+    want = oracle.split_plan(inp.ctx_lens, int(plan[1]), inp.max_ctx)
+    assert np.array_equal(plan, want), "split plan differs from the oracle planner"
+    flush(f"[parity] workload {idx}: ok")
+
+
+@pytest.mark.parametrize("idx", [0, 1, 2])
+def test_workload_parity_full(idx):
+    _check_layer(idx)
+
+
+def _sample(inp):
+    g = np.random.default_rng(7)
+    ctx = inp.ctx_lens
+    picks = {int(np.argmax(ctx)), int(np.argmin(ctx)), 0, len(ctx) - 1}
+    picks |= set(int(i) for i in g.choice(len(ctx), size=2, replace=False))
+    return sorted(picks)
+
+
+@pytest.mark.parametrize("idx", [3, 4])
+def test_workload_parity_full_size_sampled(idx):
+    _check_layer(idx, sample_requests=_sample)
