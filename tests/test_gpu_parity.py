@@ -26,16 +26,18 @@ def _check_layer(idx, sample_requests=None):
     flush(f"[parity] workload {idx}: running the layer on the GPU (max_ctx={inp.max_ctx})")
     layer = layer_from_inputs(inp)
     h0 = oracle_h0(inp)
-    assert_close(to_host64(layer.h0), h0, w.dtype, f"w{idx} h0")
+    res = {"h0": assert_close(to_host64(layer.h0), h0, w.dtype, f"w{idx} h0")}
     y, hf = oracle_scan(inp, h0)
-    assert_close(to_host64(layer.y), y, w.dtype, f"w{idx} y")
-    assert_close(to_host64(layer.h_final), hf, w.dtype, f"w{idx} h_final")
+    res["y"] = assert_close(to_host64(layer.y), y, w.dtype, f"w{idx} y")
+    res["h_final"] = assert_close(to_host64(layer.h_final), hf, w.dtype, f"w{idx} h_final")
     reqs = sample_requests(inp) if sample_requests else None
     o = oracle_attn(inp, requests=reqs)
     got = to_host64(layer.out)
     if reqs is not None:
         got, o = got[reqs], o[reqs]
-    assert_close(got, o, w.dtype, f"w{idx} attention out")
+    res["out"] = assert_close(got, o, w.dtype, f"w{idx} attention out")
+    flush(f"[parity] workload {idx}: " + ", ".join(f"{k} rel-L2 {v[0]:.2e} max-abs {v[1]:.2e}"
+                                                   for k, v in res.items()))
     # the int32 split plan at the head of the workspace, bit for bit
     plan = layer.plan().cpu().numpy()
     want = oracle.split_plan(inp.ctx_lens, int(plan[1]), inp.max_ctx)
