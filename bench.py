@@ -1,0 +1,279 @@
+"""Benchmark of the H-Spec drafter layer on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload 3] [--no-sweep] [--no-cpu]
+
+One step is one call of the whole layer (hspec_draft_layer: split plan,
+W_init projection, SSD scan, in-place paged block attention and split merge)
+over one batch of synthetic inputs already resident in HBM.  The default
+workload is the concurrency-128 case (8192-token contexts, Llama-3-8B-shaped
+attention, 4.3 GB of target KV read in place per call).  Each timed step is
+preceded by a 2 GiB write that evicts L2 and the 256 MiB Infinity Cache, so no
+step reads W_init or KV from a previous step's cache; the events bracket only
+the layer call.
+
+Printed: one JSON line with the metric (drafted block-tokens/s per drafter
+layer), the per-kernel breakdown, the roofline of the dominant kernel (the
+in-place KV attention), a concurrency sweep C = 1..128 at the same shapes, and
+the CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor peak
+BF16_DENSE_TFLOPS = 2500.0     # MI355X dense bf16 matrix peak
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", type=int, default=3)
+    p.add_argument("--kv-split-pages", type=int, default=0)
+    p.add_argument("--no-sweep", action="store_true")
+    p.add_argument("--no-cpu", action="store_true")
+    p.add_argument("--no-flush", action="store_true")
+    p.add_argument("--sweep", default="1,2,4,8,16,32,64,128")
+    return p.parse_args()
+
+
+# ----------------------------------------------------------------------------
+# device-side plumbing (torch only for memory, streams and events)
+# ----------------------------------------------------------------------------
+
+def dev(arr, torch):
+    import numpy as np
+    if arr.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(arr)).cuda()
+
+
+def build_layer(inp, kv_split_pages, torch):
+    from hybrid_mamba_attention_amd import ops
+    a = inp.arrays
+    w = inp.w
+    t = {k: dev(v, torch) for k, v in a.items()}
+    return ops.DraftLayer(
+        u=t["u"], w_init=t["w_init"], x=t["x"], delta=t["delta"], A=t["A"], B=t["B"], Cm=t["Cm"],
+        chunk=w.chunk, q=t["q"], k_blk=t["k_blk"], v_blk=t["v_blk"], k_cache=t["k_cache"],
+        v_cache=t["v_cache"], page_table=dev(inp.page_table, torch), ctx_lens=dev(inp.ctx_lens, torch),
+        max_ctx=inp.max_ctx, kv_split_pages=kv_split_pages), t
+
+
+def timed(fn, steps, warmup, flush, torch):
+    """Per-call event times (ms) with the cache flush outside the events."""
+    for _ in range(warmup):
+        flush()
+        fn()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for e0, e1 in evs:
+        flush()
+        e0.record()
+        fn()
+        e1.record()
+    torch.cuda.synchronize()
+    return [e0.elapsed_time(e1) for e0, e1 in evs]
+
+
+def stats(ts):
+    import numpy as np
+    a = np.array(ts)
+    return dict(mean=float(a.mean()), median=float(np.median(a)), p10=float(np.percentile(a, 10)),
+                p90=float(np.percentile(a, 90)))
+
+
+def attention_bytes(w, ctx_lens):
+    """Algorithmic bytes of one attention call: the target KV read in place once,
+    plus the block queries, the block's own K/V and the output."""
+    from hybrid_mamba_attention_amd import workloads as wl
+    e = 2 if w.dtype == "bf16" else 4
+    io = (w.C * w.K * w.Hq * w.D * 2 + w.C * w.K * w.Hkv * w.D * 2) * e
+    return wl.kv_bytes(w, ctx_lens) + io
+
+
+def init_bytes(w):
+    e = 2 if w.dtype == "bf16" else 4
+    return w.d_model * w.S * e + w.C * w.d_model * e + w.C * w.S * 4
+
+
+def ssd_bytes(w):
+    e = 2 if w.dtype == "bf16" else 4
+    return (w.C * w.S * 4 + w.C * w.K * w.H * w.P * (e + 4) + 2 * w.C * w.K * w.ng * w.N * e
+            + w.C * w.K * w.H * 4)
+
+
+def measure(w, inp, args, torch, flush, with_parts=True):
+    from hybrid_mamba_attention_amd import ops
+    layer, t = build_layer(inp, args.kv_split_pages, torch)
+    steps = stats(timed(layer, args.steps, args.warmup, flush, torch))
+    res = dict(step=steps)
+    if with_parts:
+        ws = layer.workspace
+        pt, cl = dev(inp.page_table, torch), dev(inp.ctx_lens, torch)
+        out = torch.empty_like(t["q"])
+
+        def attn():
+            ops.block_attn_inplace(t["q"], t["k_blk"], t["v_blk"], t["k_cache"], t["v_cache"], pt, cl,
+                                   max_ctx=inp.max_ctx, kv_split_pages=args.kv_split_pages, out=out,
+                                   workspace=ws)
+        h0 = torch.empty((w.C, w.S), dtype=torch.float32, device="cuda")
+        y = torch.empty((w.C, w.K, w.H, w.P), dtype=torch.float32, device="cuda")
+        res["attention"] = stats(timed(attn, args.steps, args.warmup, flush, torch))
+        res["init_state"] = stats(timed(lambda: ops.init_state(t["u"], t["w_init"], h0), args.steps,
+                                        args.warmup, flush, torch))
+        res["ssd_scan"] = stats(timed(lambda: ops.ssd_scan(t["x"], t["delta"], t["A"], t["B"], t["Cm"],
+                                                           chunk=w.chunk, h0=h0, y=y),
+                                      args.steps, args.warmup, flush, torch))
+        res["plan"] = layer.plan().cpu().numpy()[:4].tolist()
+    del layer, t
+    torch.cuda.empty_cache()
+    return res
+
+
+# ----------------------------------------------------------------------------
+# counters (traffic) from the committed rocprofv3 summary, if still current
+# ----------------------------------------------------------------------------
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in ("attention.hip", "common.h", "kernels.h"):
+        with open(os.path.join(ROOT, "hybrid_mamba_attention_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(workload_name):
+    path = os.path.join(PROFILE_DIR, f"k_block_attn_{workload_name}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("source_hash") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+# ----------------------------------------------------------------------------
+# CPU baseline: the oracle, untuned, on a bounded sample of the same workload
+# ----------------------------------------------------------------------------
+
+def cpu_baseline(w, inp, n_req):
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    reqs = list(range(n_req))
+    a = inp.arrays
+    t0 = time.perf_counter()
+    sub = {k: a[k][reqs] for k in ("u", "x", "delta", "B", "Cm")}
+    h0 = oracle.init_state(oracle.decode(sub["u"], w.dtype), oracle.decode(a["w_init"], w.dtype))
+    oracle.ssd_recurrence(oracle.decode(sub["x"], w.dtype), sub["delta"], a["A"],
+                          oracle.decode(sub["B"], w.dtype), oracle.decode(sub["Cm"], w.dtype),
+                          h0=h0.reshape(n_req, w.H, w.P, w.N))
+    oracle.block_attention(a["q"], a["k_blk"], a["v_blk"], a["k_cache"], a["v_cache"], inp.page_table,
+                           inp.ctx_lens, dtype=w.dtype, requests=reqs)
+    dt = time.perf_counter() - t0
+    return dict(value=n_req * w.K / dt, unit="drafted block-tokens/s", cores=int(cores), kind="oracle",
+                sample=f"{n_req} of {w.C} requests of {w.name} (whole layer: projection incl. the full "
+                       f"W_init decode, scan, attention over their {int(inp.ctx_lens[reqs].sum())} context "
+                       f"tokens); {dt:.1f} s")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the drafter layer shards by request across GPUs with no exchange).", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    from hybrid_mamba_attention_amd import ops, workloads as wl
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    ops.lib()
+    flush_buf = torch.empty(512 * 1024 * 1024, dtype=torch.float32, device="cuda")  # 2 GiB
+
+    def flush():
+        if not args.no_flush:
+            flush_buf.zero_()
+
+    w = wl.WORKLOADS[args.workload]
+    print(f"[bench] drawing inputs for {w.name}", file=sys.stderr, flush=True)
+    inp = wl.make_inputs(w)
+    print("[bench] timing the layer", file=sys.stderr, flush=True)
+    r = measure(w, inp, args, torch, flush)
+    ms = r["step"]["mean"]
+    tokens = w.C * w.K
+    kv_b = wl.kv_bytes(w, inp.ctx_lens)
+    att_b = attention_bytes(w, inp.ctx_lens)
+    att_ms = r["attention"]["mean"]
+    init_ms = r["init_state"]["mean"]
+    achieved = att_b / (att_ms * 1e-3) / 1e9
+    traffic = traffic_from_profile(w.name)
+    kernels = {
+        "attention (plan + k_block_attn + merge)": dict(ms=att_ms, algorithmic_bytes=att_b,
+                                                        gbs=achieved, hbm_frac=achieved / HBM_PEAK_GBS),
+        "init_state (k_init_state)": dict(ms=init_ms, algorithmic_bytes=init_bytes(w),
+                                          gbs=init_bytes(w) / (init_ms * 1e-3) / 1e9,
+                                          hbm_frac=init_bytes(w) / (init_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                          mfma_frac=2.0 * w.C * w.d_model * w.S / (init_ms * 1e-3) / 1e12 / BF16_DENSE_TFLOPS),
+        "ssd_scan (k_ssd_scan)": dict(ms=r["ssd_scan"]["mean"], algorithmic_bytes=ssd_bytes(w),
+                                      gbs=ssd_bytes(w) / (r["ssd_scan"]["mean"] * 1e-3) / 1e9),
+    }
+    line = {
+        "metric": "drafted block-tokens/sec per drafter layer",
+        "value": tokens / (ms * 1e-3),
+        "unit": "block-tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic (seeded; shapes and distributions of the workload)",
+        "config": {"workload": w.name, "C": w.C, "K": w.K, "ctx": list(w.ctx), "Hq": w.Hq, "Hkv": w.Hkv,
+                   "D": w.D, "d_model": w.d_model, "mamba_H_P_N_chunk": [w.H, w.P, w.N, w.chunk],
+                   "kv_bytes_in_place": kv_b, "w_init_bytes": wl.w_init_bytes(w),
+                   "kv_split_pages": r["plan"][1], "work_items": r["plan"][0],
+                   "cache_flush_between_steps": not args.no_flush},
+        "step_ms": r["step"],
+        "kernels": kernels,
+        "kv_read_gbs": kv_b / (att_ms * 1e-3) / 1e9,
+        "kv_read_frac_of_peak": kv_b / (att_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": "k_block_attn (with its split-plan launch)"},
+    }
+    if not args.no_sweep:
+        sweep = {}
+        for C in [int(c) for c in args.sweep.split(",")]:
+            ws = wl.sweep_workload(C) if C != w.C or args.workload != 3 else w
+            print(f"[bench] sweep C={C}", file=sys.stderr, flush=True)
+            si = inp if ws is w else wl.make_inputs(ws)
+            sr = r if ws is w else measure(ws, si, args, torch, flush, with_parts=True)
+            sms = sr["step"]["mean"]
+            akv = wl.kv_bytes(ws, si.ctx_lens)
+            sweep[str(C)] = dict(block_tokens_per_s=ws.C * ws.K / (sms * 1e-3), ms_per_step=sms,
+                                 attention_ms=sr["attention"]["mean"], init_ms=sr["init_state"]["mean"],
+                                 kv_read_gbs=akv / (sr["attention"]["mean"] * 1e-3) / 1e9,
+                                 kv_read_frac=akv / (sr["attention"]["mean"] * 1e-3) / 1e9 / HBM_PEAK_GBS)
+            if si is not inp:
+                del si
+        line["sweep_ctx8192"] = sweep
+    if not args.no_cpu:
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(w, inp, n_req=min(w.C, 64))
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

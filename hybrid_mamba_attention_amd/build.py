@@ -16,6 +16,14 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libhspec.so")
 SOURCES = ["api.hip", "attention.hip", "ssd.hip", "init_state.hip"]
 ARCH = "gfx950"
+# Per-file code generation flags.  attention.hip: matrix-core results stay in
+# ordinary VGPRs (its accumulators are rescaled by VALU every few stages, and
+# AGPR-resident accumulators would be copied out and back each time), and no
+# NaN semantics are honoured -- NaN-poisoned cache slots are never fed to
+# arithmetic (they are masked by selects or zero-filled first).
+FILE_FLAGS = {
+    "attention.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
 
 
 def hipcc() -> str:
@@ -25,24 +33,37 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def command(out: str = LIB, extra=()) -> list:
-    return [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-            "-Wall", "-Wno-unused-result",
-            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-            *extra, "-o", out, *[os.path.join(CSRC, s) for s in SOURCES]]
+COMMON = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-result",
+          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
-    cmd = command(tmp)
+def compile_command(src: str, obj: str, extra=()) -> list:
+    return [hipcc(), *COMMON, *FILE_FLAGS.get(src, []), *extra, "-c", os.path.join(CSRC, src), "-o", obj]
+
+
+def link_command(objs, out: str) -> list:
+    return [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", out, *objs]
+
+
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
-        raise RuntimeError(f"hipcc failed with exit code {r.returncode}")
-    if verbose and (r.stdout or r.stderr):
-        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError(f"hipcc failed with exit code {r.returncode}: {' '.join(cmd)}")
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source (in parallel) and link libhspec.so in-tree."""
+    from concurrent.futures import ThreadPoolExecutor
+    objdir = os.path.join(HERE, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    objs = [os.path.join(objdir, s.replace(".hip", ".o")) for s in SOURCES]
+    with ThreadPoolExecutor(len(SOURCES)) as ex:
+        list(ex.map(lambda so: _run(compile_command(so[0], so[1]), verbose), zip(SOURCES, objs)))
+    tmp = LIB + ".tmp"
+    _run(link_command(objs, tmp), verbose)
     os.replace(tmp, LIB)
     return LIB
 

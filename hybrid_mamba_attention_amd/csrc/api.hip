@@ -59,11 +59,14 @@ int auto_pages_per_split(int C, int Hkv, int max_ctx) {
   const int max_pages = (max_ctx + 15) / 16;
   if (max_pages <= 0) return 16;
   const int64_t base = int64_t(C) * Hkv;
-  const int64_t target = 2048;  // work items x kv heads wanted over the chip's 256 CUs
+  // Splitting only pays while (request, kv head) pairs alone leave the 256
+  // CUs short of work: every extra split adds an fp32 partial (G*K rows x
+  // (D+2)) written and read back by the merge.
+  const int64_t target = 1024;
+  if (base >= target) return max_pages;
   const int64_t splits = (target + base - 1) / base;
   int64_t pps = (max_pages + splits - 1) / splits;
   if (pps < 16) pps = 16;    // >= 256 tokens per item: partials stay small next to the KV they summarise
-  if (pps > 256) pps = 256;  // <= 4096 tokens per item: ragged contexts stay balanced
   return int((pps + 7) / 8 * 8);
 }
 

@@ -102,21 +102,27 @@ template <> struct VRow<bf16_t, 4> { uint2 v; };
 template <> struct VRow<float, 8> { float v[8]; };
 template <> struct VRow<float, 4> { float v[4]; };
 
-// Element cc of row r as raw 16-bit bf16 (bf16 only).
-__device__ __forceinline__ uint32_t vbits(const VRow<bf16_t, 8>& r, int cc) {
-  return half_of(dword_of(r.v, cc >> 1), cc & 1);
+// V^T operand for output column group cc: element e = V[token e][cc].  For
+// bf16 each dword pairs the same column of two tokens: one v_perm_b32.
+__device__ __forceinline__ uint32_t pair_lo(uint32_t a, uint32_t b) {  // a.lo | b.lo << 16
+  return __builtin_amdgcn_perm(b, a, 0x05040100u);
 }
-__device__ __forceinline__ uint32_t vbits(const VRow<bf16_t, 4>& r, int cc) {
-  return half_of((cc >> 1) ? r.v.y : r.v.x, cc & 1);
+__device__ __forceinline__ uint32_t pair_hi(uint32_t a, uint32_t b) {  // a.hi | b.hi << 16
+  return __builtin_amdgcn_perm(b, a, 0x07060302u);
 }
-
-// V^T operand for output column group cc: element e = V[token e][cc].
 template <int DPL>
 __device__ __forceinline__ void vtrans(Vec8<bf16_t>& o, const VRow<bf16_t, DPL> (&v)[8], int cc) {
-  o.v.x = vbits(v[0], cc) | (vbits(v[1], cc) << 16);
-  o.v.y = vbits(v[2], cc) | (vbits(v[3], cc) << 16);
-  o.v.z = vbits(v[4], cc) | (vbits(v[5], cc) << 16);
-  o.v.w = vbits(v[6], cc) | (vbits(v[7], cc) << 16);
+  auto dw = [&](int e) -> uint32_t {
+    if constexpr (DPL == 8) return dword_of(v[e].v, cc >> 1);
+    else return (cc >> 1) ? v[e].v.y : v[e].v.x;
+  };
+  if (cc & 1) {
+    o.v.x = pair_hi(dw(0), dw(1)); o.v.y = pair_hi(dw(2), dw(3));
+    o.v.z = pair_hi(dw(4), dw(5)); o.v.w = pair_hi(dw(6), dw(7));
+  } else {
+    o.v.x = pair_lo(dw(0), dw(1)); o.v.y = pair_lo(dw(2), dw(3));
+    o.v.z = pair_lo(dw(4), dw(5)); o.v.w = pair_lo(dw(6), dw(7));
+  }
 }
 template <int DPL>
 __device__ __forceinline__ void vtrans(Vec8<float>& o, const VRow<float, DPL> (&v)[8], int cc) {
@@ -136,9 +142,24 @@ __device__ __forceinline__ void pack_p(Vec8<float>& o, const float (&p)[8]) {
   for (int e = 0; e < 8; ++e) o.v[e] = p[e];
 }
 
+// Reductions over the four 16-lane groups of a wave (lanes l, l^16, l^32,
+// l^48 hold the same query row): gfx950 lane-swap instructions, no LDS.
+__device__ __forceinline__ float group4_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
+}
+__device__ __forceinline__ float group4_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+}
+
 template <typename T, int D, int RT> struct Acc {
   f32x4 o[RT][D / 16];
-  float m[RT], l[RT];
+  float m2[RT], l[RT];  // running max in log2 units (score * scale * log2 e), running sum
 };
 
 // Geometry of one 32-token stage in LDS: rows of D elements cut into 16-byte
@@ -149,60 +170,30 @@ template <typename T, int D> struct StageGeom {
   static constexpr int CPR = D / EPC;                 // chunks per row
   static constexpr int SWZ = CPR < 16 ? CPR : 16;
   static constexpr int ROWS = 32;                     // two pages
-  static constexpr int TILE = ROWS * CPR;             // uint4 per tensor per stage
-  __device__ static int pos(int row, int chunk) { return row * CPR + (chunk ^ (row % SWZ)); }
+  static constexpr int TILE = ROWS * CPR;             // 16-byte chunks per tensor per stage
+  __host__ __device__ static constexpr int pos(int row, int chunk) { return row * CPR + (chunk ^ (row % SWZ)); }
 };
 
-template <typename T, int D, int NW> struct AttnLds {
+template <typename T, int D> struct AttnLds {
   using G = StageGeom<T, D>;
   static constexpr size_t bytes = size_t(2) * 2 * G::TILE * 16;  // {K,V} x double buffer
 };
 
-// Read 8 consecutive elements (chunk-aligned start `e0`) of LDS row `row`.
-template <typename T, int D>
-__device__ __forceinline__ void lds_read8(Vec8<T>& out, const uint4* tile, int row, int e0) {
-  using G = StageGeom<T, D>;
-  if constexpr (sizeof(T) == 2) {
-    out.v = tile[G::pos(row, e0 / G::EPC)];
-  } else {
-    const uint4 a = tile[G::pos(row, e0 / G::EPC)];
-    const uint4 b = tile[G::pos(row, e0 / G::EPC + 1)];
-    out.v[0] = __uint_as_float(a.x); out.v[1] = __uint_as_float(a.y);
-    out.v[2] = __uint_as_float(a.z); out.v[3] = __uint_as_float(a.w);
-    out.v[4] = __uint_as_float(b.x); out.v[5] = __uint_as_float(b.y);
-    out.v[6] = __uint_as_float(b.z); out.v[7] = __uint_as_float(b.w);
-  }
-}
+// Rescale threshold (log2 units): the running max is only moved when a new
+// score exceeds it by more than this, so probabilities stay <= 2^8 and the
+// accumulators are rescaled rarely.
+constexpr float kRescaleLog2 = 8.f;
 
-// Read the D/16 elements starting at e0 of LDS row `row` as a V row.
-template <typename T, int D>
-__device__ __forceinline__ void lds_read_v(VRow<T, D / 16>& out, const uint4* tile, int row, int e0) {
-  using G = StageGeom<T, D>;
-  constexpr int DPL = D / 16;
-  if constexpr (sizeof(T) == 2 && DPL == 8) {
-    out.v = tile[G::pos(row, e0 / G::EPC)];
-  } else if constexpr (sizeof(T) == 2) {  // 4 bf16 = half a chunk
-    const uint2* h = reinterpret_cast<const uint2*>(tile + G::pos(row, e0 / G::EPC));
-    out.v = h[(e0 % G::EPC) / 4];
-  } else {
-#pragma unroll
-    for (int c = 0; c < DPL / 4; ++c) {
-      const uint4 a = tile[G::pos(row, e0 / 4 + c)];
-      out.v[4 * c + 0] = __uint_as_float(a.x);
-      out.v[4 * c + 1] = __uint_as_float(a.y);
-      out.v[4 * c + 2] = __uint_as_float(a.z);
-      out.v[4 * c + 3] = __uint_as_float(a.w);
-    }
-  }
-}
-
-template <typename T, int D, int RT, int NW>
+template <typename T, int D, int RT, int NW, int PF>
 __global__ __launch_bounds__(64 * NW) void k_block_attn(AttnArgs a) {
   using Gm = StageGeom<T, D>;
   constexpr int NT = 64 * NW;
-  constexpr int DS = D / 32, DPL = D / 16, EPC = Gm::EPC, CPR = Gm::CPR;
-  constexpr int RPR = NT / CPR;                          // rows one load round covers
-  constexpr int ROUNDS = RPR >= 32 ? 1 : 32 / RPR;
+  constexpr int DS = D / 32, DPL = D / 16, EPC = Gm::EPC, CPR = Gm::CPR, SWZ = Gm::SWZ;
+  constexpr int RPP = (NT / CPR) < 16 ? (NT / CPR) : 16;  // page rows one load round covers
+  constexpr int RND = 16 / RPP;                          // load rounds per page
+  constexpr int NLD = 2 * RND;                           // 16-byte loads per tensor per stage
+  constexpr int TILE_B = Gm::TILE * 16;
+  static_assert(PF % 2 == 0, "even prefetch depth keeps the LDS buffer parity static");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int li = lane & 15, lg = lane >> 4;
 
@@ -220,11 +211,12 @@ __global__ __launch_bounds__(64 * NW) void k_block_attn(AttnArgs a) {
   const int p_lo = split * pps;
   const int ncache = max(0, min(npages, p_lo + pps) - p_lo);
   const int nblk = (split == nsplit - 1) ? (K + 15) >> 4 : 0;
-  const int nstage = (ncache + nblk + 1) >> 1;
+  const int nvp = ncache + nblk;
+  const int nstage = (nvp + 1) >> 1;
 
   extern __shared__ __align__(16) unsigned char smem[];
-  uint4* sK = reinterpret_cast<uint4*>(smem);           // [2][TILE]
-  uint4* sV = sK + 2 * Gm::TILE;                        // [2][TILE]
+  unsigned char* sK = smem;                    // [2][TILE_B]
+  unsigned char* sV = smem + 2 * TILE_B;       // [2][TILE_B]
 
   // this wave's query rows as B operands (row li of tile rt, d group lg + 4*ds)
   const T* __restrict__ q = static_cast<const T*>(a.q);
@@ -246,145 +238,226 @@ __global__ __launch_bounds__(64 * NW) void k_block_attn(AttnArgs a) {
   Acc<T, D, RT> acc;
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
-    acc.m[rt] = -INFINITY;
+    acc.m2[rt] = -INFINITY;
     acc.l[rt] = 0.f;
 #pragma unroll
     for (int cc = 0; cc < DPL; ++cc) acc.o[rt][cc] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   const float c2 = a.scale_log2;
 
-  const T* __restrict__ kc = static_cast<const T*>(a.k_cache);
-  const T* __restrict__ vc = static_cast<const T*>(a.v_cache);
-  const T* __restrict__ kbk = static_cast<const T*>(a.k_blk);
-  const T* __restrict__ vbk = static_cast<const T*>(a.v_blk);
+  // ---- page descriptors (uniform): byte bases of K and V rows of kv head j
+  const int64_t head_off = int64_t(j) * a.head_stride * int64_t(sizeof(T));
+  const char* __restrict__ kcj = static_cast<const char*>(a.k_cache) + head_off;
+  const char* __restrict__ vcj = static_cast<const char*>(a.v_cache) + head_off;
   const int32_t* __restrict__ pt = a.page_table + size_t(b) * a.max_pages;
-  const int64_t head_off = int64_t(j) * a.head_stride;
-  const int64_t blk_ts = int64_t(Hkv) * D;
-
-  // page vp of this work item: context pages first, then the block's own
-  // keys/values (last split only).  Returns element offsets and valid tokens.
-  auto page_desc = [&](int vp, const T*& kb, const T*& vb, int64_t& ts, int& valid) {
-    kb = kc;
-    vb = vc;
-    ts = a.token_stride;
-    valid = 0;
+  const int64_t page_b = a.page_stride * int64_t(sizeof(T));
+  const int last_phys = a.num_pages - 1;
+  const char* kblk = static_cast<const char*>(a.k_blk) + ((size_t(b) * K) * Hkv + j) * D * sizeof(T);
+  const char* vblk = static_cast<const char*>(a.v_blk) + ((size_t(b) * K) * Hkv + j) * D * sizeof(T);
+  const size_t blk_page_b = size_t(16) * Hkv * D * sizeof(T);
+  // Stages [0, nhot) are two full context pages each: the hot path.  The rest
+  // (a partial last page, the block's own keys) take the general path.
+  const int nfull = max(0, min(ctx >> 4, p_lo + pps) - p_lo);
+  const int nhot = nfull >> 1;
+  struct Page {
+    const char* k;
+    const char* v;
+    int n;     // valid tokens (0 = absent)
+    bool blk;  // block page (token stride Hkv*D)
+  };
+  auto page = [&](int vp) __attribute__((always_inline)) -> Page {
+    Page pg{kcj, vcj, 0, false};
     if (vp < ncache) {
-      const int pg = p_lo + vp;
-      const int phys = pt[pg];
-      if (phys >= 0 && phys < a.num_pages) {
-        const int64_t off = int64_t(phys) * a.page_stride + head_off;
-        kb = kc + off;
-        vb = vc + off;
-        valid = min(16, ctx - pg * 16);
+      const int lp = p_lo + vp;
+      const int phys = pt[lp];
+      if (phys >= 0 && phys <= last_phys) {
+        const int64_t off = int64_t(phys) * page_b;
+        pg.k = kcj + off;
+        pg.v = vcj + off;
+        pg.n = min(16, ctx - lp * 16);
       }
-    } else if (vp < ncache + nblk) {
+    } else if (vp < nvp) {
       const int bp = vp - ncache;
-      const size_t off = ((size_t(b) * K + bp * 16) * Hkv + j) * D;
-      kb = kbk + off;
-      vb = vbk + off;
-      ts = blk_ts;
-      valid = min(16, K - bp * 16);
+      pg.k = kblk + bp * blk_page_b;
+      pg.v = vblk + bp * blk_page_b;
+      pg.n = min(16, K - bp * 16);
+      pg.blk = true;
     }
+    return pg;
   };
 
-  // loader role: thread -> (row0 + r*RPR, chunk)
-  const int lchunk = threadIdx.x % CPR;
-  const int lrow0 = threadIdx.x / CPR;
-  uint4 stk[ROUNDS], stv[ROUNDS];
-  auto issue = [&](int st) {
-    const T *kb0, *vb0, *kb1, *vb1;
-    int64_t ts0, ts1;
-    int n0, n1;
-    page_desc(2 * st, kb0, vb0, ts0, n0);
-    page_desc(2 * st + 1, kb1, vb1, ts1, n1);
+  // ---- loader geometry: thread -> (page row trow + q*RPP, 16-byte chunk tchunk)
+  const int tchunk = threadIdx.x % CPR;
+  const int trow = threadIdx.x / CPR;
+  const bool lactive = trow < RPP;
+  const uint32_t ts_b = uint32_t(a.token_stride * int64_t(sizeof(T)));
+  const uint32_t bts_b = uint32_t(Hkv * D * sizeof(T));
+  uint32_t coff[RND], wpos[NLD];
 #pragma unroll
-    for (int r = 0; r < ROUNDS; ++r) {
-      const int row = lrow0 + r * RPR;
-      const int tt = row >> 4, slot = row & 15;
-      const T* kb = tt ? kb1 : kb0;
-      const T* vb = tt ? vb1 : vb0;
-      const int64_t ts = tt ? ts1 : ts0;
-      const int nv = tt ? n1 : n0;
-      if (row < 32 && slot < nv) {
-        const int64_t off = slot * ts + lchunk * EPC;
-        stk[r] = *reinterpret_cast<const uint4*>(kb + off);
-        stv[r] = *reinterpret_cast<const uint4*>(vb + off);
-      } else {
-        stk[r] = make_uint4(0, 0, 0, 0);
-        stv[r] = make_uint4(0, 0, 0, 0);
+  for (int qq = 0; qq < RND; ++qq) {
+    const uint32_t slot = trow + qq * RPP;
+    coff[qq] = slot * ts_b + tchunk * 16;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) wpos[tt * RND + qq] = Gm::pos(tt * 16 + slot, tchunk) * 16;
+  }
+
+  auto issue = [&](int st, uint4 (&stk)[NLD], uint4 (&stv)[NLD], int (&nv)[2]) __attribute__((always_inline)) {
+    if (RPP * CPR == NT && st < nhot) {
+      // two full context pages: scalar page-table reads, unpredicated loads
+      // off scalar page bases (entries clamped into the pool: never a stray read)
+      const int lp = p_lo + 2 * st;
+      const int ph0 = min(max(pt[lp], 0), last_phys);
+      const int ph1 = min(max(pt[lp + 1], 0), last_phys);
+      const char* k0 = kcj + int64_t(ph0) * page_b;
+      const char* v0 = vcj + int64_t(ph0) * page_b;
+      const char* k1 = kcj + int64_t(ph1) * page_b;
+      const char* v1 = vcj + int64_t(ph1) * page_b;
+#pragma unroll
+      for (int qq = 0; qq < RND; ++qq) {
+        stk[qq] = *reinterpret_cast<const uint4*>(k0 + coff[qq]);
+        stv[qq] = *reinterpret_cast<const uint4*>(v0 + coff[qq]);
+        stk[RND + qq] = *reinterpret_cast<const uint4*>(k1 + coff[qq]);
+        stv[RND + qq] = *reinterpret_cast<const uint4*>(v1 + coff[qq]);
+      }
+      nv[0] = 16;
+      nv[1] = 16;
+      return;
+    }
+    const Page p0 = page(2 * st), p1 = page(2 * st + 1);
+    nv[0] = p0.n;
+    nv[1] = p1.n;
+    // (each page spelled out: selecting between the two by reference would
+    // keep the staging registers from being promoted out of memory)
+#pragma unroll
+    for (int qq = 0; qq < RND; ++qq) {
+      const int slot = trow + qq * RPP;
+      const uint32_t off = p0.blk ? uint32_t(slot) * bts_b + tchunk * 16 : coff[qq];
+      uint4 kx = make_uint4(0, 0, 0, 0), vx = make_uint4(0, 0, 0, 0);  // absent tokens: V must be 0, not NaN
+      if (lactive && slot < p0.n) {
+        kx = *reinterpret_cast<const uint4*>(p0.k + off);
+        vx = *reinterpret_cast<const uint4*>(p0.v + off);
+      }
+      stk[qq] = kx;
+      stv[qq] = vx;
+    }
+#pragma unroll
+    for (int qq = 0; qq < RND; ++qq) {
+      const int slot = trow + qq * RPP;
+      const uint32_t off = p1.blk ? uint32_t(slot) * bts_b + tchunk * 16 : coff[qq];
+      uint4 kx = make_uint4(0, 0, 0, 0), vx = make_uint4(0, 0, 0, 0);
+      if (lactive && slot < p1.n) {
+        kx = *reinterpret_cast<const uint4*>(p1.k + off);
+        vx = *reinterpret_cast<const uint4*>(p1.v + off);
+      }
+      stk[RND + qq] = kx;
+      stv[RND + qq] = vx;
+    }
+  };
+  auto commit = [&](int buf, const uint4 (&stk)[NLD], const uint4 (&stv)[NLD]) __attribute__((always_inline)) {
+    if (lactive) {
+#pragma unroll
+      for (int i = 0; i < NLD; ++i) {
+        *reinterpret_cast<uint4*>(sK + buf * TILE_B + wpos[i]) = stk[i];
+        *reinterpret_cast<uint4*>(sV + buf * TILE_B + wpos[i]) = stv[i];
       }
     }
   };
-  auto commit = [&](int buf) {
+
+  // ---- consumer geometry (compile-time buffer offsets added per stage)
+  uint32_t kpos[DS][8 / EPC];   // row li (page 0), d group lg + 4*ds
 #pragma unroll
-    for (int r = 0; r < ROUNDS; ++r) {
-      const int row = lrow0 + r * RPR;
-      if (row < 32) {
-        sK[buf * Gm::TILE + Gm::pos(row, lchunk)] = stk[r];
-        sV[buf * Gm::TILE + Gm::pos(row, lchunk)] = stv[r];
-      }
+  for (int ds = 0; ds < DS; ++ds)
+#pragma unroll
+    for (int h = 0; h < 8 / EPC; ++h) kpos[ds][h] = Gm::pos(li, (lg + 4 * ds) * 8 / EPC + h) * 16;
+  // V rows: token 4*lg + e of page 0 (page 1 is +16 rows), elements li*DPL ..
+  uint32_t vpos[4][DPL * sizeof(T) > 16 ? 2 : 1];
+  constexpr int VCH = DPL * sizeof(T) > 16 ? 2 : 1;
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+#pragma unroll
+    for (int h = 0; h < VCH; ++h) {
+      const int row = 4 * lg + e;
+      const int e0 = li * DPL + h * EPC;  // first element of this chunk piece
+      vpos[e][h] = Gm::pos(row, e0 / EPC) * 16 + (e0 % EPC) * sizeof(T);
     }
-  };
 
-  if (nstage > 0) issue(0);
-  for (int st = 0; st < nstage; ++st) {
-    const int buf = st & 1;
-    commit(buf);
-    int valid[2];
-    {
-      const T *x0, *x1;
-      int64_t y;
-      page_desc(2 * st, x0, x1, y, valid[0]);
-      page_desc(2 * st + 1, x0, x1, y, valid[1]);
-    }
-    if (st + 1 < nstage) issue(st + 1);
-    __syncthreads();
-
-    const uint4* tk = sK + buf * Gm::TILE;
-    const uint4* tv = sV + buf * Gm::TILE;
-    // S^T = K . Q^T: A operand = token li of page tt, d group lg + 4*ds
+  auto compute = [&](int buf, const int (&nv)[2]) __attribute__((always_inline)) {
+    const unsigned char* tk = sK + buf * TILE_B;
+    const unsigned char* tv = sV + buf * TILE_B;
+    const bool partial = nv[0] < 16 || nv[1] < 16;
     Vec8<T> kop[2][DS];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-      for (int ds = 0; ds < DS; ++ds) lds_read8<T, D>(kop[tt][ds], tk, tt * 16 + li, (lg + 4 * ds) * 8);
+      for (int ds = 0; ds < DS; ++ds) {
+        if constexpr (sizeof(T) == 2) {
+          kop[tt][ds].v = *reinterpret_cast<const uint4*>(tk + tt * 16 * CPR * 16 + kpos[ds][0]);
+        } else {
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const uint4 x = *reinterpret_cast<const uint4*>(tk + tt * 16 * CPR * 16 + kpos[ds][h]);
+            kop[tt][ds].v[4 * h + 0] = __uint_as_float(x.x);
+            kop[tt][ds].v[4 * h + 1] = __uint_as_float(x.y);
+            kop[tt][ds].v[4 * h + 2] = __uint_as_float(x.z);
+            kop[tt][ds].v[4 * h + 3] = __uint_as_float(x.w);
+          }
+        }
+      }
     float p[RT][8];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-      f32x4 s[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+      f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
       for (int ds = 0; ds < DS; ++ds)
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt) s[tt] = mma8(kop[tt][ds], qv[rt][ds], s[tt]);
+        for (int tt = 0; tt < 2; ++tt) sacc[tt] = mma8(kop[tt][ds], qv[rt][ds], sacc[tt]);
       float sv[8];
-      float mx = -INFINITY;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int tt = e >> 2, r = e & 3;
-        sv[e] = (4 * lg + r < valid[tt]) ? s[tt][r] : -INFINITY;
-        mx = fmaxf(mx, sv[e]);
+      for (int e = 0; e < 8; ++e) sv[e] = sacc[e >> 2][e & 3];
+      if (partial) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (4 * lg + (e & 3) >= nv[e >> 2]) sv[e] = -INFINITY;
       }
-      mx = wave_xor_max(mx, 16);
-      mx = wave_xor_max(mx, 32);
-      const float mnew = fmaxf(acc.m[rt], mx);
-      const float mu = (mnew == -INFINITY) ? 0.f : mnew;
-      const float alpha = fast_exp2((acc.m[rt] - mu) * c2);
-      const float nb = -mu * c2;
-      float ls = 0.f;
+      const float mx = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), sv[2]),
+                             fmaxf(fmaxf(sv[3], sv[4]), fmaxf(fmaxf(sv[5], sv[6]), sv[7])));
+      const float mx2 = group4_max(mx) * c2;
+      const bool need = mx2 > acc.m2[rt] + kRescaleLog2;
+      if (__any(need)) {
+        if (need) {
+          const float alpha = fast_exp2(acc.m2[rt] - mx2);
+          acc.l[rt] *= alpha;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        p[rt][e] = fast_exp2(fmaf(sv[e], c2, nb));
-        ls += p[rt][e];
+          for (int cc = 0; cc < DPL; ++cc) acc.o[rt][cc] *= alpha;
+          acc.m2[rt] = mx2;
+        }
       }
-      acc.l[rt] = acc.l[rt] * alpha + ls;
-      acc.m[rt] = mnew;
+      const float nb = acc.m2[rt] == -INFINITY ? 0.f : -acc.m2[rt];
 #pragma unroll
-      for (int cc = 0; cc < DPL; ++cc) acc.o[rt][cc] *= alpha;
+      for (int e = 0; e < 8; ++e) p[rt][e] = fast_exp2(fmaf(sv[e], c2, nb));
+      acc.l[rt] += ((p[rt][0] + p[rt][1]) + (p[rt][2] + p[rt][3])) +
+                   ((p[rt][4] + p[rt][5]) + (p[rt][6] + p[rt][7]));
     }
     // O^T += V^T . P^T: lane reads 8 token rows x D/16 values, transposes in registers
     VRow<T, DPL> vr[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) lds_read_v<T, D>(vr[e], tv, (e >> 2) * 16 + 4 * lg + (e & 3), li * DPL);
+    for (int e = 0; e < 8; ++e) {
+      const unsigned char* base = tv + (e >> 2) * 16 * CPR * 16;
+      if constexpr (sizeof(T) == 2 && DPL == 8) {
+        vr[e].v = *reinterpret_cast<const uint4*>(base + vpos[e & 3][0]);
+      } else if constexpr (sizeof(T) == 2) {
+        vr[e].v = *reinterpret_cast<const uint2*>(base + vpos[e & 3][0]);
+      } else {
+#pragma unroll
+        for (int h = 0; h < DPL / 4; ++h) {
+          const uint4 x = *reinterpret_cast<const uint4*>(base + vpos[e & 3][h]);
+          vr[e].v[4 * h + 0] = __uint_as_float(x.x);
+          vr[e].v[4 * h + 1] = __uint_as_float(x.y);
+          vr[e].v[4 * h + 2] = __uint_as_float(x.z);
+          vr[e].v[4 * h + 3] = __uint_as_float(x.w);
+        }
+      }
+    }
     Vec8<T> vt[DPL];
 #pragma unroll
     for (int cc = 0; cc < DPL; ++cc) vtrans<DPL>(vt[cc], vr, cc);
@@ -395,13 +468,36 @@ __global__ __launch_bounds__(64 * NW) void k_block_attn(AttnArgs a) {
 #pragma unroll
       for (int cc = 0; cc < DPL; ++cc) acc.o[rt][cc] = mma8(vt[cc], pv, acc.o[rt][cc]);
     }
+  };
+
+  // Software pipeline: PF stages of loads in flight in registers, two LDS
+  // buffers.  Stage st goes to LDS buffer st&1 (last read by stage st-2, which
+  // every wave finished before the previous barrier); stage st+PF is then
+  // issued into the registers just freed; one barrier; then the math.
+  uint4 stk[PF][NLD], stv[PF][NLD];
+  int nv[PF][2];
+#pragma unroll
+  for (int pp = 0; pp < PF; ++pp)
+    if (pp < nstage) issue(pp, stk[pp], stv[pp], nv[pp]);
+  for (int st0 = 0; st0 < nstage; st0 += PF) {
+#pragma unroll
+    for (int pp = 0; pp < PF; ++pp) {
+      const int st = st0 + pp;
+      if (st < nstage) {  // uniform over the workgroup
+        commit(pp & 1, stk[pp], stv[pp]);
+        const int n0 = nv[pp][0], n1 = nv[pp][1];
+        if (st + PF < nstage) issue(st + PF, stk[pp], stv[pp], nv[pp]);
+        __syncthreads();
+        const int nn[2] = {n0, n1};
+        compute(pp & 1, nn);
+      }
+    }
   }
 
   // store: lane holds row li of each tile and d = (4*lg + r)*DPL + cc
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
-    float lsum = wave_xor_sum(acc.l[rt], 16);
-    lsum = wave_xor_sum(lsum, 32);
+    const float lsum = group4_sum(acc.l[rt]);
     const int row = (wave * RT + rt) * 16 + li;
     if (row >= rows) continue;
     if (nsplit == 1) {
@@ -444,13 +540,15 @@ __global__ __launch_bounds__(64 * NW) void k_block_attn(AttnArgs a) {
           *reinterpret_cast<float4*>(dst + cc) =
               make_float4(acc.o[rt][cc][r], acc.o[rt][cc + 1][r], acc.o[rt][cc + 2][r], acc.o[rt][cc + 3][r]);
       }
-      if (lg == 0) *reinterpret_cast<float2*>(a.part_ml + prow * 2) = make_float2(acc.m[rt], lsum);
+      if (lg == 0) *reinterpret_cast<float2*>(a.part_ml + prow * 2) = make_float2(acc.m2[rt], lsum);
     }
   }
 }
 
 // ---------------------------------------------------------------------------
-// a4: merge of split partials (requests with more than one split only)
+// a4: merge of split partials (requests with more than one split only).
+// One thread per (row, 4 output columns); a single pass over the splits with
+// a running maximum, all in log2 units like the partials.
 // ---------------------------------------------------------------------------
 template <typename T, int D>
 __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
@@ -460,51 +558,55 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
   const int C = a.C;
   const int ns = plan[4 + b];
   if (ns <= 1) return;
-  const int first = plan[4 + C + b];
   const int rows = a.rows, G = a.G, K = a.K;
-  const float c2 = a.scale_log2;
-  for (int idx = threadIdx.x; idx < rows * (D / 4); idx += 256) {
-    const int row = idx / (D / 4), d4 = idx % (D / 4);
-    float M = -INFINITY;
-    for (int s = 0; s < ns; ++s)
-      M = fmaxf(M, a.part_ml[((size_t(first + s) * Hkv + j) * rows + row) * 2]);
-    const float mu = (M == -INFINITY) ? 0.f : M;
-    float4 accv = make_float4(0, 0, 0, 0);
-    float Ls = 0.f;
-    for (int s = 0; s < ns; ++s) {
-      const size_t prow = (size_t(first + s) * Hkv + j) * rows + row;
-      const float2 ml = *reinterpret_cast<const float2*>(a.part_ml + prow * 2);
-      const float f = fast_exp2((ml.x - mu) * c2);
-      const float4 v = reinterpret_cast<const float4*>(a.part_o + prow * D)[d4];
-      accv.x += f * v.x;
-      accv.y += f * v.y;
-      accv.z += f * v.z;
-      accv.w += f * v.w;
-      Ls += f * ml.y;
+  const int idx = blockIdx.y * 256 + threadIdx.x;
+  if (idx >= rows * (D / 4)) return;
+  const int row = idx / (D / 4), d4 = idx % (D / 4);
+  const int first = plan[4 + C + b];
+  float M = -INFINITY, Ls = 0.f;
+  float4 acc = make_float4(0, 0, 0, 0);
+#pragma unroll 4
+  for (int s = 0; s < ns; ++s) {
+    const size_t prow = (size_t(first + s) * Hkv + j) * rows + row;
+    const float2 ml = *reinterpret_cast<const float2*>(a.part_ml + prow * 2);
+    const float4 v = reinterpret_cast<const float4*>(a.part_o + prow * D)[d4];
+    if (ml.x > M) {
+      const float f = fast_exp2(M - ml.x);  // M = -inf gives 0
+      acc.x *= f; acc.y *= f; acc.z *= f; acc.w *= f;
+      Ls *= f;
+      M = ml.x;
     }
-    const float inv = 1.f / Ls;
-    const int t = row / G, gg = row % G;
-    T* o = static_cast<T*>(a.out) + ((size_t(b) * K + t) * a.Hq + j * G + gg) * D + d4 * 4;
-    if constexpr (sizeof(T) == 2) {
-      uint2 w;
-      w.x = pack_bf16x2(accv.x * inv, accv.y * inv);
-      w.y = pack_bf16x2(accv.z * inv, accv.w * inv);
-      *reinterpret_cast<uint2*>(o) = w;
-    } else {
-      *reinterpret_cast<float4*>(o) = make_float4(accv.x * inv, accv.y * inv, accv.z * inv, accv.w * inv);
-    }
+    const float f = ml.x == -INFINITY ? 0.f : fast_exp2(ml.x - M);
+    acc.x += f * v.x; acc.y += f * v.y; acc.z += f * v.z; acc.w += f * v.w;
+    Ls += f * ml.y;
+  }
+  const float inv = 1.f / Ls;
+  const int t = row / G, gg = row % G;
+  T* o = static_cast<T*>(a.out) + ((size_t(b) * K + t) * a.Hq + j * G + gg) * D + d4 * 4;
+  if constexpr (sizeof(T) == 2) {
+    uint2 w;
+    w.x = pack_bf16x2(acc.x * inv, acc.y * inv);
+    w.y = pack_bf16x2(acc.z * inv, acc.w * inv);
+    *reinterpret_cast<uint2*>(o) = w;
+  } else {
+    *reinterpret_cast<float4*>(o) = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
   }
 }
 
 // ---------------------------------------------------------------------------
 // host launcher
 // ---------------------------------------------------------------------------
+#ifndef HSPEC_ATTN_PREFETCH
+#define HSPEC_ATTN_PREFETCH 4
+#endif
+constexpr int kPrefetch = HSPEC_ATTN_PREFETCH;  // stages of K/V loads in flight per workgroup
+
 // (RT row tiles per wave, NW waves) for a query-row count: every wave reads the
 // whole stage from LDS, so fewer, wider waves cut LDS traffic per HBM byte.
 template <typename T, int D, int RT, int NW>
 static hipError_t launch_attn_cfg(hipStream_t st, const AttnArgs& a) {
-  const size_t lds = AttnLds<T, D, NW>::bytes;
-  auto kern = k_block_attn<T, D, RT, NW>;
+  const size_t lds = AttnLds<T, D>::bytes;
+  auto kern = k_block_attn<T, D, RT, NW, kPrefetch>;
   hipLaunchKernelGGL(kern, dim3(a.max_items * a.Hkv), dim3(64 * NW), lds, st, a);
   return hipGetLastError();
 }
@@ -521,8 +623,8 @@ static hipError_t launch_attn_d(hipStream_t st, const AttnArgs& a) {
 size_t attn_lds_bytes(int dtype, int D, int rows, int K) {
   (void)rows;
   (void)K;
-  if (dtype == 1) return D == 64 ? AttnLds<bf16_t, 64, 4>::bytes : AttnLds<bf16_t, 128, 4>::bytes;
-  return D == 64 ? AttnLds<float, 64, 4>::bytes : AttnLds<float, 128, 4>::bytes;
+  if (dtype == 1) return D == 64 ? AttnLds<bf16_t, 64>::bytes : AttnLds<bf16_t, 128>::bytes;
+  return D == 64 ? AttnLds<float, 64>::bytes : AttnLds<float, 128>::bytes;
 }
 
 hipError_t launch_block_attn(hipStream_t st, int dtype, const AttnArgs& a, int pps) {
@@ -537,12 +639,13 @@ hipError_t launch_block_attn(hipStream_t st, int dtype, const AttnArgs& a, int p
   }
   if (e != hipSuccess) return e;
   if (a.max_items > a.C) {  // some request may have several splits
+    const dim3 mg(a.C * a.Hkv, (a.rows * (a.D / 4) + 255) / 256);
     if (dtype == 1) {
-      if (a.D == 64) hipLaunchKernelGGL((k_attn_merge<bf16_t, 64>), dim3(a.C * a.Hkv), dim3(256), 0, st, a);
-      else hipLaunchKernelGGL((k_attn_merge<bf16_t, 128>), dim3(a.C * a.Hkv), dim3(256), 0, st, a);
+      if (a.D == 64) hipLaunchKernelGGL((k_attn_merge<bf16_t, 64>), mg, dim3(256), 0, st, a);
+      else hipLaunchKernelGGL((k_attn_merge<bf16_t, 128>), mg, dim3(256), 0, st, a);
     } else {
-      if (a.D == 64) hipLaunchKernelGGL((k_attn_merge<float, 64>), dim3(a.C * a.Hkv), dim3(256), 0, st, a);
-      else hipLaunchKernelGGL((k_attn_merge<float, 128>), dim3(a.C * a.Hkv), dim3(256), 0, st, a);
+      if (a.D == 64) hipLaunchKernelGGL((k_attn_merge<float, 64>), mg, dim3(256), 0, st, a);
+      else hipLaunchKernelGGL((k_attn_merge<float, 128>), mg, dim3(256), 0, st, a);
     }
     e = hipGetLastError();
   }
