@@ -7,9 +7,12 @@ W_init projection, SSD scan, in-place paged block attention and split merge)
 over one batch of synthetic inputs already resident in HBM.  The default
 workload is the concurrency-128 case (8192-token contexts, Llama-3-8B-shaped
 attention, 4.3 GB of target KV read in place per call).  Each timed step is
-preceded by a 2 GiB write that evicts L2 and the 256 MiB Infinity Cache, so no
-step reads W_init or KV from a previous step's cache; the events bracket only
-the layer call.
+preceded by a 2 GiB streaming read that evicts L2 and the 256 MiB Infinity
+Cache, so no step reads W_init or KV from a previous step's cache; the events
+bracket only the layer call.  (The flush reads rather than writes: a write
+flush would leave the Infinity Cache full of dirty lines whose write-back then
+competes with the timed kernel's reads -- measured on this chip, it halves the
+read bandwidth of a 256 MiB stream.)
 
 Printed: one JSON line with the metric (drafted block-tokens/s per drafter
 layer), the per-kernel breakdown, the roofline of the dominant kernel (the
@@ -204,11 +207,12 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     ops.lib()
-    flush_buf = torch.empty(512 * 1024 * 1024, dtype=torch.float32, device="cuda")  # 2 GiB
+    flush_buf = torch.ones(512 * 1024 * 1024, dtype=torch.float32, device="cuda")  # 2 GiB
+    flush_out = torch.empty((), dtype=torch.float32, device="cuda")
 
     def flush():
         if not args.no_flush:
-            flush_buf.zero_()
+            torch.sum(flush_buf, dim=0, out=flush_out)
 
     w = wl.WORKLOADS[args.workload]
     print(f"[bench] drawing inputs for {w.name}", file=sys.stderr, flush=True)
