@@ -58,7 +58,7 @@ def _ssd(no_y=False, **kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(K=0), INVALID), (dict(ng=3), INVALID), (dict(no_y=True), INVALID),
-    (dict(chunk=12), UNSUPPORTED), (dict(chunk=128), UNSUPPORTED), (dict(P=256), UNSUPPORTED),
+    (dict(chunk=12), UNSUPPORTED), (dict(chunk=32), UNSUPPORTED), (dict(P=256), UNSUPPORTED),
 ])
 def test_ssd_validation(kw, code):
     assert _ssd(**kw) == code

@@ -1,0 +1,240 @@
+"""GPU edge cases and invariants of each entry point, against the oracle.
+
+Attention: ragged / empty / sub-page contexts, block lengths that are not a
+multiple of 16, GQA group sizes 1..8, D = 64 and 128, fp32 and bf16, every
+split size; results must not depend on the split size beyond the tolerance,
+must repeat bit for bit for a fixed split size, must be bit-identical when the
+same context sits in a scrambled or an identity page table or in an NHD or
+HND pool, and the call must leave the KV pools untouched ("no drafter-side KV
+cache": the library reads the target's cache and writes only `out` and its
+workspace).
+Scan: multi-chunk and partial-chunk blocks, B/C groups, the skip term, a zero
+initial state.  Projection: C across the M-tile boundaries.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from hybrid_mamba_attention_amd import ops
+from hybrid_mamba_attention_amd import workloads as wl
+
+from helpers import assert_close, flush, to_dev, to_host64
+
+pytestmark = pytest.mark.gpu
+PAGE = 16
+
+
+# ----------------------------------------------------------------------------
+# attention
+# ----------------------------------------------------------------------------
+
+def make_attn_case(seed, ctx, K, Hq, Hkv, D, dtype, *, identity=False, q_scale=1.0, spare=7):
+    """Logical context per request, scattered into a NaN-poisoned paged pool."""
+    g = np.random.default_rng(seed)
+    bf = dtype == "bf16"
+    enc = (lambda a: wl.f32_to_bf16_bits(a)) if bf else (lambda a: a.astype(np.float32))
+    nan = wl.BF16_NAN if bf else np.float32("nan")
+    C = len(ctx)
+    n_pages = [-(-c // PAGE) for c in ctx]
+    pool = sum(n_pages) + spare
+    perm = np.arange(pool) if identity else np.random.default_rng(seed + 99).permutation(pool)
+    kc = np.full((pool, PAGE, Hkv, D), nan, dtype=np.uint16 if bf else np.float32)
+    vc = kc.copy()
+    pt = np.full((C, max(1, max(n_pages))), -1, np.int32)
+    off = 0
+    for b, c in enumerate(ctx):
+        kl = enc(g.standard_normal((c, Hkv, D)).astype(np.float32))
+        vl = enc(g.standard_normal((c, Hkv, D)).astype(np.float32))
+        pages = perm[off:off + n_pages[b]]
+        off += n_pages[b]
+        pt[b, :len(pages)] = pages
+        for pi, pg in enumerate(pages):
+            n = min(PAGE, c - pi * PAGE)
+            kc[pg, :n] = kl[pi * PAGE:pi * PAGE + n]
+            vc[pg, :n] = vl[pi * PAGE:pi * PAGE + n]
+    q = enc(q_scale * g.standard_normal((C, K, Hq, D)).astype(np.float32))
+    kb = enc(g.standard_normal((C, K, Hkv, D)).astype(np.float32))
+    vb = enc(g.standard_normal((C, K, Hkv, D)).astype(np.float32))
+    return dict(q=q, k_blk=kb, v_blk=vb, k_cache=kc, v_cache=vc, page_table=pt,
+                ctx_lens=np.array(ctx, np.int32), dtype=dtype)
+
+
+def run_attn(case, *, split=0, layout="NHD", out=None):
+    dt = case["dtype"]
+    t = {k: to_dev(case[k], dt) for k in ("q", "k_blk", "v_blk", "k_cache", "v_cache", "page_table", "ctx_lens")}
+    kc, vc = t["k_cache"], t["v_cache"]
+    if layout == "HND":  # the same pool stored as [pages, Hkv, 16, D]
+        kc = kc.permute(0, 2, 1, 3).contiguous()
+        vc = vc.permute(0, 2, 1, 3).contiguous()
+    max_ctx = int(case["ctx_lens"].max())
+    o, ws = ops.block_attn_inplace(t["q"], t["k_blk"], t["v_blk"], kc, vc, t["page_table"], t["ctx_lens"],
+                                   max_ctx=max_ctx, kv_split_pages=split, out=out, layout=layout)
+    torch.cuda.synchronize()
+    return o, ws, (kc, vc)
+
+
+def oracle_attn(case):
+    return oracle.block_attention(case["q"], case["k_blk"], case["v_blk"], case["k_cache"], case["v_cache"],
+                                  case["page_table"], case["ctx_lens"], dtype=case["dtype"])
+
+
+ATTN_CASES = [
+    # (name, ctx, K, Hq, Hkv, D, dtype)
+    ("bf16-llama-ragged", [0, 1, 15, 16, 17, 300, 1000], 16, 32, 8, 128, "bf16"),
+    ("bf16-d64-k13", [33, 100, 7], 13, 8, 2, 64, "bf16"),
+    ("f32-mha-k4", [50, 0], 4, 4, 4, 128, "f32"),
+    ("f32-d64-k1", [64, 3], 1, 4, 2, 64, "f32"),
+    ("bf16-g8-k32-rows256", [500, 31], 32, 16, 2, 128, "bf16"),
+    ("bf16-k64-g4-rows256", [200], 64, 8, 2, 128, "bf16"),
+    ("bf16-k33-three-block-pages", [37, 16], 33, 4, 2, 128, "bf16"),
+    ("bf16-g8-k16-rows128", [2000, 17], 16, 64, 8, 128, "bf16"),
+    ("f32-rows128", [90], 16, 16, 2, 64, "f32"),
+]
+
+
+@pytest.mark.parametrize("name,ctx,K,Hq,Hkv,D,dtype", ATTN_CASES, ids=[c[0] for c in ATTN_CASES])
+def test_attention_shapes(name, ctx, K, Hq, Hkv, D, dtype):
+    flush(f"[attn] {name}")
+    case = make_attn_case(sum(ctx) + K, ctx, K, Hq, Hkv, D, dtype)
+    want = oracle_attn(case)
+    for split in (0, 1, 3):
+        o, _, _ = run_attn(case, split=split)
+        assert_close(to_host64(o), want, dtype, f"{name} split={split}")
+
+
+def test_split_invariance_and_repeatability():
+    case = make_attn_case(5, [1000, 513, 0, 40], 16, 32, 8, 128, "bf16")
+    want = oracle_attn(case)
+    for split in (1, 2, 3, 7, 0, 10 ** 6):
+        o1, ws, _ = run_attn(case, split=split)
+        o2, _, _ = run_attn(case, split=split)
+        assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)), f"split={split} not repeatable"
+        assert_close(to_host64(o1), want, "bf16", f"split={split}")
+        plan = ws[:4 * 4].view(torch.int32).cpu().numpy()
+        M = int(plan[3])
+        plan = ws[:4 * (4 + 2 * 4 + 2 * M)].view(torch.int32).cpu().numpy()
+        assert np.array_equal(plan, oracle.split_plan(case["ctx_lens"], int(plan[1]), 1000)), split
+
+
+def test_scrambled_page_table_is_bit_identical():
+    a = make_attn_case(11, [700, 65, 16], 16, 32, 8, 128, "bf16")
+    b = make_attn_case(11, [700, 65, 16], 16, 32, 8, 128, "bf16", identity=True)
+    assert not np.array_equal(a["page_table"], b["page_table"])
+    for split in (0, 5):
+        oa, _, _ = run_attn(a, split=split)
+        ob, _, _ = run_attn(b, split=split)
+        assert torch.equal(oa.view(torch.int16), ob.view(torch.int16))
+
+
+def test_hnd_pool_layout_is_bit_identical():
+    case = make_attn_case(12, [300, 45], 16, 8, 2, 128, "bf16")
+    on, _, _ = run_attn(case, layout="NHD")
+    oh, _, (kc, _) = run_attn(case, layout="HND")
+    assert kc.shape[1] == 2 and ops.kv_strides(kc, "HND") == (16 * 2 * 128, 128, 16 * 128)
+    assert torch.equal(on.view(torch.int16), oh.view(torch.int16))
+    assert_close(to_host64(oh), oracle_attn(case), "bf16", "HND")
+
+
+def test_kv_pool_untouched_and_output_bounded():
+    case = make_attn_case(13, [400, 3], 16, 32, 8, 128, "bf16")
+    dt = case["dtype"]
+    q = to_dev(case["q"], dt)
+    canary = torch.full((q.numel() + 4096,), 12345, dtype=torch.int16, device="cuda")
+    out = canary[:q.numel()].view(torch.bfloat16).view(q.shape)
+    t = {k: to_dev(case[k], dt) for k in ("k_blk", "v_blk", "k_cache", "v_cache", "page_table", "ctx_lens")}
+    before = (t["k_cache"].view(torch.int16).clone(), t["v_cache"].view(torch.int16).clone(),
+              t["k_blk"].view(torch.int16).clone(), t["v_blk"].view(torch.int16).clone())
+    ops.block_attn_inplace(q, t["k_blk"], t["v_blk"], t["k_cache"], t["v_cache"], t["page_table"],
+                           t["ctx_lens"], max_ctx=400, out=out)
+    torch.cuda.synchronize()
+    after = (t["k_cache"].view(torch.int16), t["v_cache"].view(torch.int16),
+             t["k_blk"].view(torch.int16), t["v_blk"].view(torch.int16))
+    for x, y in zip(before, after):
+        assert torch.equal(x, y), "an input buffer was written"
+    assert (canary[q.numel():] == 12345).all(), "wrote past the output tensor"
+    assert torch.isfinite(out.float()).all()
+    assert_close(to_host64(out), oracle_attn(case), dt, "canary case")
+
+
+def test_peaked_logits():
+    """Scaled-up queries make the softmax sharp, so errors are not averaged away."""
+    case = make_attn_case(14, [900, 100], 16, 32, 8, 128, "bf16", q_scale=4.0)
+    want = oracle_attn(case)
+    for split in (0, 8):
+        o, _, _ = run_attn(case, split=split)
+        assert_close(to_host64(o), want, "bf16", f"peaked split={split}")
+
+
+# ----------------------------------------------------------------------------
+# SSD scan
+# ----------------------------------------------------------------------------
+
+SSD_CASES = [
+    # (C, K, H, P, ng, N, chunk, dtype, dskip, zero_state)
+    (2, 16, 4, 64, 1, 32, 4, "bf16", False, False),
+    (3, 13, 4, 64, 1, 32, 4, "bf16", True, False),
+    (2, 16, 8, 64, 2, 64, 16, "bf16", False, False),
+    (1, 4, 4, 64, 1, 16, 4, "f32", False, False),
+    (2, 9, 2, 32, 1, 16, 2, "f32", True, True),
+    (2, 16, 2, 128, 1, 64, 8, "f32", False, False),
+    (1, 5, 2, 64, 1, 128, 1, "bf16", False, False),
+    (4, 16, 32, 64, 1, 64, 16, "bf16", True, False),
+]
+
+
+@pytest.mark.parametrize("C,K,H,P,ng,N,chunk,dtype,dskip,zero_state", SSD_CASES)
+def test_ssd_scan(C, K, H, P, ng, N, chunk, dtype, dskip, zero_state):
+    g = np.random.default_rng(C * 1000 + K * 10 + N)
+    bf = dtype == "bf16"
+    enc = (lambda a: wl.f32_to_bf16_bits(a.astype(np.float32))) if bf else (lambda a: a.astype(np.float32))
+    x = enc(g.standard_normal((C, K, H, P)))
+    B = enc(g.standard_normal((C, K, ng, N)))
+    Cm = enc(g.standard_normal((C, K, ng, N)))
+    delta = np.logaddexp(0, g.standard_normal((C, K, H)) - 4.0).astype(np.float32)
+    A = (-np.exp(g.uniform(0, 1, H))).astype(np.float32)
+    h0 = None if zero_state else g.standard_normal((C, H, P, N)).astype(np.float32)
+    D = g.standard_normal(H).astype(np.float32) if dskip else None
+    y, hf = ops.ssd_scan(to_dev(x, dtype), to_dev(delta, dtype), to_dev(A, dtype), to_dev(B, dtype),
+                         to_dev(Cm, dtype), chunk=chunk, h0=None if h0 is None else to_dev(h0, dtype),
+                         Dskip=None if D is None else to_dev(D, dtype), want_final=True)
+    torch.cuda.synchronize()
+    yo, hfo = oracle.ssd_recurrence(oracle.decode(x, dtype), delta, A, oracle.decode(B, dtype),
+                                    oracle.decode(Cm, dtype), h0=h0, Dskip=D)
+    assert_close(to_host64(y), yo, dtype, "y")
+    assert_close(to_host64(hf), hfo, dtype, "h_final")
+
+
+# ----------------------------------------------------------------------------
+# projection
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("C,d,S,dtype", [
+    (1, 256, 4096, "f32"), (5, 512, 8192, "bf16"), (17, 256, 4096, "bf16"), (33, 4096, 2048, "bf16"),
+    (64, 1024, 4096, "bf16"), (65, 256, 4096, "bf16"), (100, 512, 4096, "f32"), (130, 256, 8192, "bf16"),
+    (256, 128, 1024, "bf16"),
+])
+def test_init_state(C, d, S, dtype):
+    g = np.random.default_rng(C + d + S)
+    bf = dtype == "bf16"
+    enc = (lambda a: wl.f32_to_bf16_bits(a.astype(np.float32))) if bf else (lambda a: a.astype(np.float32))
+    u = enc(g.standard_normal((C, d)))
+    w = enc(0.02 * g.standard_normal((d, S)))
+    h0 = ops.init_state(to_dev(u, dtype), to_dev(w, dtype))
+    torch.cuda.synchronize()
+    assert_close(to_host64(h0), oracle.init_state(oracle.decode(u, dtype), oracle.decode(w, dtype)), dtype, "h0")
+
+
+def test_layer_with_skip_term():
+    from dataclasses import replace
+    from helpers import layer_from_inputs, oracle_h0, oracle_scan
+    w = replace(wl.WORKLOADS[1], name="small-layer-dskip", C=3, ctx=("uniform", 0, 200), d_model=512,
+                H=4, N=32, seed=4242)
+    inp = wl.make_inputs(w, with_dskip=True)
+    layer = layer_from_inputs(inp, with_dskip=True)
+    h0 = oracle_h0(inp)
+    y, hf = oracle_scan(inp, h0)
+    assert_close(to_host64(layer.y), y, "bf16", "y with skip")
+    assert_close(to_host64(layer.h_final), hf, "bf16", "h_final with skip")
