@@ -47,6 +47,8 @@ def parse():
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--no-flush", action="store_true")
     p.add_argument("--sweep", default="1,2,4,8,16,32,64,128")
+    p.add_argument("--calib-copy", action="store_true",
+                   help="also launch a plain 1 GiB device copy (counter calibration under rocprofv3)")
     return p.parse_args()
 
 
@@ -214,6 +216,16 @@ def main():
         if not args.no_flush:
             torch.sum(flush_buf, dim=0, out=flush_out)
 
+    if args.calib_copy:
+        # a plain copy of known size: its FETCH_SIZE / WRITE_SIZE per dispatch
+        # calibrate the HBM-traffic counters of the kernels profiled alongside
+        src = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            flush()
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     w = wl.WORKLOADS[args.workload]
     print(f"[bench] drawing inputs for {w.name}", file=sys.stderr, flush=True)
     inp = wl.make_inputs(w)
