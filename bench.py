@@ -172,28 +172,38 @@ def traffic_from_profile(workload_name):
 # CPU baseline: the oracle, untuned, on a bounded sample of the same workload
 # ----------------------------------------------------------------------------
 
-def cpu_baseline(w, inp, n_req):
-    import numpy as np
+def cpu_baseline(w, inp, n_req, min_seconds=10.0, max_seconds=30.0):
+    """The oracle (untuned) on batches of n_req requests of the workload, repeated
+    over successive request batches until at least min_seconds of work."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         cores = os.cpu_count() or 1
-    reqs = list(range(n_req))
     a = inp.arrays
     t0 = time.perf_counter()
-    sub = {k: a[k][reqs] for k in ("u", "x", "delta", "B", "Cm")}
-    h0 = oracle.init_state(oracle.decode(sub["u"], w.dtype), oracle.decode(a["w_init"], w.dtype))
-    oracle.ssd_recurrence(oracle.decode(sub["x"], w.dtype), sub["delta"], a["A"],
-                          oracle.decode(sub["B"], w.dtype), oracle.decode(sub["Cm"], w.dtype),
-                          h0=h0.reshape(n_req, w.H, w.P, w.N))
-    oracle.block_attention(a["q"], a["k_blk"], a["v_blk"], a["k_cache"], a["v_cache"], inp.page_table,
-                           inp.ctx_lens, dtype=w.dtype, requests=reqs)
-    dt = time.perf_counter() - t0
-    return dict(value=n_req * w.K / dt, unit="drafted block-tokens/s", cores=int(cores), kind="oracle",
-                sample=f"{n_req} of {w.C} requests of {w.name} (whole layer: projection incl. the full "
-                       f"W_init decode, scan, attention over their {int(inp.ctx_lens[reqs].sum())} context "
+    done = 0
+    ctx_tokens = 0
+    batch = 0
+    while True:
+        reqs = [(batch * n_req + i) % w.C for i in range(n_req)]
+        sub = {k: a[k][reqs] for k in ("u", "x", "delta", "B", "Cm")}
+        h0 = oracle.init_state(oracle.decode(sub["u"], w.dtype), oracle.decode(a["w_init"], w.dtype))
+        oracle.ssd_recurrence(oracle.decode(sub["x"], w.dtype), sub["delta"], a["A"],
+                              oracle.decode(sub["B"], w.dtype), oracle.decode(sub["Cm"], w.dtype),
+                              h0=h0.reshape(n_req, w.H, w.P, w.N))
+        oracle.block_attention(a["q"], a["k_blk"], a["v_blk"], a["k_cache"], a["v_cache"], inp.page_table,
+                               inp.ctx_lens, dtype=w.dtype, requests=reqs)
+        done += n_req
+        ctx_tokens += int(inp.ctx_lens[reqs].sum())
+        batch += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds or dt * (batch + 1) / batch > max_seconds:
+            break
+    return dict(value=done * w.K / dt, unit="drafted block-tokens/s", cores=int(cores), kind="oracle",
+                sample=f"{batch} batch(es) of {n_req} requests of {w.name} ({done} request-layers: projection "
+                       f"incl. the full W_init decode per batch, scan, attention over {ctx_tokens} context "
                        f"tokens); {dt:.1f} s")
 
 

@@ -611,11 +611,15 @@ static hipError_t launch_attn_cfg(hipStream_t st, const AttnArgs& a) {
   return hipGetLastError();
 }
 
+#ifndef HSPEC_ATTN_RT64
+#define HSPEC_ATTN_RT64 1  // row tiles per wave for 33..64 query rows (waves = 4 / this)
+#endif
+
 template <typename T, int D>
 static hipError_t launch_attn_d(hipStream_t st, const AttnArgs& a) {
   if (a.rows <= 16) return launch_attn_cfg<T, D, 1, 1>(st, a);
   if (a.rows <= 32) return launch_attn_cfg<T, D, 1, 2>(st, a);
-  if (a.rows <= 64) return launch_attn_cfg<T, D, 1, 4>(st, a);
+  if (a.rows <= 64) return launch_attn_cfg<T, D, HSPEC_ATTN_RT64, 4 / HSPEC_ATTN_RT64>(st, a);
   if (a.rows <= 128) return launch_attn_cfg<T, D, 2, 4>(st, a);
   return launch_attn_cfg<T, D, 4, 4>(st, a);
 }
