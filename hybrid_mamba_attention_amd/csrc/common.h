@@ -12,13 +12,29 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace hspec {
+
+// f(std::integral_constant<int, I>{}) for I = B .. E-1: register-array
+// indices derived from I are constants before any loop unrolling, so the
+// arrays always live in registers.
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
 
 struct bf16_t {
   uint16_t bits;
 };
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+// Native 16-byte vector for register rings: arrays of it are split into
+// registers, where arrays of the uint4 struct can end up in scratch.
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
 
 // Eight contraction-adjacent elements held by one lane.
@@ -81,6 +97,16 @@ __device__ __forceinline__ f32x4 mma8(const Vec8<T>& a, const Vec8<T>& b, f32x4 
 template <>
 __device__ __forceinline__ f32x4 mma8<bf16_t>(const Vec8<bf16_t>& a, const Vec8<bf16_t>& b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8v, a.v),
+                                                 __builtin_bit_cast(bf16x8v, b.v), c, 0, 0, 0);
+}
+// 32x32 output tile over 16 contraction indices, bf16 in, fp32 accumulate
+// (v_mfma_f32_32x32x16_bf16): lane l supplies row/column (l % 32) and the
+// eight contraction indices 8*(l/32) .. 8*(l/32)+7; result element i of lane
+// l is column (l % 32), row 8*(i/4) + 4*(l/32) + (i%4).  One wave keeps this
+// instruction at the matrix-core peak with as few as two accumulator chains.
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+__device__ __forceinline__ f32x16 mma32(const Vec8<bf16_t>& a, const Vec8<bf16_t>& b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8v, a.v),
                                                  __builtin_bit_cast(bf16x8v, b.v), c, 0, 0, 0);
 }
 template <>

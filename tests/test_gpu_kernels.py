@@ -212,9 +212,15 @@ def test_ssd_scan(C, K, H, P, ng, N, chunk, dtype, dskip, zero_state):
 # ----------------------------------------------------------------------------
 
 @pytest.mark.parametrize("C,d,S,dtype", [
-    (1, 256, 4096, "f32"), (5, 512, 8192, "bf16"), (17, 256, 4096, "bf16"), (33, 4096, 2048, "bf16"),
-    (64, 1024, 4096, "bf16"), (65, 256, 4096, "bf16"), (100, 512, 4096, "f32"), (130, 256, 8192, "bf16"),
-    (256, 128, 1024, "bf16"),
+    # 128-column kernel (bf16, d % 64 == 0, S % 128 == 0): 32/64/128-row blocks,
+    # several row blocks, column-block counts with and without a multiple of 8,
+    # step counts below, at and above the prefetch depth
+    (1, 256, 4096, "bf16"), (5, 512, 8192, "bf16"), (17, 256, 4096, "bf16"), (33, 4096, 2048, "bf16"),
+    (64, 1024, 4096, "bf16"), (65, 256, 4096, "bf16"), (130, 256, 8192, "bf16"), (256, 128, 1024, "bf16"),
+    (3, 256, 640, "bf16"), (200, 192, 1152, "bf16"), (97, 320, 1024, "bf16"),
+    # general kernel: fp32, or d % 64 == 32, or S % 128 == 64
+    (1, 256, 4096, "f32"), (100, 512, 4096, "f32"), (7, 96, 4096, "bf16"), (40, 256, 4160, "bf16"),
+    (129, 160, 1088, "bf16"),
 ])
 def test_init_state(C, d, S, dtype):
     g = np.random.default_rng(C + d + S)
