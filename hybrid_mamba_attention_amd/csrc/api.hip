@@ -44,7 +44,7 @@ int check_ssd(int dtype, int C, int K, int H, int P, int ng, int N, int chunk, c
   if (H % ng) return HSPEC_ERR_INVALID_ARG;
   if (!x || !delta || !A || !B || !Cm || !y) return HSPEC_ERR_INVALID_ARG;
   if (chunk > 16 || (chunk & (chunk - 1))) return HSPEC_ERR_UNSUPPORTED;
-  if (P > 128 || N > 128 || P * N > 8192) return HSPEC_ERR_UNSUPPORTED;
+  if (P > 128 || N > 128) return HSPEC_ERR_UNSUPPORTED;
   if (ssd_lds_bytes(P, N, chunk) > kMaxLds) return HSPEC_ERR_UNSUPPORTED;
   if (int64_t(C) * H > 0x7fffffff) return HSPEC_ERR_UNSUPPORTED;
   return HSPEC_OK;

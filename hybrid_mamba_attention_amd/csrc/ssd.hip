@@ -10,240 +10,272 @@
 //   H_out   = exp(lam_end) H_in + sum_s exp(lam_end - lam_s) delta_s x_s (outer) B_s
 // with H_in of the first chunk = h0, the projected last-token state.
 //
-// One workgroup per (request, head).  The state lives in registers for the
-// whole block: N/8 waves per 64 state rows, each holding 8 columns of every
-// row, and every thread keeps one accumulator per chunk position for its
-// outputs (no serial reduction chains).  The chunk's B and
-// Cm rows, the decay-weighted C.B^T matrix M and the cumulative log-decays sit
-// in LDS and are read as float4 broadcasts.  The cumulative sum runs across
-// one wave's lanes with shuffles.  Memory traffic per (request, head):
-// h0 in (P*N fp32), x/B/Cm in, y out (and h_final when asked for).
+// The work per (request, head) is a few thousand multiply-adds against
+// P*N*4 bytes of state in and out, so the kernel is laid out for latency:
+// one wave per 64 state rows of a head, each lane holding its whole state
+// row (N values) in registers for the whole block, so every state-row
+// product is a lane-local multiply-add chain fed by LDS broadcasts and no
+// partial sums cross lanes or waves.  A workgroup takes up to 4 heads of one
+// request that share a B/Cm group: the chunk's B and Cm rows and the
+// head-independent Cm.B^T products are staged and formed once per workgroup;
+// each wave then scales them by its own head's decays.  The in-chunk
+// cumulative sum runs across one wave's lanes with shuffles.
 #include "common.h"
 #include "kernels.h"
 
 namespace hspec {
 
-// Workgroup: NWQ = NB/8 waves per 64 state rows (at most 16 waves, since
-// P*N <= 8192).  Wave w (nq = w % NWQ, row block rb = w / NWQ) owns columns
-// [8*nq, 8*nq + 8) of rows rb*64 + lane, so every LDS operand a wave reads is
-// the same address in all its lanes (a broadcast) and per-thread registers
-// stay small for every state size.  The waves' partial outputs meet in LDS.
-template <int NWQ> struct SsdLayout {
-  static constexpr int NB = 8 * NWQ, QB = 16;
-  // dynamic LDS, in floats
-  static constexpr int oB = 0;                       // sB[QB][NB]   B rows by position
-  static constexpr int oCT = oB + QB * NB;           // sCT[NB][QB]  Cm, position-minor
-  static constexpr int oMT = oCT + NB * QB;          // sMT[QB][QB]  M[t][s] at [s][t]
-  static constexpr int oLam = oMT + QB * QB;         // lam[QB], w[QB], dt[QB], pad
-  static constexpr int oX = oLam + 4 * QB;           // sX[RB][QB][64]
-  static size_t floats(int RB) { return size_t(oX) + size_t(RB) * QB * 64 + size_t(RB) * NWQ * QB * 64; }
+constexpr int kSsdQ = 16;  // largest chunk (positions staged per pass)
+
+// Static LDS, in floats.  sB / sC rows are padded to NMAX + 4 so the
+// per-thread Cm.B^T dot products (rows t and s in different lanes) spread
+// over the banks; every other read is a wave-wide broadcast.
+template <int NMAX> struct SsdLds {
+  static constexpr int LDB = NMAX + 4;
+  static constexpr int oB = 0;                        // sB[Q][LDB]   B_s
+  static constexpr int oC = oB + kSsdQ * LDB;         // sC[Q][LDB]   Cm_t
+  static constexpr int oCB = oC + kSsdQ * LDB;        // sCB[Q][Q]    Cm_t . B_s at [t][s]
+  static constexpr int oWave = oCB + kSsdQ * kSsdQ;   // per wave: lam[Q], w[Q], dt[Q], pad[Q], M[Q][Q]
+  static constexpr int WAVE = 4 * kSsdQ + kSsdQ * kSsdQ;
+  static constexpr int floats = oWave + 4 * WAVE;
 };
 
-template <typename T, int NWQ>
-__global__ __launch_bounds__(1024) void k_ssd_scan(SsdArgs a) {
-  using L = SsdLayout<NWQ>;
-  constexpr int NB = L::NB, QB = L::QB, NQ = 8;
-  const int H = a.H, P = a.P, N = a.N, K = a.K, Q = a.chunk;
-  const int RB = (P + 63) >> 6;
-  const int b = blockIdx.x / H, h = blockIdx.x % H;
-  const int grp = h / (H / a.ng);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int nq = wave % NWQ, rb = wave / NWQ;
-  const int p = rb * 64 + lane;  // state row
-  const bool own = p < P;
-  const int n0 = nq * NQ;        // first owned column
+// Heads per workgroup: as many as fit in 4 waves and divide the heads of one
+// B/Cm group (so a workgroup never spans two groups).
+__host__ __device__ inline int ssd_heads_per_block(int H, int ng, int P) {
+  const int RB = (P + 63) / 64;
+  const int hg = H / ng;
+  for (int hpw = 4 / RB; hpw > 1; hpw >>= 1)
+    if (hg % hpw == 0) return hpw;
+  return 1;
+}
 
-  extern __shared__ __align__(16) float lds[];
+// Workgroup = 4 waves; wave w handles head hfirst + w / RB, state rows
+// (w % RB) * 64 + lane, for w < HPW * RB (the rest only help staging).  Every
+// global load of a chunk is issued before the first wait, with clamped
+// indices and selects instead of per-element branches (a load under a branch
+// gets its own wait, which would serialize the loads' memory latencies).
+template <typename T, int NMAX, bool V4>
+__global__ __launch_bounds__(256) void k_ssd_scan(SsdArgs a) {
+  using L = SsdLds<NMAX>;
+  constexpr int Q = kSsdQ, LDB = L::LDB;
+  constexpr int E = Q * NMAX / 256;  // B and Cm entries staged per thread
+  __shared__ __align__(16) float lds[L::floats];
+  const int H = a.H, P = a.P, N = a.N, K = a.K, QC = a.chunk;
+  const int RB = (P + 63) >> 6;
+  const int HPW = ssd_heads_per_block(H, a.ng, P);
+  const int hblocks = H / HPW;
+  const int b = blockIdx.x / hblocks, hfirst = (blockIdx.x % hblocks) * HPW;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const bool active = wave < HPW * RB;
+  const int h = min(hfirst + wave / RB, H - 1), p = (wave % RB) * 64 + lane;
+  const bool own = active && p < P;
+  const int pc = min(p, P - 1);
+  const int grp = hfirst / (H / a.ng);
+
   float* sB = lds + L::oB;
-  float* sCT = lds + L::oCT;
-  float* sMT = lds + L::oMT;
-  float* slam = lds + L::oLam;
-  float* sw = slam + QB;
-  float* sdt = sw + QB;
-  float* sX = lds + L::oX;                              // [RB][QB][64]
-  float* sZ = sX + size_t(RB) * QB * 64;                // [RB][NWQ][QB][64]
+  float* sC = lds + L::oC;
+  float* sCB = lds + L::oCB;
+  float* wl = lds + L::oWave + wave * L::WAVE;
+  float* slam = wl;
+  float* sw = wl + Q;
+  float* sdt = wl + 2 * Q;
+  float* sM = wl + 4 * Q;  // M[t][s] at [t * Q + s]
 
   const T* __restrict__ Bm = static_cast<const T*>(a.B);
   const T* __restrict__ Cm = static_cast<const T*>(a.Cm);
   const float Ah = a.A[h];
   const float Dh = a.Dskip ? a.Dskip[h] : 0.f;
-  // per-position rows as uniform bases + the lane's row p
   const size_t HP = size_t(H) * P;
-  const T* __restrict__ xrow = static_cast<const T*>(a.x) + (size_t(b) * K * H + h) * P;
-  float* __restrict__ yrow = a.y + (size_t(b) * K * H + h) * P;
+  const T* __restrict__ xrow = static_cast<const T*>(a.x) + (size_t(b) * K * H + h) * P + pc;
+  float* __restrict__ yrow = a.y + (size_t(b) * K * H + h) * P + p;
 
-  float Hs[NQ];
-  {
-    const float* h0 = (a.h0 && own) ? a.h0 + ((size_t(b) * H + h) * P + p) * N + n0 : nullptr;
-    if (h0 && n0 + NQ <= N && (N & 3) == 0) {
-      const float4 v0 = reinterpret_cast<const float4*>(h0)[0];
-      const float4 v1 = reinterpret_cast<const float4*>(h0)[1];
-      Hs[0] = v0.x; Hs[1] = v0.y; Hs[2] = v0.z; Hs[3] = v0.w;
-      Hs[4] = v1.x; Hs[5] = v1.y; Hs[6] = v1.z; Hs[7] = v1.w;
+  // the lane's state row H[p, 0..N), zero past N (and for idle lanes)
+  float Hs[NMAX];
+#pragma unroll
+  for (int k = 0; k < NMAX; ++k) Hs[k] = 0.f;
+  if (a.h0) {
+    const float* hrow = a.h0 + ((size_t(b) * H + h) * P + pc) * N;
+    if constexpr (V4) {  // N % 4 == 0: 16-byte loads
+#pragma unroll
+      for (int k = 0; k < NMAX; k += 4) {
+        const float4 v = *reinterpret_cast<const float4*>(hrow + min(k, N - 4));
+        Hs[k] = v.x; Hs[k + 1] = v.y; Hs[k + 2] = v.z; Hs[k + 3] = v.w;
+      }
     } else {
 #pragma unroll
-      for (int k = 0; k < NQ; ++k) Hs[k] = (h0 && n0 + k < N) ? h0[k] : 0.f;
+      for (int k = 0; k < NMAX; ++k) Hs[k] = hrow[min(k, N - 1)];
     }
   }
+  bool hmasked = false;  // the selects on Hs run after the first chunk's loads are issued
 
-  for (int c0 = 0; c0 < K; c0 += Q) {
-    const int q = min(Q, K - c0);
-    for (int i = tid; i < QB * NB; i += blockDim.x) {
-      const int t = i / NB, n = i % NB;
-      float bv = 0.f, cv = 0.f;
-      if (t < q && n < N) {
-        const size_t src = ((size_t(b) * K + c0 + t) * a.ng + grp) * N + n;
-        bv = to_f32(Bm[src]);
-        cv = to_f32(Cm[src]);
-      }
-      sB[t * NB + n] = bv;
-      sCT[n * QB + t] = cv;
-    }
-    if (nq == 0) {  // one wave per row block brings the chunk's x of its rows
+  for (int c0 = 0; c0 < K; c0 += QC) {
+    const int q = min(QC, K - c0);
+    // issue: the lane's x[c0 + s, p], this thread's B / Cm entries, the lane's delta
+    float xs[Q];
 #pragma unroll
-      for (int s = 0; s < QB; ++s)
-        sX[(rb * QB + s) * 64 + lane] = (own && s < q) ? to_f32(xrow[size_t(c0 + s) * HP + p]) : 0.f;
+    for (int s = 0; s < Q; ++s) xs[s] = to_f32(xrow[size_t(min(c0 + s, K - 1)) * HP]);
+    float bv[E], cv[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int i = tid + 256 * e, t = i / NMAX, n = i % NMAX;
+      const size_t src = ((size_t(b) * K + min(c0 + t, K - 1)) * a.ng + grp) * N + min(n, N - 1);
+      bv[e] = to_f32(Bm[src]);
+      cv[e] = to_f32(Cm[src]);
     }
-    if (wave == 0) {
-      // in-chunk cumulative log-decay: inclusive scan across the wave's lanes
-      const float dt = lane < q ? a.delta[(size_t(b) * K + c0 + lane) * H + h] : 0.f;
+    const float dv = a.delta[(size_t(b) * K + min(c0 + lane, K - 1)) * H + h];
+    if (!hmasked) {
+#pragma unroll
+      for (int k = 0; k < NMAX; ++k) Hs[k] = (own && k < N) ? Hs[k] : 0.f;
+      hmasked = true;
+    }
+#pragma unroll
+    for (int s = 0; s < Q; ++s) xs[s] = (own && s < q) ? xs[s] : 0.f;
+    // the chunk's B and Cm rows of this group, zero-padded to Q x NMAX
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int i = tid + 256 * e, t = i / NMAX, n = i % NMAX;
+      const bool in = t < q && n < N;
+      sB[t * LDB + n] = in ? bv[e] : 0.f;
+      sC[t * LDB + n] = in ? cv[e] : 0.f;
+    }
+    // this head's in-chunk cumulative log-decay (inclusive scan over lanes)
+    {
+      const float dt = lane < q ? dv : 0.f;
       float v = dt * Ah;
 #pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
+      for (int off = 1; off < Q; off <<= 1) {
         const float u = __shfl_up(v, off, 64);
         if (lane >= off) v += u;
       }
       const float lend = __shfl(v, q - 1, 64);
-      if (lane < QB) {
+      if (lane < Q) {
         slam[lane] = v;
         sdt[lane] = dt;
         sw[lane] = lane < q ? __expf(lend - v) * dt : 0.f;
       }
     }
     __syncthreads();
-    // decay-weighted C.B^T, masked before the exponential: M[t][s] -> sMT[s][t]
-    for (int i = tid; i < QB * QB; i += blockDim.x) {
-      const int t = i % QB, s = i / QB;
-      float v = 0.f;
-      if (s <= t && t < q) {
-        float d0 = 0.f, d1 = 0.f;
-        for (int n = 0; n + 1 < N; n += 2) {
-          d0 = fmaf(sCT[n * QB + t], sB[s * NB + n], d0);
-          d1 = fmaf(sCT[(n + 1) * QB + t], sB[s * NB + n + 1], d1);
-        }
-        if (N & 1) d0 = fmaf(sCT[(N - 1) * QB + t], sB[s * NB + N - 1], d0);
-        v = __expf(slam[t] - slam[s]) * (d0 + d1) * sdt[s];
+    // head-independent Cm_t . B_s of the group (one entry per thread)
+    {
+      const int t = tid / Q, s = tid % Q;
+      const float* cr = sC + t * LDB;
+      const float* br = sB + s * LDB;
+      float d0 = 0.f, d1 = 0.f;
+#pragma unroll
+      for (int n = 0; n < NMAX; n += 4) {
+        const float4 c = *reinterpret_cast<const float4*>(cr + n);
+        const float4 bb = *reinterpret_cast<const float4*>(br + n);
+        d0 = fmaf(c.x, bb.x, d0);
+        d1 = fmaf(c.y, bb.y, d1);
+        d0 = fmaf(c.z, bb.z, d0);
+        d1 = fmaf(c.w, bb.w, d1);
       }
-      sMT[s * QB + t] = v;
+      sCB[tid] = d0 + d1;
     }
     __syncthreads();
-    // this wave's share of y[t][p]: owned columns for the state term,
-    // positions s = nq, nq + NWQ, ... for the in-chunk term
-    float z[QB];
+    // this head's decay-weighted M, masked before the exponential
 #pragma unroll
-    for (int t = 0; t < QB; ++t) z[t] = 0.f;
+    for (int j = 0; j < Q * Q / 64; ++j) {
+      const int i = lane + 64 * j;
+      const int t = i / Q, s = i % Q;
+      float v = 0.f;
+      if (s <= t && t < q) v = __expf(slam[t] - slam[s]) * sCB[i] * sdt[s];
+      sM[i] = v;
+    }
+    __syncthreads();
+    // y[t, p] = exp(lam_t) H_in[p, :] . Cm_t + sum_{s <= t} M[t, s] x[s, p] + D x[t, p]
+    if (own) {
 #pragma unroll
-    for (int k = 0; k < NQ; ++k) {
-      const float hk = Hs[k];
+      for (int t = 0; t < Q; ++t) {
+        if (t < q) {
+          const float* cr = sC + t * LDB;
+          float z0 = 0.f, z1 = 0.f;
 #pragma unroll
-      for (int t = 0; t < QB; t += 4) {
-        const float4 c = *reinterpret_cast<const float4*>(sCT + (n0 + k) * QB + t);
-        z[t] = fmaf(hk, c.x, z[t]);
-        z[t + 1] = fmaf(hk, c.y, z[t + 1]);
-        z[t + 2] = fmaf(hk, c.z, z[t + 2]);
-        z[t + 3] = fmaf(hk, c.w, z[t + 3]);
+          for (int n = 0; n < NMAX; n += 4) {
+            const float4 c = *reinterpret_cast<const float4*>(cr + n);
+            z0 = fmaf(Hs[n], c.x, z0);
+            z1 = fmaf(Hs[n + 1], c.y, z1);
+            z0 = fmaf(Hs[n + 2], c.z, z0);
+            z1 = fmaf(Hs[n + 3], c.w, z1);
+          }
+          float z = (z0 + z1) * __expf(slam[t]);
+          const float* mr = sM + t * Q;
+#pragma unroll
+          for (int s = 0; s <= t; s += 4) {
+            const float4 m = *reinterpret_cast<const float4*>(mr + s);
+            z = fmaf(m.x, xs[s], z);
+            if (s + 1 <= t) z = fmaf(m.y, xs[s + 1], z);
+            if (s + 2 <= t) z = fmaf(m.z, xs[s + 2], z);
+            if (s + 3 <= t) z = fmaf(m.w, xs[s + 3], z);
+          }
+          yrow[size_t(c0 + t) * HP] = fmaf(Dh, xs[t], z);
+        }
       }
     }
-#pragma unroll
-    for (int t = 0; t < QB; ++t) z[t] *= __expf(slam[t]);
-    for (int s = nq; s < QB; s += NWQ) {
-      const float xv = sX[(rb * QB + s) * 64 + lane];
-#pragma unroll
-      for (int t = 0; t < QB; t += 4) {
-        const float4 m = *reinterpret_cast<const float4*>(sMT + s * QB + t);
-        z[t] = fmaf(m.x, xv, z[t]);
-        z[t + 1] = fmaf(m.y, xv, z[t + 1]);
-        z[t + 2] = fmaf(m.z, xv, z[t + 2]);
-        z[t + 3] = fmaf(m.w, xv, z[t + 3]);
-      }
-    }
-    float* zs = sZ + (size_t(rb) * NWQ + nq) * QB * 64 + lane;
-#pragma unroll
-    for (int t = 0; t < QB; ++t) zs[t * 64] = z[t];
-    // state passing to the next chunk (owned columns)
+    // state passing: H_out[p, n] = exp(lam_end) H_in[p, n] + sum_s w_s x[s, p] B[s, n]
+    // (after the last chunk only h_final needs it)
+    if (c0 + QC >= K && !a.h_final) break;
     const float dend = __expf(slam[q - 1]);
 #pragma unroll
-    for (int k = 0; k < NQ; ++k) Hs[k] *= dend;
-    for (int s = 0; s < q; ++s) {
-      const float coef = sw[s] * sX[(rb * QB + s) * 64 + lane];
-      const float4 b0 = *reinterpret_cast<const float4*>(sB + s * NB + n0);
-      const float4 b1 = *reinterpret_cast<const float4*>(sB + s * NB + n0 + 4);
-      Hs[0] = fmaf(coef, b0.x, Hs[0]); Hs[1] = fmaf(coef, b0.y, Hs[1]);
-      Hs[2] = fmaf(coef, b0.z, Hs[2]); Hs[3] = fmaf(coef, b0.w, Hs[3]);
-      Hs[4] = fmaf(coef, b1.x, Hs[4]); Hs[5] = fmaf(coef, b1.y, Hs[5]);
-      Hs[6] = fmaf(coef, b1.z, Hs[6]); Hs[7] = fmaf(coef, b1.w, Hs[7]);
-    }
-    __syncthreads();
-    // sum the waves' shares: wave nq writes positions t = nq, nq + NWQ, ...
-    if (own) {
-      for (int t = nq; t < q; t += NWQ) {
-        const float* zr = sZ + size_t(rb) * NWQ * QB * 64 + t * 64 + lane;
-        float yv = 0.f;
+    for (int n = 0; n < NMAX; ++n) Hs[n] *= dend;
 #pragma unroll
-        for (int w = 0; w < NWQ; ++w) yv += zr[w * QB * 64];
-        yrow[size_t(c0 + t) * HP + p] = yv + Dh * sX[(rb * QB + t) * 64 + lane];
+    for (int s = 0; s < Q; ++s) {
+      if (s < q) {
+        const float coef = sw[s] * xs[s];
+        const float* br = sB + s * LDB;
+#pragma unroll
+        for (int n = 0; n < NMAX; n += 4) {
+          const float4 bb = *reinterpret_cast<const float4*>(br + n);
+          Hs[n] = fmaf(coef, bb.x, Hs[n]);
+          Hs[n + 1] = fmaf(coef, bb.y, Hs[n + 1]);
+          Hs[n + 2] = fmaf(coef, bb.z, Hs[n + 2]);
+          Hs[n + 3] = fmaf(coef, bb.w, Hs[n + 3]);
+        }
       }
     }
-    __syncthreads();  // LDS is rewritten by the next chunk
+    if (c0 + QC < K) __syncthreads();  // the next chunk rewrites LDS
   }
   if (a.h_final && own) {
-    float* hf = a.h_final + ((size_t(b) * H + h) * P + p) * N + n0;
-    if (n0 + NQ <= N && (N & 3) == 0) {
-      reinterpret_cast<float4*>(hf)[0] = make_float4(Hs[0], Hs[1], Hs[2], Hs[3]);
-      reinterpret_cast<float4*>(hf)[1] = make_float4(Hs[4], Hs[5], Hs[6], Hs[7]);
+    float* hf = a.h_final + ((size_t(b) * H + h) * P + p) * N;
+    if constexpr (V4) {
+#pragma unroll
+      for (int k = 0; k < NMAX; k += 4)
+        if (k < N) *reinterpret_cast<float4*>(hf + k) = make_float4(Hs[k], Hs[k + 1], Hs[k + 2], Hs[k + 3]);
     } else {
 #pragma unroll
-      for (int k = 0; k < NQ; ++k)
-        if (n0 + k < N) hf[k] = Hs[k];
+      for (int k = 0; k < NMAX; ++k)
+        if (k < N) hf[k] = Hs[k];
     }
   }
 }
 
-static int nwq_for(int N) { return N <= 16 ? 2 : N <= 32 ? 4 : N <= 64 ? 8 : 16; }
-
 size_t ssd_lds_bytes(int P, int N, int Q) {
+  (void)P;
   (void)Q;
-  const int RB = (P + 63) / 64;
-  switch (nwq_for(N)) {
-    case 2: return SsdLayout<2>::floats(RB) * sizeof(float);
-    case 4: return SsdLayout<4>::floats(RB) * sizeof(float);
-    case 8: return SsdLayout<8>::floats(RB) * sizeof(float);
-    default: return SsdLayout<16>::floats(RB) * sizeof(float);
-  }
+  if (N <= 16) return SsdLds<16>::floats * sizeof(float);
+  if (N <= 32) return SsdLds<32>::floats * sizeof(float);
+  if (N <= 64) return SsdLds<64>::floats * sizeof(float);
+  return SsdLds<128>::floats * sizeof(float);
 }
 
-template <typename T, int NWQ>
-static hipError_t launch_w(hipStream_t st, const SsdArgs& a) {
-  const int RB = (a.P + 63) / 64;
-  const size_t lds = SsdLayout<NWQ>::floats(RB) * sizeof(float);
-  auto kern = k_ssd_scan<T, NWQ>;
-  if (lds > 64 * 1024) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
-    if (e != hipSuccess) return e;
-  }
-  hipLaunchKernelGGL(kern, dim3(a.C * a.H), dim3(64 * NWQ * RB), lds, st, a);
+template <typename T, int NMAX>
+static hipError_t launch_n(hipStream_t st, const SsdArgs& a) {
+  const int hpw = ssd_heads_per_block(a.H, a.ng, a.P);
+  const dim3 grid(a.C * (a.H / hpw)), block(256);
+  if (a.N % 4 == 0)
+    hipLaunchKernelGGL((k_ssd_scan<T, NMAX, true>), grid, block, 0, st, a);
+  else
+    hipLaunchKernelGGL((k_ssd_scan<T, NMAX, false>), grid, block, 0, st, a);
   return hipGetLastError();
 }
 
 template <typename T>
 static hipError_t launch_t(hipStream_t st, const SsdArgs& a) {
-  switch (nwq_for(a.N)) {
-    case 2: return launch_w<T, 2>(st, a);
-    case 4: return launch_w<T, 4>(st, a);
-    case 8: return launch_w<T, 8>(st, a);
-    default: return launch_w<T, 16>(st, a);
-  }
+  if (a.N <= 16) return launch_n<T, 16>(st, a);
+  if (a.N <= 32) return launch_n<T, 32>(st, a);
+  if (a.N <= 64) return launch_n<T, 64>(st, a);
+  return launch_n<T, 128>(st, a);
 }
 
 hipError_t launch_ssd_scan(hipStream_t st, int dtype, const SsdArgs& a) {

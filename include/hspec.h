@@ -86,7 +86,7 @@ int hspec_init_state(void* stream, int dtype, int C, int d_model, int S,
  *   h0      fp32 [C, H, P, N] or NULL (NULL = zero state); the layout of a1's h0
  *   y       fp32 [C, K, H, P]     output
  *   h_final fp32 [C, H, P, N] or NULL: the state after the last block position
- * Limits: chunk in {1,2,4,8,16}; P <= 128; N <= 128; P*N <= 8192; ng
+ * Limits: chunk in {1,2,4,8,16}; P <= 128; N <= 128; ng
  * divides H (else INVALID_ARG / UNSUPPORTED).
  */
 int hspec_ssd_scan(void* stream, int dtype, int C, int K, int H, int P, int ng, int N, int chunk,

@@ -182,6 +182,17 @@ SSD_CASES = [
     (2, 16, 2, 128, 1, 64, 8, "f32", False, False),
     (1, 5, 2, 64, 1, 128, 1, "bf16", False, False),
     (4, 16, 32, 64, 1, 64, 16, "bf16", True, False),
+    # two row blocks per head with the largest state; partial row block
+    (2, 16, 2, 128, 1, 128, 16, "bf16", True, False),
+    (2, 16, 4, 100, 1, 24, 16, "bf16", False, False),
+    # N not a multiple of 4 (scalar state-row loads); heads per group not a
+    # multiple of 4 (2- and 1-head workgroups)
+    (2, 11, 6, 64, 1, 7, 4, "f32", True, False),
+    (3, 16, 12, 64, 4, 32, 8, "bf16", False, False),
+    (2, 16, 6, 128, 2, 16, 16, "f32", False, False),
+    # many chunks
+    (2, 64, 4, 64, 1, 32, 16, "bf16", False, False),
+    (1, 64, 4, 64, 1, 32, 1, "f32", True, False),
 ]
 
 
