@@ -51,7 +51,7 @@ int check_ssd(int dtype, int C, int K, int H, int P, int ng, int N, int chunk, c
 }
 
 struct AttnPlanShape {
-  int pps, M;
+  int pps, M, MS;  // pages per split, C * MS work items, splits of a max_ctx request
   size_t plan_bytes, part_o_off, part_ml_off, total;
 };
 
@@ -59,10 +59,12 @@ int auto_pages_per_split(int C, int Hkv, int max_ctx) {
   const int max_pages = (max_ctx + 15) / 16;
   if (max_pages <= 0) return 16;
   const int64_t base = int64_t(C) * Hkv;
-  // Splitting only pays while (request, kv head) pairs alone leave the 256
-  // CUs short of work: every extra split adds an fp32 partial (G*K rows x
-  // (D+2)) written and read back by the merge.
-  const int64_t target = 1024;
+  // Aim at about 512 work items -- two per CU, one resident round at the
+  // attention kernel's occupancy: measured at 8192-token contexts, C = 2..64,
+  // 512 items beat both 256 (too little in flight) and 1024 (twice the
+  // per-item prologue and fp32 partials: G*K rows x (D+2) written and read
+  // back by the merge).  Past 512 (request, kv head) pairs nothing is split.
+  const int64_t target = 512;
   if (base >= target) return max_pages;
   const int64_t splits = (target + base - 1) / base;
   int64_t pps = (max_pages + splits - 1) / splits;
@@ -75,6 +77,7 @@ AttnPlanShape plan_shape(int C, int K, int Hq, int Hkv, int D, int max_ctx, int 
   p.pps = kv_split_pages > 0 ? kv_split_pages : auto_pages_per_split(C, Hkv, max_ctx);
   const int64_t max_pages = (int64_t(max_ctx) + 15) / 16;
   const int64_t max_splits = std::max<int64_t>(1, (max_pages + p.pps - 1) / p.pps);
+  p.MS = int(std::min<int64_t>(max_splits, 0x7fffffff));
   p.M = int(std::min<int64_t>(int64_t(C) * max_splits, 0x7fffffff));
   const size_t rows = size_t(Hq / Hkv) * K;
   p.plan_bytes = align256(size_t(4 + 2 * size_t(C) + 2 * size_t(p.M)) * 4);
@@ -110,7 +113,7 @@ int check_attn(int dtype, int C, int K, int Hq, int Hkv, int D, const void* q, c
   if (int64_t(Hq / Hkv) * K > 256) return HSPEC_ERR_UNSUPPORTED;
   if (attn_lds_bytes(dtype, D, (Hq / Hkv) * K, K) > kMaxLds) return HSPEC_ERR_UNSUPPORTED;
   const AttnPlanShape p = plan_shape(C, K, Hq, Hkv, D, max_ctx, kv_split_pages);
-  if (int64_t(p.M) * Hkv > 0x7fffffff || int64_t(C) * Hkv > 0x7fffffff) return HSPEC_ERR_UNSUPPORTED;
+  if (int64_t(C) * p.MS * Hkv > 0x7fffffff) return HSPEC_ERR_UNSUPPORTED;
   return HSPEC_OK;
 }
 
@@ -130,11 +133,13 @@ int run_attn(hipStream_t st, int dtype, int C, int K, int Hq, int Hkv, int D, co
   a.scale_log2 = sc * 1.4426950408889634f;
   a.out = out;
   unsigned char* base = static_cast<unsigned char*>(ws);
-  a.plan = reinterpret_cast<const int32_t*>(base);
+  a.plan = reinterpret_cast<int32_t*>(base);
   a.part_o = reinterpret_cast<float*>(base + p.part_o_off);
   a.part_ml = reinterpret_cast<float*>(base + p.part_ml_off);
   a.max_items = p.M;
-  return status_of(launch_block_attn(st, dtype, a, p.pps));
+  a.pps = p.pps;
+  a.max_splits = p.MS;
+  return status_of(launch_block_attn(st, dtype, a));
 }
 
 }  // namespace

@@ -2,9 +2,14 @@
 // in place (H-Spec, Abstract: attention modules reuse the target KV where it
 // lies; there is no drafter-side KV cache).
 //
-// a0  k_split_plan       one workgroup turns ctx_lens into the int32 split plan
-// a3  k_block_attn       one workgroup per (work item = request x split, kv head)
+// a3  k_block_attn       one workgroup per (work item = request x split, kv head);
+//                        workgroup 0 also writes the int32 split plan (a0)
 // a4  k_attn_merge       log-sum-exp merge of the splits of multi-split requests
+//
+// Work items are numbered request * max_splits + split, so every kernel finds
+// its request and split from its block index and ctx_lens alone; items past a
+// request's own split count exit at once.  The plan in the workspace lists the
+// same decomposition (compacted, in request order) for callers and tests.
 //
 // k_block_attn, per workgroup of NW waves (one work item, one kv head j):
 //   * The G*K query rows of kv head j (row r -> block position r / G, head
@@ -33,37 +38,38 @@
 namespace hspec {
 
 // ---------------------------------------------------------------------------
-// a0: split plan.  Layout documented in include/hspec.h.
+// a0: split plan, written by workgroup 0 of k_block_attn after its own item
+// (NT threads, `scan` = NT + 1 ints of LDS).  Layout documented in
+// include/hspec.h: splits_b = max(1, ceil(ceil(ctx_b / 16) / pps)), items
+// listed request by request.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(1024) void k_split_plan(const int32_t* __restrict__ ctx_lens, int C,
-                                                     int max_ctx, int pps, int M,
-                                                     int32_t* __restrict__ plan) {
-  __shared__ int s_scan[1024];
-  __shared__ int s_carry;
+template <int NT>
+__device__ void write_split_plan(const AttnArgs& a, int* scan) {
   const int tid = threadIdx.x;
-  if (tid == 0) s_carry = 0;
-  __syncthreads();
+  const int C = a.C, M = a.max_items, pps = a.pps;
+  int32_t* plan = a.plan;
   int32_t* n_splits = plan + 4;
   int32_t* first = plan + 4 + C;
   int32_t* req = plan + 4 + 2 * C;
   int32_t* spl = req + M;
-  for (int base = 0; base < C; base += 1024) {
+  int carry = 0;
+  for (int base = 0; base < C; base += NT) {
     const int b = base + tid;
     int ns = 0;
     if (b < C) {
-      const int ctx = min(max(ctx_lens[b], 0), max_ctx);
-      const int np = (ctx + 15) >> 4;
-      ns = max(1, (np + pps - 1) / pps);
+      const int ctx = min(max(a.ctx_lens[b], 0), a.max_ctx);
+      ns = max(1, (((ctx + 15) >> 4) + pps - 1) / pps);
     }
-    s_scan[tid] = ns;
     __syncthreads();
-    for (int off = 1; off < 1024; off <<= 1) {
-      const int v = tid >= off ? s_scan[tid - off] : 0;
+    scan[tid] = ns;
+    __syncthreads();
+    for (int off = 1; off < NT; off <<= 1) {
+      const int v = tid >= off ? scan[tid - off] : 0;
       __syncthreads();
-      s_scan[tid] += v;
+      scan[tid] += v;
       __syncthreads();
     }
-    const int excl = s_carry + s_scan[tid] - ns;
+    const int excl = carry + scan[tid] - ns;
     if (b < C) {
       n_splits[b] = ns;
       first[b] = excl;
@@ -74,12 +80,10 @@ __global__ __launch_bounds__(1024) void k_split_plan(const int32_t* __restrict__
         }
       }
     }
-    __syncthreads();
-    if (tid == 1023) s_carry += s_scan[1023];
-    __syncthreads();
+    carry += scan[NT - 1];
   }
-  const int total = min(s_carry, M);
-  for (int i = total + tid; i < M; i += 1024) {
+  const int total = min(carry, M);
+  for (int i = total + tid; i < M; i += NT) {
     req[i] = -1;
     spl[i] = -1;
   }
@@ -199,15 +203,13 @@ __global__ __launch_bounds__(64 * NW) void k_block_attn(AttnArgs a) {
 
   const int Hkv = a.Hkv;
   const int item = blockIdx.x / Hkv, j = blockIdx.x % Hkv;
-  const int32_t* plan = a.plan;
-  if (item >= plan[0]) return;  // uniform over the workgroup
-  const int C = a.C, K = a.K, G = a.G, rows = a.rows;
-  const int pps = plan[1];
-  const int b = plan[4 + 2 * C + item];
-  const int split = plan[4 + 2 * C + a.max_items + item];
-  const int nsplit = plan[4 + b];
+  const int K = a.K, G = a.G, rows = a.rows;
+  const int pps = a.pps;
+  const int b = item / a.max_splits, split = item % a.max_splits;
   const int ctx = min(max(a.ctx_lens[b], 0), a.max_ctx);
   const int npages = (ctx + 15) >> 4;
+  const int nsplit = max(1, (npages + pps - 1) / pps);
+  if (split >= nsplit) return;  // uniform over the workgroup; item 0 always exists
   const int p_lo = split * pps;
   const int ncache = max(0, min(npages, p_lo + pps) - p_lo);
   const int nblk = (split == nsplit - 1) ? (K + 15) >> 4 : 0;
@@ -543,43 +545,74 @@ __global__ __launch_bounds__(64 * NW) void k_block_attn(AttnArgs a) {
       if (lg == 0) *reinterpret_cast<float2*>(a.part_ml + prow * 2) = make_float2(acc.m2[rt], lsum);
     }
   }
+  if (blockIdx.x == 0) write_split_plan<NT>(a, reinterpret_cast<int*>(smem));
 }
 
 // ---------------------------------------------------------------------------
 // a4: merge of split partials (requests with more than one split only).
-// One thread per (row, 4 output columns); a single pass over the splits with
-// a running maximum, all in log2 units like the partials.
+// LPO lanes (1 or 4) per (row, 4 output columns), in log2 units like the
+// partials: lane q takes splits q, q+LPO, ..., loading U of them at a time
+// (clamped indices, no data-dependent branches) and keeping a running
+// maximum; with LPO = 4 the quad then combines its four (m, l, O) with two
+// xor-shuffles.  A request with up to LPO*U splits costs one round of
+// independent loads; LPO and U are sized to the largest split count at launch
+// so few loads are clamped repeats and few lanes idle.
 // ---------------------------------------------------------------------------
-template <typename T, int D>
+template <typename T, int D, int LPO, int U>
 __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
+  constexpr int OPB = 256 / LPO;  // outputs per block
   const int Hkv = a.Hkv;
   const int b = blockIdx.x / Hkv, j = blockIdx.x % Hkv;
-  const int32_t* plan = a.plan;
-  const int C = a.C;
-  const int ns = plan[4 + b];
+  const int ctx = min(max(a.ctx_lens[b], 0), a.max_ctx);
+  const int ns = max(1, (((ctx + 15) >> 4) + a.pps - 1) / a.pps);
   if (ns <= 1) return;
   const int rows = a.rows, G = a.G, K = a.K;
-  const int idx = blockIdx.y * 256 + threadIdx.x;
-  if (idx >= rows * (D / 4)) return;
-  const int row = idx / (D / 4), d4 = idx % (D / 4);
-  const int first = plan[4 + C + b];
+  const int idx = blockIdx.y * OPB + int(threadIdx.x) / LPO, q = int(threadIdx.x) % LPO;
+  const bool live = idx < rows * (D / 4);  // whole quads agree
+  const int row = min(idx / (D / 4), rows - 1), d4 = idx % (D / 4);
+  const size_t stride = size_t(Hkv) * rows;  // partial rows between consecutive splits
+  const size_t p0 = (size_t(b) * a.max_splits * Hkv + j) * rows + row;
   float M = -INFINITY, Ls = 0.f;
   float4 acc = make_float4(0, 0, 0, 0);
-#pragma unroll 4
-  for (int s = 0; s < ns; ++s) {
-    const size_t prow = (size_t(first + s) * Hkv + j) * rows + row;
-    const float2 ml = *reinterpret_cast<const float2*>(a.part_ml + prow * 2);
-    const float4 v = reinterpret_cast<const float4*>(a.part_o + prow * D)[d4];
-    if (ml.x > M) {
-      const float f = fast_exp2(M - ml.x);  // M = -inf gives 0
-      acc.x *= f; acc.y *= f; acc.z *= f; acc.w *= f;
-      Ls *= f;
-      M = ml.x;
+  for (int s0 = q; s0 < ns; s0 += LPO * U) {
+    float2 ml[U];
+    float4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const size_t pr = p0 + size_t(min(s0 + LPO * u, ns - 1)) * stride;
+      ml[u] = *reinterpret_cast<const float2*>(a.part_ml + pr * 2);
+      v[u] = reinterpret_cast<const float4*>(a.part_o + pr * D)[d4];
     }
-    const float f = ml.x == -INFINITY ? 0.f : fast_exp2(ml.x - M);
-    acc.x += f * v.x; acc.y += f * v.y; acc.z += f * v.z; acc.w += f * v.w;
-    Ls += f * ml.y;
+    float mr = M;  // every split holds at least one token: its maximum is finite
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (s0 + LPO * u < ns) mr = fmaxf(mr, ml[u].x);
+    const float sc = M == -INFINITY ? 0.f : fast_exp2(M - mr);
+    acc.x *= sc; acc.y *= sc; acc.z *= sc; acc.w *= sc;
+    Ls *= sc;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float f = s0 + LPO * u < ns ? fast_exp2(ml[u].x - mr) : 0.f;
+      acc.x += f * v[u].x; acc.y += f * v[u].y; acc.z += f * v[u].z; acc.w += f * v[u].w;
+      Ls += f * ml[u].y;
+    }
+    M = mr;
   }
+  // combine the quad (a lane without splits has M = -inf, Ls = 0, acc = 0)
+#pragma unroll
+  for (int x = 1; x < LPO; x <<= 1) {
+    const float Mo = __shfl_xor(M, x, 64), Lo = __shfl_xor(Ls, x, 64);
+    const float ox = __shfl_xor(acc.x, x, 64), oy = __shfl_xor(acc.y, x, 64);
+    const float oz = __shfl_xor(acc.z, x, 64), ow = __shfl_xor(acc.w, x, 64);
+    const float Mn = fmaxf(M, Mo);
+    const float f1 = M == -INFINITY ? 0.f : fast_exp2(M - Mn);
+    const float f2 = Mo == -INFINITY ? 0.f : fast_exp2(Mo - Mn);
+    acc.x = acc.x * f1 + ox * f2; acc.y = acc.y * f1 + oy * f2;
+    acc.z = acc.z * f1 + oz * f2; acc.w = acc.w * f1 + ow * f2;
+    Ls = Ls * f1 + Lo * f2;
+    M = Mn;
+  }
+  if (!live || q != 0) return;
   const float inv = 1.f / Ls;
   const int t = row / G, gg = row % G;
   T* o = static_cast<T*>(a.out) + ((size_t(b) * K + t) * a.Hq + j * G + gg) * D + d4 * 4;
@@ -631,11 +664,24 @@ size_t attn_lds_bytes(int dtype, int D, int rows, int K) {
   return D == 64 ? AttnLds<float, 64>::bytes : AttnLds<float, 128>::bytes;
 }
 
-hipError_t launch_block_attn(hipStream_t st, int dtype, const AttnArgs& a, int pps) {
-  hipLaunchKernelGGL(k_split_plan, dim3(1), dim3(1024), 0, st, a.ctx_lens, a.C, a.max_ctx, pps,
-                     a.max_items, const_cast<int32_t*>(a.plan));
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+template <typename T, int D, int LPO, int U>
+static hipError_t launch_merge_cfg(hipStream_t st, const AttnArgs& a) {
+  const dim3 mg(a.C * a.Hkv, (a.rows * (D / 4) + 256 / LPO - 1) / (256 / LPO));
+  hipLaunchKernelGGL((k_attn_merge<T, D, LPO, U>), mg, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+static hipError_t launch_merge(hipStream_t st, const AttnArgs& a) {
+  const int ms = a.max_splits;
+  if (ms <= 4) return launch_merge_cfg<T, D, 1, 4>(st, a);
+  if (ms <= 8) return launch_merge_cfg<T, D, 1, 8>(st, a);
+  if (ms <= 16) return launch_merge_cfg<T, D, 4, 4>(st, a);
+  return launch_merge_cfg<T, D, 4, 8>(st, a);
+}
+
+hipError_t launch_block_attn(hipStream_t st, int dtype, const AttnArgs& a) {
+  hipError_t e;
   if (dtype == 1) {
     e = a.D == 64 ? launch_attn_d<bf16_t, 64>(st, a) : launch_attn_d<bf16_t, 128>(st, a);
   } else {
@@ -643,15 +689,11 @@ hipError_t launch_block_attn(hipStream_t st, int dtype, const AttnArgs& a, int p
   }
   if (e != hipSuccess) return e;
   if (a.max_items > a.C) {  // some request may have several splits
-    const dim3 mg(a.C * a.Hkv, (a.rows * (a.D / 4) + 255) / 256);
     if (dtype == 1) {
-      if (a.D == 64) hipLaunchKernelGGL((k_attn_merge<bf16_t, 64>), mg, dim3(256), 0, st, a);
-      else hipLaunchKernelGGL((k_attn_merge<bf16_t, 128>), mg, dim3(256), 0, st, a);
+      e = a.D == 64 ? launch_merge<bf16_t, 64>(st, a) : launch_merge<bf16_t, 128>(st, a);
     } else {
-      if (a.D == 64) hipLaunchKernelGGL((k_attn_merge<float, 64>), mg, dim3(256), 0, st, a);
-      else hipLaunchKernelGGL((k_attn_merge<float, 128>), mg, dim3(256), 0, st, a);
+      e = a.D == 64 ? launch_merge<float, 64>(st, a) : launch_merge<float, 128>(st, a);
     }
-    e = hipGetLastError();
   }
   return e;
 }

@@ -22,14 +22,15 @@ struct AttnArgs {
   int C, K, Hq, Hkv, G, D, rows;  // rows = G * K query rows per kv head
   float scale_log2;               // softmax scale * log2(e)
   void* out;
-  const int32_t* plan;            // workspace head (written by the plan kernel)
-  float* part_o;                  // [max_items, Hkv, rows, D]
+  int32_t* plan;                  // workspace head: the split plan (written by block 0)
+  float* part_o;                  // [max_items, Hkv, rows, D], item = request * max_splits + split
   float* part_ml;                 // [max_items, Hkv, rows, 2]
-  int max_items;
+  int max_items;                  // C * max_splits
+  int pps, max_splits;            // context pages per split; splits of a max_ctx request
 };
 
 // a0 + a3 + a4 on `st`.
-hipError_t launch_block_attn(hipStream_t st, int dtype, const AttnArgs& a, int pps);
+hipError_t launch_block_attn(hipStream_t st, int dtype, const AttnArgs& a);
 // dynamic LDS bytes of the attention kernel for a shape (host planning only)
 size_t attn_lds_bytes(int dtype, int D, int rows, int K);
 
