@@ -250,9 +250,9 @@ def main():
     achieved = att_b / (att_ms * 1e-3) / 1e9
     traffic = traffic_from_profile(w.name)
     kernels = {
-        "attention (plan + k_block_attn + merge)": dict(ms=att_ms, algorithmic_bytes=att_b,
+        "attention (k_block_attn; k_attn_merge when split)": dict(ms=att_ms, algorithmic_bytes=att_b,
                                                         gbs=achieved, hbm_frac=achieved / HBM_PEAK_GBS),
-        "init_state (k_init_state)": dict(ms=init_ms, algorithmic_bytes=init_bytes(w),
+        "init_state (k_init_wide)": dict(ms=init_ms, algorithmic_bytes=init_bytes(w),
                                           gbs=init_bytes(w) / (init_ms * 1e-3) / 1e9,
                                           hbm_frac=init_bytes(w) / (init_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                                           mfma_frac=2.0 * w.C * w.d_model * w.S / (init_ms * 1e-3) / 1e12 / BF16_DENSE_TFLOPS),
@@ -277,7 +277,7 @@ def main():
         "kv_read_frac_of_peak": kv_b / (att_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "k_block_attn (with its split-plan launch)"},
+                     "kernel": "k_block_attn"},
     }
     if not args.no_sweep:
         sweep = {}
