@@ -192,7 +192,7 @@ template <typename T, int D, int RT, int NW, int PF>
 __global__ __launch_bounds__(64 * NW) void k_block_attn(AttnArgs a) {
   using Gm = StageGeom<T, D>;
   constexpr int NT = 64 * NW;
-  constexpr int DS = D / 32, DPL = D / 16, EPC = Gm::EPC, CPR = Gm::CPR, SWZ = Gm::SWZ;
+  constexpr int DS = D / 32, DPL = D / 16, EPC = Gm::EPC, CPR = Gm::CPR;
   constexpr int RPP = (NT / CPR) < 16 ? (NT / CPR) : 16;  // page rows one load round covers
   constexpr int RND = 16 / RPP;                          // load rounds per page
   constexpr int NLD = 2 * RND;                           // 16-byte loads per tensor per stage
@@ -303,13 +303,28 @@ __global__ __launch_bounds__(64 * NW) void k_block_attn(AttnArgs a) {
     for (int tt = 0; tt < 2; ++tt) wpos[tt * RND + qq] = Gm::pos(tt * 16 + slot, tchunk) * 16;
   }
 
+  // Page-table window of the hot path: lane l holds the item's entries
+  // p_lo + 128*w + l and p_lo + 128*w + 64 + l of the current window w, and a
+  // stage takes its two entries with v_readlane.  The window is one vector
+  // load per 64 stages (a scalar read waited on at every issue, missing the
+  // scalar cache every 8 stages, cost ~4% at 256 stages per item).  Entries
+  // past the table row are clamped into it.
+  int pwlo = 0, pwhi = 0;
+  auto load_window = [&](int w) __attribute__((always_inline)) {
+    pwlo = pt[min(p_lo + 128 * w + lane, a.max_pages - 1)];
+    pwhi = pt[min(p_lo + 128 * w + 64 + lane, a.max_pages - 1)];
+  };
+  if (RPP * CPR == NT && nhot > 0) load_window(0);
+
   auto issue = [&](int st, uint4 (&stk)[NLD], uint4 (&stv)[NLD], int (&nv)[2]) __attribute__((always_inline)) {
     if (RPP * CPR == NT && st < nhot) {
-      // two full context pages: scalar page-table reads, unpredicated loads
-      // off scalar page bases (entries clamped into the pool: never a stray read)
-      const int lp = p_lo + 2 * st;
-      const int ph0 = min(max(pt[lp], 0), last_phys);
-      const int ph1 = min(max(pt[lp + 1], 0), last_phys);
+      // two full context pages: page numbers from the window, unpredicated
+      // loads off scalar page bases (entries clamped into the pool: never a
+      // stray read)
+      const int o = (2 * st) & 127, l0 = o & 63;
+      const int v = (o >> 6) ? pwhi : pwlo;
+      const int ph0 = min(max(__builtin_amdgcn_readlane(v, l0), 0), last_phys);
+      const int ph1 = min(max(__builtin_amdgcn_readlane(v, l0 + 1), 0), last_phys);
       const char* k0 = kcj + int64_t(ph0) * page_b;
       const char* v0 = vcj + int64_t(ph0) * page_b;
       const char* k1 = kcj + int64_t(ph1) * page_b;
@@ -478,22 +493,27 @@ __global__ __launch_bounds__(64 * NW) void k_block_attn(AttnArgs a) {
   // issued into the registers just freed; one barrier; then the math.
   uint4 stk[PF][NLD], stv[PF][NLD];
   int nv[PF][2];
-#pragma unroll
-  for (int pp = 0; pp < PF; ++pp)
+  static_for<0, PF>([&](auto P) __attribute__((always_inline)) {
+    constexpr int pp = decltype(P)::value;
     if (pp < nstage) issue(pp, stk[pp], stv[pp], nv[pp]);
+  });
   for (int st0 = 0; st0 < nstage; st0 += PF) {
-#pragma unroll
-    for (int pp = 0; pp < PF; ++pp) {
+    static_for<0, PF>([&](auto P) __attribute__((always_inline)) {
+      constexpr int pp = decltype(P)::value;
       const int st = st0 + pp;
       if (st < nstage) {  // uniform over the workgroup
         commit(pp & 1, stk[pp], stv[pp]);
         const int n0 = nv[pp][0], n1 = nv[pp][1];
-        if (st + PF < nstage) issue(st + PF, stk[pp], stv[pp], nv[pp]);
+        if (st + PF < nstage) {
+          const int sn = st + PF;
+          if ((sn & 63) == 0 && sn < nhot) load_window(sn >> 6);  // entering the next window
+          issue(sn, stk[pp], stv[pp], nv[pp]);
+        }
         __syncthreads();
         const int nn[2] = {n0, n1};
         compute(pp & 1, nn);
       }
-    }
+    });
   }
 
   // store: lane holds row li of each tile and d = (4*lg + r)*DPL + cc
