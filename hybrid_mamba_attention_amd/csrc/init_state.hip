@@ -278,10 +278,12 @@ __global__ __launch_bounds__(256) void k_init_wide(InitArgs a) {
     const char* base = wk + size_t(jj) * step_b;
 #pragma unroll
     for (int t = 0; t < Cfg::NU; ++t) ud[t] = *reinterpret_cast<const u32x4*>(usrc[t] + 64 * jj);
+    // W is read exactly once per call: nontemporal loads
 #pragma unroll
-    for (int e = 0; e < 8; ++e) w[e] = *reinterpret_cast<const uint32_t*>(base + roff[e]);
+    for (int e = 0; e < 8; ++e) w[e] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(base + roff[e]));
 #pragma unroll
-    for (int e = 0; e < 8; ++e) w[8 + e] = *reinterpret_cast<const uint32_t*>(base + half_b + roff[e]);
+    for (int e = 0; e < 8; ++e)
+      w[8 + e] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(base + half_b + roff[e]));
   };
   auto put_u = [&](int buf, const u32x4 (&ud)[Cfg::NU]) __attribute__((always_inline)) {
 #pragma unroll
