@@ -659,9 +659,13 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
 // host launcher
 // ---------------------------------------------------------------------------
 #ifndef HSPEC_ATTN_PREFETCH
-#define HSPEC_ATTN_PREFETCH 4
+#define HSPEC_ATTN_PREFETCH 2
 #endif
-constexpr int kPrefetch = HSPEC_ATTN_PREFETCH;  // stages of K/V loads in flight per workgroup
+// Stages of K/V loads in flight per workgroup.  With nontemporal loads two
+// stages keep pace with four at 64 query rows (C = 128: 707 vs 729 us) and
+// leave the 128-row tiles at two waves per SIMD instead of one (workload 4:
+// 660 vs 771 us).
+constexpr int kPrefetch = HSPEC_ATTN_PREFETCH;
 
 // (RT row tiles per wave, NW waves) for a query-row count: every wave reads the
 // whole stage from LDS, so fewer, wider waves cut LDS traffic per HBM byte.
