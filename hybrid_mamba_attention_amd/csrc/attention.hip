@@ -215,11 +215,42 @@ __global__ __launch_bounds__(64 * NW) void k_block_attn(AttnArgs a) {
   const int K = a.K, G = a.G, rows = a.rows;
   const int pps = a.pps;
   const int b = item / a.max_splits, split = item % a.max_splits;
+  const int p_lo = split * pps;
+
+  // Loads that depend only on the block index go out before ctx_lens[b]
+  // comes back, so their round trips overlap: the query rows and the first
+  // page-table window.
+  // This wave's query rows as B operands (row li of tile rt, d group lg + 4*ds);
+  // rows past G*K repeat the last row (their outputs are never stored).
+  const T* __restrict__ q = static_cast<const T*>(a.q);
+  Vec8<T> qv[RT][DS];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int row = min((wave * RT + rt) * 16 + li, rows - 1);
+    const int t = row / G, gg = row % G;
+    const T* qp = q + ((size_t(b) * K + t) * a.Hq + j * G + gg) * D;
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) load8(qv[rt][ds], qp + (lg + 4 * ds) * 8);
+  }
+  const int32_t* __restrict__ pt = a.page_table + size_t(b) * a.max_pages;
+  // Page-table window of the hot path: lane l holds the item's entries
+  // p_lo + 128*w + l and p_lo + 128*w + 64 + l of the current window w, and a
+  // stage takes its two entries with v_readlane.  The window is one vector
+  // load per 64 stages (a scalar read waited on at every issue, missing the
+  // scalar cache every 8 stages, cost ~4% at 256 stages per item).  Entries
+  // past the table row are clamped into it.
+  int pwlo = 0, pwhi = 0;
+  auto load_window = [&](int w) __attribute__((always_inline)) {
+    pwlo = pt[min(p_lo + 128 * w + lane, a.max_pages - 1)];
+    pwhi = pt[min(p_lo + 128 * w + 64 + lane, a.max_pages - 1)];
+  };
+  load_window(0);
+
   const int ctx = min(max(a.ctx_lens[b], 0), a.max_ctx);
   const int npages = (ctx + 15) >> 4;
   const int nsplit = max(1, (npages + pps - 1) / pps);
-  if (split >= nsplit) return;  // uniform over the workgroup; item 0 always exists
-  const int p_lo = split * pps;
+  // Items past the request's own split count (split >= nsplit) get no pages
+  // and no stages and store nothing; item 0 always exists.
   const int ncache = max(0, min(npages, p_lo + pps) - p_lo);
   const int nblk = (split == nsplit - 1) ? (K + 15) >> 4 : 0;
   const int nvp = ncache + nblk;
@@ -228,23 +259,6 @@ __global__ __launch_bounds__(64 * NW) void k_block_attn(AttnArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   unsigned char* sK = smem;                    // [2][TILE_B]
   unsigned char* sV = smem + 2 * TILE_B;       // [2][TILE_B]
-
-  // this wave's query rows as B operands (row li of tile rt, d group lg + 4*ds)
-  const T* __restrict__ q = static_cast<const T*>(a.q);
-  Vec8<T> qv[RT][DS];
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    const int row = (wave * RT + rt) * 16 + li;
-    if (row < rows) {
-      const int t = row / G, gg = row % G;
-      const T* qp = q + ((size_t(b) * K + t) * a.Hq + j * G + gg) * D;
-#pragma unroll
-      for (int ds = 0; ds < DS; ++ds) load8(qv[rt][ds], qp + (lg + 4 * ds) * 8);
-    } else {
-#pragma unroll
-      for (int ds = 0; ds < DS; ++ds) zero8(qv[rt][ds]);
-    }
-  }
 
   Acc<T, D, RT> acc;
 #pragma unroll
@@ -260,7 +274,6 @@ __global__ __launch_bounds__(64 * NW) void k_block_attn(AttnArgs a) {
   const int64_t head_off = int64_t(j) * a.head_stride * int64_t(sizeof(T));
   const char* __restrict__ kcj = static_cast<const char*>(a.k_cache) + head_off;
   const char* __restrict__ vcj = static_cast<const char*>(a.v_cache) + head_off;
-  const int32_t* __restrict__ pt = a.page_table + size_t(b) * a.max_pages;
   const int64_t page_b = a.page_stride * int64_t(sizeof(T));
   const int last_phys = a.num_pages - 1;
   const char* kblk = static_cast<const char*>(a.k_blk) + ((size_t(b) * K) * Hkv + j) * D * sizeof(T);
@@ -312,18 +325,6 @@ __global__ __launch_bounds__(64 * NW) void k_block_attn(AttnArgs a) {
     for (int tt = 0; tt < 2; ++tt) wpos[tt * RND + qq] = Gm::pos(tt * 16 + slot, tchunk) * 16;
   }
 
-  // Page-table window of the hot path: lane l holds the item's entries
-  // p_lo + 128*w + l and p_lo + 128*w + 64 + l of the current window w, and a
-  // stage takes its two entries with v_readlane.  The window is one vector
-  // load per 64 stages (a scalar read waited on at every issue, missing the
-  // scalar cache every 8 stages, cost ~4% at 256 stages per item).  Entries
-  // past the table row are clamped into it.
-  int pwlo = 0, pwhi = 0;
-  auto load_window = [&](int w) __attribute__((always_inline)) {
-    pwlo = pt[min(p_lo + 128 * w + lane, a.max_pages - 1)];
-    pwhi = pt[min(p_lo + 128 * w + 64 + lane, a.max_pages - 1)];
-  };
-  if (RPP * CPR == NT && nhot > 0) load_window(0);
 
   auto issue = [&](int st, uint4 (&stk)[NLD], uint4 (&stv)[NLD], int (&nv)[2]) __attribute__((always_inline)) {
     if (RPP * CPR == NT && st < nhot) {
@@ -530,7 +531,7 @@ __global__ __launch_bounds__(64 * NW) void k_block_attn(AttnArgs a) {
   for (int rt = 0; rt < RT; ++rt) {
     const float lsum = group4_sum(acc.l[rt]);
     const int row = (wave * RT + rt) * 16 + li;
-    if (row >= rows) continue;
+    if (row >= rows || nstage == 0) continue;  // nstage == 0: no such split
     if (nsplit == 1) {
       const int t = row / G, gg = row % G;
       T* o = static_cast<T*>(a.out) + ((size_t(b) * K + t) * a.Hq + j * G + gg) * D;
