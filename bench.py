@@ -46,6 +46,7 @@ def parse():
     p.add_argument("--no-sweep", action="store_true")
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--no-flush", action="store_true")
+    p.add_argument("--no-probe", action="store_true", help="skip the stream-read bandwidth probe")
     p.add_argument("--sweep", default="1,2,4,8,16,32,64,128")
     p.add_argument("--calib-copy", action="store_true",
                    help="also launch a plain 1 GiB device copy (counter calibration under rocprofv3)")
@@ -150,6 +151,30 @@ def measure(w, inp, args, torch, flush, with_parts=True):
 # counters (traffic) from the committed rocprofv3 summary, if still current
 # ----------------------------------------------------------------------------
 
+def stream_read_probe(torch, gib=4, reps=6):
+    """Sustained HBM read bandwidth of this GPU (hspec_probe_stream_read over a
+    buffer far larger than L2 and the Infinity Cache), median of reps runs."""
+    import numpy as np
+    from hybrid_mamba_attention_amd import ops
+    print("[bench] stream-read probe", file=sys.stderr, flush=True)
+    buf = torch.zeros(gib << 30, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ts = []
+    for i in range(reps + 1):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        ops.stream_read_probe(buf, sink)
+        e1.record()
+        torch.cuda.synchronize()
+        if i:
+            ts.append(e0.elapsed_time(e1))
+    nbytes = buf.numel()
+    del buf
+    torch.cuda.empty_cache()
+    ms = float(np.median(ts))
+    return dict(bytes=nbytes, ms=ms, gbs=nbytes / (ms * 1e-3) / 1e9)
+
+
 def kernel_source_hash():
     h = hashlib.sha256()
     for f in ("attention.hip", "common.h", "kernels.h"):
@@ -236,6 +261,7 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    probe = None if args.no_probe else stream_read_probe(torch)
     w = wl.WORKLOADS[args.workload]
     print(f"[bench] drawing inputs for {w.name}", file=sys.stderr, flush=True)
     inp = wl.make_inputs(w)
@@ -279,6 +305,8 @@ def main():
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": "k_block_attn"},
     }
+    if probe is not None:
+        line["stream_read_probe"] = dict(probe, attention_frac_of_probe=achieved / probe["gbs"])
     if not args.no_sweep:
         sweep = {}
         for C in [int(c) for c in args.sweep.split(",")]:

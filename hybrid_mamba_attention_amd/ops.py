@@ -289,3 +289,16 @@ class DraftLayer:
 def draft_layer(**kw):
     """One drafter-layer call; returns the DraftLayer holding h0, y, h_final, out."""
     return DraftLayer(**kw)()
+
+
+# ---------------------------------------------------------------------------
+# measurement aid (include/hspec_probe.h)
+# ---------------------------------------------------------------------------
+
+def stream_read_probe(buf: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
+    """Enqueue one nontemporal streaming read of all of `buf` (see hspec_probe.h)."""
+    L = lib()
+    f = L.hspec_probe_stream_read
+    f.restype = _i
+    f.argtypes = [_vp, _vp, _sz, _vp]
+    _check("hspec_probe_stream_read", f(_stream(stream), _ptr(buf), buf.numel() * buf.element_size(), _ptr(sink)))

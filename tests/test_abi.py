@@ -10,22 +10,24 @@ import pytest
 from hybrid_mamba_attention_amd import ops
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "hspec.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("hspec.h", "hspec_probe.h")]
 OK, INVALID, UNSUPPORTED, WORKSPACE = 0, -1, -2, -3
 FAKE = 1 << 20   # aligned, never dereferenced on the host (validation fails or size query)
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(hspec_[a-z_0-9]+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(hspec_[a-z_0-9]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_loads_and_exports_every_declared_symbol():
     L = ops.lib()
     names = declared_functions()
     assert {"hspec_init_state", "hspec_ssd_scan", "hspec_block_attn_inplace",
-            "hspec_draft_layer"} <= set(names)
+            "hspec_draft_layer", "hspec_probe_stream_read"} <= set(names)
     for n in names:
         assert hasattr(L, n), f"{n} declared in hspec.h but not exported"
     assert L.hspec_abi_version() == 1
@@ -97,3 +99,13 @@ def test_attention_workspace_query():
     assert code1 == OK and n1 == 256
     # a real (non-NULL) workspace that is too small is refused before any launch
     assert _attn(ws=FAKE, nbytes=n - 1, split=32)[0] == WORKSPACE
+
+
+def test_probe_validation():
+    f = ops.lib().hspec_probe_stream_read
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    assert f(None, FAKE, 0, FAKE) == INVALID
+    assert f(None, FAKE, 100, FAKE) == INVALID          # not a multiple of 16
+    assert f(None, FAKE + 8, 1 << 20, FAKE) == INVALID  # misaligned
+    assert f(None, None, 1 << 20, FAKE) == INVALID
