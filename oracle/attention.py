@@ -17,6 +17,10 @@ a token that should be valid, raises PoisonedRead.  The workloads fill spare
 pages and the tail slots past ctx_b with NaN, so reading the wrong page or the
 wrong slot cannot go unnoticed.
 
+Block-causal variant (block_causal=True): block query t sees every context
+key and the block keys s <= t only (mask inside the block); the no-mask form
+above is the default reading.
+
 block_attention is the definition.  block_attention_splits restates it as
 split-KV: each split of the plan yields a partial (running max m, sum l,
 unnormalised output); partials merge as
@@ -59,8 +63,19 @@ def _scale(D, scale):
     return 1.0 / np.sqrt(D) if not scale else float(scale)
 
 
+def block_mask(K: int, G: int, ctx: int, block_causal: bool) -> np.ndarray:
+    """Visibility [K*G, ctx+K] of the keys to the query rows (row r is block
+    position r // G): all True, except block keys s > t when block_causal."""
+    vis = np.ones((K * G, ctx + K), dtype=bool)
+    if block_causal:
+        t = np.arange(K * G)[:, None] // G
+        s = np.arange(K)[None, :]
+        vis[:, ctx:] = s <= t
+    return vis
+
+
 def block_attention(q, k_blk, v_blk, k_cache, v_cache, page_table, ctx_lens, *,
-                    dtype: str, scale=None, requests=None) -> np.ndarray:
+                    dtype: str, scale=None, requests=None, block_causal=False) -> np.ndarray:
     """Brute-force attention over (context read through the page table) + block.
 
     q [C,K,Hq,D], k_blk/v_blk [C,K,Hkv,D] and the caches in stored form.
@@ -81,6 +96,7 @@ def block_attention(q, k_blk, v_blk, k_cache, v_cache, page_table, ctx_lens, *,
             vall = np.concatenate([gather_context(v_cache, page_table[b], ctx_lens[b], j, dtype), vb[:, j]])
             qj = qb[:, j * G:(j + 1) * G, :].reshape(K * G, D)
             s = sc * (qj @ kall.T)                                     # [K*G, ctx+K]
+            s = np.where(block_mask(K, G, int(ctx_lens[b]), block_causal), s, -np.inf)
             s = s - s.max(axis=1, keepdims=True)
             p = np.exp(s)
             p /= p.sum(axis=1, keepdims=True)
@@ -88,8 +104,9 @@ def block_attention(q, k_blk, v_blk, k_cache, v_cache, page_table, ctx_lens, *,
     return out
 
 
-def split_partials(qj, kall, vall, sc, bounds):
-    """Partials (m [R], l [R], O [R,D]) of query rows qj over key ranges `bounds`."""
+def split_partials(qj, kall, vall, sc, bounds, vis=None):
+    """Partials (m [R], l [R], O [R,D]) of query rows qj over key ranges `bounds`;
+    vis [R, keys] (optional) hides keys from rows."""
     parts = []
     for lo, hi in bounds:
         R = qj.shape[0]
@@ -97,6 +114,8 @@ def split_partials(qj, kall, vall, sc, bounds):
             parts.append((np.full(R, -np.inf), np.zeros(R), np.zeros((R, vall.shape[1]))))
             continue
         s = sc * (qj @ kall[lo:hi].T)
+        if vis is not None:
+            s = np.where(vis[:, lo:hi], s, -np.inf)
         m = s.max(axis=1)
         p = np.exp(s - m[:, None])
         parts.append((m, p.sum(axis=1), p @ vall[lo:hi]))
@@ -114,7 +133,7 @@ def merge_partials(parts):
 
 
 def block_attention_splits(q, k_blk, v_blk, k_cache, v_cache, page_table, ctx_lens, pps, *,
-                           dtype: str, scale=None, requests=None) -> np.ndarray:
+                           dtype: str, scale=None, requests=None, block_causal=False) -> np.ndarray:
     """Split-KV restatement of block_attention: pps context pages per split,
     block keys in the last split, partials merged as in the module docstring."""
     C, K, Hq, D = q.shape
@@ -137,6 +156,7 @@ def block_attention_splits(q, k_blk, v_blk, k_cache, v_cache, page_table, ctx_le
             kall = np.concatenate([gather_context(k_cache, page_table[b], ctx, j, dtype), kb[:, j]])
             vall = np.concatenate([gather_context(v_cache, page_table[b], ctx, j, dtype), vb[:, j]])
             qj = qb[:, j * G:(j + 1) * G, :].reshape(K * G, D)
-            o = merge_partials(split_partials(qj, kall, vall, sc, bounds))
+            vis = block_mask(K, G, ctx, block_causal)
+            o = merge_partials(split_partials(qj, kall, vall, sc, bounds, vis))
             out[b, :, j * G:(j + 1) * G, :] = o.reshape(K, G, D)
     return out

@@ -209,3 +209,51 @@ def test_merge_is_overflow_safe():
     p = np.exp(s - s.max(1, keepdims=True))
     assert np.isfinite(o).all()
     _close(o, (p / p.sum(1, keepdims=True)) @ vall)
+
+
+# ---------------------------------------------------------------------------
+# block-causal variant: block query t sees the context and block keys s <= t
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("ctx_lens,Hkv,G,K", [([37, 16, 5], 2, 2, 4), ([0, 20], 2, 4, 3), ([64], 1, 1, 5)])
+def test_block_causal_matches_torch_sdpa_with_mask(ctx_lens, Hkv, G, K):
+    D = 8
+    d = _paged(ctx_lens, Hkv, D, seed=sum(ctx_lens) + 31 * G + K, Hq=G * Hkv, K=K)
+    o = _run(d, block_causal=True)
+    for b, c in enumerate(ctx_lens):
+        kall = np.concatenate([d["kctx"][b], d["k_blk"][b]])
+        vall = np.concatenate([d["vctx"][b], d["v_blk"][b]])
+        allowed = torch.ones(K, c + K, dtype=torch.bool)
+        for t in range(K):
+            allowed[t, c + t + 1:] = False              # later block positions are hidden
+        qt = torch.from_numpy(d["q"][b].astype(np.float64)).permute(1, 0, 2)[None]
+        kt = torch.from_numpy(kall.astype(np.float64)).permute(1, 0, 2).repeat_interleave(G, 0)[None]
+        vt = torch.from_numpy(vall.astype(np.float64)).permute(1, 0, 2).repeat_interleave(G, 0)[None]
+        ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=allowed)
+        _close(o[b], ref[0].permute(1, 0, 2).numpy())
+
+
+def test_block_causal_with_one_position_is_the_unmasked_form():
+    d = _paged([40, 0, 17], 2, 8, seed=12, K=1)
+    _close(_run(d, block_causal=True), _run(d), 0.0)
+
+
+def test_block_causal_ignores_later_block_keys():
+    d = _paged([30, 5], 2, 8, seed=13, K=5)
+    o = _run(d, block_causal=True)
+    e = {k: (v.copy() if isinstance(v, np.ndarray) else v) for k, v in d.items()}
+    e["k_blk"][:, 3:] += 2.0
+    e["v_blk"][:, 3:] -= 1.5
+    o2 = _run(e, block_causal=True)
+    assert np.array_equal(o[:, :3], o2[:, :3])           # positions 0..2 never see keys 3, 4
+    assert not np.allclose(o[:, 3:], o2[:, 3:])
+    assert not np.allclose(_run(d)[:, :3], _run(e)[:, :3])  # the unmasked form does
+
+
+@pytest.mark.parametrize("pps", [1, 3, 1000])
+def test_block_causal_split_invariance(pps):
+    d = _paged([100, 0, 16, 33], 2, 8, seed=14, K=6)
+    ref = _run(d, block_causal=True)
+    o = oracle.block_attention_splits(d["q"], d["k_blk"], d["v_blk"], d["k_cache"], d["v_cache"],
+                                      d["page_table"], d["ctx_lens"], pps, dtype="f32", block_causal=True)
+    _close(o, ref)
