@@ -47,6 +47,8 @@ def parse():
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--no-flush", action="store_true")
     p.add_argument("--no-probe", action="store_true", help="skip the stream-read bandwidth probe")
+    p.add_argument("--no-variants", action="store_true",
+                   help="skip the block-causal and direct-reuse-only layer timings")
     p.add_argument("--sweep", default="1,2,4,8,16,32,64,128")
     p.add_argument("--calib-copy", action="store_true",
                    help="also launch a plain 1 GiB device copy (counter calibration under rocprofv3)")
@@ -64,16 +66,18 @@ def dev(arr, torch):
     return torch.from_numpy(np.ascontiguousarray(arr)).cuda()
 
 
-def build_layer(inp, kv_split_pages, torch):
+def build_layer(inp, kv_split_pages, torch, block_causal=False, no_init=False):
+    """The layer of a workload; no_init: direct-reuse-only ablation (no state projection)."""
     from hybrid_mamba_attention_amd import ops
     a = inp.arrays
     w = inp.w
     t = {k: dev(v, torch) for k, v in a.items()}
     return ops.DraftLayer(
-        u=t["u"], w_init=t["w_init"], x=t["x"], delta=t["delta"], A=t["A"], B=t["B"], Cm=t["Cm"],
+        u=None if no_init else t["u"], w_init=None if no_init else t["w_init"], x=t["x"],
+        delta=t["delta"], A=t["A"], B=t["B"], Cm=t["Cm"],
         chunk=w.chunk, q=t["q"], k_blk=t["k_blk"], v_blk=t["v_blk"], k_cache=t["k_cache"],
         v_cache=t["v_cache"], page_table=dev(inp.page_table, torch), ctx_lens=dev(inp.ctx_lens, torch),
-        max_ctx=inp.max_ctx, kv_split_pages=kv_split_pages), t
+        max_ctx=inp.max_ctx, kv_split_pages=kv_split_pages, block_causal=block_causal), t
 
 
 def timed(fn, steps, warmup, flush, torch):
@@ -145,6 +149,18 @@ def measure(w, inp, args, torch, flush, with_parts=True):
     del layer, t
     torch.cuda.empty_cache()
     return res
+
+
+def measure_variants(w, inp, args, torch, flush):
+    """The layer with the block-causal mask, and the direct-reuse-only ablation."""
+    out = {}
+    for name, kw in (("block_causal", dict(block_causal=True)), ("direct_reuse_only", dict(no_init=True))):
+        layer, t = build_layer(inp, args.kv_split_pages, torch, **kw)
+        st = stats(timed(layer, args.steps, args.warmup, flush, torch))
+        out[name] = dict(ms_per_step=st["mean"], block_tokens_per_s=w.C * w.K / (st["mean"] * 1e-3))
+        del layer, t
+        torch.cuda.empty_cache()
+    return out
 
 
 # ----------------------------------------------------------------------------
@@ -307,6 +323,9 @@ def main():
     }
     if probe is not None:
         line["stream_read_probe"] = dict(probe, attention_frac_of_probe=achieved / probe["gbs"])
+    if not args.no_variants:
+        print("[bench] timing the layer variants", file=sys.stderr, flush=True)
+        line["variants"] = measure_variants(w, inp, args, torch, flush)
     if not args.no_sweep:
         sweep = {}
         for C in [int(c) for c in args.sweep.split(",")]:

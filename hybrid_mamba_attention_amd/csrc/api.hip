@@ -95,7 +95,8 @@ AttnPlanShape plan_shape(int C, int K, int Hq, int Hkv, int D, int max_ctx, int 
 int check_attn(int dtype, int C, int K, int Hq, int Hkv, int D, const void* q, const void* kb,
                const void* vb, const void* kc, const void* vc, int64_t ps, int64_t ts, int64_t hs,
                int num_pages, const int32_t* pt, int max_pages, const int32_t* ctx, int max_ctx,
-               int kv_split_pages, float scale, const void* out, const size_t* ws_bytes) {
+               int kv_split_pages, float scale, int block_causal, const void* out,
+               const size_t* ws_bytes) {
   if (!dtype_ok(dtype) || C < 1 || K < 1 || Hq < 1 || Hkv < 1) return HSPEC_ERR_INVALID_ARG;
   if (Hq % Hkv) return HSPEC_ERR_INVALID_ARG;
   if (!q || !kb || !vb || !kc || !vc || !pt || !ctx || !out || !ws_bytes) return HSPEC_ERR_INVALID_ARG;
@@ -108,6 +109,7 @@ int check_attn(int dtype, int C, int K, int Hq, int Hkv, int D, const void* q, c
   if (num_pages < 1 || max_ctx < 0 || kv_split_pages < 0) return HSPEC_ERR_INVALID_ARG;
   if (int64_t(max_pages) < std::max<int64_t>(1, (int64_t(max_ctx) + 15) / 16)) return HSPEC_ERR_INVALID_ARG;
   if (!(scale >= 0.f) || !std::isfinite(scale)) return HSPEC_ERR_INVALID_ARG;
+  if (block_causal != 0 && block_causal != 1) return HSPEC_ERR_INVALID_ARG;
   if (D != 64 && D != 128) return HSPEC_ERR_UNSUPPORTED;
   if (K > 64) return HSPEC_ERR_UNSUPPORTED;
   if (int64_t(Hq / Hkv) * K > 256) return HSPEC_ERR_UNSUPPORTED;
@@ -120,7 +122,8 @@ int check_attn(int dtype, int C, int K, int Hq, int Hkv, int D, const void* q, c
 int run_attn(hipStream_t st, int dtype, int C, int K, int Hq, int Hkv, int D, const void* q,
              const void* kb, const void* vb, const void* kc, const void* vc, int64_t ps, int64_t ts,
              int64_t hs, int num_pages, const int32_t* pt, int max_pages, const int32_t* ctx,
-             int max_ctx, int kv_split_pages, float scale, void* out, void* ws, size_t ws_bytes) {
+             int max_ctx, int kv_split_pages, float scale, int block_causal, void* out, void* ws,
+             size_t ws_bytes) {
   const AttnPlanShape p = plan_shape(C, K, Hq, Hkv, D, max_ctx, kv_split_pages);
   if (!ws || !aligned(ws, 256) || ws_bytes < p.total) return HSPEC_ERR_WORKSPACE;
   AttnArgs a{};
@@ -139,6 +142,7 @@ int run_attn(hipStream_t st, int dtype, int C, int K, int Hq, int Hkv, int D, co
   a.max_items = p.M;
   a.pps = p.pps;
   a.max_splits = p.MS;
+  a.block_causal = block_causal;
   return status_of(launch_block_attn(st, dtype, a));
 }
 
@@ -183,11 +187,11 @@ int hspec_block_attn_inplace(void* stream, int dtype, int C, int K, int Hq, int 
                              const void* k_cache, const void* v_cache, int64_t page_stride,
                              int64_t token_stride, int64_t head_stride, int num_pages,
                              const int32_t* page_table, int max_pages, const int32_t* ctx_lens,
-                             int max_ctx, int kv_split_pages, float scale, void* out,
-                             void* workspace, size_t* workspace_bytes) {
+                             int max_ctx, int kv_split_pages, float scale, int block_causal,
+                             void* out, void* workspace, size_t* workspace_bytes) {
   const int st = check_attn(dtype, C, K, Hq, Hkv, D, q, k_blk, v_blk, k_cache, v_cache, page_stride,
                             token_stride, head_stride, num_pages, page_table, max_pages, ctx_lens,
-                            max_ctx, kv_split_pages, scale, out, workspace_bytes);
+                            max_ctx, kv_split_pages, scale, block_causal, out, workspace_bytes);
   if (st != HSPEC_OK) return st;
   if (!workspace) {
     *workspace_bytes = plan_shape(C, K, Hq, Hkv, D, max_ctx, kv_split_pages).total;
@@ -195,7 +199,7 @@ int hspec_block_attn_inplace(void* stream, int dtype, int C, int K, int Hq, int 
   }
   return run_attn(static_cast<hipStream_t>(stream), dtype, C, K, Hq, Hkv, D, q, k_blk, v_blk,
                   k_cache, v_cache, page_stride, token_stride, head_stride, num_pages, page_table,
-                  max_pages, ctx_lens, max_ctx, kv_split_pages, scale, out, workspace,
+                  max_pages, ctx_lens, max_ctx, kv_split_pages, scale, block_causal, out, workspace,
                   *workspace_bytes);
 }
 
@@ -206,13 +210,17 @@ int hspec_draft_layer(void* stream, const hspec_layer_args* a, size_t* required_
   if (st != HSPEC_OK) return st;
   if (int64_t(a->H) * a->P * a->N > 0x7fffffff) return HSPEC_ERR_UNSUPPORTED;
   const int S = a->H * a->P * a->N;
-  st = check_init(a->dtype, a->C, a->d_model, S, a->u, a->w_init, a->h0);
-  if (st != HSPEC_OK) return st;
+  // u and w_init both NULL: the direct-reuse-only ablation (no a1, zero state)
+  const bool no_init = !a->u && !a->w_init;
+  if (!no_init) {
+    st = check_init(a->dtype, a->C, a->d_model, S, a->u, a->w_init, a->h0);
+    if (st != HSPEC_OK) return st;
+  }
   size_t dummy = 0;
   st = check_attn(a->dtype, a->C, a->K, a->Hq, a->Hkv, a->D, a->q, a->k_blk, a->v_blk, a->k_cache,
                   a->v_cache, a->page_stride, a->token_stride, a->head_stride, a->num_pages,
                   a->page_table, a->max_pages, a->ctx_lens, a->max_ctx, a->kv_split_pages, a->scale,
-                  a->out, &dummy);
+                  a->block_causal, a->out, &dummy);
   if (st != HSPEC_OK) return st;
   const size_t need = plan_shape(a->C, a->K, a->Hq, a->Hkv, a->D, a->max_ctx, a->kv_split_pages).total;
   if (required_bytes) *required_bytes = need;
@@ -221,12 +229,14 @@ int hspec_draft_layer(void* stream, const hspec_layer_args* a, size_t* required_
   st = run_attn(s, a->dtype, a->C, a->K, a->Hq, a->Hkv, a->D, a->q, a->k_blk, a->v_blk, a->k_cache,
                 a->v_cache, a->page_stride, a->token_stride, a->head_stride, a->num_pages,
                 a->page_table, a->max_pages, a->ctx_lens, a->max_ctx, a->kv_split_pages, a->scale,
-                a->out, a->workspace, a->workspace_bytes);
+                a->block_causal, a->out, a->workspace, a->workspace_bytes);
   if (st != HSPEC_OK) return st;
-  InitArgs ia{a->u, a->w_init, a->h0, a->C, a->d_model, S};
-  st = status_of(launch_init_state(s, a->dtype, ia));
-  if (st != HSPEC_OK) return st;
-  SsdArgs sa{a->x, a->delta, a->A, a->B, a->Cm, a->Dskip, a->h0, a->y, a->h_final,
+  if (!no_init) {
+    InitArgs ia{a->u, a->w_init, a->h0, a->C, a->d_model, S};
+    st = status_of(launch_init_state(s, a->dtype, ia));
+    if (st != HSPEC_OK) return st;
+  }
+  SsdArgs sa{a->x, a->delta, a->A, a->B, a->Cm, a->Dskip, no_init ? nullptr : a->h0, a->y, a->h_final,
              a->C, a->K, a->H, a->P, a->ng, a->N, a->chunk};
   return status_of(launch_ssd_scan(s, a->dtype, sa));
 }

@@ -23,7 +23,9 @@
 //     are bank-conflict free.
 //   * The draft block's own K keys and values ("transient intra-block KV")
 //     are the last stages of the last split: they pass through the same LDS
-//     buffers and are never written anywhere.
+//     buffers and are never written anywhere.  With the block-causal mask,
+//     those stages also drop block key s for query rows at block position
+//     t < s; context pages are never masked.
 //   * S^T = K . Q^T on MFMA: lane l then holds the scores of query row l%16
 //     for tokens 4*(l/16)+r of each page, so a row's softmax statistics stay
 //     in the lane (two xor-shuffles give the row max, the sum is deferred).
@@ -288,9 +290,10 @@ __global__ __launch_bounds__(64 * NW) void k_block_attn(AttnArgs a) {
     const char* v;
     int n;     // valid tokens (0 = absent)
     bool blk;  // block page (token stride Hkv*D)
+    int cb;    // block-causal block page: 1 + its index among the block pages, else 0
   };
   auto page = [&](int vp) __attribute__((always_inline)) -> Page {
-    Page pg{kcj, vcj, 0, false};
+    Page pg{kcj, vcj, 0, false, 0};
     if (vp < ncache) {
       const int lp = p_lo + vp;
       const int phys = pt[lp];
@@ -306,6 +309,7 @@ __global__ __launch_bounds__(64 * NW) void k_block_attn(AttnArgs a) {
       pg.v = vblk + bp * blk_page_b;
       pg.n = min(16, K - bp * 16);
       pg.blk = true;
+      pg.cb = a.block_causal ? bp + 1 : 0;
     }
     return pg;
   };
@@ -351,8 +355,10 @@ __global__ __launch_bounds__(64 * NW) void k_block_attn(AttnArgs a) {
       return;
     }
     const Page p0 = page(2 * st), p1 = page(2 * st + 1);
-    nv[0] = p0.n;
-    nv[1] = p1.n;
+    // valid-token count, with the block-causal page index above bit 8: a
+    // stage is on the unmasked fast path exactly when both words equal 16
+    nv[0] = p0.n | (p0.cb << 8);
+    nv[1] = p1.n | (p1.cb << 8);
     // (each page spelled out: selecting between the two by reference would
     // keep the staging registers from being promoted out of memory)
 #pragma unroll
@@ -408,10 +414,16 @@ __global__ __launch_bounds__(64 * NW) void k_block_attn(AttnArgs a) {
       vpos[e][h] = Gm::pos(row, e0 / EPC) * 16 + (e0 % EPC) * sizeof(T);
     }
 
+  // Block position of each query row this lane scores (rows past G*K repeat
+  // the last row, as the query loads do).
+  int tq[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) tq[rt] = min((wave * RT + rt) * 16 + li, rows - 1) / G;
+
   auto compute = [&](int buf, const int (&nv)[2]) __attribute__((always_inline)) {
     const unsigned char* tk = sK + buf * TILE_B;
     const unsigned char* tv = sV + buf * TILE_B;
-    const bool partial = nv[0] < 16 || nv[1] < 16;
+    const bool partial = nv[0] != 16 || nv[1] != 16;
     Vec8<T> kop[2][DS];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
@@ -442,9 +454,18 @@ __global__ __launch_bounds__(64 * NW) void k_block_attn(AttnArgs a) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) sv[e] = sacc[e >> 2][e & 3];
       if (partial) {
+        // token 4*lg + (e&3) of page e>>2 is kept when it is one of the page's
+        // valid tokens and, on a block-causal block page with index cb-1, its
+        // block position 16*(cb-1) + token is at most this row's position
+        int lim[2];
+#pragma unroll
+        for (int pg = 0; pg < 2; ++pg) {
+          const int n = nv[pg] & 255, cb = nv[pg] >> 8;
+          lim[pg] = cb ? min(n, tq[rt] - 16 * (cb - 1) + 1) : n;
+        }
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-          if (4 * lg + (e & 3) >= nv[e >> 2]) sv[e] = -INFINITY;
+          if (4 * lg + (e & 3) >= lim[e >> 2]) sv[e] = -INFINITY;
       }
       const float mx = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), sv[2]),
                              fmaxf(fmaxf(sv[3], sv[4]), fmaxf(fmaxf(sv[5], sv[6]), sv[7])));

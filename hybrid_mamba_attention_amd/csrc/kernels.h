@@ -27,6 +27,7 @@ struct AttnArgs {
   float* part_ml;                 // [max_items, Hkv, rows, 2]
   int max_items;                  // C * max_splits
   int pps, max_splits;            // context pages per split; splits of a max_ctx request
+  int block_causal;               // 1: block query t sees block keys s <= t only
 };
 
 // a0 + a3 + a4 on `st`.

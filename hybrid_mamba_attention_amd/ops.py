@@ -36,7 +36,7 @@ class LayerArgs(ctypes.Structure):
         ("page_stride", _i64), ("token_stride", _i64), ("head_stride", _i64),
         ("num_pages", _i), ("page_table", _vp), ("max_pages", _i),
         ("ctx_lens", _vp), ("max_ctx", _i),
-        ("kv_split_pages", _i), ("scale", _f), ("out", _vp),
+        ("kv_split_pages", _i), ("scale", _f), ("block_causal", _i), ("out", _vp),
         ("workspace", _vp), ("workspace_bytes", _sz),
     ]
 
@@ -63,11 +63,11 @@ def lib() -> ctypes.CDLL:
     L.hspec_ssd_scan.argtypes = [_vp, _i] + [_i] * 7 + [_vp] * 9
     L.hspec_block_attn_inplace.restype = _i
     L.hspec_block_attn_inplace.argtypes = ([_vp, _i, _i, _i, _i, _i, _i] + [_vp] * 5 +
-                                           [_i64, _i64, _i64, _i, _vp, _i, _vp, _i, _i, _f, _vp,
-                                            _vp, ctypes.POINTER(_sz)])
+                                           [_i64, _i64, _i64, _i, _vp, _i, _vp, _i, _i, _f, _i,
+                                            _vp, _vp, ctypes.POINTER(_sz)])
     L.hspec_draft_layer.restype = _i
     L.hspec_draft_layer.argtypes = [_vp, ctypes.POINTER(LayerArgs), ctypes.POINTER(_sz)]
-    if L.hspec_abi_version() != 1:
+    if L.hspec_abi_version() != 2:
         raise RuntimeError("libhspec.so ABI version mismatch")
     if L.hspec_layer_args_size() != ctypes.sizeof(LayerArgs):
         raise RuntimeError("hspec_layer_args layout mismatch between library and binding")
@@ -174,7 +174,7 @@ def kv_strides(k_cache: torch.Tensor, layout: str = "NHD"):
 
 
 def _attn_call(L, stream, q, k_blk, v_blk, k_cache, v_cache, page_table, ctx_lens, max_ctx,
-               kv_split_pages, scale, out, ws, ws_bytes, layout):
+               kv_split_pages, scale, block_causal, out, ws, ws_bytes, layout):
     C, K, Hq, D = q.shape
     Hkv = k_blk.shape[2]
     ps, ts, hs = kv_strides(k_cache, layout)
@@ -184,24 +184,25 @@ def _attn_call(L, stream, q, k_blk, v_blk, k_cache, v_cache, page_table, ctx_len
         stream, _dtype_code(q), C, K, Hq, Hkv, D, _ptr(q), _ptr(k_blk), _ptr(v_blk),
         _ptr(k_cache), _ptr(v_cache), ps, ts, hs, k_cache.shape[0], _ptr(page_table),
         page_table.shape[1], _ptr(ctx_lens), int(max_ctx), int(kv_split_pages), float(scale),
-        _ptr(out), ws, ctypes.byref(ws_bytes))
+        int(bool(block_causal)), _ptr(out), ws, ctypes.byref(ws_bytes))
 
 
 def attn_workspace_bytes(q, k_blk, v_blk, k_cache, v_cache, page_table, ctx_lens, *, max_ctx,
-                         kv_split_pages=0, scale=0.0, layout="NHD") -> int:
+                         kv_split_pages=0, scale=0.0, block_causal=False, layout="NHD") -> int:
     n = _sz(0)
     out = torch.empty(1, dtype=q.dtype, device=q.device)  # never written by a size query
     _check("hspec_block_attn_inplace", _attn_call(
         lib(), _stream(None), q, k_blk, v_blk, k_cache, v_cache, page_table, ctx_lens, max_ctx,
-        kv_split_pages, scale, out, None, n, layout))
+        kv_split_pages, scale, block_causal, out, None, n, layout))
     return n.value
 
 
 def block_attn_inplace(q, k_blk, v_blk, k_cache, v_cache, page_table, ctx_lens, *, max_ctx,
-                       kv_split_pages=0, scale=0.0, out=None, workspace=None, layout="NHD",
-                       stream=None):
+                       kv_split_pages=0, scale=0.0, block_causal=False, out=None, workspace=None,
+                       layout="NHD", stream=None):
     """out[C,K,Hq,D] = attention of the block queries over paged target KV + block KV.
 
+    block_causal: block query t sees block keys s <= t only (context keys all).
     workspace: a uint8 CUDA tensor of at least attn_workspace_bytes(...) bytes
     (allocated here if None).  Returns (out, workspace)."""
     _contig(q, k_blk, v_blk, page_table, ctx_lens, out)
@@ -213,12 +214,12 @@ def block_attn_inplace(q, k_blk, v_blk, k_cache, v_cache, page_table, ctx_lens, 
     if workspace is None:
         nbytes = attn_workspace_bytes(q, k_blk, v_blk, k_cache, v_cache, page_table, ctx_lens,
                                       max_ctx=max_ctx, kv_split_pages=kv_split_pages, scale=scale,
-                                      layout=layout)
+                                      block_causal=block_causal, layout=layout)
         workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q.device)
     n = _sz(workspace.numel())
     _check("hspec_block_attn_inplace", _attn_call(
         L, _stream(stream), q, k_blk, v_blk, k_cache, v_cache, page_table, ctx_lens, max_ctx,
-        kv_split_pages, scale, out, _ptr(workspace), n, layout))
+        kv_split_pages, scale, block_causal, out, _ptr(workspace), n, layout))
     return out, workspace
 
 
@@ -228,29 +229,36 @@ def block_attn_inplace(q, k_blk, v_blk, k_cache, v_cache, page_table, ctx_lens, 
 
 class DraftLayer:
     """Holds the marshalled argument block of one drafter-layer configuration so
-    that repeated calls (benchmarks, serving loops) only re-issue the C call."""
+    that repeated calls (benchmarks, serving loops) only re-issue the C call.
+
+    u = w_init = None is the direct-reuse-only ablation: no state projection,
+    the scan starts from the zero state and h0 stays None."""
 
     def __init__(self, *, u, w_init, x, delta, A, B, Cm, chunk, q, k_blk, v_blk, k_cache, v_cache,
-                 page_table, ctx_lens, max_ctx, kv_split_pages=0, scale=0.0, Dskip=None,
-                 want_final=False, layout="NHD"):
+                 page_table, ctx_lens, max_ctx, kv_split_pages=0, scale=0.0, block_causal=False,
+                 Dskip=None, want_final=False, layout="NHD"):
         _contig(u, w_init, x, delta, A, B, Cm, q, k_blk, v_blk, page_table, ctx_lens, Dskip)
-        dev = u.device
-        C, d = u.shape
-        _, K, H, P = x.shape
+        if (u is None) != (w_init is None):
+            raise ValueError("u and w_init are given together (or both None for the ablation)")
+        dev = x.device
+        C, K, H, P = x.shape
+        d = u.shape[1] if u is not None else 0
         ng, N = B.shape[2], B.shape[3]
         _, _, Hq, D = q.shape
         Hkv = k_blk.shape[2]
-        self.h0 = torch.empty((C, H * P * N), dtype=torch.float32, device=dev)
+        self.h0 = (torch.empty((C, H * P * N), dtype=torch.float32, device=dev)
+                   if u is not None else None)
         self.y = torch.empty((C, K, H, P), dtype=torch.float32, device=dev)
         self.h_final = (torch.empty((C, H, P, N), dtype=torch.float32, device=dev)
                         if want_final else None)
         self.out = torch.empty_like(q)
         ps, ts, hs = kv_strides(k_cache, layout)
         a = LayerArgs()
-        a.dtype = _dtype_code(u)
+        a.dtype = _dtype_code(x)
         a.C, a.K = C, K
         a.d_model, a.H, a.P, a.ng, a.N, a.chunk = d, H, P, ng, N, chunk
-        a.u, a.w_init, a.h0 = u.data_ptr(), w_init.data_ptr(), self.h0.data_ptr()
+        if u is not None:
+            a.u, a.w_init, a.h0 = u.data_ptr(), w_init.data_ptr(), self.h0.data_ptr()
         a.x, a.delta, a.A = x.data_ptr(), delta.data_ptr(), A.data_ptr()
         a.B, a.Cm = B.data_ptr(), Cm.data_ptr()
         a.Dskip = Dskip.data_ptr() if Dskip is not None else None
@@ -264,6 +272,7 @@ class DraftLayer:
         a.page_table, a.max_pages = page_table.data_ptr(), page_table.shape[1]
         a.ctx_lens, a.max_ctx = ctx_lens.data_ptr(), int(max_ctx)
         a.kv_split_pages, a.scale = int(kv_split_pages), float(scale)
+        a.block_causal = int(bool(block_causal))
         a.out = self.out.data_ptr()
         a.workspace, a.workspace_bytes = None, 0
         need = _sz(0)

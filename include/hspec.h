@@ -48,7 +48,7 @@ typedef enum {
 const char* hspec_status_string(int status);
 
 /* ABI version of this header; bumped on any incompatible change. */
-#define HSPEC_ABI_VERSION 1
+#define HSPEC_ABI_VERSION 2
 int hspec_abi_version(void);
 
 /*
@@ -105,6 +105,11 @@ int hspec_ssd_scan(void* stream, int dtype, int C, int K, int H, int P, int ng, 
  *   keys   = Kc[page_table[b][n/16], n%16, j] (n < ctx_lens[b])  ++  k_blk[b, :, j]
  *   out[b, :, i] = softmax(scale * q[b, :, i] @ keys^T) @ values
  *
+ * block_causal = 1 selects the block-causal variant instead (the pages fix
+ * no mask; this is the masked alternative, with the mask applied only among
+ * the block keys): block query t then sees every context key and the block
+ * keys s <= t.  0 is the mask-free form above; any other value is INVALID.
+ *
  *   q            act [C, K, Hq, D]
  *   k_blk, v_blk act [C, K, Hkv, D]   the block's own keys / values (transient)
  *   k_cache,     act pools, read only; element (page, slot, j, d) sits at
@@ -144,7 +149,7 @@ int hspec_block_attn_inplace(void* stream, int dtype, int C, int K, int Hq, int 
                              int64_t page_stride, int64_t token_stride, int64_t head_stride,
                              int num_pages, const int32_t* page_table, int max_pages,
                              const int32_t* ctx_lens, int max_ctx,
-                             int kv_split_pages, float scale, void* out,
+                             int kv_split_pages, float scale, int block_causal, void* out,
                              void* workspace, size_t* workspace_bytes);
 
 /*
@@ -153,6 +158,11 @@ int hspec_block_attn_inplace(void* stream, int dtype, int C, int K, int Hq, int 
  * H-Spec, Abstract: the two kinds of target context (last-token hidden
  * state, in-place target KV) enter through the two complementary modules.
  * `h0` is written by a1 and read by a2; `h_final` and `Dskip` may be NULL.
+ * `u` and `w_init` both NULL select the direct-reuse-only ablation (H-Spec,
+ * Section 3.1 / Figure 4 and the source ablation of Figure 7a: target KV
+ * reused in place with no hidden-state initialisation): a1 is skipped,
+ * a2 starts from the zero state and `h0` is neither read nor written (it may
+ * be NULL).  Exactly one of them NULL is INVALID_ARG.
  * `workspace` == NULL is a size query exactly as for a3.
  */
 typedef struct hspec_layer_args {
@@ -170,7 +180,7 @@ typedef struct hspec_layer_args {
   int64_t page_stride, token_stride, head_stride;
   int num_pages; const int32_t* page_table; int max_pages;
   const int32_t* ctx_lens; int max_ctx;
-  int kv_split_pages; float scale; void* out;
+  int kv_split_pages; float scale; int block_causal; void* out;
   void* workspace; size_t workspace_bytes;
 } hspec_layer_args;
 

@@ -50,19 +50,23 @@ def assert_close(got, want, dtype: str, what: str):
     return rel, mx
 
 
-def layer_from_inputs(inp, *, kv_split_pages=0, want_final=True, with_dskip=False):
-    """Build and run one drafter-layer call on the GPU for a workload's inputs."""
+def layer_from_inputs(inp, *, kv_split_pages=0, want_final=True, with_dskip=False,
+                      block_causal=False, no_init=False):
+    """Build and run one drafter-layer call on the GPU for a workload's inputs
+    (no_init: the direct-reuse-only ablation, u = w_init = None)."""
     from hybrid_mamba_attention_amd import ops
     w, a = inp.w, inp.arrays
     dt = w.dtype
     layer = ops.DraftLayer(
-        u=to_dev(a["u"], dt), w_init=to_dev(a["w_init"], dt), x=to_dev(a["x"], dt),
+        u=None if no_init else to_dev(a["u"], dt),
+        w_init=None if no_init else to_dev(a["w_init"], dt), x=to_dev(a["x"], dt),
         delta=to_dev(a["delta"], dt), A=to_dev(a["A"], dt), B=to_dev(a["B"], dt),
         Cm=to_dev(a["Cm"], dt), chunk=w.chunk, q=to_dev(a["q"], dt), k_blk=to_dev(a["k_blk"], dt),
         v_blk=to_dev(a["v_blk"], dt), k_cache=to_dev(a["k_cache"], dt),
         v_cache=to_dev(a["v_cache"], dt), page_table=to_dev(inp.page_table, dt),
         ctx_lens=to_dev(inp.ctx_lens, dt), max_ctx=inp.max_ctx, kv_split_pages=kv_split_pages,
-        Dskip=to_dev(a["Dskip"], dt) if with_dskip else None, want_final=want_final)
+        block_causal=block_causal, Dskip=to_dev(a["Dskip"], dt) if with_dskip else None,
+        want_final=want_final)
     layer()
     torch.cuda.synchronize()
     return layer

@@ -30,7 +30,7 @@ def test_loads_and_exports_every_declared_symbol():
             "hspec_draft_layer", "hspec_probe_stream_read"} <= set(names)
     for n in names:
         assert hasattr(L, n), f"{n} declared in hspec.h but not exported"
-    assert L.hspec_abi_version() == 1
+    assert L.hspec_abi_version() == 2
     assert L.hspec_layer_args_size() == ctypes.sizeof(ops.LayerArgs)
     assert L.hspec_status_string(-2) == b"HSPEC_ERR_UNSUPPORTED"
 
@@ -68,19 +68,20 @@ def test_ssd_validation(kw, code):
 
 def _attn(ws=None, nbytes=0, **kw):
     a = dict(dtype=1, C=4, K=16, Hq=32, Hkv=8, D=128, ps=16 * 8 * 128, ts=8 * 128, hs=128,
-             num_pages=100, max_pages=64, max_ctx=1000, split=0, scale=0.0)
+             num_pages=100, max_pages=64, max_ctx=1000, split=0, scale=0.0, causal=0)
     a.update(kw)
     n = ctypes.c_size_t(nbytes)
     code = ops.lib().hspec_block_attn_inplace(
         None, a["dtype"], a["C"], a["K"], a["Hq"], a["Hkv"], a["D"], FAKE, FAKE, FAKE, FAKE, FAKE,
         a["ps"], a["ts"], a["hs"], a["num_pages"], FAKE, a["max_pages"], FAKE, a["max_ctx"],
-        a["split"], a["scale"], FAKE, ws, ctypes.byref(n))
+        a["split"], a["scale"], a["causal"], FAKE, ws, ctypes.byref(n))
     return code, n.value
 
 
 @pytest.mark.parametrize("kw,code", [
     (dict(Hq=30), INVALID), (dict(ts=100), INVALID), (dict(max_pages=10), INVALID),
     (dict(scale=-1.0), INVALID), (dict(split=-1), INVALID), (dict(K=0), INVALID),
+    (dict(causal=2), INVALID), (dict(causal=-1), INVALID),
     (dict(D=96), UNSUPPORTED), (dict(K=65), UNSUPPORTED), (dict(Hq=64, Hkv=2, K=16), UNSUPPORTED),
 ])
 def test_attention_validation(kw, code):
@@ -109,3 +110,32 @@ def test_probe_validation():
     assert f(None, FAKE, 100, FAKE) == INVALID          # not a multiple of 16
     assert f(None, FAKE + 8, 1 << 20, FAKE) == INVALID  # misaligned
     assert f(None, None, 1 << 20, FAKE) == INVALID
+
+
+def _layer(**kw):
+    """hspec_draft_layer size query (workspace NULL) with a valid bf16 shape."""
+    a = ops.LayerArgs()
+    a.dtype, a.C, a.K = 1, 4, 16
+    a.d_model, a.H, a.P, a.ng, a.N, a.chunk = 4096, 32, 64, 1, 64, 16
+    a.u = a.w_init = a.h0 = FAKE
+    a.x = a.delta = a.A = a.B = a.Cm = a.y = FAKE
+    a.Hq, a.Hkv, a.D = 32, 8, 128
+    a.q = a.k_blk = a.v_blk = a.k_cache = a.v_cache = a.page_table = a.ctx_lens = a.out = FAKE
+    a.page_stride, a.token_stride, a.head_stride = 16 * 8 * 128, 8 * 128, 128
+    a.num_pages, a.max_pages, a.max_ctx = 100, 64, 1000
+    for k, v in kw.items():
+        setattr(a, k, v)
+    n = ctypes.c_size_t(0)
+    return ops.lib().hspec_draft_layer(None, ctypes.byref(a), ctypes.byref(n)), n.value
+
+
+def test_layer_validation_and_ablation():
+    code, n = _layer()
+    assert code == OK and n > 0
+    # direct-reuse-only ablation: u and w_init both NULL, h0 may be NULL too
+    assert _layer(u=None, w_init=None, h0=None) == (OK, n)
+    assert _layer(u=None)[0] == INVALID
+    assert _layer(w_init=None)[0] == INVALID
+    assert _layer(h0=None)[0] == INVALID          # a1 runs and needs h0
+    assert _layer(block_causal=1) == (OK, n)
+    assert _layer(block_causal=3)[0] == INVALID

@@ -62,7 +62,7 @@ def make_attn_case(seed, ctx, K, Hq, Hkv, D, dtype, *, identity=False, q_scale=1
                 ctx_lens=np.array(ctx, np.int32), dtype=dtype)
 
 
-def run_attn(case, *, split=0, layout="NHD", out=None):
+def run_attn(case, *, split=0, layout="NHD", out=None, causal=False):
     dt = case["dtype"]
     t = {k: to_dev(case[k], dt) for k in ("q", "k_blk", "v_blk", "k_cache", "v_cache", "page_table", "ctx_lens")}
     kc, vc = t["k_cache"], t["v_cache"]
@@ -71,14 +71,16 @@ def run_attn(case, *, split=0, layout="NHD", out=None):
         vc = vc.permute(0, 2, 1, 3).contiguous()
     max_ctx = int(case["ctx_lens"].max())
     o, ws = ops.block_attn_inplace(t["q"], t["k_blk"], t["v_blk"], kc, vc, t["page_table"], t["ctx_lens"],
-                                   max_ctx=max_ctx, kv_split_pages=split, out=out, layout=layout)
+                                   max_ctx=max_ctx, kv_split_pages=split, out=out, layout=layout,
+                                   block_causal=causal)
     torch.cuda.synchronize()
     return o, ws, (kc, vc)
 
 
-def oracle_attn(case):
+def oracle_attn(case, causal=False):
     return oracle.block_attention(case["q"], case["k_blk"], case["v_blk"], case["k_cache"], case["v_cache"],
-                                  case["page_table"], case["ctx_lens"], dtype=case["dtype"])
+                                  case["page_table"], case["ctx_lens"], dtype=case["dtype"],
+                                  block_causal=causal)
 
 
 ATTN_CASES = [
@@ -103,6 +105,44 @@ def test_attention_shapes(name, ctx, K, Hq, Hkv, D, dtype):
     for split in (0, 1, 3):
         o, _, _ = run_attn(case, split=split)
         assert_close(to_host64(o), want, dtype, f"{name} split={split}")
+
+
+CAUSAL_CASES = [
+    # (name, ctx, K, Hq, Hkv, D, dtype): partial and multiple block pages,
+    # a block alone (empty context), GQA groups 1..8, both types
+    ("bf16-llama", [0, 5, 16, 300, 1000], 16, 32, 8, 128, "bf16"),
+    ("bf16-k33-three-block-pages", [37, 0], 33, 4, 2, 128, "bf16"),
+    ("bf16-k64-rows256", [200, 1], 64, 8, 2, 128, "bf16"),
+    ("bf16-g8-k7", [64, 90], 7, 64, 8, 128, "bf16"),
+    ("f32-d64-k13", [33, 100, 0], 13, 8, 2, 64, "f32"),
+    ("f32-mha-k20", [17], 20, 4, 4, 128, "f32"),
+]
+
+
+@pytest.mark.parametrize("name,ctx,K,Hq,Hkv,D,dtype", CAUSAL_CASES, ids=[c[0] for c in CAUSAL_CASES])
+def test_attention_block_causal(name, ctx, K, Hq, Hkv, D, dtype):
+    flush(f"[attn causal] {name}")
+    case = make_attn_case(3 * sum(ctx) + K, ctx, K, Hq, Hkv, D, dtype)
+    want = oracle_attn(case, causal=True)
+    for split in (0, 1, 3):
+        o, _, _ = run_attn(case, split=split, causal=True)
+        assert_close(to_host64(o), want, dtype, f"{name} causal split={split}")
+
+
+def test_block_causal_edges():
+    """K = 1 (the mask removes nothing) is bit-identical to the mask-free call;
+    the last block position sees every key, so its output matches the
+    mask-free one to the tolerance; earlier positions differ from it."""
+    c1 = make_attn_case(21, [100, 0, 17], 1, 32, 8, 128, "bf16")
+    a, _, _ = run_attn(c1, causal=True)
+    b, _, _ = run_attn(c1, causal=False)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    c = make_attn_case(22, [300, 40], 16, 32, 8, 128, "bf16")
+    oc, _, _ = run_attn(c, causal=True)
+    of, _, _ = run_attn(c, causal=False)
+    oc, of = to_host64(oc), to_host64(of)
+    assert_close(oc[:, -1], of[:, -1], "bf16", "last block position")
+    assert np.abs(oc[:, 0] - of[:, 0]).max() > 0.05
 
 
 def test_split_invariance_and_repeatability():
@@ -255,3 +295,24 @@ def test_layer_with_skip_term():
     y, hf = oracle_scan(inp, h0)
     assert_close(to_host64(layer.y), y, "bf16", "y with skip")
     assert_close(to_host64(layer.h_final), hf, "bf16", "h_final with skip")
+
+
+def test_layer_block_causal_and_direct_reuse_ablation():
+    """The layer with the block-causal mask, and the direct-reuse-only
+    ablation (no state projection: the scan starts from the zero state)."""
+    from dataclasses import replace
+    from helpers import layer_from_inputs, oracle_attn as oracle_attn_inp, oracle_h0, oracle_scan
+    w = replace(wl.WORKLOADS[1], name="small-layer-ablation", C=3, ctx=("uniform", 0, 300), d_model=512,
+                H=4, N=32, seed=4343)
+    inp = wl.make_inputs(w)
+    full = layer_from_inputs(inp, block_causal=True)
+    assert_close(to_host64(full.out), oracle_attn_inp(inp, block_causal=True), "bf16", "causal out")
+    y, hf = oracle_scan(inp, oracle_h0(inp))
+    assert_close(to_host64(full.y), y, "bf16", "y")
+    abl = layer_from_inputs(inp, no_init=True)
+    assert abl.h0 is None
+    y0, hf0 = oracle_scan(inp, np.zeros((w.C, w.S)))
+    assert_close(to_host64(abl.y), y0, "bf16", "y from the zero state")
+    assert_close(to_host64(abl.h_final), hf0, "bf16", "h_final from the zero state")
+    assert_close(to_host64(abl.out), oracle_attn_inp(inp), "bf16", "ablation out")
+    assert np.abs(to_host64(abl.y) - y).max() > 1e-3, "the projected state must matter"
