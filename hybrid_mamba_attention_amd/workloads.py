@@ -275,6 +275,62 @@ def make_inputs(w: Workload, *, ctx_lens=None, identity_pages: bool = False,
     return inp
 
 
+# ----------------------------------------------------------------------------
+# the Mamba-2 block around the scan
+# ----------------------------------------------------------------------------
+
+BLOCK_STREAMS = ("hidden", "w_in", "conv_w", "conv_b", "norm_w", "w_out", "h0", "A", "Dskip")
+BLOCK_DT_BIAS = -4.0
+BLOCK_EPS = 1e-5
+
+
+def block_sizes(w: Workload):
+    """(d_inner, conv_dim, d_in_proj) of the Mamba-2 block of workload w."""
+    d_inner = w.H * w.P
+    conv_dim = d_inner + 2 * w.ng * w.N
+    return d_inner, conv_dim, 2 * d_inner + 2 * w.ng * w.N + w.H
+
+
+def make_block_inputs(w: Workload, *, with_dskip: bool = True, with_h0: bool = True) -> dict:
+    """Inputs of one Mamba-2 block call over workload w's draft blocks.
+
+    Recipe (its own seed branch, so the layer's streams are unchanged):
+      * hidden [C,K,d_model]: N(0,1); h0 [C,H,P,N] fp32: N(0,1)
+      * w_in [2*H*P + 2*ng*N + H, d_model] and w_out [d_model, H*P]: N(0, 0.02^2)
+      * conv_w [conv_dim, 4], conv_b [conv_dim]: U(-0.5, 0.5) (fan-in 4)
+      * dt_bias [H] = -4, so delta = softplus(dt_raw - 4) as in the layer recipe
+      * A [H] = -exp(U(0,1)); Dskip [H]: N(0,1); norm_w [H*P]: 1 + 0.1 N(0,1)
+      * eps = 1e-5; fp32 for everything but hidden, w_in and w_out (act dtype)
+    """
+    root = np.random.SeedSequence([w.seed, 77])
+    ss = dict(zip(BLOCK_STREAMS, root.spawn(len(BLOCK_STREAMS))))
+    bf16 = w.dtype == "bf16"
+    d_inner, conv_dim, d_proj = block_sizes(w)
+
+    def normal(name, shape, std=1.0):
+        return _normal_chunked(ss[name], int(np.prod(shape)), std, bf16).reshape(shape)
+
+    def rng(name):
+        return np.random.default_rng(ss[name])
+
+    a = dict(
+        hidden=normal("hidden", (w.C, w.K, w.d_model)),
+        w_in=normal("w_in", (d_proj, w.d_model), 0.02),
+        conv_w=rng("conv_w").uniform(-0.5, 0.5, (conv_dim, 4)).astype(np.float32),
+        conv_b=rng("conv_b").uniform(-0.5, 0.5, conv_dim).astype(np.float32),
+        dt_bias=np.full(w.H, BLOCK_DT_BIAS, np.float32),
+        A=(-np.exp(rng("A").uniform(0.0, 1.0, w.H))).astype(np.float32),
+        norm_w=(1.0 + 0.1 * rng("norm_w").standard_normal(d_inner)).astype(np.float32),
+        w_out=normal("w_out", (w.d_model, d_inner), 0.02),
+        eps=BLOCK_EPS,
+    )
+    if with_dskip:
+        a["Dskip"] = rng("Dskip").standard_normal(w.H).astype(np.float32)
+    if with_h0:
+        a["h0"] = rng("h0").standard_normal((w.C, w.H, w.P, w.N), dtype=np.float32)
+    return a
+
+
 def kv_bytes(w: Workload, ctx_lens) -> int:
     """Bytes of target KV a layer call must read in place (K and V, valid tokens)."""
     e = 2 if w.dtype == "bf16" else 4

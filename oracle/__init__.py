@@ -14,7 +14,9 @@ Sources:
     the target's KV cache in place with no drafter-side cache; Mamba's parallel
     scan keeps drafting block-parallel.
   * Mamba-2 (Dao & Gu, 2024, "Transformers are SSMs"), the SSD recurrence and
-    its chunked form, for the scan arithmetic the pages name but do not print.
+    its chunked form, for the scan arithmetic the pages name but do not print,
+    and the Mamba-2 block around the scan (projections, short convolution,
+    gated normalisation).
 
 Every function below is pinned by tests/test_oracle_*.py against closed forms,
 brute force, library routines or hand-derived golden values.  The layer's
@@ -28,10 +30,13 @@ from .attention import (PoisonedRead, gather_context, block_attention,
                         block_attention_splits, split_partials, merge_partials)
 from .plan import split_plan, plan_len, max_items_for
 from .layer import draft_layer
+from .mamba_block import (mamba_block, causal_conv, gated_rmsnorm, silu, softplus,
+                          in_proj_sizes)
 
 __all__ = [
     "decode", "BF16", "F32", "init_state", "ssd_recurrence", "ssd_chunked",
     "PoisonedRead", "gather_context", "block_attention", "block_attention_splits",
     "split_partials", "merge_partials", "split_plan", "plan_len", "max_items_for",
-    "draft_layer",
+    "draft_layer", "mamba_block", "causal_conv", "gated_rmsnorm", "silu", "softplus",
+    "in_proj_sizes",
 ]

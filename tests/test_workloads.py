@@ -89,3 +89,21 @@ def test_shapes_of_all_workloads():
         assert w.Hq % w.Hkv == 0 and w.H % w.ng == 0
     assert wl.WORKLOADS[1].S == 32768 and wl.WORKLOADS[4].S == 131072 and wl.WORKLOADS[0].S == 4096
     assert wl.kv_bytes(wl.WORKLOADS[3], [8192] * 128) == 2 ** 32
+
+
+def test_block_inputs_shapes_and_reproducibility():
+    w = wl.WORKLOADS[1]
+    small = wl.replace(w, C=2, d_model=256)
+    a, b = wl.make_block_inputs(small), wl.make_block_inputs(small)
+    d_inner, conv_dim, d_proj = wl.block_sizes(small)
+    assert (d_inner, conv_dim, d_proj) == (1024, 1088, 2128)
+    assert a["hidden"].shape == (2, 16, 256) and a["hidden"].dtype == np.uint16
+    assert a["w_in"].shape == (d_proj, 256) and a["w_out"].shape == (256, d_inner)
+    assert a["conv_w"].shape == (conv_dim, 4) and a["conv_w"].dtype == np.float32
+    assert a["h0"].shape == (2, 16, 64, 32) and np.all(a["dt_bias"] == -4.0)
+    for k in a:
+        if isinstance(a[k], np.ndarray):
+            assert np.array_equal(a[k], b[k]), k
+    # the block's streams leave the layer's inputs untouched
+    assert np.array_equal(wl.make_inputs(small, parts=("mamba",)).arrays["u"],
+                          wl.make_inputs(small, parts=("mamba",)).arrays["u"])
