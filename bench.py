@@ -49,6 +49,8 @@ def parse():
     p.add_argument("--no-probe", action="store_true", help="skip the stream-read bandwidth probe")
     p.add_argument("--no-variants", action="store_true",
                    help="skip the block-causal and direct-reuse-only layer timings")
+    p.add_argument("--no-block", action="store_true",
+                   help="skip the Mamba-2 block (projections, conv, scan, gated norm) timings")
     p.add_argument("--sweep", default="1,2,4,8,16,32,64,128")
     p.add_argument("--calib-copy", action="store_true",
                    help="also launch a plain 1 GiB device copy (counter calibration under rocprofv3)")
@@ -161,6 +163,36 @@ def measure_variants(w, inp, args, torch, flush):
         del layer, t
         torch.cuda.empty_cache()
     return out
+
+
+def block_flops(w):
+    """Matrix-core flops of one Mamba-2 block call: both projections."""
+    from hybrid_mamba_attention_amd import workloads as wl
+    d_inner, _, d_proj = wl.block_sizes(w)
+    T = w.C * w.K
+    return 2 * T * w.d_model * d_proj + 2 * T * d_inner * w.d_model
+
+
+def measure_block(w, args, torch, flush):
+    """The Mamba-2 block around the scan (projections, conv, scan, gated norm)."""
+    from hybrid_mamba_attention_amd import ops, workloads as wl
+    a = wl.make_block_inputs(w)
+    f32 = lambda k: dev(a[k].astype("float32"), torch)
+    blk = ops.MambaBlock(hidden=dev(a["hidden"], torch), w_in=dev(a["w_in"], torch), conv_w=f32("conv_w"),
+                         conv_b=f32("conv_b"), dt_bias=f32("dt_bias"), A=f32("A"), Dskip=f32("Dskip"),
+                         h0=f32("h0"), norm_w=f32("norm_w"), w_out=dev(a["w_out"], torch), eps=a["eps"],
+                         H=w.H, P=w.P, N=w.N, ng=w.ng, chunk=w.chunk, want_final=True)
+    st = stats(timed(blk, args.steps, args.warmup, flush, torch))
+    fl = block_flops(w)
+    d_inner, _, d_proj = wl.block_sizes(w)
+    e = 2 if w.dtype == "bf16" else 4
+    wbytes = (d_proj + d_inner) * w.d_model * e
+    del blk
+    torch.cuda.empty_cache()
+    return dict(ms=st["mean"], block_tokens_per_s=w.C * w.K / (st["mean"] * 1e-3),
+                projection_gflop=fl / 1e9, tflops_whole_block=fl / (st["mean"] * 1e-3) / 1e12,
+                mfma_frac_whole_block=fl / (st["mean"] * 1e-3) / 1e12 / BF16_DENSE_TFLOPS,
+                weight_bytes=wbytes)
 
 
 # ----------------------------------------------------------------------------
@@ -326,6 +358,9 @@ def main():
     if not args.no_variants:
         print("[bench] timing the layer variants", file=sys.stderr, flush=True)
         line["variants"] = measure_variants(w, inp, args, torch, flush)
+    if not args.no_block:
+        print("[bench] timing the Mamba-2 block", file=sys.stderr, flush=True)
+        line["mamba_block"] = measure_block(w, args, torch, flush)
     if not args.no_sweep:
         sweep = {}
         for C in [int(c) for c in args.sweep.split(",")]:
@@ -335,10 +370,14 @@ def main():
             sr = r if ws is w else measure(ws, si, args, torch, flush, with_parts=True)
             sms = sr["step"]["mean"]
             akv = wl.kv_bytes(ws, si.ctx_lens)
+            if not args.no_block:
+                sweep_block = line["mamba_block"]["ms"] if ws is w else measure_block(ws, args, torch, flush)["ms"]
             sweep[str(C)] = dict(block_tokens_per_s=ws.C * ws.K / (sms * 1e-3), ms_per_step=sms,
                                  attention_ms=sr["attention"]["mean"], init_ms=sr["init_state"]["mean"],
                                  kv_read_gbs=akv / (sr["attention"]["mean"] * 1e-3) / 1e9,
                                  kv_read_frac=akv / (sr["attention"]["mean"] * 1e-3) / 1e9 / HBM_PEAK_GBS)
+            if not args.no_block:
+                sweep[str(C)]["mamba_block_ms"] = sweep_block
             if si is not inp:
                 del si
         line["sweep_ctx8192"] = sweep

@@ -37,16 +37,23 @@ int check_init(int dtype, int C, int d, int S, const void* u, const void* w, con
   return HSPEC_OK;
 }
 
-int check_ssd(int dtype, int C, int K, int H, int P, int ng, int N, int chunk, const void* x,
-              const float* delta, const float* A, const void* B, const void* Cm, const float* y) {
+// shape limits of the scan (pointers are checked by the callers)
+int check_ssd_shape(int dtype, int C, int K, int H, int P, int ng, int N, int chunk) {
   if (!dtype_ok(dtype) || C < 1 || K < 1 || H < 1 || P < 1 || N < 1 || ng < 1 || chunk < 1)
     return HSPEC_ERR_INVALID_ARG;
   if (H % ng) return HSPEC_ERR_INVALID_ARG;
-  if (!x || !delta || !A || !B || !Cm || !y) return HSPEC_ERR_INVALID_ARG;
   if (chunk > 16 || (chunk & (chunk - 1))) return HSPEC_ERR_UNSUPPORTED;
   if (P > 128 || N > 128) return HSPEC_ERR_UNSUPPORTED;
   if (ssd_lds_bytes(P, N, chunk) > kMaxLds) return HSPEC_ERR_UNSUPPORTED;
   if (int64_t(C) * H > 0x7fffffff) return HSPEC_ERR_UNSUPPORTED;
+  return HSPEC_OK;
+}
+
+int check_ssd(int dtype, int C, int K, int H, int P, int ng, int N, int chunk, const void* x,
+              const float* delta, const float* A, const void* B, const void* Cm, const float* y) {
+  const int st = check_ssd_shape(dtype, C, K, H, P, ng, N, chunk);
+  if (st != HSPEC_OK) return st;
+  if (!x || !delta || !A || !B || !Cm || !y) return HSPEC_ERR_INVALID_ARG;
   return HSPEC_OK;
 }
 
@@ -146,6 +153,93 @@ int run_attn(hipStream_t st, int dtype, int C, int K, int Hq, int Hkv, int D, co
   return status_of(launch_block_attn(st, dtype, a));
 }
 
+// Workspace of the Mamba-2 block: fp32 projection, scan inputs and output,
+// the normalised activations, and split-K partials of either projection.
+struct BlockPlan {
+  int T, d_inner, conv_dim, d_proj, ngN;
+  GemmPlan in_p, out_p;
+  size_t zx_off, x_off, b_off, c_off, dt_off, y_off, n_off, part_off, total;
+};
+
+BlockPlan block_plan(const hspec_mamba_args* a) {
+  BlockPlan p{};
+  p.T = a->C * a->K;
+  p.d_inner = a->H * a->P;
+  p.ngN = a->ng * a->N;
+  p.conv_dim = p.d_inner + 2 * p.ngN;
+  p.d_proj = 2 * p.d_inner + 2 * p.ngN + a->H;
+  p.in_p = gemm_plan(a->dtype, p.T, p.d_proj, a->d_model);
+  p.out_p = gemm_plan(a->dtype, p.T, a->d_model, p.d_inner);
+  size_t off = 0;
+  auto take = [&](size_t bytes) { const size_t o = off; off += align256(bytes); return o; };
+  const size_t T = size_t(p.T);
+  p.zx_off = take(T * p.d_proj * 4);
+  p.x_off = take(T * p.d_inner * 4);
+  p.b_off = take(T * p.ngN * 4);
+  p.c_off = take(T * p.ngN * 4);
+  p.dt_off = take(T * a->H * 4);
+  p.y_off = take(T * p.d_inner * 4);
+  p.n_off = take(T * p.d_inner * esize(a->dtype));
+  p.part_off = take(std::max(p.in_p.part_floats, p.out_p.part_floats) * 4);
+  p.total = std::max<size_t>(off, 256);
+  return p;
+}
+
+int check_block(const hspec_mamba_args* a) {
+  if (!a) return HSPEC_ERR_INVALID_ARG;
+  if (!dtype_ok(a->dtype) || a->C < 1 || a->K < 1 || a->d_model < 1) return HSPEC_ERR_INVALID_ARG;
+  if (!a->hidden || !a->w_in || !a->conv_w || !a->dt_bias || !a->A || !a->norm_w || !a->w_out || !a->out)
+    return HSPEC_ERR_INVALID_ARG;
+  const void* al16[] = {a->hidden, a->w_in, a->w_out, a->out, a->conv_w, a->norm_w};
+  for (const void* q : al16)
+    if (!aligned(q, 16)) return HSPEC_ERR_INVALID_ARG;
+  if (!(a->norm_eps >= 0.f) || !std::isfinite(a->norm_eps)) return HSPEC_ERR_INVALID_ARG;
+  // the scan's own limits (its inputs are workspace buffers here)
+  const int st = check_ssd_shape(HSPEC_F32, a->C, a->K, a->H, a->P, a->ng, a->N, a->chunk);
+  if (st != HSPEC_OK) return st;
+  const int64_t d_inner = int64_t(a->H) * a->P;
+  const int64_t d_proj = 2 * d_inner + 2 * int64_t(a->ng) * a->N + a->H;
+  const int64_t T = int64_t(a->C) * a->K;
+  if (a->d_model % 8 || d_inner % 8) return HSPEC_ERR_UNSUPPORTED;
+  // row and column counts stay ints; requests index grid.y of the conv kernel
+  if (T > (1 << 30) || d_proj > (1 << 30) || a->C > 65535) return HSPEC_ERR_UNSUPPORTED;
+  return HSPEC_OK;
+}
+
+int run_block(hipStream_t s, const hspec_mamba_args* a, const BlockPlan& p) {
+  unsigned char* ws = static_cast<unsigned char*>(a->workspace);
+  float* zx = reinterpret_cast<float*>(ws + p.zx_off);
+  float* xs = reinterpret_cast<float*>(ws + p.x_off);
+  float* bs = reinterpret_cast<float*>(ws + p.b_off);
+  float* cs = reinterpret_cast<float*>(ws + p.c_off);
+  float* dt = reinterpret_cast<float*>(ws + p.dt_off);
+  float* y = reinterpret_cast<float*>(ws + p.y_off);
+  void* normed = ws + p.n_off;
+  float* part = reinterpret_cast<float*>(ws + p.part_off);
+  GemmArgs gi{};
+  gi.a = a->hidden; gi.b = a->w_in; gi.c = zx; gi.part = part;
+  gi.M = p.T; gi.N = p.d_proj; gi.K = a->d_model;
+  gi.lda = a->d_model; gi.ldb = a->d_model; gi.ldc = p.d_proj;
+  int st = status_of(launch_gemm_tn(s, a->dtype, 1, gi, p.in_p));
+  if (st != HSPEC_OK) return st;
+  ConvActArgs ca{zx, a->conv_w, a->conv_b, a->dt_bias, xs, bs, cs, dt,
+                 a->C, a->K, p.d_inner, p.ngN, a->H, p.d_proj};
+  st = status_of(launch_conv_act(s, ca));
+  if (st != HSPEC_OK) return st;
+  SsdArgs sa{xs, dt, a->A, bs, cs, a->Dskip, a->h0, y, a->h_final,
+             a->C, a->K, a->H, a->P, a->ng, a->N, a->chunk};
+  st = status_of(launch_ssd_scan(s, HSPEC_F32, sa));
+  if (st != HSPEC_OK) return st;
+  GateNormArgs gn{y, zx, a->norm_w, a->norm_eps, normed, p.T, p.d_inner, p.d_proj};
+  st = status_of(launch_gate_norm(s, a->dtype, gn));
+  if (st != HSPEC_OK) return st;
+  GemmArgs go{};
+  go.a = normed; go.b = a->w_out; go.c = a->out; go.part = part;
+  go.M = p.T; go.N = a->d_model; go.K = p.d_inner;
+  go.lda = p.d_inner; go.ldb = p.d_inner; go.ldc = a->d_model;
+  return status_of(launch_gemm_tn(s, a->dtype, 0, go, p.out_p));
+}
+
 }  // namespace
 
 extern "C" {
@@ -239,6 +333,18 @@ int hspec_draft_layer(void* stream, const hspec_layer_args* a, size_t* required_
   SsdArgs sa{a->x, a->delta, a->A, a->B, a->Cm, a->Dskip, no_init ? nullptr : a->h0, a->y, a->h_final,
              a->C, a->K, a->H, a->P, a->ng, a->N, a->chunk};
   return status_of(launch_ssd_scan(s, a->dtype, sa));
+}
+
+size_t hspec_mamba_args_size(void) { return sizeof(hspec_mamba_args); }
+
+int hspec_mamba_block(void* stream, const hspec_mamba_args* a, size_t* required_bytes) {
+  const int st = check_block(a);
+  if (st != HSPEC_OK) return st;
+  const BlockPlan p = block_plan(a);
+  if (required_bytes) *required_bytes = p.total;
+  if (!a->workspace) return required_bytes ? HSPEC_OK : HSPEC_ERR_WORKSPACE;
+  if (!aligned(a->workspace, 256) || a->workspace_bytes < p.total) return HSPEC_ERR_WORKSPACE;
+  return run_block(static_cast<hipStream_t>(stream), a, p);
 }
 
 }  // extern "C"

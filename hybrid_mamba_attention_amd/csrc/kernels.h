@@ -57,4 +57,49 @@ struct InitArgs {
 };
 hipError_t launch_init_state(hipStream_t st, int dtype, const InitArgs& a);
 
+// C[M, N] = A[M, K] . B[N, K]^T (row strides in elements); K % 8 == 0.
+struct GemmArgs {
+  const void* a;
+  const void* b;
+  void* c;          // OutT [M, ldc]
+  float* part;      // fp32 [splits, M, N] split-K partials (splits > 1)
+  int M, N, K, lda, ldb, ldc;
+  int tiles_m, splits, kchunk;  // filled in by the launcher from the plan
+};
+// One launch over output columns [n0, n0 + n).
+struct GemmPart {
+  int cfg, bm, bn, tiles_m, tiles, splits, kchunk, n0, n;
+};
+struct GemmPlan {
+  GemmPart part[2];     // the columns, or the whole tiles and a ragged tail
+  int nparts;
+  size_t part_floats;   // workspace floats the split-K partials need
+};
+GemmPlan gemm_plan(int dtype, int M, int N, int K);
+// out_f32: store fp32 (else the activation type of dtype)
+hipError_t launch_gemm_tn(hipStream_t st, int dtype, int out_f32, const GemmArgs& g, const GemmPlan& p);
+
+struct ConvActArgs {
+  const float* zx;      // fp32 [C*K, d_proj]: z | x | B | C | dt
+  const float* conv_w;  // fp32 [conv_dim, 4]
+  const float* conv_b;  // fp32 [conv_dim] or null
+  const float* dt_bias; // fp32 [H]
+  float* x;             // fp32 [C*K, d_inner]
+  float* B;             // fp32 [C*K, ngN]
+  float* Cm;            // fp32 [C*K, ngN]
+  float* delta;         // fp32 [C*K, H]
+  int C, K, d_inner, ngN, H, d_proj;
+};
+hipError_t launch_conv_act(hipStream_t st, const ConvActArgs& c);
+
+struct GateNormArgs {
+  const float* y;       // fp32 [T, d_inner]
+  const float* zx;      // fp32 [T, d_proj], z in columns [0, d_inner)
+  const float* norm_w;  // fp32 [d_inner]
+  float eps;
+  void* out;            // act [T, d_inner]
+  int T, d_inner, d_proj;
+};
+hipError_t launch_gate_norm(hipStream_t st, int dtype, const GateNormArgs& a);
+
 }  // namespace hspec

@@ -41,6 +41,21 @@ class LayerArgs(ctypes.Structure):
     ]
 
 
+class MambaArgs(ctypes.Structure):
+    """Mirror of hspec_mamba_args (field order and types as in include/hspec.h)."""
+    _fields_ = [
+        ("dtype", _i), ("C", _i), ("K", _i), ("d_model", _i), ("H", _i), ("P", _i), ("ng", _i),
+        ("N", _i), ("chunk", _i),
+        ("hidden", _vp), ("w_in", _vp),
+        ("conv_w", _vp), ("conv_b", _vp), ("dt_bias", _vp),
+        ("A", _vp), ("Dskip", _vp), ("h0", _vp),
+        ("norm_w", _vp), ("norm_eps", _f),
+        ("w_out", _vp),
+        ("out", _vp), ("h_final", _vp),
+        ("workspace", _vp), ("workspace_bytes", _sz),
+    ]
+
+
 _lib = None
 
 
@@ -67,10 +82,15 @@ def lib() -> ctypes.CDLL:
                                             _vp, _vp, ctypes.POINTER(_sz)])
     L.hspec_draft_layer.restype = _i
     L.hspec_draft_layer.argtypes = [_vp, ctypes.POINTER(LayerArgs), ctypes.POINTER(_sz)]
-    if L.hspec_abi_version() != 2:
+    L.hspec_mamba_args_size.restype = _sz
+    L.hspec_mamba_block.restype = _i
+    L.hspec_mamba_block.argtypes = [_vp, ctypes.POINTER(MambaArgs), ctypes.POINTER(_sz)]
+    if L.hspec_abi_version() != 3:
         raise RuntimeError("libhspec.so ABI version mismatch")
     if L.hspec_layer_args_size() != ctypes.sizeof(LayerArgs):
         raise RuntimeError("hspec_layer_args layout mismatch between library and binding")
+    if L.hspec_mamba_args_size() != ctypes.sizeof(MambaArgs):
+        raise RuntimeError("hspec_mamba_args layout mismatch between library and binding")
     _lib = L
     return L
 
@@ -298,6 +318,53 @@ class DraftLayer:
 def draft_layer(**kw):
     """One drafter-layer call; returns the DraftLayer holding h0, y, h_final, out."""
     return DraftLayer(**kw)()
+
+
+# ---------------------------------------------------------------------------
+# the Mamba-2 block around the scan
+# ---------------------------------------------------------------------------
+
+class MambaBlock:
+    """Marshalled arguments of one Mamba-2 block configuration (hspec_mamba_block).
+
+    hidden [C,K,d_model] and w_in [d_proj,d_model], w_out [d_model,H*P] in the
+    activation type; conv_w [conv_dim,4], conv_b, dt_bias, A, Dskip, norm_w and
+    h0 [C,H,P,N] fp32 (conv_b, Dskip and h0 may be None)."""
+
+    def __init__(self, *, hidden, w_in, conv_w, dt_bias, A, norm_w, w_out, H, P, N, chunk, ng=1,
+                 conv_b=None, Dskip=None, h0=None, eps=1e-5, want_final=False):
+        _contig(hidden, w_in, conv_w, conv_b, dt_bias, A, Dskip, h0, norm_w, w_out)
+        dev = hidden.device
+        C, K, d = hidden.shape
+        self.out = torch.empty_like(hidden)
+        self.h_final = (torch.empty((C, H, P, N), dtype=torch.float32, device=dev)
+                        if want_final else None)
+        a = MambaArgs()
+        a.dtype = _dtype_code(hidden)
+        a.C, a.K, a.d_model, a.H, a.P, a.ng, a.N, a.chunk = C, K, d, H, P, ng, N, chunk
+        ptr = lambda t: t.data_ptr() if t is not None else None
+        a.hidden, a.w_in = ptr(hidden), ptr(w_in)
+        a.conv_w, a.conv_b, a.dt_bias = ptr(conv_w), ptr(conv_b), ptr(dt_bias)
+        a.A, a.Dskip, a.h0 = ptr(A), ptr(Dskip), ptr(h0)
+        a.norm_w, a.norm_eps = ptr(norm_w), float(eps)
+        a.w_out = ptr(w_out)
+        a.out, a.h_final = ptr(self.out), ptr(self.h_final)
+        a.workspace, a.workspace_bytes = None, 0
+        need = _sz(0)
+        _check("hspec_mamba_block", lib().hspec_mamba_block(None, ctypes.byref(a), ctypes.byref(need)))
+        self.workspace = torch.empty(max(need.value, 256), dtype=torch.uint8, device=dev)
+        a.workspace, a.workspace_bytes = self.workspace.data_ptr(), self.workspace.numel()
+        self._args = a
+        self._keep = (hidden, w_in, conv_w, conv_b, dt_bias, A, Dskip, h0, norm_w, w_out)
+
+    def __call__(self, stream=None):
+        _check("hspec_mamba_block", lib().hspec_mamba_block(_stream(stream), ctypes.byref(self._args), None))
+        return self
+
+
+def mamba_block(**kw):
+    """One Mamba-2 block call; returns the MambaBlock holding out and h_final."""
+    return MambaBlock(**kw)()
 
 
 # ---------------------------------------------------------------------------

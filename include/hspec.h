@@ -48,7 +48,7 @@ typedef enum {
 const char* hspec_status_string(int status);
 
 /* ABI version of this header; bumped on any incompatible change. */
-#define HSPEC_ABI_VERSION 2
+#define HSPEC_ABI_VERSION 3
 int hspec_abi_version(void);
 
 /*
@@ -190,6 +190,62 @@ size_t hspec_layer_args_size(void);
 /* `required_bytes` receives the workspace size a5 needs (may be NULL when
  * a->workspace is set). */
 int hspec_draft_layer(void* stream, const hspec_layer_args* a, size_t* required_bytes);
+
+/*
+ * The Mamba-2 block around a2: input projection, short causal convolution,
+ * the scan, gated RMS normalisation and output projection.  H-Spec, Abstract:
+ * the drafter's Mamba modules are Mamba-2 modules; the block is Mamba-2's
+ * (Dao & Gu 2024, "Transformers are SSMs"), which the pages do not print.
+ * Per request b and block position t (token row r = b*K + t):
+ *
+ *   zxbcdt[r] = w_in . hidden[r]                 rows z | x | B | C | dt
+ *   xBC[r, c] = SiLU(conv_b[c] + sum_j conv_w[c, j] * xBC_raw[r - 3 + j, c])
+ *               (positions before the block start are zero)
+ *   delta[r, h] = softplus(dt_raw[r, h] + dt_bias[h])
+ *   y = a2 scan of (x, delta, A, B, C) from h0, with the skip term Dskip
+ *   normed[r] = g / sqrt(mean(g^2) + eps) * norm_w,   g = y[r] * SiLU(z[r])
+ *   out[r] = w_out . normed[r]
+ *
+ * Shapes (d_inner = H*P, conv_dim = d_inner + 2*ng*N,
+ * d_proj = 2*d_inner + 2*ng*N + H):
+ *   hidden  act  [C, K, d_model]
+ *   w_in    act  [d_proj, d_model]    ([out, in], rows z | x | B | C | dt)
+ *   conv_w  fp32 [conv_dim, 4]        tap 3 multiplies the current token
+ *   conv_b  fp32 [conv_dim] or NULL
+ *   dt_bias fp32 [H];  A fp32 [H] (negative);  Dskip fp32 [H] or NULL
+ *   h0      fp32 [C, H, P, N] or NULL (zero state)
+ *   norm_w  fp32 [d_inner];  norm_eps >= 0
+ *   w_out   act  [d_model, d_inner]
+ *   out     act  [C, K, d_model]
+ *   h_final fp32 [C, H, P, N] or NULL
+ * x channel h*P + p is head h, element p; B and C channel g*N + n is group g.
+ * Projections run on bf16 matrix cores with fp32 accumulation (fp32 FMA for
+ * fp32 activations); the convolution, scan and norm run in fp32 and the
+ * normalised activations are rounded to the activation type before the
+ * output projection.  `workspace` == NULL is a size query as for a3
+ * (256-byte aligned device memory otherwise).
+ * Limits: d_model % 8 == 0, d_inner % 8 == 0, the scan limits of a2
+ * (else UNSUPPORTED); hidden, w_in, w_out, out, conv_w and norm_w 16-byte
+ * aligned (else INVALID_ARG).
+ */
+typedef struct hspec_mamba_args {
+  int dtype;
+  int C, K, d_model, H, P, ng, N, chunk;
+  const void* hidden; const void* w_in;
+  const float* conv_w; const float* conv_b; const float* dt_bias;
+  const float* A; const float* Dskip; const float* h0;
+  const float* norm_w; float norm_eps;
+  const void* w_out;
+  void* out; float* h_final;
+  void* workspace; size_t workspace_bytes;
+} hspec_mamba_args;
+
+/* sizeof(hspec_mamba_args) as compiled into the library (binding check). */
+size_t hspec_mamba_args_size(void);
+
+/* `required_bytes` receives the workspace size (may be NULL when
+ * a->workspace is set). */
+int hspec_mamba_block(void* stream, const hspec_mamba_args* a, size_t* required_bytes);
 
 #ifdef __cplusplus
 }

@@ -27,11 +27,12 @@ def test_loads_and_exports_every_declared_symbol():
     L = ops.lib()
     names = declared_functions()
     assert {"hspec_init_state", "hspec_ssd_scan", "hspec_block_attn_inplace",
-            "hspec_draft_layer", "hspec_probe_stream_read"} <= set(names)
+            "hspec_draft_layer", "hspec_mamba_block", "hspec_probe_stream_read"} <= set(names)
     for n in names:
         assert hasattr(L, n), f"{n} declared in hspec.h but not exported"
-    assert L.hspec_abi_version() == 2
+    assert L.hspec_abi_version() == 3
     assert L.hspec_layer_args_size() == ctypes.sizeof(ops.LayerArgs)
+    assert L.hspec_mamba_args_size() == ctypes.sizeof(ops.MambaArgs)
     assert L.hspec_status_string(-2) == b"HSPEC_ERR_UNSUPPORTED"
 
 
@@ -139,3 +140,40 @@ def test_layer_validation_and_ablation():
     assert _layer(h0=None)[0] == INVALID          # a1 runs and needs h0
     assert _layer(block_causal=1) == (OK, n)
     assert _layer(block_causal=3)[0] == INVALID
+
+
+def _block(**kw):
+    """hspec_mamba_block size query with a valid bf16 shape (C=128 requests)."""
+    a = ops.MambaArgs()
+    a.dtype, a.C, a.K, a.d_model = 1, 128, 16, 4096
+    a.H, a.P, a.ng, a.N, a.chunk = 16, 64, 1, 32, 16
+    a.hidden = a.w_in = a.conv_w = a.dt_bias = a.A = a.norm_w = a.w_out = a.out = FAKE
+    a.norm_eps = 1e-5
+    for k, v in kw.items():
+        setattr(a, k, v)
+    n = ctypes.c_size_t(0)
+    return ops.lib().hspec_mamba_block(None, ctypes.byref(a), ctypes.byref(n)), n.value
+
+
+def test_mamba_block_validation_and_workspace():
+    code, n = _block()
+    assert code == OK
+    T, d_inner, ngN, H, d_proj = 128 * 16, 1024, 32, 16, 2128
+    al = lambda b: -(-b // 256) * 256
+    fixed = (al(T * d_proj * 4) + 2 * al(T * d_inner * 4) + 2 * al(T * ngN * 4) + al(T * H * 4)
+             + al(T * d_inner * 2))
+    assert n >= fixed and n - fixed < (1 << 30)           # + split-K partials, if any
+    assert _block(conv_b=FAKE, Dskip=FAKE, h0=FAKE, h_final=FAKE) == (OK, n)
+    assert _block(hidden=None)[0] == INVALID
+    assert _block(A=None)[0] == INVALID
+    assert _block(conv_w=FAKE + 4)[0] == INVALID           # float4 taps need 16-byte alignment
+    assert _block(norm_w=FAKE + 4)[0] == INVALID
+    assert _block(norm_eps=-1.0)[0] == INVALID
+    assert _block(dtype=5)[0] == INVALID
+    assert _block(ng=3)[0] == INVALID
+    assert _block(d_model=4100)[0] == UNSUPPORTED          # d_model % 8
+    assert _block(P=128 + 8)[0] == UNSUPPORTED             # scan limit P <= 128
+    assert _block(chunk=32)[0] == UNSUPPORTED
+    assert _block(workspace=FAKE, workspace_bytes=n - 1)[0] == WORKSPACE
+    assert _block(workspace=FAKE + 16, workspace_bytes=n)[0] == WORKSPACE
+    assert ops.lib().hspec_mamba_block(None, None, None) == INVALID
