@@ -330,26 +330,30 @@ __global__ __launch_bounds__(64 * NW) void k_block_attn(AttnArgs a) {
   }
 
 
-  auto issue = [&](int st, uint4 (&stk)[NLD], uint4 (&stv)[NLD], int (&nv)[2]) __attribute__((always_inline)) {
-    if (RPP * CPR == NT && st < nhot) {
-      // two full context pages: page numbers from the window, unpredicated
-      // loads off scalar page bases (entries clamped into the pool: never a
-      // stray read)
-      const int o = (2 * st) & 127, l0 = o & 63;
-      const int v = (o >> 6) ? pwhi : pwlo;
-      const int ph0 = min(max(__builtin_amdgcn_readlane(v, l0), 0), last_phys);
-      const int ph1 = min(max(__builtin_amdgcn_readlane(v, l0 + 1), 0), last_phys);
-      const char* k0 = kcj + int64_t(ph0) * page_b;
-      const char* v0 = vcj + int64_t(ph0) * page_b;
-      const char* k1 = kcj + int64_t(ph1) * page_b;
-      const char* v1 = vcj + int64_t(ph1) * page_b;
+  // Two full context pages (stage st < nhot): page numbers from the window,
+  // unpredicated loads off scalar page bases (entries clamped into the pool:
+  // never a stray read).
+  constexpr bool kHot = RPP * CPR == NT;
+  auto issue_hot = [&](int st, uint4 (&stk)[NLD], uint4 (&stv)[NLD]) __attribute__((always_inline)) {
+    const int o = (2 * st) & 127, l0 = o & 63;
+    const int v = (o >> 6) ? pwhi : pwlo;
+    const int ph0 = min(max(__builtin_amdgcn_readlane(v, l0), 0), last_phys);
+    const int ph1 = min(max(__builtin_amdgcn_readlane(v, l0 + 1), 0), last_phys);
+    const char* k0 = kcj + int64_t(ph0) * page_b;
+    const char* v0 = vcj + int64_t(ph0) * page_b;
+    const char* k1 = kcj + int64_t(ph1) * page_b;
+    const char* v1 = vcj + int64_t(ph1) * page_b;
 #pragma unroll
-      for (int qq = 0; qq < RND; ++qq) {
-        stk[qq] = ld_stream(k0 + coff[qq]);
-        stv[qq] = ld_stream(v0 + coff[qq]);
-        stk[RND + qq] = ld_stream(k1 + coff[qq]);
-        stv[RND + qq] = ld_stream(v1 + coff[qq]);
-      }
+    for (int qq = 0; qq < RND; ++qq) {
+      stk[qq] = ld_stream(k0 + coff[qq]);
+      stv[qq] = ld_stream(v0 + coff[qq]);
+      stk[RND + qq] = ld_stream(k1 + coff[qq]);
+      stv[RND + qq] = ld_stream(v1 + coff[qq]);
+    }
+  };
+  auto issue = [&](int st, uint4 (&stk)[NLD], uint4 (&stv)[NLD], int (&nv)[2]) __attribute__((always_inline)) {
+    if (kHot && st < nhot) {
+      issue_hot(st, stk, stv);
       nv[0] = 16;
       nv[1] = 16;
       return;
@@ -524,11 +528,42 @@ __global__ __launch_bounds__(64 * NW) void k_block_attn(AttnArgs a) {
   // issued into the registers just freed; one barrier; then the math.
   uint4 stk[PF][NLD], stv[PF][NLD];
   int nv[PF][2];
-  static_for<0, PF>([&](auto P) __attribute__((always_inline)) {
-    constexpr int pp = decltype(P)::value;
-    if (pp < nstage) issue(pp, stk[pp], stv[pp], nv[pp]);
-  });
-  for (int st0 = 0; st0 < nstage; st0 += PF) {
+  int st0 = 0;
+  if (kHot && nhot >= 2 * PF) {  // uniform over the workgroup
+    // Hot loop: every stage it issues is two full context pages, so every
+    // slot issues its loads on every path and each wait before a commit
+    // counts exactly the newer stage in flight.  The page-table window is
+    // refreshed once per 64 stages with an explicit full wait, so the page
+    // numbers read by every issue are never a pending load.
+    static_for<0, PF>([&](auto P) __attribute__((always_inline)) {
+      constexpr int pp = decltype(P)::value;
+      issue_hot(pp, stk[pp], stv[pp]);
+    });
+    for (; st0 + 2 * PF <= nhot; st0 += PF) {
+      static_for<0, PF>([&](auto P) __attribute__((always_inline)) {
+        constexpr int pp = decltype(P)::value;
+        const int sn = st0 + pp + PF;   // < nhot
+        commit(pp & 1, stk[pp], stv[pp]);
+        if ((sn & 63) == 0) {
+          load_window(sn >> 6);
+          __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+        }
+        issue_hot(sn, stk[pp], stv[pp]);
+        __syncthreads();
+        const int full[2] = {16, 16};
+        compute(pp & 1, full);
+      });
+    }
+#pragma unroll
+    for (int pp = 0; pp < PF; ++pp) nv[pp][0] = nv[pp][1] = 16;
+  } else {
+    static_for<0, PF>([&](auto P) __attribute__((always_inline)) {
+      constexpr int pp = decltype(P)::value;
+      if (pp < nstage) issue(pp, stk[pp], stv[pp], nv[pp]);
+    });
+  }
+  // the remaining stages: the hot tail, a partial last page, the block's keys
+  for (; st0 < nstage; st0 += PF) {
     static_for<0, PF>([&](auto P) __attribute__((always_inline)) {
       constexpr int pp = decltype(P)::value;
       const int st = st0 + pp;
@@ -686,7 +721,8 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
 // Stages of K/V loads in flight per workgroup.  With nontemporal loads two
 // stages keep pace with four at 64 query rows (C = 128: 707 vs 729 us) and
 // leave the 128-row tiles at two waves per SIMD instead of one (workload 4:
-// 660 vs 771 us).
+// 660 vs 771 us).  (Those figures predate the hot loop below; with it, depth
+// 2 runs at 96% of a plain streaming read, and depth 4 does not compile.)
 constexpr int kPrefetch = HSPEC_ATTN_PREFETCH;
 
 // (RT row tiles per wave, NW waves) for a query-row count: every wave reads the
