@@ -331,6 +331,44 @@ def make_block_inputs(w: Workload, *, with_dskip: bool = True, with_h0: bool = T
     return a
 
 
+# ----------------------------------------------------------------------------
+# drafter-side KV injection (the contrast workload)
+# ----------------------------------------------------------------------------
+
+def make_inject_inputs(w: Workload, n_new: int, *, ctx_lens=None, spare: int = 8) -> dict:
+    """Inputs of one injection step: n_new new positions per request after
+    ctx_lens[b] existing ones, written into a drafter-side paged pool shaped
+    like the target's ([pages, 16, Hkv, D], shuffled page table).
+
+      * hidden [C, n_new, d_model]: N(0,1); w_kv [2*Hkv*D, d_model]: N(0, 0.02^2)
+      * the pools hold N(0,1) values (the existing cache) plus NaN in spare pages
+      * start = ctx_lens (drawn as for the layer unless given)
+    """
+    root = np.random.SeedSequence([w.seed, 91])
+    ss = dict(zip(("ctx", "perm", "hidden", "w_kv", "k", "v"), root.spawn(6)))
+    bf16 = w.dtype == "bf16"
+    if ctx_lens is None:
+        ctx_lens = draw_ctx_lens(w, ss["ctx"])
+    start = np.asarray(ctx_lens, dtype=np.int32)
+    pt, pool, pages_of = build_page_table(start.astype(np.int64) + n_new, ss["perm"], spare=spare)
+
+    def normal(name, shape, std=1.0):
+        return _normal_chunked(ss[name], int(np.prod(shape)), std, bf16).reshape(shape)
+
+    a = dict(hidden=normal("hidden", (w.C, n_new, w.d_model)),
+             w_kv=normal("w_kv", (2 * w.Hkv * w.D, w.d_model), 0.02),
+             page_table=pt, start=start, num_pages=pool)
+    used = np.concatenate(pages_of) if pages_of else np.zeros(0, np.int64)
+    nan = BF16_NAN if bf16 else F32_NAN
+    for name in ("k", "v"):
+        arr = normal(name, (pool, PAGE, w.Hkv, w.D))
+        spare_mask = np.ones(pool, dtype=bool)
+        spare_mask[used] = False
+        arr[spare_mask] = nan
+        a[name + "_cache"] = arr
+    return a
+
+
 def kv_bytes(w: Workload, ctx_lens) -> int:
     """Bytes of target KV a layer call must read in place (K and V, valid tokens)."""
     e = 2 if w.dtype == "bf16" else 4
