@@ -51,6 +51,8 @@ def parse():
                    help="skip the block-causal and direct-reuse-only layer timings")
     p.add_argument("--no-block", action="store_true",
                    help="skip the Mamba-2 block (projections, conv, scan, gated norm) timings")
+    p.add_argument("--no-inject", action="store_true",
+                   help="skip the drafter-side KV injection contrast timings")
     p.add_argument("--sweep", default="1,2,4,8,16,32,64,128")
     p.add_argument("--calib-copy", action="store_true",
                    help="also launch a plain 1 GiB device copy (counter calibration under rocprofv3)")
@@ -193,6 +195,41 @@ def measure_block(w, args, torch, flush):
                 projection_gflop=fl / 1e9, tflops_whole_block=fl / (st["mean"] * 1e-3) / 1e12,
                 mfma_frac_whole_block=fl / (st["mean"] * 1e-3) / 1e12 / BF16_DENSE_TFLOPS,
                 weight_bytes=wbytes)
+
+
+def measure_injection(w, args, torch, flush, Cs=(4, 8, 16, 32, 64, 128)):
+    """The contrast workload: one drafter-side KV injection step (hspec_kv_inject)
+    of the K block positions per request after a ctx-token context, at each C.
+    Each request's new positions fall in one page of its own, so the pools need
+    only C pages; the projection and the paged writes are the full step."""
+    import numpy as np
+    from hybrid_mamba_attention_amd import ops
+    ctx = w.ctx[1] if w.ctx[0] == "fixed" else w.ctx[2]
+    e = 2 if w.dtype == "bf16" else 4
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    out = {}
+    for C in Cs:
+        g = torch.Generator(device="cuda").manual_seed(5000 + C)
+        hidden = torch.randn((C, w.K, w.d_model), generator=g, device="cuda").to(dt)
+        w_kv = (0.02 * torch.randn((2 * w.Hkv * w.D, w.d_model), generator=g, device="cuda")).to(dt)
+        kc = torch.zeros((C, 16, w.Hkv, w.D), dtype=dt, device="cuda")
+        vc = torch.zeros_like(kc)
+        max_pages = (ctx + w.K + 15) // 16
+        pt = np.full((C, max_pages), -1, np.int32)
+        pt[:, ctx // 16] = np.arange(C)          # ctx % 16 + K <= 16 here (ctx 8192, K 16)
+        pt = torch.from_numpy(pt).cuda()
+        start = torch.full((C,), ctx, dtype=torch.int32, device="cuda")
+        ws = ops.kv_inject(hidden, w_kv, kc, vc, pt, start)
+        st = stats(timed(lambda: ops.kv_inject(hidden, w_kv, kc, vc, pt, start, workspace=ws),
+                         args.steps, args.warmup, flush, torch))
+        out[str(C)] = dict(ms=st["mean"], written_bytes=C * w.K * 2 * w.Hkv * w.D * e,
+                           drafter_cache_bytes_one_layer=C * (ctx + w.K) * 2 * w.Hkv * w.D * e)
+        del hidden, w_kv, kc, vc, pt, start, ws
+    torch.cuda.empty_cache()
+    lo, hi = str(Cs[0]), str(Cs[-1])
+    return dict(per_C=out, growth_C4_to_C128=out[hi]["ms"] / out[lo]["ms"],
+                extra_kv_bytes_per_token_per_layer=2 * w.Hkv * w.D * e,
+                note="what H-Spec avoids: per-position projection into a drafter-side paged KV cache")
 
 
 # ----------------------------------------------------------------------------
@@ -361,6 +398,9 @@ def main():
     if not args.no_block:
         print("[bench] timing the Mamba-2 block", file=sys.stderr, flush=True)
         line["mamba_block"] = measure_block(w, args, torch, flush)
+    if not args.no_inject:
+        print("[bench] timing the drafter-side KV injection contrast", file=sys.stderr, flush=True)
+        line["kv_injection_contrast"] = measure_injection(w, args, torch, flush)
     if not args.no_sweep:
         sweep = {}
         for C in [int(c) for c in args.sweep.split(",")]:

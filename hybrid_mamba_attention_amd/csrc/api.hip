@@ -240,6 +240,22 @@ int run_block(hipStream_t s, const hspec_mamba_args* a, const BlockPlan& p) {
   return status_of(launch_gemm_tn(s, a->dtype, 0, go, p.out_p));
 }
 
+int check_inject(int dtype, int C, int n_new, int d, int Hkv, int D, const void* hidden,
+                 const void* w_kv, const void* kc, const void* vc, int64_t ps, int64_t ts, int64_t hs,
+                 int num_pages, const int32_t* pt, int max_pages, const int32_t* start,
+                 const size_t* ws_bytes) {
+  if (!dtype_ok(dtype) || C < 1 || n_new < 1 || d < 1 || Hkv < 1 || D < 1) return HSPEC_ERR_INVALID_ARG;
+  if (!hidden || !w_kv || !kc || !vc || !pt || !start || !ws_bytes) return HSPEC_ERR_INVALID_ARG;
+  if (!aligned(hidden, 16) || !aligned(w_kv, 16) || !aligned(pt, 4) || !aligned(start, 4))
+    return HSPEC_ERR_INVALID_ARG;
+  const int vec = 16 / esize(dtype);
+  if (ps <= 0 || ts <= 0 || hs <= 0 || ps % vec || ts % vec || hs % vec) return HSPEC_ERR_INVALID_ARG;
+  if (num_pages < 1 || max_pages < 1) return HSPEC_ERR_INVALID_ARG;
+  if (d % 8) return HSPEC_ERR_UNSUPPORTED;
+  if (int64_t(C) * n_new > (1 << 30) || int64_t(Hkv) * D > (1 << 28)) return HSPEC_ERR_UNSUPPORTED;
+  return HSPEC_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -345,6 +361,32 @@ int hspec_mamba_block(void* stream, const hspec_mamba_args* a, size_t* required_
   if (!a->workspace) return required_bytes ? HSPEC_OK : HSPEC_ERR_WORKSPACE;
   if (!aligned(a->workspace, 256) || a->workspace_bytes < p.total) return HSPEC_ERR_WORKSPACE;
   return run_block(static_cast<hipStream_t>(stream), a, p);
+}
+
+int hspec_kv_inject(void* stream, int dtype, int C, int n_new, int d_model, int Hkv, int D,
+                    const void* hidden, const void* w_kv, void* k_cache, void* v_cache,
+                    int64_t page_stride, int64_t token_stride, int64_t head_stride, int num_pages,
+                    const int32_t* page_table, int max_pages, const int32_t* start_pos,
+                    void* workspace, size_t* workspace_bytes) {
+  const int st = check_inject(dtype, C, n_new, d_model, Hkv, D, hidden, w_kv, k_cache, v_cache,
+                              page_stride, token_stride, head_stride, num_pages, page_table, max_pages,
+                              start_pos, workspace_bytes);
+  if (st != HSPEC_OK) return st;
+  const int M = C * n_new, N = 2 * Hkv * D;
+  const GemmPlan p = gemm_plan(dtype, M, N, d_model);
+  const size_t need = std::max<size_t>(256, align256(p.part_floats * 4));
+  if (!workspace) {
+    *workspace_bytes = need;
+    return HSPEC_OK;
+  }
+  if (!aligned(workspace, 256) || *workspace_bytes < need) return HSPEC_ERR_WORKSPACE;
+  GemmArgs g{};
+  g.a = hidden; g.b = w_kv; g.c = nullptr; g.part = static_cast<float*>(workspace);
+  g.M = M; g.N = N; g.K = d_model; g.lda = d_model; g.ldb = d_model; g.ldc = N;
+  g.scatter = 1;
+  g.sc = KvScatter{page_table, start_pos, k_cache, v_cache, page_stride, token_stride, head_stride,
+                   n_new, max_pages, num_pages, Hkv * D, D};
+  return status_of(launch_gemm_tn(static_cast<hipStream_t>(stream), dtype, 0, g, p));
 }
 
 }  // extern "C"

@@ -116,6 +116,20 @@ __device__ __forceinline__ f32x4 mma8<float>(const Vec8<float>& a, const Vec8<fl
   return c;
 }
 
+// Stores of fp32 results in the element type of an output tensor.
+template <typename T> __device__ __forceinline__ void store_out(T* p, float v);
+template <> __device__ __forceinline__ void store_out<float>(float* p, float v) { *p = v; }
+template <> __device__ __forceinline__ void store_out<bf16_t>(bf16_t* p, float v) { p->bits = f32_to_bf16(v); }
+
+// four consecutive outputs (16-byte aligned fp32, 8-byte aligned bf16)
+template <typename T> __device__ __forceinline__ void store_out4(T* p, float4 v);
+template <> __device__ __forceinline__ void store_out4<float>(float* p, float4 v) {
+  *reinterpret_cast<float4*>(p) = v;
+}
+template <> __device__ __forceinline__ void store_out4<bf16_t>(bf16_t* p, float4 v) {
+  *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
+}
+
 // Element e of a Vec8 as fp32 (used by register transposes and conversions).
 __device__ __forceinline__ uint32_t half_of(uint32_t dw, int hi) { return hi ? (dw >> 16) : (dw & 0xFFFFu); }
 

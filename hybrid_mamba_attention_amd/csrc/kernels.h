@@ -57,14 +57,28 @@ struct InitArgs {
 };
 hipError_t launch_init_state(hipStream_t st, int dtype, const InitArgs& a);
 
+// Paged destination of a KV-injection GEMM: output row m = b * n_new + i is
+// token position start[b] + i of request b; columns [0, HD) are its K row,
+// [HD, 2*HD) its V row (head h at h*D .. h*D + D - 1).
+struct KvScatter {
+  const int32_t* page_table;  // [C, max_pages]
+  const int32_t* start;       // [C]
+  void* k_cache;
+  void* v_cache;
+  int64_t ps, ts, hs;         // page, token, head strides in elements
+  int n_new, max_pages, num_pages, HD, D;
+};
+
 // C[M, N] = A[M, K] . B[N, K]^T (row strides in elements); K % 8 == 0.
 struct GemmArgs {
   const void* a;
   const void* b;
-  void* c;          // OutT [M, ldc]
+  void* c;          // OutT [M, ldc] (unused when scattering)
   float* part;      // fp32 [splits, M, N] split-K partials (splits > 1)
   int M, N, K, lda, ldb, ldc;
   int tiles_m, splits, kchunk;  // filled in by the launcher from the plan
+  int scatter;                  // 1: write through `sc` instead of `c`
+  KvScatter sc;
 };
 // One launch over output columns [n0, n0 + n).
 struct GemmPart {

@@ -85,7 +85,10 @@ def lib() -> ctypes.CDLL:
     L.hspec_mamba_args_size.restype = _sz
     L.hspec_mamba_block.restype = _i
     L.hspec_mamba_block.argtypes = [_vp, ctypes.POINTER(MambaArgs), ctypes.POINTER(_sz)]
-    if L.hspec_abi_version() != 3:
+    L.hspec_kv_inject.restype = _i
+    L.hspec_kv_inject.argtypes = ([_vp, _i, _i, _i, _i, _i, _i] + [_vp] * 4 +
+                                  [_i64, _i64, _i64, _i, _vp, _i, _vp, _vp, ctypes.POINTER(_sz)])
+    if L.hspec_abi_version() != 4:
         raise RuntimeError("libhspec.so ABI version mismatch")
     if L.hspec_layer_args_size() != ctypes.sizeof(LayerArgs):
         raise RuntimeError("hspec_layer_args layout mismatch between library and binding")
@@ -365,6 +368,42 @@ class MambaBlock:
 def mamba_block(**kw):
     """One Mamba-2 block call; returns the MambaBlock holding out and h_final."""
     return MambaBlock(**kw)()
+
+
+# ---------------------------------------------------------------------------
+# contrast workload: drafter-side KV injection
+# ---------------------------------------------------------------------------
+
+def _inject_call(stream, hidden, w_kv, k_cache, v_cache, page_table, start_pos, ws, n, layout):
+    C, n_new, d = hidden.shape
+    Hkv, D = (k_cache.shape[2], k_cache.shape[3]) if layout == "NHD" else (k_cache.shape[1], k_cache.shape[3])
+    if w_kv.shape != (2 * Hkv * D, d):
+        raise ValueError("w_kv must be [2*Hkv*D, d_model]")
+    ps, ts, hs = kv_strides(k_cache, layout)
+    if kv_strides(v_cache, layout) != (ps, ts, hs):
+        raise ValueError("K and V pools must share strides")
+    return lib().hspec_kv_inject(
+        stream, _dtype_code(hidden), C, n_new, d, Hkv, D, _ptr(hidden), _ptr(w_kv), _ptr(k_cache),
+        _ptr(v_cache), ps, ts, hs, k_cache.shape[0], _ptr(page_table), page_table.shape[1],
+        _ptr(start_pos), ws, ctypes.byref(n))
+
+
+def kv_inject(hidden, w_kv, k_cache, v_cache, page_table, start_pos, *, workspace=None, layout="NHD",
+              stream=None):
+    """Write w_kv . hidden[b, i] as K | V rows of positions start_pos[b] + i into
+    the paged pools (in place).  Returns the workspace."""
+    _contig(hidden, w_kv, page_table, start_pos)
+    if page_table.dtype != torch.int32 or start_pos.dtype != torch.int32:
+        raise TypeError("page_table and start_pos must be int32")
+    if workspace is None:
+        n = _sz(0)
+        _check("hspec_kv_inject", _inject_call(_stream(stream), hidden, w_kv, k_cache, v_cache, page_table,
+                                               start_pos, None, n, layout))
+        workspace = torch.empty(max(n.value, 256), dtype=torch.uint8, device=hidden.device)
+    n = _sz(workspace.numel())
+    _check("hspec_kv_inject", _inject_call(_stream(stream), hidden, w_kv, k_cache, v_cache, page_table,
+                                           start_pos, _ptr(workspace), n, layout))
+    return workspace
 
 
 # ---------------------------------------------------------------------------

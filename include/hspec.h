@@ -48,7 +48,7 @@ typedef enum {
 const char* hspec_status_string(int status);
 
 /* ABI version of this header; bumped on any incompatible change. */
-#define HSPEC_ABI_VERSION 3
+#define HSPEC_ABI_VERSION 4
 int hspec_abi_version(void);
 
 /*
@@ -246,6 +246,37 @@ size_t hspec_mamba_args_size(void);
 /* `required_bytes` receives the workspace size (may be NULL when
  * a->workspace is set). */
 int hspec_mamba_block(void* stream, const hspec_mamba_args* a, size_t* required_bytes);
+
+/*
+ * Contrast workload, not part of H-Spec's path: the drafter-side KV
+ * injection of the parallel drafters H-Spec is compared with (H-Spec,
+ * Abstract, Table 1 and Figure 3: a projection of the target hidden state at
+ * every new position into a drafter KV cache; H-Spec never runs this step).
+ * Per request b and new position i < n_new, token position
+ * p = start_pos[b] + i:
+ *
+ *   kv = w_kv . hidden[b, i]                    (w_kv: K rows, then V rows)
+ *   k_cache[page_table[b][p/16], p%16, h, :] = kv[h*D .. h*D + D)
+ *   v_cache[page_table[b][p/16], p%16, h, :] = kv[Hkv*D + h*D .. Hkv*D + h*D + D)
+ *
+ * written in the activation type; nothing else in the pools changes.
+ *   hidden      act [C, n_new, d_model]
+ *   w_kv        act [2*Hkv*D, d_model]       ([out, in])
+ *   k_cache,    act pools written in place, strides in elements as for
+ *   v_cache         hspec_block_attn_inplace (multiples of 8)
+ *   page_table  int32 [C, max_pages] device;  start_pos int32 [C] device
+ * A position whose page-table slot lies past max_pages, or whose entry lies
+ * outside [0, num_pages), is skipped (never a stray write).  Requests must
+ * own distinct pages: writes to one slot from two requests race.
+ * Runs on bf16 matrix cores (fp32 FMA for fp32), fp32 accumulation.
+ * `workspace` == NULL is a size query as for a3 (split-K partials).
+ * Limits: d_model % 8 == 0 (else UNSUPPORTED); hidden, w_kv 16-byte aligned.
+ */
+int hspec_kv_inject(void* stream, int dtype, int C, int n_new, int d_model, int Hkv, int D,
+                    const void* hidden, const void* w_kv, void* k_cache, void* v_cache,
+                    int64_t page_stride, int64_t token_stride, int64_t head_stride, int num_pages,
+                    const int32_t* page_table, int max_pages, const int32_t* start_pos,
+                    void* workspace, size_t* workspace_bytes);
 
 #ifdef __cplusplus
 }

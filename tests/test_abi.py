@@ -27,10 +27,11 @@ def test_loads_and_exports_every_declared_symbol():
     L = ops.lib()
     names = declared_functions()
     assert {"hspec_init_state", "hspec_ssd_scan", "hspec_block_attn_inplace",
-            "hspec_draft_layer", "hspec_mamba_block", "hspec_probe_stream_read"} <= set(names)
+            "hspec_draft_layer", "hspec_mamba_block", "hspec_kv_inject",
+            "hspec_probe_stream_read"} <= set(names)
     for n in names:
         assert hasattr(L, n), f"{n} declared in hspec.h but not exported"
-    assert L.hspec_abi_version() == 3
+    assert L.hspec_abi_version() == 4
     assert L.hspec_layer_args_size() == ctypes.sizeof(ops.LayerArgs)
     assert L.hspec_mamba_args_size() == ctypes.sizeof(ops.MambaArgs)
     assert L.hspec_status_string(-2) == b"HSPEC_ERR_UNSUPPORTED"
@@ -177,3 +178,27 @@ def test_mamba_block_validation_and_workspace():
     assert _block(workspace=FAKE, workspace_bytes=n - 1)[0] == WORKSPACE
     assert _block(workspace=FAKE + 16, workspace_bytes=n)[0] == WORKSPACE
     assert ops.lib().hspec_mamba_block(None, None, None) == INVALID
+
+
+def _inject(ws=None, nbytes=0, **kw):
+    a = dict(dtype=1, C=128, n=16, d=4096, Hkv=8, D=128, ps=16 * 8 * 128, ts=8 * 128, hs=128,
+             num_pages=1000, max_pages=600, hidden=FAKE, w=FAKE)
+    a.update(kw)
+    n = ctypes.c_size_t(nbytes)
+    code = ops.lib().hspec_kv_inject(None, a["dtype"], a["C"], a["n"], a["d"], a["Hkv"], a["D"], a["hidden"],
+                                     a["w"], FAKE, FAKE, a["ps"], a["ts"], a["hs"], a["num_pages"], FAKE,
+                                     a["max_pages"], FAKE, ws, ctypes.byref(n))
+    return code, n.value
+
+
+def test_kv_inject_validation_and_workspace():
+    code, n = _inject()
+    assert code == OK and n == 256                         # 2048 x 2048 x 4096: no K slices
+    code, n1 = _inject(C=1)                                 # 16 rows: K sliced, partials needed
+    assert code == OK and n1 > 256 and n1 % 256 == 0
+    assert _inject(n=0)[0] == INVALID
+    assert _inject(hidden=FAKE + 8)[0] == INVALID
+    assert _inject(ts=100)[0] == INVALID
+    assert _inject(num_pages=0)[0] == INVALID
+    assert _inject(d=4100)[0] == UNSUPPORTED
+    assert _inject(ws=FAKE, nbytes=n1 - 1, C=1)[0] == WORKSPACE
