@@ -164,14 +164,14 @@ def draw_ctx_lens(w: Workload, ss: np.random.SeedSequence) -> np.ndarray:
 
 
 def build_page_table(ctx_lens: np.ndarray, ss: np.random.SeedSequence,
-                     spare: int = SPARE_PAGES, identity: bool = False):
-    """Shared page pool with interleaved pages.
+                     spare: int = SPARE_PAGES, identity: bool = False, page_size: int = PAGE):
+    """Shared page pool with interleaved pages of page_size tokens.
 
     Returns (page_table int32 [C, max_pages] with -1 padding, num_pages, pages_of
     list of int arrays).  identity=True hands out pages in order (no shuffle).
     """
     ctx_lens = np.asarray(ctx_lens, dtype=np.int64)
-    n_pages = (ctx_lens + PAGE - 1) // PAGE
+    n_pages = (ctx_lens + page_size - 1) // page_size
     total = int(n_pages.sum())
     pool = total + spare
     if identity:

@@ -12,6 +12,10 @@ Definition, per request b and query head i (kv head j = i // G, G = Hq/Hkv):
     Kctx_b,j[n] = Kc[PT[b, n // 16], n % 16, j]     for n < ctx_b
     o[b, :, i] = softmax(scale * q[b, :, i] @ Kall^T) @ Vall,   scale = 1/sqrt(D)
 
+Pages hold page_size tokens (the pool's second extent; 16 in the workloads,
+other sizes are the same tokens laid out in bigger pages).  The split-KV form
+below counts its splits in 16-token slabs whatever the page size.
+
 Page reads here are strict: a page-table entry outside the pool, or a NaN in
 a token that should be valid, raises PoisonedRead.  The workloads fill spare
 pages and the tail slots past ctx_b with NaN, so reading the wrong page or the
@@ -41,18 +45,21 @@ class PoisonedRead(RuntimeError):
 def gather_context(cache, page_row, ctx_len: int, j: int, dtype: str) -> np.ndarray:
     """Target keys (or values) of one request and kv head as [ctx_len, D] float64.
 
-    cache: stored pool [num_pages, 16, Hkv, D]; page_row: that request's page
-    table row.  Reads only the pages and slots that hold valid tokens.
+    cache: stored pool [num_pages, page_size, Hkv, D] (the page size is the
+    pool's second extent, 16 in the workloads); page_row: that request's page
+    table row, token n at slot n % page_size of page page_row[n // page_size].
+    Reads only the pages and slots that hold valid tokens.
     """
     ctx_len = int(ctx_len)
+    P = cache.shape[1]
     D = cache.shape[-1]
     if ctx_len == 0:
         return np.zeros((0, D))
-    n_pages = -(-ctx_len // PAGE)
+    n_pages = -(-ctx_len // P)
     pages = np.asarray(page_row[:n_pages], dtype=np.int64)
     if len(pages) < n_pages or (pages < 0).any() or (pages >= cache.shape[0]).any():
         raise PoisonedRead(f"page table entry out of range: {pages}")
-    rows = np.asarray(cache[pages, :, j, :]).reshape(n_pages * PAGE, D)[:ctx_len]
+    rows = np.asarray(cache[pages, :, j, :]).reshape(n_pages * P, D)[:ctx_len]
     rows = decode(rows, dtype)
     if np.isnan(rows).any():
         raise PoisonedRead("read a NaN-poisoned token")

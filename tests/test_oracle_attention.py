@@ -257,3 +257,53 @@ def test_block_causal_split_invariance(pps):
     o = oracle.block_attention_splits(d["q"], d["k_blk"], d["v_blk"], d["k_cache"], d["v_cache"],
                                       d["page_table"], d["ctx_lens"], pps, dtype="f32", block_causal=True)
     _close(o, ref)
+
+
+def test_gather_with_bigger_pages_returns_the_logical_rows():
+    """Pools of 32- and 64-token pages, built here by explicit loops from the
+    logical context rows and a scrambled page table, gather back to those rows;
+    slots past ctx are poisoned, so an off-by-one read raises."""
+    g = np.random.default_rng(41)
+    Hkv, D = 2, 8
+    for P in (32, 64):
+        for ctx in (1, P - 1, P, P + 1, 3 * P + 5):
+            rows = g.standard_normal((ctx, Hkv, D)).astype(np.float32)
+            n_pages = -(-ctx // P)
+            perm = g.permutation(n_pages + 3)
+            pool = np.full((n_pages + 3, P, Hkv, D), np.nan, np.float32)
+            for n in range(ctx):
+                pool[perm[n // P], n % P] = rows[n]
+            row = np.full(n_pages + 2, -1, np.int32)
+            row[:n_pages] = perm[:n_pages]
+            for j in range(Hkv):
+                np.testing.assert_array_equal(oracle.gather_context(pool, row, ctx, j, "f32"), rows[:, j])
+            with pytest.raises(oracle.PoisonedRead):   # a poisoned slot, or a -1 page entry
+                oracle.gather_context(pool, row, ctx + 1, 0, "f32")
+
+
+def test_attention_is_independent_of_the_page_size():
+    """The same context stored in 16- and 64-token pages gives the same output."""
+    g = np.random.default_rng(42)
+    C, K, Hq, Hkv, D = 2, 4, 4, 2, 16
+    ctx = np.array([70, 129], np.int32)
+    q = g.standard_normal((C, K, Hq, D)).astype(np.float32)
+    kb = g.standard_normal((C, K, Hkv, D)).astype(np.float32)
+    vb = g.standard_normal((C, K, Hkv, D)).astype(np.float32)
+    outs = []
+    for P in (16, 64):
+        kl = [g.standard_normal((c, Hkv, D)).astype(np.float32) for c in ctx] if P == 16 else kl
+        vl = [g.standard_normal((c, Hkv, D)).astype(np.float32) for c in ctx] if P == 16 else vl
+        pages = [-(-int(c) // P) for c in ctx]
+        pool_k = np.full((sum(pages), P, Hkv, D), np.nan, np.float32)
+        pool_v = pool_k.copy()
+        pt = np.full((C, max(pages)), -1, np.int32)
+        perm = g.permutation(sum(pages))
+        off = 0
+        for b, c in enumerate(ctx):
+            pt[b, :pages[b]] = perm[off:off + pages[b]]
+            off += pages[b]
+            for n in range(int(c)):
+                pool_k[pt[b, n // P], n % P] = kl[b][n]
+                pool_v[pt[b, n // P], n % P] = vl[b][n]
+        outs.append(oracle.block_attention(q, kb, vb, pool_k, pool_v, pt, ctx, dtype="f32"))
+    np.testing.assert_array_equal(outs[0], outs[1])
