@@ -156,7 +156,10 @@ def measure(w, inp, args, torch, flush, with_parts=True):
 
 
 def measure_variants(w, inp, args, torch, flush):
-    """The layer with the block-causal mask, and the direct-reuse-only ablation."""
+    """The layer with the block-causal mask, the direct-reuse-only ablation,
+    and the attention over the same pools viewed as 64-token pages."""
+    import numpy as np
+    from hybrid_mamba_attention_amd import ops
     out = {}
     for name, kw in (("block_causal", dict(block_causal=True)), ("direct_reuse_only", dict(no_init=True))):
         layer, t = build_layer(inp, args.kv_split_pages, torch, **kw)
@@ -164,6 +167,34 @@ def measure_variants(w, inp, args, torch, flush):
         out[name] = dict(ms_per_step=st["mean"], block_tokens_per_s=w.C * w.K / (st["mean"] * 1e-3))
         del layer, t
         torch.cuda.empty_cache()
+    # 64-token pages: the pool memory regrouped four 16-token pages at a time
+    # and a fresh shuffled table of 64-token pages (same context lengths; the
+    # token values differ, which does not change the work)
+    t = {k: dev(inp.arrays[k], torch) for k in ("q", "k_blk", "v_blk", "k_cache", "v_cache")}
+    n64 = t["k_cache"].shape[0] // 4
+    kc = t["k_cache"][:4 * n64].view(n64, 64, w.Hkv, w.D)
+    vc = t["v_cache"][:4 * n64].view(n64, 64, w.Hkv, w.D)
+    need = [-(-int(c) // 64) for c in inp.ctx_lens]
+    if sum(need) <= n64:
+        perm = np.random.default_rng(w.seed + 64).permutation(n64)
+        pt = np.full((w.C, max(need)), 0, np.int32)
+        off = 0
+        for b, n in enumerate(need):
+            pt[b, :n] = perm[off:off + n]
+            off += n
+        pt, cl = dev(pt, torch), dev(inp.ctx_lens, torch)
+        o = torch.empty_like(t["q"])
+        ws = None
+
+        def attn64():
+            ops.block_attn_inplace(t["q"], t["k_blk"], t["v_blk"], kc, vc, pt, cl, max_ctx=inp.max_ctx,
+                                   out=o, workspace=ws)
+        _, ws = ops.block_attn_inplace(t["q"], t["k_blk"], t["v_blk"], kc, vc, pt, cl, max_ctx=inp.max_ctx, out=o)
+        st = stats(timed(attn64, args.steps, args.warmup, flush, torch))
+        out["page_size_64"] = dict(attention_ms=st["mean"],
+                                   algorithmic_gbs=attention_bytes(w, inp.ctx_lens) / (st["mean"] * 1e-3) / 1e9)
+    del t
+    torch.cuda.empty_cache()
     return out
 
 

@@ -58,11 +58,20 @@ int check_ssd(int dtype, int C, int K, int H, int P, int ng, int N, int chunk, c
 }
 
 struct AttnPlanShape {
-  int pps, M, MS;  // pages per split, C * MS work items, splits of a max_ctx request
+  int pps, M, MS;  // 16-token slabs per split, C * MS work items, splits of a max_ctx request
   size_t plan_bytes, part_o_off, part_ml_off, total;
 };
 
-int auto_pages_per_split(int C, int Hkv, int max_ctx) {
+// log2(page_size / 16) for a supported page size, else -1
+int page_shift(int page_size) {
+  for (int l = 0; l <= 4; ++l)
+    if (page_size == (16 << l)) return l;
+  return -1;
+}
+
+// Slabs (16 tokens) per split; splits start on page boundaries, so the result
+// is a multiple of the page's slab count spp.
+int auto_pages_per_split(int C, int Hkv, int max_ctx, int spp) {
   const int max_pages = (max_ctx + 15) / 16;
   if (max_pages <= 0) return 16;
   const int64_t base = int64_t(C) * Hkv;
@@ -72,16 +81,19 @@ int auto_pages_per_split(int C, int Hkv, int max_ctx) {
   // per-item prologue and fp32 partials: G*K rows x (D+2) written and read
   // back by the merge).  Past 512 (request, kv head) pairs nothing is split.
   const int64_t target = 512;
-  if (base >= target) return max_pages;
+  if (base >= target) return (max_pages + spp - 1) / spp * spp;
   const int64_t splits = (target + base - 1) / base;
   int64_t pps = (max_pages + splits - 1) / splits;
   if (pps < 16) pps = 16;    // >= 256 tokens per item: partials stay small next to the KV they summarise
-  return int((pps + 7) / 8 * 8);
+  const int64_t m = std::max(8, spp);
+  return int((pps + m - 1) / m * m);
 }
 
-AttnPlanShape plan_shape(int C, int K, int Hq, int Hkv, int D, int max_ctx, int kv_split_pages) {
+AttnPlanShape plan_shape(int C, int K, int Hq, int Hkv, int D, int max_ctx, int kv_split_pages,
+                         int page_size) {
   AttnPlanShape p{};
-  p.pps = kv_split_pages > 0 ? kv_split_pages : auto_pages_per_split(C, Hkv, max_ctx);
+  const int spp = page_size / 16;
+  p.pps = kv_split_pages > 0 ? kv_split_pages * spp : auto_pages_per_split(C, Hkv, max_ctx, spp);
   const int64_t max_pages = (int64_t(max_ctx) + 15) / 16;
   const int64_t max_splits = std::max<int64_t>(1, (max_pages + p.pps - 1) / p.pps);
   p.MS = int(std::min<int64_t>(max_splits, 0x7fffffff));
@@ -101,8 +113,8 @@ AttnPlanShape plan_shape(int C, int K, int Hq, int Hkv, int D, int max_ctx, int 
 
 int check_attn(int dtype, int C, int K, int Hq, int Hkv, int D, const void* q, const void* kb,
                const void* vb, const void* kc, const void* vc, int64_t ps, int64_t ts, int64_t hs,
-               int num_pages, const int32_t* pt, int max_pages, const int32_t* ctx, int max_ctx,
-               int kv_split_pages, float scale, int block_causal, const void* out,
+               int num_pages, int page_size, const int32_t* pt, int max_pages, const int32_t* ctx,
+               int max_ctx, int kv_split_pages, float scale, int block_causal, const void* out,
                const size_t* ws_bytes) {
   if (!dtype_ok(dtype) || C < 1 || K < 1 || Hq < 1 || Hkv < 1) return HSPEC_ERR_INVALID_ARG;
   if (Hq % Hkv) return HSPEC_ERR_INVALID_ARG;
@@ -113,25 +125,28 @@ int check_attn(int dtype, int C, int K, int Hq, int Hkv, int D, const void* q, c
   for (const void* p : {q, kb, vb, kc, vc, out})
     if (!aligned(p, 16)) return HSPEC_ERR_INVALID_ARG;
   if (!aligned(pt, 4) || !aligned(ctx, 4)) return HSPEC_ERR_INVALID_ARG;
-  if (num_pages < 1 || max_ctx < 0 || kv_split_pages < 0) return HSPEC_ERR_INVALID_ARG;
-  if (int64_t(max_pages) < std::max<int64_t>(1, (int64_t(max_ctx) + 15) / 16)) return HSPEC_ERR_INVALID_ARG;
+  if (num_pages < 1 || max_ctx < 0 || kv_split_pages < 0 || page_size < 1) return HSPEC_ERR_INVALID_ARG;
+  if (page_shift(page_size) < 0) return HSPEC_ERR_UNSUPPORTED;
+  if (kv_split_pages > 0x7fffffff / (page_size / 16)) return HSPEC_ERR_UNSUPPORTED;
+  if (int64_t(max_pages) < std::max<int64_t>(1, (int64_t(max_ctx) + page_size - 1) / page_size))
+    return HSPEC_ERR_INVALID_ARG;
   if (!(scale >= 0.f) || !std::isfinite(scale)) return HSPEC_ERR_INVALID_ARG;
   if (block_causal != 0 && block_causal != 1) return HSPEC_ERR_INVALID_ARG;
   if (D != 64 && D != 128) return HSPEC_ERR_UNSUPPORTED;
   if (K > 64) return HSPEC_ERR_UNSUPPORTED;
   if (int64_t(Hq / Hkv) * K > 256) return HSPEC_ERR_UNSUPPORTED;
   if (attn_lds_bytes(dtype, D, (Hq / Hkv) * K, K) > kMaxLds) return HSPEC_ERR_UNSUPPORTED;
-  const AttnPlanShape p = plan_shape(C, K, Hq, Hkv, D, max_ctx, kv_split_pages);
+  const AttnPlanShape p = plan_shape(C, K, Hq, Hkv, D, max_ctx, kv_split_pages, page_size);
   if (int64_t(C) * p.MS * Hkv > 0x7fffffff) return HSPEC_ERR_UNSUPPORTED;
   return HSPEC_OK;
 }
 
 int run_attn(hipStream_t st, int dtype, int C, int K, int Hq, int Hkv, int D, const void* q,
              const void* kb, const void* vb, const void* kc, const void* vc, int64_t ps, int64_t ts,
-             int64_t hs, int num_pages, const int32_t* pt, int max_pages, const int32_t* ctx,
-             int max_ctx, int kv_split_pages, float scale, int block_causal, void* out, void* ws,
-             size_t ws_bytes) {
-  const AttnPlanShape p = plan_shape(C, K, Hq, Hkv, D, max_ctx, kv_split_pages);
+             int64_t hs, int num_pages, int page_size, const int32_t* pt, int max_pages,
+             const int32_t* ctx, int max_ctx, int kv_split_pages, float scale, int block_causal,
+             void* out, void* ws, size_t ws_bytes) {
+  const AttnPlanShape p = plan_shape(C, K, Hq, Hkv, D, max_ctx, kv_split_pages, page_size);
   if (!ws || !aligned(ws, 256) || ws_bytes < p.total) return HSPEC_ERR_WORKSPACE;
   AttnArgs a{};
   a.q = q; a.k_blk = kb; a.v_blk = vb; a.k_cache = kc; a.v_cache = vc;
@@ -150,6 +165,7 @@ int run_attn(hipStream_t st, int dtype, int C, int K, int Hq, int Hkv, int D, co
   a.pps = p.pps;
   a.max_splits = p.MS;
   a.block_causal = block_causal;
+  a.lsp = page_shift(page_size);
   return status_of(launch_block_attn(st, dtype, a));
 }
 
@@ -242,7 +258,7 @@ int run_block(hipStream_t s, const hspec_mamba_args* a, const BlockPlan& p) {
 
 int check_inject(int dtype, int C, int n_new, int d, int Hkv, int D, const void* hidden,
                  const void* w_kv, const void* kc, const void* vc, int64_t ps, int64_t ts, int64_t hs,
-                 int num_pages, const int32_t* pt, int max_pages, const int32_t* start,
+                 int num_pages, int page_size, const int32_t* pt, int max_pages, const int32_t* start,
                  const size_t* ws_bytes) {
   if (!dtype_ok(dtype) || C < 1 || n_new < 1 || d < 1 || Hkv < 1 || D < 1) return HSPEC_ERR_INVALID_ARG;
   if (!hidden || !w_kv || !kc || !vc || !pt || !start || !ws_bytes) return HSPEC_ERR_INVALID_ARG;
@@ -250,7 +266,8 @@ int check_inject(int dtype, int C, int n_new, int d, int Hkv, int D, const void*
     return HSPEC_ERR_INVALID_ARG;
   const int vec = 16 / esize(dtype);
   if (ps <= 0 || ts <= 0 || hs <= 0 || ps % vec || ts % vec || hs % vec) return HSPEC_ERR_INVALID_ARG;
-  if (num_pages < 1 || max_pages < 1) return HSPEC_ERR_INVALID_ARG;
+  if (num_pages < 1 || max_pages < 1 || page_size < 1) return HSPEC_ERR_INVALID_ARG;
+  if (page_shift(page_size) < 0) return HSPEC_ERR_UNSUPPORTED;
   if (d % 8) return HSPEC_ERR_UNSUPPORTED;
   if (int64_t(C) * n_new > (1 << 30) || int64_t(Hkv) * D > (1 << 28)) return HSPEC_ERR_UNSUPPORTED;
   return HSPEC_OK;
@@ -295,21 +312,21 @@ int hspec_ssd_scan(void* stream, int dtype, int C, int K, int H, int P, int ng, 
 int hspec_block_attn_inplace(void* stream, int dtype, int C, int K, int Hq, int Hkv, int D,
                              const void* q, const void* k_blk, const void* v_blk,
                              const void* k_cache, const void* v_cache, int64_t page_stride,
-                             int64_t token_stride, int64_t head_stride, int num_pages,
+                             int64_t token_stride, int64_t head_stride, int num_pages, int page_size,
                              const int32_t* page_table, int max_pages, const int32_t* ctx_lens,
                              int max_ctx, int kv_split_pages, float scale, int block_causal,
                              void* out, void* workspace, size_t* workspace_bytes) {
   const int st = check_attn(dtype, C, K, Hq, Hkv, D, q, k_blk, v_blk, k_cache, v_cache, page_stride,
-                            token_stride, head_stride, num_pages, page_table, max_pages, ctx_lens,
-                            max_ctx, kv_split_pages, scale, block_causal, out, workspace_bytes);
+                            token_stride, head_stride, num_pages, page_size, page_table, max_pages,
+                            ctx_lens, max_ctx, kv_split_pages, scale, block_causal, out, workspace_bytes);
   if (st != HSPEC_OK) return st;
   if (!workspace) {
-    *workspace_bytes = plan_shape(C, K, Hq, Hkv, D, max_ctx, kv_split_pages).total;
+    *workspace_bytes = plan_shape(C, K, Hq, Hkv, D, max_ctx, kv_split_pages, page_size).total;
     return HSPEC_OK;
   }
   return run_attn(static_cast<hipStream_t>(stream), dtype, C, K, Hq, Hkv, D, q, k_blk, v_blk,
-                  k_cache, v_cache, page_stride, token_stride, head_stride, num_pages, page_table,
-                  max_pages, ctx_lens, max_ctx, kv_split_pages, scale, block_causal, out, workspace,
+                  k_cache, v_cache, page_stride, token_stride, head_stride, num_pages, page_size,
+                  page_table, max_pages, ctx_lens, max_ctx, kv_split_pages, scale, block_causal, out, workspace,
                   *workspace_bytes);
 }
 
@@ -329,16 +346,19 @@ int hspec_draft_layer(void* stream, const hspec_layer_args* a, size_t* required_
   size_t dummy = 0;
   st = check_attn(a->dtype, a->C, a->K, a->Hq, a->Hkv, a->D, a->q, a->k_blk, a->v_blk, a->k_cache,
                   a->v_cache, a->page_stride, a->token_stride, a->head_stride, a->num_pages,
-                  a->page_table, a->max_pages, a->ctx_lens, a->max_ctx, a->kv_split_pages, a->scale,
+                  a->page_size, a->page_table, a->max_pages, a->ctx_lens, a->max_ctx, a->kv_split_pages,
+                  a->scale,
                   a->block_causal, a->out, &dummy);
   if (st != HSPEC_OK) return st;
-  const size_t need = plan_shape(a->C, a->K, a->Hq, a->Hkv, a->D, a->max_ctx, a->kv_split_pages).total;
+  const size_t need = plan_shape(a->C, a->K, a->Hq, a->Hkv, a->D, a->max_ctx, a->kv_split_pages,
+                                 a->page_size).total;
   if (required_bytes) *required_bytes = need;
   if (!a->workspace) return required_bytes ? HSPEC_OK : HSPEC_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   st = run_attn(s, a->dtype, a->C, a->K, a->Hq, a->Hkv, a->D, a->q, a->k_blk, a->v_blk, a->k_cache,
                 a->v_cache, a->page_stride, a->token_stride, a->head_stride, a->num_pages,
-                a->page_table, a->max_pages, a->ctx_lens, a->max_ctx, a->kv_split_pages, a->scale,
+                a->page_size, a->page_table, a->max_pages, a->ctx_lens, a->max_ctx, a->kv_split_pages,
+                a->scale,
                 a->block_causal, a->out, a->workspace, a->workspace_bytes);
   if (st != HSPEC_OK) return st;
   if (!no_init) {
@@ -366,11 +386,11 @@ int hspec_mamba_block(void* stream, const hspec_mamba_args* a, size_t* required_
 int hspec_kv_inject(void* stream, int dtype, int C, int n_new, int d_model, int Hkv, int D,
                     const void* hidden, const void* w_kv, void* k_cache, void* v_cache,
                     int64_t page_stride, int64_t token_stride, int64_t head_stride, int num_pages,
-                    const int32_t* page_table, int max_pages, const int32_t* start_pos,
+                    int page_size, const int32_t* page_table, int max_pages, const int32_t* start_pos,
                     void* workspace, size_t* workspace_bytes) {
   const int st = check_inject(dtype, C, n_new, d_model, Hkv, D, hidden, w_kv, k_cache, v_cache,
-                              page_stride, token_stride, head_stride, num_pages, page_table, max_pages,
-                              start_pos, workspace_bytes);
+                              page_stride, token_stride, head_stride, num_pages, page_size, page_table,
+                              max_pages, start_pos, workspace_bytes);
   if (st != HSPEC_OK) return st;
   const int M = C * n_new, N = 2 * Hkv * D;
   const GemmPlan p = gemm_plan(dtype, M, N, d_model);
@@ -385,7 +405,7 @@ int hspec_kv_inject(void* stream, int dtype, int C, int n_new, int d_model, int 
   g.M = M; g.N = N; g.K = d_model; g.lda = d_model; g.ldb = d_model; g.ldc = N;
   g.scatter = 1;
   g.sc = KvScatter{page_table, start_pos, k_cache, v_cache, page_stride, token_stride, head_stride,
-                   n_new, max_pages, num_pages, Hkv * D, D};
+                   n_new, max_pages, num_pages, Hkv * D, D, 4 + page_shift(page_size)};
   return status_of(launch_gemm_tn(static_cast<hipStream_t>(stream), dtype, 0, g, p));
 }
 

@@ -235,16 +235,22 @@ __global__ __launch_bounds__(64 * NW) void k_block_attn(AttnArgs a) {
     for (int ds = 0; ds < DS; ++ds) load8(qv[rt][ds], qp + (lg + 4 * ds) * 8);
   }
   const int32_t* __restrict__ pt = a.page_table + size_t(b) * a.max_pages;
+  // The kernel walks the context in slabs of 16 tokens; a page holds
+  // 2^lsp slabs (page size 16 << lsp), so slab q lies in page q >> lsp at
+  // token offset 16 * (q & (2^lsp - 1)).  Splits start on page boundaries.
+  const int lsp = a.lsp, smask = (1 << lsp) - 1;
   // Page-table window of the hot path: lane l holds the item's entries
-  // p_lo + 128*w + l and p_lo + 128*w + 64 + l of the current window w, and a
-  // stage takes its two entries with v_readlane.  The window is one vector
-  // load per 64 stages (a scalar read waited on at every issue, missing the
-  // scalar cache every 8 stages, cost ~4% at 256 stages per item).  Entries
-  // past the table row are clamped into it.
+  // pg_lo + 128*w + l and pg_lo + 128*w + 64 + l of the current window w
+  // (pg_lo = the split's first page), and a stage takes its entries with
+  // v_readlane.  The window is one vector load per 128 pages (a scalar read
+  // waited on at every issue, missing the scalar cache every 8 stages, cost
+  // ~4% at 256 stages per item).  Entries past the table row are clamped into
+  // it.
   int pwlo = 0, pwhi = 0;
   auto load_window = [&](int w) __attribute__((always_inline)) {
-    pwlo = pt[min(p_lo + 128 * w + lane, a.max_pages - 1)];
-    pwhi = pt[min(p_lo + 128 * w + 64 + lane, a.max_pages - 1)];
+    const int base = (p_lo >> lsp) + 128 * w;
+    pwlo = pt[min(base + lane, a.max_pages - 1)];
+    pwhi = pt[min(base + 64 + lane, a.max_pages - 1)];
   };
   load_window(0);
 
@@ -277,6 +283,7 @@ __global__ __launch_bounds__(64 * NW) void k_block_attn(AttnArgs a) {
   const char* __restrict__ kcj = static_cast<const char*>(a.k_cache) + head_off;
   const char* __restrict__ vcj = static_cast<const char*>(a.v_cache) + head_off;
   const int64_t page_b = a.page_stride * int64_t(sizeof(T));
+  const int64_t slab_b = 16 * a.token_stride * int64_t(sizeof(T));
   const int last_phys = a.num_pages - 1;
   const char* kblk = static_cast<const char*>(a.k_blk) + ((size_t(b) * K) * Hkv + j) * D * sizeof(T);
   const char* vblk = static_cast<const char*>(a.v_blk) + ((size_t(b) * K) * Hkv + j) * D * sizeof(T);
@@ -296,9 +303,9 @@ __global__ __launch_bounds__(64 * NW) void k_block_attn(AttnArgs a) {
     Page pg{kcj, vcj, 0, false, 0};
     if (vp < ncache) {
       const int lp = p_lo + vp;
-      const int phys = pt[lp];
+      const int phys = pt[lp >> lsp];
       if (phys >= 0 && phys <= last_phys) {
-        const int64_t off = int64_t(phys) * page_b;
+        const int64_t off = int64_t(phys) * page_b + int64_t(lp & smask) * slab_b;
         pg.k = kcj + off;
         pg.v = vcj + off;
         pg.n = min(16, ctx - lp * 16);
@@ -335,14 +342,18 @@ __global__ __launch_bounds__(64 * NW) void k_block_attn(AttnArgs a) {
   // never a stray read).
   constexpr bool kHot = RPP * CPR == NT;
   auto issue_hot = [&](int st, uint4 (&stk)[NLD], uint4 (&stv)[NLD]) __attribute__((always_inline)) {
-    const int o = (2 * st) & 127, l0 = o & 63;
-    const int v = (o >> 6) ? pwhi : pwlo;
-    const int ph0 = min(max(__builtin_amdgcn_readlane(v, l0), 0), last_phys);
-    const int ph1 = min(max(__builtin_amdgcn_readlane(v, l0 + 1), 0), last_phys);
-    const char* k0 = kcj + int64_t(ph0) * page_b;
-    const char* v0 = vcj + int64_t(ph0) * page_b;
-    const char* k1 = kcj + int64_t(ph1) * page_b;
-    const char* v1 = vcj + int64_t(ph1) * page_b;
+    // slabs 2st and 2st+1 of the split: window entries o0, o1 (the same page
+    // unless pages are 16 tokens; an even o0 keeps both in one lane half)
+    const int q0 = 2 * st, o0 = (q0 >> lsp) & 127, o1 = ((q0 + 1) >> lsp) & 127;
+    const int v = (o0 >> 6) ? pwhi : pwlo;
+    const int ph0 = min(max(__builtin_amdgcn_readlane(v, o0 & 63), 0), last_phys);
+    const int ph1 = min(max(__builtin_amdgcn_readlane(v, o1 & 63), 0), last_phys);
+    const int64_t off0 = int64_t(ph0) * page_b + int64_t(q0 & smask) * slab_b;
+    const int64_t off1 = int64_t(ph1) * page_b + int64_t((q0 + 1) & smask) * slab_b;
+    const char* k0 = kcj + off0;
+    const char* v0 = vcj + off0;
+    const char* k1 = kcj + off1;
+    const char* v1 = vcj + off1;
 #pragma unroll
     for (int qq = 0; qq < RND; ++qq) {
       stk[qq] = ld_stream(k0 + coff[qq]);
@@ -544,8 +555,8 @@ __global__ __launch_bounds__(64 * NW) void k_block_attn(AttnArgs a) {
         constexpr int pp = decltype(P)::value;
         const int sn = st0 + pp + PF;   // < nhot
         commit(pp & 1, stk[pp], stv[pp]);
-        if ((sn & 63) == 0) {
-          load_window(sn >> 6);
+        if ((sn & ((64 << lsp) - 1)) == 0) {   // first stage of a 128-page window
+          load_window(sn >> (6 + lsp));
           __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
         }
         issue_hot(sn, stk[pp], stv[pp]);
@@ -572,7 +583,7 @@ __global__ __launch_bounds__(64 * NW) void k_block_attn(AttnArgs a) {
         const int n0 = nv[pp][0], n1 = nv[pp][1];
         if (st + PF < nstage) {
           const int sn = st + PF;
-          if ((sn & 63) == 0 && sn < nhot) load_window(sn >> 6);  // entering the next window
+          if ((sn & ((64 << lsp) - 1)) == 0 && sn < nhot) load_window(sn >> (6 + lsp));  // next window
           issue(sn, stk[pp], stv[pp], nv[pp]);
         }
         __syncthreads();

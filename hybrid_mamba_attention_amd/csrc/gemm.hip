@@ -38,10 +38,10 @@ namespace hspec {
 // row is not written), and of output column n (which pool, offset).
 __device__ __forceinline__ int64_t scatter_row(const KvScatter& s, int m) {
   const int b = m / s.n_new, p = s.start[b] + (m - b * s.n_new);
-  if (p < 0 || (p >> 4) >= s.max_pages) return -1;
-  const int page = s.page_table[size_t(b) * s.max_pages + (p >> 4)];
+  if (p < 0 || (p >> s.lpt) >= s.max_pages) return -1;
+  const int page = s.page_table[size_t(b) * s.max_pages + (p >> s.lpt)];
   if (page < 0 || page >= s.num_pages) return -1;
-  return int64_t(page) * s.ps + int64_t(p & 15) * s.ts;
+  return int64_t(page) * s.ps + int64_t(p & ((1 << s.lpt) - 1)) * s.ts;
 }
 template <typename OutT>
 __device__ __forceinline__ OutT* scatter_col(const KvScatter& s, int n) {

@@ -26,8 +26,9 @@ struct AttnArgs {
   float* part_o;                  // [max_items, Hkv, rows, D], item = request * max_splits + split
   float* part_ml;                 // [max_items, Hkv, rows, 2]
   int max_items;                  // C * max_splits
-  int pps, max_splits;            // context pages per split; splits of a max_ctx request
+  int pps, max_splits;            // 16-token slabs per split; splits of a max_ctx request
   int block_causal;               // 1: block query t sees block keys s <= t only
+  int lsp;                        // log2(page size / 16)
 };
 
 // a0 + a3 + a4 on `st`.
@@ -67,6 +68,7 @@ struct KvScatter {
   void* v_cache;
   int64_t ps, ts, hs;         // page, token, head strides in elements
   int n_new, max_pages, num_pages, HD, D;
+  int lpt;                    // log2(tokens per page)
 };
 
 // C[M, N] = A[M, K] . B[N, K]^T (row strides in elements); K % 8 == 0.

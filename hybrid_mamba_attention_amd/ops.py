@@ -34,7 +34,7 @@ class LayerArgs(ctypes.Structure):
         ("q", _vp), ("k_blk", _vp), ("v_blk", _vp),
         ("k_cache", _vp), ("v_cache", _vp),
         ("page_stride", _i64), ("token_stride", _i64), ("head_stride", _i64),
-        ("num_pages", _i), ("page_table", _vp), ("max_pages", _i),
+        ("num_pages", _i), ("page_size", _i), ("page_table", _vp), ("max_pages", _i),
         ("ctx_lens", _vp), ("max_ctx", _i),
         ("kv_split_pages", _i), ("scale", _f), ("block_causal", _i), ("out", _vp),
         ("workspace", _vp), ("workspace_bytes", _sz),
@@ -78,7 +78,7 @@ def lib() -> ctypes.CDLL:
     L.hspec_ssd_scan.argtypes = [_vp, _i] + [_i] * 7 + [_vp] * 9
     L.hspec_block_attn_inplace.restype = _i
     L.hspec_block_attn_inplace.argtypes = ([_vp, _i, _i, _i, _i, _i, _i] + [_vp] * 5 +
-                                           [_i64, _i64, _i64, _i, _vp, _i, _vp, _i, _i, _f, _i,
+                                           [_i64, _i64, _i64, _i, _i, _vp, _i, _vp, _i, _i, _f, _i,
                                             _vp, _vp, ctypes.POINTER(_sz)])
     L.hspec_draft_layer.restype = _i
     L.hspec_draft_layer.argtypes = [_vp, ctypes.POINTER(LayerArgs), ctypes.POINTER(_sz)]
@@ -87,8 +87,8 @@ def lib() -> ctypes.CDLL:
     L.hspec_mamba_block.argtypes = [_vp, ctypes.POINTER(MambaArgs), ctypes.POINTER(_sz)]
     L.hspec_kv_inject.restype = _i
     L.hspec_kv_inject.argtypes = ([_vp, _i, _i, _i, _i, _i, _i] + [_vp] * 4 +
-                                  [_i64, _i64, _i64, _i, _vp, _i, _vp, _vp, ctypes.POINTER(_sz)])
-    if L.hspec_abi_version() != 4:
+                                  [_i64, _i64, _i64, _i, _i, _vp, _i, _vp, _vp, ctypes.POINTER(_sz)])
+    if L.hspec_abi_version() != 5:
         raise RuntimeError("libhspec.so ABI version mismatch")
     if L.hspec_layer_args_size() != ctypes.sizeof(LayerArgs):
         raise RuntimeError("hspec_layer_args layout mismatch between library and binding")
@@ -182,10 +182,15 @@ def ssd_scan(x, delta, A, B, Cm, *, chunk: int, h0=None, Dskip=None, y=None, h_f
 # a0 + a3 + a4
 # ---------------------------------------------------------------------------
 
+def page_size_of(k_cache: torch.Tensor, layout: str = "NHD") -> int:
+    """Tokens per page of a pool tensor: [pages, P, Hkv, D] (NHD) or [pages, Hkv, P, D] (HND)."""
+    return int(k_cache.shape[1] if layout == "NHD" else k_cache.shape[2])
+
+
 def kv_strides(k_cache: torch.Tensor, layout: str = "NHD"):
     """(page, token, head) strides in elements of a pool tensor.
 
-    NHD pools are [pages, 16, Hkv, D]; HND pools are [pages, Hkv, 16, D]."""
+    NHD pools are [pages, P, Hkv, D]; HND pools are [pages, Hkv, P, D]."""
     s = k_cache.stride()
     if k_cache.stride(-1) != 1:
         raise ValueError("the head dimension of the KV pool must be contiguous")
@@ -205,8 +210,8 @@ def _attn_call(L, stream, q, k_blk, v_blk, k_cache, v_cache, page_table, ctx_len
         raise ValueError("K and V pools must share strides")
     return L.hspec_block_attn_inplace(
         stream, _dtype_code(q), C, K, Hq, Hkv, D, _ptr(q), _ptr(k_blk), _ptr(v_blk),
-        _ptr(k_cache), _ptr(v_cache), ps, ts, hs, k_cache.shape[0], _ptr(page_table),
-        page_table.shape[1], _ptr(ctx_lens), int(max_ctx), int(kv_split_pages), float(scale),
+        _ptr(k_cache), _ptr(v_cache), ps, ts, hs, k_cache.shape[0], page_size_of(k_cache, layout),
+        _ptr(page_table), page_table.shape[1], _ptr(ctx_lens), int(max_ctx), int(kv_split_pages), float(scale),
         int(bool(block_causal)), _ptr(out), ws, ctypes.byref(ws_bytes))
 
 
@@ -292,6 +297,7 @@ class DraftLayer:
         a.k_cache, a.v_cache = k_cache.data_ptr(), v_cache.data_ptr()
         a.page_stride, a.token_stride, a.head_stride = ps, ts, hs
         a.num_pages = k_cache.shape[0]
+        a.page_size = page_size_of(k_cache, layout)
         a.page_table, a.max_pages = page_table.data_ptr(), page_table.shape[1]
         a.ctx_lens, a.max_ctx = ctx_lens.data_ptr(), int(max_ctx)
         a.kv_split_pages, a.scale = int(kv_split_pages), float(scale)
@@ -384,8 +390,8 @@ def _inject_call(stream, hidden, w_kv, k_cache, v_cache, page_table, start_pos, 
         raise ValueError("K and V pools must share strides")
     return lib().hspec_kv_inject(
         stream, _dtype_code(hidden), C, n_new, d, Hkv, D, _ptr(hidden), _ptr(w_kv), _ptr(k_cache),
-        _ptr(v_cache), ps, ts, hs, k_cache.shape[0], _ptr(page_table), page_table.shape[1],
-        _ptr(start_pos), ws, ctypes.byref(n))
+        _ptr(v_cache), ps, ts, hs, k_cache.shape[0], page_size_of(k_cache, layout), _ptr(page_table),
+        page_table.shape[1], _ptr(start_pos), ws, ctypes.byref(n))
 
 
 def kv_inject(hidden, w_kv, k_cache, v_cache, page_table, start_pos, *, workspace=None, layout="NHD",

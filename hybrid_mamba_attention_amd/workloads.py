@@ -335,10 +335,11 @@ def make_block_inputs(w: Workload, *, with_dskip: bool = True, with_h0: bool = T
 # drafter-side KV injection (the contrast workload)
 # ----------------------------------------------------------------------------
 
-def make_inject_inputs(w: Workload, n_new: int, *, ctx_lens=None, spare: int = 8) -> dict:
+def make_inject_inputs(w: Workload, n_new: int, *, ctx_lens=None, spare: int = 8,
+                       page_size: int = PAGE) -> dict:
     """Inputs of one injection step: n_new new positions per request after
     ctx_lens[b] existing ones, written into a drafter-side paged pool shaped
-    like the target's ([pages, 16, Hkv, D], shuffled page table).
+    like the target's ([pages, page_size, Hkv, D], shuffled page table).
 
       * hidden [C, n_new, d_model]: N(0,1); w_kv [2*Hkv*D, d_model]: N(0, 0.02^2)
       * the pools hold N(0,1) values (the existing cache) plus NaN in spare pages
@@ -350,7 +351,8 @@ def make_inject_inputs(w: Workload, n_new: int, *, ctx_lens=None, spare: int = 8
     if ctx_lens is None:
         ctx_lens = draw_ctx_lens(w, ss["ctx"])
     start = np.asarray(ctx_lens, dtype=np.int32)
-    pt, pool, pages_of = build_page_table(start.astype(np.int64) + n_new, ss["perm"], spare=spare)
+    pt, pool, pages_of = build_page_table(start.astype(np.int64) + n_new, ss["perm"], spare=spare,
+                                          page_size=page_size)
 
     def normal(name, shape, std=1.0):
         return _normal_chunked(ss[name], int(np.prod(shape)), std, bf16).reshape(shape)
@@ -361,7 +363,7 @@ def make_inject_inputs(w: Workload, n_new: int, *, ctx_lens=None, spare: int = 8
     used = np.concatenate(pages_of) if pages_of else np.zeros(0, np.int64)
     nan = BF16_NAN if bf16 else F32_NAN
     for name in ("k", "v"):
-        arr = normal(name, (pool, PAGE, w.Hkv, w.D))
+        arr = normal(name, (pool, page_size, w.Hkv, w.D))
         spare_mask = np.ones(pool, dtype=bool)
         spare_mask[used] = False
         arr[spare_mask] = nan

@@ -48,7 +48,7 @@ typedef enum {
 const char* hspec_status_string(int status);
 
 /* ABI version of this header; bumped on any incompatible change. */
-#define HSPEC_ABI_VERSION 4
+#define HSPEC_ABI_VERSION 5
 int hspec_abi_version(void);
 
 /*
@@ -102,7 +102,7 @@ int hspec_ssd_scan(void* stream, int dtype, int C, int K, int H, int P, int ng, 
  * inside the block, to the ctx_lens[b] context tokens read through the page
  * table plus the K block keys:
  *
- *   keys   = Kc[page_table[b][n/16], n%16, j] (n < ctx_lens[b])  ++  k_blk[b, :, j]
+ *   keys   = Kc[page_table[b][n/P], n%P, j] (n < ctx_lens[b])  ++  k_blk[b, :, j]
  *   out[b, :, i] = softmax(scale * q[b, :, i] @ keys^T) @ values
  *
  * block_causal = 1 selects the block-causal variant instead (the pages fix
@@ -115,16 +115,17 @@ int hspec_ssd_scan(void* stream, int dtype, int C, int K, int H, int P, int ng, 
  *   k_cache,     act pools, read only; element (page, slot, j, d) sits at
  *   v_cache          page*page_stride + slot*token_stride + j*head_stride + d
  *                    (strides in elements, multiples of 8; d contiguous;
- *                    16 slots per page).  NHD [pages,16,Hkv,D] and HND
- *                    [pages,Hkv,16,D] pools are both just strides.
+ *                    P = page_size slots per page).  NHD [pages,P,Hkv,D] and
+ *                    HND [pages,Hkv,P,D] pools are both just strides.
  *   num_pages    pages in each pool (entries must lie in [0, num_pages))
+ *   page_size    tokens per page P: 16, 32, 64, 128 or 256 (else UNSUPPORTED)
  *   page_table   int32 [C, max_pages] device; row b lists request b's pages
- *                in context order; entries past ceil(ctx_lens[b]/16) are unused
+ *                in context order; entries past ceil(ctx_lens[b]/P) are unused
  *   ctx_lens     int32 [C] device; 0 <= ctx_lens[b] <= max_ctx
  *   max_ctx      host upper bound of ctx_lens (sizes the grid and workspace);
- *                max_pages >= ceil(max_ctx/16)
- *   kv_split_pages  context pages per split-KV work item (0 = pick
- *                automatically); results do not depend on it beyond fp32
+ *                max_pages >= ceil(max_ctx/P)
+ *   kv_split_pages  context pages (of P tokens) per split-KV work item (0 =
+ *                pick automatically); results do not depend on it beyond fp32
  *                rounding, and are bitwise repeatable for a fixed value
  *   scale        softmax scale; 0.f means 1/sqrt(D)
  *   out          act [C, K, Hq, D]
@@ -134,20 +135,20 @@ int hspec_ssd_scan(void* stream, int dtype, int C, int K, int H, int P, int ng, 
  *       the capacity of `workspace` (device, 256-byte aligned), which must be
  *       at least the queried size.  The workspace starts with the int32 split
  *       plan:
- *         [0] items  [1] pages per split  [2] C  [3] capacity M
+ *         [0] items  [1] 16-token slabs per split  [2] C  [3] capacity M
  *         [4, 4+C) splits of request b    [4+C, 4+2C) first item of request b
  *         [4+2C, 4+2C+M) request of item i (-1 unused)
  *         [4+2C+M, 4+2C+2M) split of item i (-1 unused)
- *       with splits_b = max(1, ceil(ceil(ctx_b/16) / pages_per_split)) and
- *       M = C * max(1, ceil(ceil(max_ctx/16) / pages_per_split)); the rest
- *       holds fp32 split partials.
+ *       with splits_b = max(1, ceil(ceil(ctx_b/16) / slabs_per_split)) and
+ *       M = C * max(1, ceil(ceil(max_ctx/16) / slabs_per_split)); the rest
+ *       holds fp32 split partials (slabs per split is a multiple of P/16).
  * Limits: D in {64, 128}; 1 <= K <= 64; Hq % Hkv == 0; (Hq/Hkv)*K <= 256.
  */
 int hspec_block_attn_inplace(void* stream, int dtype, int C, int K, int Hq, int Hkv, int D,
                              const void* q, const void* k_blk, const void* v_blk,
                              const void* k_cache, const void* v_cache,
                              int64_t page_stride, int64_t token_stride, int64_t head_stride,
-                             int num_pages, const int32_t* page_table, int max_pages,
+                             int num_pages, int page_size, const int32_t* page_table, int max_pages,
                              const int32_t* ctx_lens, int max_ctx,
                              int kv_split_pages, float scale, int block_causal, void* out,
                              void* workspace, size_t* workspace_bytes);
@@ -178,7 +179,7 @@ typedef struct hspec_layer_args {
   const void* q; const void* k_blk; const void* v_blk;
   const void* k_cache; const void* v_cache;
   int64_t page_stride, token_stride, head_stride;
-  int num_pages; const int32_t* page_table; int max_pages;
+  int num_pages; int page_size; const int32_t* page_table; int max_pages;
   const int32_t* ctx_lens; int max_ctx;
   int kv_split_pages; float scale; int block_causal; void* out;
   void* workspace; size_t workspace_bytes;
@@ -256,14 +257,14 @@ int hspec_mamba_block(void* stream, const hspec_mamba_args* a, size_t* required_
  * p = start_pos[b] + i:
  *
  *   kv = w_kv . hidden[b, i]                    (w_kv: K rows, then V rows)
- *   k_cache[page_table[b][p/16], p%16, h, :] = kv[h*D .. h*D + D)
- *   v_cache[page_table[b][p/16], p%16, h, :] = kv[Hkv*D + h*D .. Hkv*D + h*D + D)
+ *   k_cache[page_table[b][p/P], p%P, h, :] = kv[h*D .. h*D + D)
+ *   v_cache[page_table[b][p/P], p%P, h, :] = kv[Hkv*D + h*D .. Hkv*D + h*D + D)
  *
  * written in the activation type; nothing else in the pools changes.
  *   hidden      act [C, n_new, d_model]
  *   w_kv        act [2*Hkv*D, d_model]       ([out, in])
- *   k_cache,    act pools written in place, strides in elements as for
- *   v_cache         hspec_block_attn_inplace (multiples of 8)
+ *   k_cache,    act pools written in place, strides in elements and the page
+ *   v_cache         size P as for hspec_block_attn_inplace
  *   page_table  int32 [C, max_pages] device;  start_pos int32 [C] device
  * A position whose page-table slot lies past max_pages, or whose entry lies
  * outside [0, num_pages), is skipped (never a stray write).  Requests must
@@ -275,7 +276,7 @@ int hspec_mamba_block(void* stream, const hspec_mamba_args* a, size_t* required_
 int hspec_kv_inject(void* stream, int dtype, int C, int n_new, int d_model, int Hkv, int D,
                     const void* hidden, const void* w_kv, void* k_cache, void* v_cache,
                     int64_t page_stride, int64_t token_stride, int64_t head_stride, int num_pages,
-                    const int32_t* page_table, int max_pages, const int32_t* start_pos,
+                    int page_size, const int32_t* page_table, int max_pages, const int32_t* start_pos,
                     void* workspace, size_t* workspace_bytes);
 
 #ifdef __cplusplus

@@ -11,7 +11,8 @@ paged cache laid out like the target's:
 
     kv[b, i, :] = w_kv . hidden[b, i, :]             (w_kv is [2*Hkv*D, d_model])
     K rows are kv[..., :Hkv*D], V rows kv[..., Hkv*D:], head h at columns h*D .. h*D+D-1
-    position p = start[b] + i  ->  page page_table[b, p // 16], slot p % 16
+    position p = start[b] + i  ->  page page_table[b, p // P], slot p % P
+    (P = tokens per page, the pools' second extent)
 
 Everything else in the pools is left as it was.  float64 throughout; the
 returned pools hold float64 values (the caller compares written slots within
@@ -34,17 +35,18 @@ def kv_inject(hidden, w_kv, k_cache, v_cache, page_table, start, *, Hkv: int, D:
     positions written, and the projected rows [C, n, 2*Hkv*D].
 
     hidden [C, n, d] and w_kv are stored activations (decoded here); the pools
-    are stored arrays [pages, 16, Hkv, D] (NHD)."""
+    are stored arrays [pages, P, Hkv, D] (NHD)."""
     kv = kv_project(decode(hidden, dtype), decode(w_kv, dtype))
     kp = decode(k_cache, dtype).copy()
     vp = decode(v_cache, dtype).copy()
     C, n, _ = kv.shape
     HD = Hkv * D
+    P = kp.shape[1]
     for b in range(C):
         for i in range(n):
             p = int(start[b]) + i
-            page = int(page_table[b, p // PAGE])
-            slot = p % PAGE
+            page = int(page_table[b, p // P])
+            slot = p % P
             kp[page, slot] = kv[b, i, :HD].reshape(Hkv, D)
             vp[page, slot] = kv[b, i, HD:].reshape(Hkv, D)
     return kp, vp, kv

@@ -31,7 +31,7 @@ def test_loads_and_exports_every_declared_symbol():
             "hspec_probe_stream_read"} <= set(names)
     for n in names:
         assert hasattr(L, n), f"{n} declared in hspec.h but not exported"
-    assert L.hspec_abi_version() == 4
+    assert L.hspec_abi_version() == 5
     assert L.hspec_layer_args_size() == ctypes.sizeof(ops.LayerArgs)
     assert L.hspec_mamba_args_size() == ctypes.sizeof(ops.MambaArgs)
     assert L.hspec_status_string(-2) == b"HSPEC_ERR_UNSUPPORTED"
@@ -70,12 +70,12 @@ def test_ssd_validation(kw, code):
 
 def _attn(ws=None, nbytes=0, **kw):
     a = dict(dtype=1, C=4, K=16, Hq=32, Hkv=8, D=128, ps=16 * 8 * 128, ts=8 * 128, hs=128,
-             num_pages=100, max_pages=64, max_ctx=1000, split=0, scale=0.0, causal=0)
+             num_pages=100, max_pages=64, max_ctx=1000, split=0, scale=0.0, causal=0, page=16)
     a.update(kw)
     n = ctypes.c_size_t(nbytes)
     code = ops.lib().hspec_block_attn_inplace(
         None, a["dtype"], a["C"], a["K"], a["Hq"], a["Hkv"], a["D"], FAKE, FAKE, FAKE, FAKE, FAKE,
-        a["ps"], a["ts"], a["hs"], a["num_pages"], FAKE, a["max_pages"], FAKE, a["max_ctx"],
+        a["ps"], a["ts"], a["hs"], a["num_pages"], a["page"], FAKE, a["max_pages"], FAKE, a["max_ctx"],
         a["split"], a["scale"], a["causal"], FAKE, ws, ctypes.byref(n))
     return code, n.value
 
@@ -84,6 +84,8 @@ def _attn(ws=None, nbytes=0, **kw):
     (dict(Hq=30), INVALID), (dict(ts=100), INVALID), (dict(max_pages=10), INVALID),
     (dict(scale=-1.0), INVALID), (dict(split=-1), INVALID), (dict(K=0), INVALID),
     (dict(causal=2), INVALID), (dict(causal=-1), INVALID),
+    (dict(page=0), INVALID), (dict(page=48), UNSUPPORTED), (dict(page=8), UNSUPPORTED),
+    (dict(page=512), UNSUPPORTED), (dict(page=32, max_pages=31), INVALID),
     (dict(D=96), UNSUPPORTED), (dict(K=65), UNSUPPORTED), (dict(Hq=64, Hkv=2, K=16), UNSUPPORTED),
 ])
 def test_attention_validation(kw, code):
@@ -124,7 +126,7 @@ def _layer(**kw):
     a.Hq, a.Hkv, a.D = 32, 8, 128
     a.q = a.k_blk = a.v_blk = a.k_cache = a.v_cache = a.page_table = a.ctx_lens = a.out = FAKE
     a.page_stride, a.token_stride, a.head_stride = 16 * 8 * 128, 8 * 128, 128
-    a.num_pages, a.max_pages, a.max_ctx = 100, 64, 1000
+    a.num_pages, a.max_pages, a.max_ctx, a.page_size = 100, 64, 1000, 16
     for k, v in kw.items():
         setattr(a, k, v)
     n = ctypes.c_size_t(0)
@@ -182,11 +184,11 @@ def test_mamba_block_validation_and_workspace():
 
 def _inject(ws=None, nbytes=0, **kw):
     a = dict(dtype=1, C=128, n=16, d=4096, Hkv=8, D=128, ps=16 * 8 * 128, ts=8 * 128, hs=128,
-             num_pages=1000, max_pages=600, hidden=FAKE, w=FAKE)
+             num_pages=1000, max_pages=600, hidden=FAKE, w=FAKE, page=16)
     a.update(kw)
     n = ctypes.c_size_t(nbytes)
     code = ops.lib().hspec_kv_inject(None, a["dtype"], a["C"], a["n"], a["d"], a["Hkv"], a["D"], a["hidden"],
-                                     a["w"], FAKE, FAKE, a["ps"], a["ts"], a["hs"], a["num_pages"], FAKE,
+                                     a["w"], FAKE, FAKE, a["ps"], a["ts"], a["hs"], a["num_pages"], a["page"], FAKE,
                                      a["max_pages"], FAKE, ws, ctypes.byref(n))
     return code, n.value
 
@@ -201,4 +203,21 @@ def test_kv_inject_validation_and_workspace():
     assert _inject(ts=100)[0] == INVALID
     assert _inject(num_pages=0)[0] == INVALID
     assert _inject(d=4100)[0] == UNSUPPORTED
+    assert _inject(page=24)[0] == UNSUPPORTED
     assert _inject(ws=FAKE, nbytes=n1 - 1, C=1)[0] == WORKSPACE
+
+
+def test_attention_workspace_with_bigger_pages():
+    """Splits are counted in 16-token slabs and start on page boundaries."""
+    code, n16 = _attn(split=0, page=16, max_pages=64)
+    assert code == OK
+    for P in (32, 64, 128, 256):
+        code, n = _attn(split=0, page=P, max_pages=-(-1000 // P))
+        assert code == OK and n > 0
+    # a user split of 4 pages of 64 tokens is 16 slabs: ceil(63 / 16) = 4 splits per request
+    code, n = _attn(split=4, page=64, max_pages=16)
+    C, M = 4, 4 * 4
+    plan = (4 + 2 * C + 2 * M) * 4
+    rows = 4 * 16
+    expect = -(-plan // 256) * 256 + -(-(M * 8 * rows * 128 * 4) // 256) * 256 + -(-(M * 8 * rows * 2 * 4) // 256) * 256
+    assert code == OK and n == expect

@@ -31,17 +31,18 @@ PAGE = 16
 # attention
 # ----------------------------------------------------------------------------
 
-def make_attn_case(seed, ctx, K, Hq, Hkv, D, dtype, *, identity=False, q_scale=1.0, spare=7):
-    """Logical context per request, scattered into a NaN-poisoned paged pool."""
+def make_attn_case(seed, ctx, K, Hq, Hkv, D, dtype, *, identity=False, q_scale=1.0, spare=7, page=PAGE):
+    """Logical context per request, scattered into a NaN-poisoned pool of
+    `page`-token pages (the logical rows do not depend on the page size)."""
     g = np.random.default_rng(seed)
     bf = dtype == "bf16"
     enc = (lambda a: wl.f32_to_bf16_bits(a)) if bf else (lambda a: a.astype(np.float32))
     nan = wl.BF16_NAN if bf else np.float32("nan")
     C = len(ctx)
-    n_pages = [-(-c // PAGE) for c in ctx]
+    n_pages = [-(-c // page) for c in ctx]
     pool = sum(n_pages) + spare
     perm = np.arange(pool) if identity else np.random.default_rng(seed + 99).permutation(pool)
-    kc = np.full((pool, PAGE, Hkv, D), nan, dtype=np.uint16 if bf else np.float32)
+    kc = np.full((pool, page, Hkv, D), nan, dtype=np.uint16 if bf else np.float32)
     vc = kc.copy()
     pt = np.full((C, max(1, max(n_pages))), -1, np.int32)
     off = 0
@@ -52,9 +53,9 @@ def make_attn_case(seed, ctx, K, Hq, Hkv, D, dtype, *, identity=False, q_scale=1
         off += n_pages[b]
         pt[b, :len(pages)] = pages
         for pi, pg in enumerate(pages):
-            n = min(PAGE, c - pi * PAGE)
-            kc[pg, :n] = kl[pi * PAGE:pi * PAGE + n]
-            vc[pg, :n] = vl[pi * PAGE:pi * PAGE + n]
+            n = min(page, c - pi * page)
+            kc[pg, :n] = kl[pi * page:pi * page + n]
+            vc[pg, :n] = vl[pi * page:pi * page + n]
     q = enc(q_scale * g.standard_normal((C, K, Hq, D)).astype(np.float32))
     kb = enc(g.standard_normal((C, K, Hkv, D)).astype(np.float32))
     vb = enc(g.standard_normal((C, K, Hkv, D)).astype(np.float32))
@@ -143,6 +144,34 @@ def test_block_causal_edges():
     oc, of = to_host64(oc), to_host64(of)
     assert_close(oc[:, -1], of[:, -1], "bf16", "last block position")
     assert np.abs(oc[:, 0] - of[:, 0]).max() > 0.05
+
+
+@pytest.mark.parametrize("P", [32, 64, 128, 256])
+def test_bigger_pages(P):
+    """Pages of P tokens: parity with the oracle at several splits, and the
+    same bits as the 16-token layout of the same context at the same split
+    (in slabs), since the kernel walks both in the same 16-token slabs."""
+    flush(f"[attn page {P}]")
+    ctx = [0, 1, P - 1, P, P + 1, 1000, 3000]
+    case = make_attn_case(900 + P, ctx, 16, 32, 8, 128, "bf16", page=P)
+    ref16 = make_attn_case(900 + P, ctx, 16, 32, 8, 128, "bf16", page=16)
+    want = oracle_attn(case)
+    for split in (0, 1, 3):
+        o, _, _ = run_attn(case, split=split)
+        assert_close(to_host64(o), want, "bf16", f"page {P} split={split}")
+        if split:
+            o16, _, _ = run_attn(ref16, split=split * (P // 16))
+            assert torch.equal(o.view(torch.int16), o16.view(torch.int16)), f"page {P} split={split}"
+    oc, _, _ = run_attn(case, split=1, causal=True)
+    assert_close(to_host64(oc), oracle_attn(case, causal=True), "bf16", f"page {P} causal")
+
+
+def test_bigger_pages_hnd():
+    case = make_attn_case(950, [300, 45, 700], 16, 8, 2, 128, "bf16", page=64)
+    on, _, _ = run_attn(case, layout="NHD")
+    oh, _, _ = run_attn(case, layout="HND")
+    assert torch.equal(on.view(torch.int16), oh.view(torch.int16))
+    assert_close(to_host64(oh), oracle_attn(case), "bf16", "HND page 64")
 
 
 def test_split_invariance_and_repeatability():

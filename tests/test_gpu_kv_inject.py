@@ -20,15 +20,16 @@ pytestmark = pytest.mark.gpu
 
 def written_mask(a, n_new):
     m = np.zeros(a["k_cache"].shape[:2], dtype=bool)
+    P = a["k_cache"].shape[1]
     for b, s in enumerate(a["start"]):
         for i in range(n_new):
             p = int(s) + i
-            m[a["page_table"][b, p // 16], p % 16] = True
+            m[a["page_table"][b, p // P], p % P] = True
     return m
 
 
-def run_and_check(w, n_new, starts, layout="NHD"):
-    a = wl.make_inject_inputs(w, n_new, ctx_lens=starts)
+def run_and_check(w, n_new, starts, layout="NHD", page_size=16):
+    a = wl.make_inject_inputs(w, n_new, ctx_lens=starts, page_size=page_size)
     dt = w.dtype
     kc, vc = to_dev(a["k_cache"], dt), to_dev(a["v_cache"], dt)
     if layout == "HND":
@@ -65,6 +66,11 @@ def test_kv_inject(name, C, n, d, Hkv, D, dtype, starts):
     w = replace(wl.WORKLOADS[1], name=name, C=C, d_model=d, Hkv=Hkv, Hq=Hkv, D=D, dtype=dtype,
                 ctx=("uniform", 0, 200), seed=700 + [c[0] for c in CASES].index(name))
     run_and_check(w, n, starts)
+
+
+def test_kv_inject_bigger_pages():
+    w = replace(wl.WORKLOADS[1], name="inject-p64", C=4, d_model=256, seed=779)
+    run_and_check(w, 16, [0, 60, 100, 127], page_size=64)
 
 
 def test_kv_inject_hnd_layout():

@@ -10,6 +10,7 @@ must be bit-identical.
 from dataclasses import replace
 
 import numpy as np
+import pytest
 import torch
 import torch.nn.functional as F
 
@@ -19,9 +20,10 @@ from hybrid_mamba_attention_amd import workloads as wl
 W = replace(wl.WORKLOADS[0], name="inject-pins", C=3, d_model=64, Hkv=2, D=64, seed=31)
 
 
-def test_written_rows_come_back_through_the_page_table():
+@pytest.mark.parametrize("P", [16, 64])
+def test_written_rows_come_back_through_the_page_table(P):
     n = 21                                               # crosses page boundaries
-    a = wl.make_inject_inputs(W, n, ctx_lens=[0, 13, 40])
+    a = wl.make_inject_inputs(W, n, ctx_lens=[0, 13, 60], page_size=P)
     kp, vp, kv = oracle.kv_inject(a["hidden"], a["w_kv"], a["k_cache"], a["v_cache"], a["page_table"],
                                   a["start"], Hkv=W.Hkv, D=W.D, dtype=W.dtype)
     HD = W.Hkv * W.D
