@@ -371,6 +371,68 @@ def make_inject_inputs(w: Workload, n_new: int, *, ctx_lens=None, spare: int = 8
     return a
 
 
+# ----------------------------------------------------------------------------
+# a drafter stack of hybrid layers
+# ----------------------------------------------------------------------------
+
+def make_stack_inputs(w: Workload, kinds=("MA", "MA"), *, ctx_lens=None) -> dict:
+    """Inputs of a drafter stack: kinds[l] holds "M" (Mamba half) and/or "A"
+    (attention half) for layer l.  Every layer gets its own weights and, for
+    an attention half, its own target KV pools (the target layer it reads);
+    the page table and context lengths are shared, as a target's layers
+    share them.
+
+      * hidden_in [C, K, d_model], u [C, d_model]: N(0,1)
+      * pre_norm_w: 1 + 0.1 N(0,1); Mamba half as the block recipe, plus
+        w_init [d_model, S] N(0, 0.02^2) and h0 from u
+      * wq [Hq*D, d], wk/wv [Hkv*D, d], wo [d, Hq*D]: N(0, 0.02^2)
+      * pools: N(0,1) with NaN in spare pages and tail slots, as the layer's
+    """
+    root = np.random.SeedSequence([w.seed, 123])
+    nl = len(kinds)
+    kids = root.spawn(3 + nl)
+    bf16 = w.dtype == "bf16"
+
+    def normal(ss, shape, std=1.0):
+        return _normal_chunked(ss, int(np.prod(shape)), std, bf16).reshape(shape)
+
+    g_ctx, g_perm, g_io = kids[0], kids[1], kids[2].spawn(2)
+    if ctx_lens is None:
+        ctx_lens = draw_ctx_lens(w, g_ctx)
+    ctx_lens = np.asarray(ctx_lens, np.int32)
+    pt, pool, pages_of = build_page_table(ctx_lens, g_perm)
+    used = np.concatenate(pages_of) if pages_of else np.zeros(0, np.int64)
+    nan = BF16_NAN if bf16 else F32_NAN
+    out = dict(hidden_in=normal(g_io[0], (w.C, w.K, w.d_model)), u=normal(g_io[1], (w.C, w.d_model)),
+               page_table=pt, ctx_lens=ctx_lens, num_pages=pool, layers=[])
+    d_inner, conv_dim, d_proj = block_sizes(w)
+    for l, kind in enumerate(kinds):
+        ss = kids[3 + l].spawn(16)
+        rng = lambda i: np.random.default_rng(ss[i])
+        L = dict(pre_norm_w=(1.0 + 0.1 * rng(0).standard_normal(w.d_model)).astype(np.float32), eps=BLOCK_EPS)
+        if "M" in kind:
+            L.update(w_init=normal(ss[1], (w.d_model, w.S), 0.02),
+                     w_in=normal(ss[2], (d_proj, w.d_model), 0.02),
+                     conv_w=rng(3).uniform(-0.5, 0.5, (conv_dim, 4)).astype(np.float32),
+                     conv_b=rng(4).uniform(-0.5, 0.5, conv_dim).astype(np.float32),
+                     dt_bias=np.full(w.H, BLOCK_DT_BIAS, np.float32),
+                     A=(-np.exp(rng(5).uniform(0.0, 1.0, w.H))).astype(np.float32),
+                     Dskip=rng(6).standard_normal(w.H).astype(np.float32),
+                     norm_w=(1.0 + 0.1 * rng(7).standard_normal(d_inner)).astype(np.float32),
+                     w_out=normal(ss[8], (w.d_model, d_inner), 0.02))
+        if "A" in kind:
+            L.update(wq=normal(ss[9], (w.Hq * w.D, w.d_model), 0.02),
+                     wk=normal(ss[10], (w.Hkv * w.D, w.d_model), 0.02),
+                     wv=normal(ss[11], (w.Hkv * w.D, w.d_model), 0.02),
+                     wo=normal(ss[12], (w.d_model, w.Hq * w.D), 0.02))
+            for name, i in (("k_cache", 13), ("v_cache", 14)):
+                arr = normal(ss[i], (pool, PAGE, w.Hkv, w.D))
+                _poison_kv(arr, ctx_lens, pages_of, used, nan)
+                L[name] = arr
+        out["layers"].append(L)
+    return out
+
+
 def kv_bytes(w: Workload, ctx_lens) -> int:
     """Bytes of target KV a layer call must read in place (K and V, valid tokens)."""
     e = 2 if w.dtype == "bf16" else 4

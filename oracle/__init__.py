@@ -33,11 +33,13 @@ from .layer import draft_layer
 from .mamba_block import (mamba_block, causal_conv, gated_rmsnorm, silu, softplus,
                           in_proj_sizes)
 from .kv_inject import kv_project, kv_inject, extra_kv_bytes_per_token
+from .stack import stack_forward, rmsnorm
 
 __all__ = [
     "decode", "BF16", "F32", "init_state", "ssd_recurrence", "ssd_chunked",
     "PoisonedRead", "gather_context", "block_attention", "block_attention_splits",
     "split_partials", "merge_partials", "split_plan", "plan_len", "max_items_for",
     "draft_layer", "mamba_block", "causal_conv", "gated_rmsnorm", "silu", "softplus",
-    "in_proj_sizes", "kv_project", "kv_inject", "extra_kv_bytes_per_token",
+    "in_proj_sizes", "kv_project", "kv_inject", "extra_kv_bytes_per_token", "stack_forward",
+    "rmsnorm",
 ]

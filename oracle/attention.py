@@ -82,10 +82,12 @@ def block_mask(K: int, G: int, ctx: int, block_causal: bool) -> np.ndarray:
 
 
 def block_attention(q, k_blk, v_blk, k_cache, v_cache, page_table, ctx_lens, *,
-                    dtype: str, scale=None, requests=None, block_causal=False) -> np.ndarray:
+                    dtype: str, scale=None, requests=None, block_causal=False,
+                    block_dtype=None) -> np.ndarray:
     """Brute-force attention over (context read through the page table) + block.
 
-    q [C,K,Hq,D], k_blk/v_blk [C,K,Hkv,D] and the caches in stored form.
+    q [C,K,Hq,D], k_blk/v_blk [C,K,Hkv,D] and the caches in stored form
+    (q and the block K/V decoded with block_dtype, default dtype).
     Returns o [C,K,Hq,D] float64 (rows of requests not in `requests` stay 0).
     """
     C, K, Hq, D = q.shape
@@ -95,9 +97,10 @@ def block_attention(q, k_blk, v_blk, k_cache, v_cache, page_table, ctx_lens, *,
     out = np.zeros((C, K, Hq, D))
     reqs = range(C) if requests is None else requests
     for b in reqs:
-        qb = decode(q[b], dtype)                                       # [K,Hq,D]
-        kb = decode(k_blk[b], dtype)
-        vb = decode(v_blk[b], dtype)
+        bd = dtype if block_dtype is None else block_dtype
+        qb = decode(q[b], bd)                                          # [K,Hq,D]
+        kb = decode(k_blk[b], bd)
+        vb = decode(v_blk[b], bd)
         for j in range(Hkv):
             kall = np.concatenate([gather_context(k_cache, page_table[b], ctx_lens[b], j, dtype), kb[:, j]])
             vall = np.concatenate([gather_context(v_cache, page_table[b], ctx_lens[b], j, dtype), vb[:, j]])

@@ -3,6 +3,7 @@ import numpy as np
 
 BF16 = "bf16"
 F32 = "f32"
+F64 = "f64"   # float64 intermediates of the oracle itself, taken as they are
 
 
 def decode(a, dtype: str) -> np.ndarray:
@@ -17,4 +18,6 @@ def decode(a, dtype: str) -> np.ndarray:
         return bits.view(np.float32).astype(np.float64)
     if dtype == F32:
         return a.astype(np.float32).astype(np.float64)
+    if dtype == F64:
+        return a.astype(np.float64)
     raise ValueError(f"unknown dtype {dtype!r}")
