@@ -53,6 +53,8 @@ def parse():
                    help="skip the Mamba-2 block (projections, conv, scan, gated norm) timings")
     p.add_argument("--no-inject", action="store_true",
                    help="skip the drafter-side KV injection contrast timings")
+    p.add_argument("--no-stack", action="store_true",
+                   help="skip the drafter-stack (eager vs HIP graph) timings")
     p.add_argument("--sweep", default="1,2,4,8,16,32,64,128")
     p.add_argument("--calib-copy", action="store_true",
                    help="also launch a plain 1 GiB device copy (counter calibration under rocprofv3)")
@@ -263,6 +265,56 @@ def measure_injection(w, args, torch, flush, Cs=(4, 8, 16, 32, 64, 128)):
                 note="what H-Spec avoids: per-position projection into a drafter-side paged KV cache")
 
 
+def measure_stack(w, args, torch, flush, kinds=("MA", "MA"), Cs=(1, 4, 16, 64, 128)):
+    """The drafter stack (hspec_draft_stack) eager on one stream and as one HIP
+    graph (hspec_draft_stack_graph), at several C, ctx as the workload.  Inputs
+    are drawn on the device from seeded generators (N(0,1) activations and
+    pools, N(0, 0.02^2) weights, the block recipe's fp32 parameters); each
+    attention half reads its own pools through one shared shuffled page table."""
+    from hybrid_mamba_attention_amd import ops, workloads as wl
+    ctx = w.ctx[1] if w.ctx[0] == "fixed" else w.ctx[2]
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    g = torch.Generator(device="cuda").manual_seed(w.seed + 4242)
+    rn = lambda shape, std=1.0: (std * torch.randn(shape, generator=g, device="cuda")).to(dt)
+    rf = lambda shape: torch.randn(shape, generator=g, device="cuda")
+    d_inner, conv_dim, d_proj = wl.block_sizes(w)
+    Cmax = max(Cs)
+    pages_per = (ctx + 15) // 16
+    layers = []
+    for kind in kinds:
+        L = dict(pre_norm_w=1.0 + 0.1 * rf(w.d_model))
+        if "M" in kind:
+            L.update(w_init=rn((w.d_model, w.S), 0.02), w_in=rn((d_proj, w.d_model), 0.02),
+                     conv_w=torch.rand((conv_dim, 4), generator=g, device="cuda") - 0.5,
+                     conv_b=torch.rand(conv_dim, generator=g, device="cuda") - 0.5,
+                     dt_bias=torch.full((w.H,), wl.BLOCK_DT_BIAS, device="cuda"),
+                     A=-torch.exp(torch.rand(w.H, generator=g, device="cuda")), Dskip=rf(w.H),
+                     norm_w=1.0 + 0.1 * rf(d_inner), w_out=rn((w.d_model, d_inner), 0.02))
+        if "A" in kind:
+            L.update(wq=rn((w.Hq * w.D, w.d_model), 0.02), wk=rn((w.Hkv * w.D, w.d_model), 0.02),
+                     wv=rn((w.Hkv * w.D, w.d_model), 0.02), wo=rn((w.d_model, w.Hq * w.D), 0.02),
+                     k_cache=rn((Cmax * pages_per, 16, w.Hkv, w.D)), v_cache=rn((Cmax * pages_per, 16, w.Hkv, w.D)))
+        layers.append(L)
+    perm = torch.randperm(Cmax * pages_per, generator=g, device="cuda").to(torch.int32)
+    pt_all = perm.view(Cmax, pages_per)
+    out = {}
+    for C in Cs:
+        print(f"[bench] stack C={C}", file=sys.stderr, flush=True)
+        st = ops.DraftStack(hidden_in=rn((C, w.K, w.d_model)), u=rn((C, w.d_model)), layers=layers,
+                            page_table=pt_all[:C].contiguous(),
+                            ctx_lens=torch.full((C,), ctx, dtype=torch.int32, device="cuda"), max_ctx=ctx,
+                            H=w.H, P=w.P, N=w.N, chunk=w.chunk, Hq=w.Hq, Hkv=w.Hkv, D=w.D, eps=wl.BLOCK_EPS)
+        eager = stats(timed(st, args.steps, args.warmup, flush, torch))
+        st.graph()
+        graph = stats(timed(st.launch_graph, args.steps, args.warmup, flush, torch))
+        out[str(C)] = dict(eager_ms=eager["mean"], graph_ms=graph["mean"],
+                           block_tokens_per_s=C * w.K / (graph["mean"] * 1e-3))
+        del st
+    del layers, pt_all, perm
+    torch.cuda.empty_cache()
+    return dict(layers="+".join(kinds), ctx=ctx, per_C=out)
+
+
 # ----------------------------------------------------------------------------
 # counters (traffic) from the committed rocprofv3 summary, if still current
 # ----------------------------------------------------------------------------
@@ -432,6 +484,9 @@ def main():
     if not args.no_inject:
         print("[bench] timing the drafter-side KV injection contrast", file=sys.stderr, flush=True)
         line["kv_injection_contrast"] = measure_injection(w, args, torch, flush)
+    if not args.no_stack:
+        print("[bench] timing the drafter stack", file=sys.stderr, flush=True)
+        line["stack"] = measure_stack(w, args, torch, flush)
     if not args.no_sweep:
         sweep = {}
         for C in [int(c) for c in args.sweep.split(",")]:

@@ -14,7 +14,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libhspec.so")
-SOURCES = ["api.hip", "attention.hip", "ssd.hip", "init_state.hip", "gemm.hip", "mamba_block.hip", "probe.hip"]
+SOURCES = ["api.hip", "attention.hip", "ssd.hip", "init_state.hip", "gemm.hip", "mamba_block.hip", "stack.hip", "probe.hip"]
 ARCH = "gfx950"
 # Per-file code generation flags.  attention.hip: matrix-core results stay in
 # ordinary VGPRs (its accumulators are rescaled by VALU every few stages, and

@@ -118,4 +118,18 @@ struct GateNormArgs {
 };
 hipError_t launch_gate_norm(hipStream_t st, int dtype, const GateNormArgs& a);
 
+// Residual stream between stack layers: h = src ? src : h + add0 + add1, then
+// x = RMSNorm(h) * norm_w when norm_w is set.
+struct AddNormArgs {
+  float* h;             // fp32 [T, d], in place
+  const void* src;      // act [T, d] or null
+  const void* add0;     // act [T, d] or null
+  const void* add1;     // act [T, d] or null
+  const float* norm_w;  // fp32 [d] or null (no x)
+  float eps;
+  void* x;              // act [T, d]
+  int T, d;
+};
+hipError_t launch_add_norm(hipStream_t st, int dtype, const AddNormArgs& a);
+
 }  // namespace hspec

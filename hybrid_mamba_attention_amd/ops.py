@@ -56,6 +56,31 @@ class MambaArgs(ctypes.Structure):
     ]
 
 
+class StackLayer(ctypes.Structure):
+    """Mirror of hspec_stack_layer."""
+    _fields_ = [
+        ("pre_norm_w", _vp),
+        ("w_init", _vp), ("w_in", _vp), ("conv_w", _vp), ("conv_b", _vp), ("dt_bias", _vp),
+        ("A", _vp), ("Dskip", _vp), ("norm_w", _vp), ("w_out", _vp),
+        ("wq", _vp), ("wk", _vp), ("wv", _vp), ("wo", _vp), ("k_cache", _vp), ("v_cache", _vp),
+    ]
+
+
+class StackArgs(ctypes.Structure):
+    """Mirror of hspec_stack_args."""
+    _fields_ = [
+        ("dtype", _i), ("C", _i), ("K", _i), ("d_model", _i), ("n_layers", _i),
+        ("H", _i), ("P", _i), ("ng", _i), ("N", _i), ("chunk", _i), ("eps", _f),
+        ("Hq", _i), ("Hkv", _i), ("D", _i),
+        ("page_stride", _i64), ("token_stride", _i64), ("head_stride", _i64),
+        ("num_pages", _i), ("page_size", _i), ("page_table", _vp), ("max_pages", _i),
+        ("ctx_lens", _vp), ("max_ctx", _i), ("kv_split_pages", _i), ("scale", _f),
+        ("hidden_in", _vp), ("u", _vp), ("hidden_out", _vp),
+        ("layers", ctypes.POINTER(StackLayer)),
+        ("workspace", _vp), ("workspace_bytes", _sz),
+    ]
+
+
 _lib = None
 
 
@@ -88,12 +113,23 @@ def lib() -> ctypes.CDLL:
     L.hspec_kv_inject.restype = _i
     L.hspec_kv_inject.argtypes = ([_vp, _i, _i, _i, _i, _i, _i] + [_vp] * 4 +
                                   [_i64, _i64, _i64, _i, _i, _vp, _i, _vp, _vp, ctypes.POINTER(_sz)])
-    if L.hspec_abi_version() != 5:
+    L.hspec_stack_args_size.restype = _sz
+    L.hspec_draft_stack.restype = _i
+    L.hspec_draft_stack.argtypes = [_vp, ctypes.POINTER(StackArgs), ctypes.POINTER(_sz)]
+    L.hspec_draft_stack_graph.restype = _i
+    L.hspec_draft_stack_graph.argtypes = [ctypes.POINTER(StackArgs), ctypes.POINTER(_vp)]
+    L.hspec_graph_launch.restype = _i
+    L.hspec_graph_launch.argtypes = [_vp, _vp]
+    L.hspec_graph_destroy.restype = _i
+    L.hspec_graph_destroy.argtypes = [_vp]
+    if L.hspec_abi_version() != 6:
         raise RuntimeError("libhspec.so ABI version mismatch")
     if L.hspec_layer_args_size() != ctypes.sizeof(LayerArgs):
         raise RuntimeError("hspec_layer_args layout mismatch between library and binding")
     if L.hspec_mamba_args_size() != ctypes.sizeof(MambaArgs):
         raise RuntimeError("hspec_mamba_args layout mismatch between library and binding")
+    if L.hspec_stack_args_size() != ctypes.sizeof(StackArgs):
+        raise RuntimeError("hspec_stack_args layout mismatch between library and binding")
     _lib = L
     return L
 
@@ -374,6 +410,85 @@ class MambaBlock:
 def mamba_block(**kw):
     """One Mamba-2 block call; returns the MambaBlock holding out and h_final."""
     return MambaBlock(**kw)()
+
+
+# ---------------------------------------------------------------------------
+# the drafter stack
+# ---------------------------------------------------------------------------
+
+_MAMBA_KEYS = ("w_init", "w_in", "conv_w", "conv_b", "dt_bias", "A", "Dskip", "norm_w", "w_out")
+_ATTN_KEYS = ("wq", "wk", "wv", "wo", "k_cache", "v_cache")
+
+
+class DraftStack:
+    """Marshalled arguments of one drafter-stack configuration.
+
+    layers: list of dicts of device tensors: 'pre_norm_w', and the Mamba half
+    (_MAMBA_KEYS, w_in present) and/or the attention half (_ATTN_KEYS, wq
+    present).  Calling the object runs the stack eagerly; graph() captures it
+    once into a HIP graph (hspec_draft_stack_graph) and launch_graph() replays
+    it.  hidden_out (fp32 [C, K, d_model]) holds the result either way."""
+
+    def __init__(self, *, hidden_in, u, layers, page_table, ctx_lens, max_ctx, H, P, N, chunk, Hq, Hkv, D,
+                 ng=1, eps=1e-5, kv_split_pages=0, scale=0.0, layout="NHD"):
+        _contig(hidden_in, u, page_table, ctx_lens)
+        dev = hidden_in.device
+        C, K, d = hidden_in.shape
+        self.hidden_out = torch.empty((C, K, d), dtype=torch.float32, device=dev)
+        arr = (StackLayer * len(layers))()
+        pools = None
+        for l, Ld in enumerate(layers):
+            ptr = lambda k: Ld[k].data_ptr() if Ld.get(k) is not None else None
+            arr[l].pre_norm_w = ptr("pre_norm_w")
+            for k in _MAMBA_KEYS + _ATTN_KEYS:
+                setattr(arr[l], k, ptr(k))
+            if Ld.get("k_cache") is not None:
+                pools = Ld["k_cache"]
+        a = StackArgs()
+        a.dtype = _dtype_code(hidden_in)
+        a.C, a.K, a.d_model, a.n_layers = C, K, d, len(layers)
+        a.H, a.P, a.ng, a.N, a.chunk, a.eps = H, P, ng, N, chunk, float(eps)
+        a.Hq, a.Hkv, a.D = Hq, Hkv, D
+        if pools is not None:
+            a.page_stride, a.token_stride, a.head_stride = kv_strides(pools, layout)
+            a.num_pages, a.page_size = pools.shape[0], page_size_of(pools, layout)
+        else:
+            a.page_stride, a.token_stride, a.head_stride, a.num_pages, a.page_size = 8, 8, 8, 1, 16
+        a.page_table, a.max_pages = page_table.data_ptr(), page_table.shape[1]
+        a.ctx_lens, a.max_ctx = ctx_lens.data_ptr(), int(max_ctx)
+        a.kv_split_pages, a.scale = int(kv_split_pages), float(scale)
+        a.hidden_in, a.u, a.hidden_out = hidden_in.data_ptr(), u.data_ptr(), self.hidden_out.data_ptr()
+        a.layers = arr
+        need = _sz(0)
+        _check("hspec_draft_stack", lib().hspec_draft_stack(None, ctypes.byref(a), ctypes.byref(need)))
+        self.workspace = torch.empty(max(need.value, 256), dtype=torch.uint8, device=dev)
+        a.workspace, a.workspace_bytes = self.workspace.data_ptr(), self.workspace.numel()
+        self._args, self._layers = a, arr
+        self._keep = (hidden_in, u, layers, page_table, ctx_lens)
+        self._graph = None
+
+    def __call__(self, stream=None):
+        _check("hspec_draft_stack", lib().hspec_draft_stack(_stream(stream), ctypes.byref(self._args), None))
+        return self
+
+    def graph(self):
+        """Capture the stack into a HIP graph (once); returns self."""
+        if self._graph is None:
+            g = _vp()
+            _check("hspec_draft_stack_graph", lib().hspec_draft_stack_graph(ctypes.byref(self._args), ctypes.byref(g)))
+            self._graph = g
+        return self
+
+    def launch_graph(self, stream=None):
+        self.graph()
+        _check("hspec_graph_launch", lib().hspec_graph_launch(self._graph, _stream(stream)))
+        return self
+
+    def __del__(self):
+        g = getattr(self, "_graph", None)
+        if g is not None and _lib is not None:
+            _lib.hspec_graph_destroy(g)
+            self._graph = None
 
 
 # ---------------------------------------------------------------------------

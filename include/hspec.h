@@ -48,7 +48,7 @@ typedef enum {
 const char* hspec_status_string(int status);
 
 /* ABI version of this header; bumped on any incompatible change. */
-#define HSPEC_ABI_VERSION 5
+#define HSPEC_ABI_VERSION 6
 int hspec_abi_version(void);
 
 /*
@@ -278,6 +278,75 @@ int hspec_kv_inject(void* stream, int dtype, int C, int n_new, int d_model, int 
                     int64_t page_stride, int64_t token_stride, int64_t head_stride, int num_pages,
                     int page_size, const int32_t* page_table, int max_pages, const int32_t* start_pos,
                     void* workspace, size_t* workspace_bytes);
+
+/*
+ * A drafter stack of hybrid layers over the draft block, eager on one stream
+ * or captured once into a HIP graph.  H-Spec, Abstract (a backbone of Mamba-2
+ * and attention modules) and the runtime analysis of Figure 8 (the deeper
+ * stack is slower at low concurrency); the pages print no stack, and the
+ * wiring is this reading, with fp32 residual stream h:
+ *
+ *   h = hidden_in
+ *   for each layer l:
+ *     x  = RMSNorm(h) * pre_norm_w[l]                       (eps)
+ *     ym = Mamba-2 block of x (as hspec_mamba_block) from h0 = u . w_init[l]
+ *                                                 (a1; layers with w_in set)
+ *     ya = (block attention of x.wq^T, x.wk^T, x.wv^T over the layer's
+ *           target KV pools, read in place, as hspec_block_attn_inplace) . wo^T
+ *                                                 (layers with wq set)
+ *     h  = h + ym + ya
+ *   hidden_out = h
+ *
+ * A layer may hold either half or both; all layers share the page table,
+ * context lengths and shapes.  Weights are [out, in] in the activation type
+ * except w_init [d_model, S] (as a1).  Intermediate activations are rounded
+ * to the activation type.  No RoPE, biases or MLP.
+ *   hidden_in  act [C, K, d_model];  u act [C, d_model] (last-token target hidden)
+ *   hidden_out fp32 [C, K, d_model]
+ *   layers     host array [n_layers]; the pointers inside are device memory
+ *   workspace  as for a3: NULL = size query into *required_bytes
+ * Limits: those of a1 (d_model % 32, S % 64), of the Mamba-2 block and of
+ * a3; d_model % 8 == 0; pre_norm_w 16-byte aligned.
+ */
+typedef struct hspec_stack_layer {
+  const float* pre_norm_w;      /* [d_model] */
+  /* Mamba half (w_in NULL: none) */
+  const void* w_init; const void* w_in;
+  const float* conv_w; const float* conv_b; const float* dt_bias;
+  const float* A; const float* Dskip; const float* norm_w; const void* w_out;
+  /* attention half (wq NULL: none) */
+  const void* wq; const void* wk; const void* wv; const void* wo;
+  const void* k_cache; const void* v_cache;
+} hspec_stack_layer;
+
+typedef struct hspec_stack_args {
+  int dtype;
+  int C, K, d_model, n_layers;
+  int H, P, ng, N, chunk;
+  float eps;
+  int Hq, Hkv, D;
+  int64_t page_stride, token_stride, head_stride;
+  int num_pages; int page_size; const int32_t* page_table; int max_pages;
+  const int32_t* ctx_lens; int max_ctx; int kv_split_pages; float scale;
+  const void* hidden_in; const void* u; float* hidden_out;
+  const hspec_stack_layer* layers;
+  void* workspace; size_t workspace_bytes;
+} hspec_stack_args;
+
+size_t hspec_stack_args_size(void);
+
+/* Eager: every kernel of the stack on `stream`, in layer order. */
+int hspec_draft_stack(void* stream, const hspec_stack_args* a, size_t* required_bytes);
+
+/* Graph form: captures the stack once (the state projections and Mamba
+ * halves on a forked branch, concurrent with the attention halves) into an
+ * executable HIP graph bound to the buffers and the workspace in `a`
+ * (which must stay allocated; their contents may change between launches).
+ * Creating it launches nothing and allocates no device memory. */
+typedef struct hspec_graph_s* hspec_graph;
+int hspec_draft_stack_graph(const hspec_stack_args* a, hspec_graph* out);
+int hspec_graph_launch(hspec_graph g, void* stream);
+int hspec_graph_destroy(hspec_graph g);
 
 #ifdef __cplusplus
 }

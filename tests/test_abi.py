@@ -27,13 +27,15 @@ def test_loads_and_exports_every_declared_symbol():
     L = ops.lib()
     names = declared_functions()
     assert {"hspec_init_state", "hspec_ssd_scan", "hspec_block_attn_inplace",
-            "hspec_draft_layer", "hspec_mamba_block", "hspec_kv_inject",
+            "hspec_draft_layer", "hspec_mamba_block", "hspec_kv_inject", "hspec_draft_stack",
+            "hspec_draft_stack_graph", "hspec_graph_launch", "hspec_graph_destroy",
             "hspec_probe_stream_read"} <= set(names)
     for n in names:
         assert hasattr(L, n), f"{n} declared in hspec.h but not exported"
-    assert L.hspec_abi_version() == 5
+    assert L.hspec_abi_version() == 6
     assert L.hspec_layer_args_size() == ctypes.sizeof(ops.LayerArgs)
     assert L.hspec_mamba_args_size() == ctypes.sizeof(ops.MambaArgs)
+    assert L.hspec_stack_args_size() == ctypes.sizeof(ops.StackArgs)
     assert L.hspec_status_string(-2) == b"HSPEC_ERR_UNSUPPORTED"
 
 
@@ -221,3 +223,49 @@ def test_attention_workspace_with_bigger_pages():
     rows = 4 * 16
     expect = -(-plan // 256) * 256 + -(-(M * 8 * rows * 128 * 4) // 256) * 256 + -(-(M * 8 * rows * 2 * 4) // 256) * 256
     assert code == OK and n == expect
+
+
+def _stack(kinds=("MA", "MA"), mutate=None, **kw):
+    """hspec_draft_stack size query for a bf16 stack of the C=128 shapes."""
+    layers = (ops.StackLayer * len(kinds))()
+    for l, kind in enumerate(kinds):
+        layers[l].pre_norm_w = FAKE
+        if "M" in kind:
+            for k in ops._MAMBA_KEYS:
+                setattr(layers[l], k, FAKE)
+        if "A" in kind:
+            for k in ops._ATTN_KEYS:
+                setattr(layers[l], k, FAKE)
+    a = ops.StackArgs()
+    a.dtype, a.C, a.K, a.d_model, a.n_layers = 1, 128, 16, 4096, len(kinds)
+    a.H, a.P, a.ng, a.N, a.chunk, a.eps = 16, 64, 1, 32, 16, 1e-5
+    a.Hq, a.Hkv, a.D = 32, 8, 128
+    a.page_stride, a.token_stride, a.head_stride = 16 * 8 * 128, 8 * 128, 128
+    a.num_pages, a.page_size, a.page_table, a.max_pages = 70000, 16, FAKE, 512
+    a.ctx_lens, a.max_ctx = FAKE, 8192
+    a.hidden_in = a.u = a.hidden_out = FAKE
+    a.layers = layers
+    if mutate:
+        mutate(layers)
+    for k, v in kw.items():
+        setattr(a, k, v)
+    n = ctypes.c_size_t(0)
+    return ops.lib().hspec_draft_stack(None, ctypes.byref(a), ctypes.byref(n)), n.value, layers
+
+
+def test_stack_validation_and_workspace():
+    code, n, _ = _stack()
+    assert code == OK and n > 0
+    assert _stack(("M", "A", "M", "A"))[:2] == (OK, n)      # same buffers whatever the layer mix
+    assert _stack(n_layers=0)[0] == INVALID
+    assert _stack(hidden_out=None)[0] == INVALID
+    assert _stack(eps=-1.0)[0] == INVALID
+    assert _stack(d_model=4100)[0] == UNSUPPORTED
+    assert _stack(mutate=lambda L: setattr(L[1], "wk", None))[0] == INVALID   # half without a weight
+    assert _stack(mutate=lambda L: setattr(L[0], "pre_norm_w", FAKE + 4))[0] == INVALID
+    assert _stack(mutate=lambda L: setattr(L[0], "w_init", None))[0] == INVALID
+    assert ops.lib().hspec_draft_stack(None, None, None) == INVALID
+    g = ctypes.c_void_p()
+    assert ops.lib().hspec_draft_stack_graph(None, ctypes.byref(g)) == INVALID
+    assert ops.lib().hspec_graph_launch(None, None) == INVALID
+    assert ops.lib().hspec_graph_destroy(None) == INVALID
