@@ -133,7 +133,8 @@ def measure(w, inp, args, torch, flush, with_parts=True):
     from hybrid_mamba_attention_amd import ops
     layer, t = build_layer(inp, args.kv_split_pages, torch)
     steps = stats(timed(layer, args.steps, args.warmup, flush, torch))
-    res = dict(step=steps)
+    layer.graph()
+    res = dict(step=steps, step_graph=stats(timed(layer.launch_graph, args.steps, args.warmup, flush, torch)))
     if with_parts:
         ws = layer.workspace
         pt, cl = dev(inp.page_table, torch), dev(inp.ctx_lens, torch)
@@ -466,6 +467,7 @@ def main():
                    "kv_split_pages": r["plan"][1], "work_items": r["plan"][0],
                    "cache_flush_between_steps": not args.no_flush},
         "step_ms": r["step"],
+        "step_ms_graph": r["step_graph"],
         "kernels": kernels,
         "kv_read_gbs": kv_b / (att_ms * 1e-3) / 1e9,
         "kv_read_frac_of_peak": kv_b / (att_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
@@ -499,6 +501,7 @@ def main():
             if not args.no_block:
                 sweep_block = line["mamba_block"]["ms"] if ws is w else measure_block(ws, args, torch, flush)["ms"]
             sweep[str(C)] = dict(block_tokens_per_s=ws.C * ws.K / (sms * 1e-3), ms_per_step=sms,
+                                 ms_per_step_graph=sr["step_graph"]["mean"],
                                  attention_ms=sr["attention"]["mean"], init_ms=sr["init_state"]["mean"],
                                  kv_read_gbs=akv / (sr["attention"]["mean"] * 1e-3) / 1e9,
                                  kv_read_frac=akv / (sr["attention"]["mean"] * 1e-3) / 1e9 / HBM_PEAK_GBS)

@@ -427,12 +427,94 @@ int enqueue_stack(const hspec_stack_args* a, const StackPlan& p, hipStream_t s0,
   return st;
 }
 
+int check_layer(const hspec_layer_args* a, size_t* need) {
+  if (!a) return HSPEC_ERR_INVALID_ARG;
+  int st = check_ssd(a->dtype, a->C, a->K, a->H, a->P, a->ng, a->N, a->chunk, a->x, a->delta, a->A,
+                     a->B, a->Cm, a->y);
+  if (st != HSPEC_OK) return st;
+  if (int64_t(a->H) * a->P * a->N > 0x7fffffff) return HSPEC_ERR_UNSUPPORTED;
+  // u and w_init both NULL: the direct-reuse-only ablation (no a1, zero state)
+  if (a->u || a->w_init) {
+    st = check_init(a->dtype, a->C, a->d_model, a->H * a->P * a->N, a->u, a->w_init, a->h0);
+    if (st != HSPEC_OK) return st;
+  }
+  size_t dummy = 0;
+  st = check_attn(a->dtype, a->C, a->K, a->Hq, a->Hkv, a->D, a->q, a->k_blk, a->v_blk, a->k_cache,
+                  a->v_cache, a->page_stride, a->token_stride, a->head_stride, a->num_pages,
+                  a->page_size, a->page_table, a->max_pages, a->ctx_lens, a->max_ctx, a->kv_split_pages,
+                  a->scale, a->block_causal, a->out, &dummy);
+  if (st != HSPEC_OK) return st;
+  *need = plan_shape(a->C, a->K, a->Hq, a->Hkv, a->D, a->max_ctx, a->kv_split_pages, a->page_size).total;
+  return HSPEC_OK;
+}
+
+// The layer: attention half (a0/a3/a4) on s0; Mamba half (a1 -> a2) after it
+// on the same stream, or, with ev (2 events), forked onto s1 and joined.
+int enqueue_layer(const hspec_layer_args* a, hipStream_t s0, hipStream_t s1, hipEvent_t* ev) {
+  const bool no_init = !a->u && !a->w_init;
+  if (ev && (hipEventRecord(ev[0], s0) != hipSuccess || hipStreamWaitEvent(s1, ev[0], 0) != hipSuccess))
+    return HSPEC_ERR_HIP;
+  int st = run_attn(s0, a->dtype, a->C, a->K, a->Hq, a->Hkv, a->D, a->q, a->k_blk, a->v_blk, a->k_cache,
+                    a->v_cache, a->page_stride, a->token_stride, a->head_stride, a->num_pages,
+                    a->page_size, a->page_table, a->max_pages, a->ctx_lens, a->max_ctx, a->kv_split_pages,
+                    a->scale, a->block_causal, a->out, a->workspace, a->workspace_bytes);
+  if (st != HSPEC_OK) return st;
+  if (!no_init) {
+    InitArgs ia{a->u, a->w_init, a->h0, a->C, a->d_model, a->H * a->P * a->N};
+    st = status_of(launch_init_state(s1, a->dtype, ia));
+    if (st != HSPEC_OK) return st;
+  }
+  SsdArgs sa{a->x, a->delta, a->A, a->B, a->Cm, a->Dskip, no_init ? nullptr : a->h0, a->y, a->h_final,
+             a->C, a->K, a->H, a->P, a->ng, a->N, a->chunk};
+  st = status_of(launch_ssd_scan(s1, a->dtype, sa));
+  if (st != HSPEC_OK) return st;
+  if (ev && (hipEventRecord(ev[1], s1) != hipSuccess || hipStreamWaitEvent(s0, ev[1], 0) != hipSuccess))
+    return HSPEC_ERR_HIP;
+  return HSPEC_OK;
+}
+
 }  // namespace
 
 struct hspec_graph_s {
   hipGraph_t graph;
   hipGraphExec_t exec;
 };
+
+namespace {
+
+// Capture `enqueue(s0, s1, events)` on two private streams into an
+// executable graph: n_events events for the fork / join points.
+template <typename F>
+int capture_graph(int n_events, F&& enqueue, hspec_graph* out) {
+  hipStream_t s0 = nullptr, s1 = nullptr;
+  std::vector<hipEvent_t> ev(n_events, nullptr);
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+  int st = HSPEC_OK;
+  bool ok = hipStreamCreateWithFlags(&s0, hipStreamNonBlocking) == hipSuccess &&
+            hipStreamCreateWithFlags(&s1, hipStreamNonBlocking) == hipSuccess;
+  for (auto& e : ev) ok = ok && hipEventCreateWithFlags(&e, hipEventDisableTiming) == hipSuccess;
+  if (ok && hipStreamBeginCapture(s0, hipStreamCaptureModeThreadLocal) == hipSuccess) {
+    st = enqueue(s0, s1, ev.data());
+    const hipError_t ec = hipStreamEndCapture(s0, &graph);
+    ok = st == HSPEC_OK && ec == hipSuccess && hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0) == hipSuccess;
+  } else {
+    ok = false;
+  }
+  for (auto& e : ev)
+    if (e) hipEventDestroy(e);
+  if (s1) hipStreamDestroy(s1);
+  if (s0) hipStreamDestroy(s0);
+  if (!ok) {
+    if (exec) hipGraphExecDestroy(exec);
+    if (graph) hipGraphDestroy(graph);
+    return st != HSPEC_OK ? st : HSPEC_ERR_HIP;
+  }
+  *out = new hspec_graph_s{graph, exec};
+  return HSPEC_OK;
+}
+
+}  // namespace
 
 extern "C" {
 
@@ -490,44 +572,28 @@ int hspec_block_attn_inplace(void* stream, int dtype, int C, int K, int Hq, int 
 }
 
 int hspec_draft_layer(void* stream, const hspec_layer_args* a, size_t* required_bytes) {
-  if (!a) return HSPEC_ERR_INVALID_ARG;
-  int st = check_ssd(a->dtype, a->C, a->K, a->H, a->P, a->ng, a->N, a->chunk, a->x, a->delta, a->A,
-                     a->B, a->Cm, a->y);
+  size_t need = 0;
+  const int st = check_layer(a, &need);
   if (st != HSPEC_OK) return st;
-  if (int64_t(a->H) * a->P * a->N > 0x7fffffff) return HSPEC_ERR_UNSUPPORTED;
-  const int S = a->H * a->P * a->N;
-  // u and w_init both NULL: the direct-reuse-only ablation (no a1, zero state)
-  const bool no_init = !a->u && !a->w_init;
-  if (!no_init) {
-    st = check_init(a->dtype, a->C, a->d_model, S, a->u, a->w_init, a->h0);
-    if (st != HSPEC_OK) return st;
-  }
-  size_t dummy = 0;
-  st = check_attn(a->dtype, a->C, a->K, a->Hq, a->Hkv, a->D, a->q, a->k_blk, a->v_blk, a->k_cache,
-                  a->v_cache, a->page_stride, a->token_stride, a->head_stride, a->num_pages,
-                  a->page_size, a->page_table, a->max_pages, a->ctx_lens, a->max_ctx, a->kv_split_pages,
-                  a->scale,
-                  a->block_causal, a->out, &dummy);
-  if (st != HSPEC_OK) return st;
-  const size_t need = plan_shape(a->C, a->K, a->Hq, a->Hkv, a->D, a->max_ctx, a->kv_split_pages,
-                                 a->page_size).total;
   if (required_bytes) *required_bytes = need;
   if (!a->workspace) return required_bytes ? HSPEC_OK : HSPEC_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  st = run_attn(s, a->dtype, a->C, a->K, a->Hq, a->Hkv, a->D, a->q, a->k_blk, a->v_blk, a->k_cache,
-                a->v_cache, a->page_stride, a->token_stride, a->head_stride, a->num_pages,
-                a->page_size, a->page_table, a->max_pages, a->ctx_lens, a->max_ctx, a->kv_split_pages,
-                a->scale,
-                a->block_causal, a->out, a->workspace, a->workspace_bytes);
+  return enqueue_layer(a, s, s, nullptr);
+}
+
+int hspec_draft_layer_graph(const hspec_layer_args* a, hspec_graph* out) {
+  if (!out) return HSPEC_ERR_INVALID_ARG;
+  *out = nullptr;
+  size_t need = 0;
+  const int st = check_layer(a, &need);
   if (st != HSPEC_OK) return st;
-  if (!no_init) {
-    InitArgs ia{a->u, a->w_init, a->h0, a->C, a->d_model, S};
-    st = status_of(launch_init_state(s, a->dtype, ia));
-    if (st != HSPEC_OK) return st;
-  }
-  SsdArgs sa{a->x, a->delta, a->A, a->B, a->Cm, a->Dskip, no_init ? nullptr : a->h0, a->y, a->h_final,
-             a->C, a->K, a->H, a->P, a->ng, a->N, a->chunk};
-  return status_of(launch_ssd_scan(s, a->dtype, sa));
+  if (!a->workspace || !aligned(a->workspace, 256) || a->workspace_bytes < need) return HSPEC_ERR_WORKSPACE;
+  // One branch: the Mamba half forked beside the attention half was measured
+  // slower at every C (C = 1: 88 vs 75 us; C = 128: 841 vs 767 us) -- both
+  // halves are HBM-bound, so running them together only interferes.
+  return capture_graph(0, [&](hipStream_t s0, hipStream_t, hipEvent_t*) {
+    return enqueue_layer(a, s0, s0, nullptr);
+  }, out);
 }
 
 size_t hspec_mamba_args_size(void) { return sizeof(hspec_mamba_args); }
@@ -584,36 +650,13 @@ int hspec_draft_stack(void* stream, const hspec_stack_args* a, size_t* required_
 int hspec_draft_stack_graph(const hspec_stack_args* a, hspec_graph* out) {
   if (!out) return HSPEC_ERR_INVALID_ARG;
   *out = nullptr;
-  int st = check_stack(a);
+  const int st = check_stack(a);
   if (st != HSPEC_OK) return st;
   const StackPlan p = stack_plan(a);
   if (!a->workspace || !aligned(a->workspace, 256) || a->workspace_bytes < p.total) return HSPEC_ERR_WORKSPACE;
-  hipStream_t s0 = nullptr, s1 = nullptr;
-  std::vector<hipEvent_t> ev(2 * a->n_layers, nullptr);
-  hipGraph_t graph = nullptr;
-  hipGraphExec_t exec = nullptr;
-  bool ok = hipStreamCreateWithFlags(&s0, hipStreamNonBlocking) == hipSuccess &&
-            hipStreamCreateWithFlags(&s1, hipStreamNonBlocking) == hipSuccess;
-  for (auto& e : ev) ok = ok && hipEventCreateWithFlags(&e, hipEventDisableTiming) == hipSuccess;
-  if (ok && hipStreamBeginCapture(s0, hipStreamCaptureModeThreadLocal) == hipSuccess) {
-    st = enqueue_stack(a, p, s0, s1, ev.data());
-    const hipError_t ec = hipStreamEndCapture(s0, &graph);
-    ok = st == HSPEC_OK && ec == hipSuccess &&
-         hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0) == hipSuccess;
-  } else {
-    ok = false;
-  }
-  for (auto& e : ev)
-    if (e) hipEventDestroy(e);
-  if (s1) hipStreamDestroy(s1);
-  if (s0) hipStreamDestroy(s0);
-  if (!ok) {
-    if (exec) hipGraphExecDestroy(exec);
-    if (graph) hipGraphDestroy(graph);
-    return st != HSPEC_OK ? st : HSPEC_ERR_HIP;
-  }
-  *out = new hspec_graph_s{graph, exec};
-  return HSPEC_OK;
+  return capture_graph(2 * a->n_layers, [&](hipStream_t s0, hipStream_t s1, hipEvent_t* ev) {
+    return enqueue_stack(a, p, s0, s1, ev);
+  }, out);
 }
 
 int hspec_graph_launch(hspec_graph g, void* stream) {

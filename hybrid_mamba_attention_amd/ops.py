@@ -116,6 +116,8 @@ def lib() -> ctypes.CDLL:
     L.hspec_stack_args_size.restype = _sz
     L.hspec_draft_stack.restype = _i
     L.hspec_draft_stack.argtypes = [_vp, ctypes.POINTER(StackArgs), ctypes.POINTER(_sz)]
+    L.hspec_draft_layer_graph.restype = _i
+    L.hspec_draft_layer_graph.argtypes = [ctypes.POINTER(LayerArgs), ctypes.POINTER(_vp)]
     L.hspec_draft_stack_graph.restype = _i
     L.hspec_draft_stack_graph.argtypes = [ctypes.POINTER(StackArgs), ctypes.POINTER(_vp)]
     L.hspec_graph_launch.restype = _i
@@ -351,6 +353,25 @@ class DraftLayer:
     def __call__(self, stream=None):
         _check("hspec_draft_layer", lib().hspec_draft_layer(_stream(stream), ctypes.byref(self._args), None))
         return self
+
+    def graph(self):
+        """Capture the layer into a HIP graph (once; the Mamba half on its own branch)."""
+        if getattr(self, "_graph", None) is None:
+            g = _vp()
+            _check("hspec_draft_layer_graph", lib().hspec_draft_layer_graph(ctypes.byref(self._args), ctypes.byref(g)))
+            self._graph = g
+        return self
+
+    def launch_graph(self, stream=None):
+        self.graph()
+        _check("hspec_graph_launch", lib().hspec_graph_launch(self._graph, _stream(stream)))
+        return self
+
+    def __del__(self):
+        g = getattr(self, "_graph", None)
+        if g is not None and _lib is not None:
+            _lib.hspec_graph_destroy(g)
+            self._graph = None
 
     def plan(self) -> torch.Tensor:
         """The int32 split plan at the head of the workspace (see include/hspec.h)."""

@@ -192,6 +192,15 @@ size_t hspec_layer_args_size(void);
  * a->workspace is set). */
 int hspec_draft_layer(void* stream, const hspec_layer_args* a, size_t* required_bytes);
 
+/* Executable HIP graph of a layer or a stack (see hspec_draft_stack_graph). */
+typedef struct hspec_graph_s* hspec_graph;
+
+/* a5 captured once into a HIP graph (its kernels in the order of
+ * hspec_draft_layer), for callers that replay graphs; bound to the buffers
+ * and workspace in `a` (contents may change between launches).  Creating it
+ * launches nothing and allocates no device memory. */
+int hspec_draft_layer_graph(const hspec_layer_args* a, hspec_graph* out);
+
 /*
  * The Mamba-2 block around a2: input projection, short causal convolution,
  * the scan, gated RMS normalisation and output projection.  H-Spec, Abstract:
@@ -343,7 +352,6 @@ int hspec_draft_stack(void* stream, const hspec_stack_args* a, size_t* required_
  * executable HIP graph bound to the buffers and the workspace in `a`
  * (which must stay allocated; their contents may change between launches).
  * Creating it launches nothing and allocates no device memory. */
-typedef struct hspec_graph_s* hspec_graph;
 int hspec_draft_stack_graph(const hspec_stack_args* a, hspec_graph* out);
 int hspec_graph_launch(hspec_graph g, void* stream);
 int hspec_graph_destroy(hspec_graph g);

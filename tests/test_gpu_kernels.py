@@ -345,3 +345,30 @@ def test_layer_block_causal_and_direct_reuse_ablation():
     assert_close(to_host64(abl.h_final), hf0, "bf16", "h_final from the zero state")
     assert_close(to_host64(abl.out), oracle_attn_inp(inp), "bf16", "ablation out")
     assert np.abs(to_host64(abl.y) - y).max() > 1e-3, "the projected state must matter"
+
+
+def test_layer_graph_replays_match_eager():
+    """The layer's HIP graph (Mamba half on its own branch) against the eager
+    layer, bit for bit, over replays with eager work in between."""
+    from helpers import layer_from_inputs
+    w = wl.sweep_workload(4)
+    w = replace_workload(w, ctx=("uniform", 100, 3000), seed=4545)
+    inp = wl.make_inputs(w)
+    layer = layer_from_inputs(inp)
+    ref = [t.clone() for t in (layer.out, layer.y, layer.h0, layer.h_final)]
+    layer.graph()
+    for rep in range(3):
+        for t in (layer.out, layer.y, layer.h0, layer.h_final):
+            t.zero_()
+        layer.launch_graph()
+        torch.cuda.synchronize()
+        for got, want in zip((layer.out, layer.y, layer.h0, layer.h_final), ref):
+            assert torch.equal(got.view(torch.int16) if got.dtype == torch.bfloat16 else got,
+                               want.view(torch.int16) if want.dtype == torch.bfloat16 else want), rep
+        torch.randn(1 << 18, device="cuda").sum()
+        torch.cuda.synchronize()
+
+
+def replace_workload(w, **kw):
+    from dataclasses import replace
+    return replace(w, **kw)
