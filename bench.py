@@ -345,10 +345,17 @@ def stream_read_probe(torch, gib=4, reps=6):
 
 
 def kernel_source_hash():
+    """Hash of what k_block_attn is compiled from: attention.hip, common.h and
+    the AttnArgs definition in kernels.h (the rest of that header serves other
+    kernels), so the committed counters are used only while they still apply."""
     h = hashlib.sha256()
-    for f in ("attention.hip", "common.h", "kernels.h"):
-        with open(os.path.join(ROOT, "hybrid_mamba_attention_amd", "csrc", f), "rb") as fh:
+    csrc = os.path.join(ROOT, "hybrid_mamba_attention_amd", "csrc")
+    for f in ("attention.hip", "common.h"):
+        with open(os.path.join(csrc, f), "rb") as fh:
             h.update(fh.read())
+    text = open(os.path.join(csrc, "kernels.h")).read()
+    i = text.index("struct AttnArgs")
+    h.update(text[i:text.index("};", i) + 2].encode())
     return h.hexdigest()[:16]
 
 
