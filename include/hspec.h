@@ -6,8 +6,18 @@
  * page, Summary): a Mamba-2 module whose state starts from a projection of the
  * target's last-token hidden state and scans the K-token draft block in
  * parallel, and an attention module whose K block queries read the target's
- * paged KV cache in place -- the library has no argument through which it
+ * paged KV cache in place -- the layer has no argument through which it
  * could write a drafter-side KV cache.
+ *
+ * Entry points
+ *   hspec_init_state, hspec_ssd_scan,       the layer's steps (a1, a2, a0+a3+a4)
+ *   hspec_block_attn_inplace
+ *   hspec_draft_layer (+ _graph)            the layer (a5)
+ *   hspec_mamba_block                       the Mamba-2 block around the scan
+ *   hspec_draft_stack (+ _graph)            a stack of hybrid layers
+ *   hspec_kv_inject                         contrast workload: the drafter-side
+ *                                           KV injection H-Spec avoids
+ *   hspec_graph_launch, hspec_graph_destroy the graph objects of the _graph forms
  *
  * Conventions shared by every entry point
  *   - `stream` is a hipStream_t (NULL = the default stream).  Every call only
@@ -16,9 +26,11 @@
  *     come back as HSPEC_ERR_HIP; faults inside kernels surface at the
  *     caller's next synchronisation.
  *   - All pointers except the integer metadata noted below are device
- *     pointers.  The caller owns every buffer; the library allocates nothing
- *     and keeps no state between calls, so calls on different streams may run
- *     concurrently as long as their output and workspace buffers differ.
+ *     pointers.  The caller owns every buffer; the library allocates no
+ *     device memory and keeps no state between calls (the _graph forms create
+ *     host-side HIP graph objects, freed by hspec_graph_destroy), so calls on
+ *     different streams may run concurrently as long as their output and
+ *     workspace buffers differ.
  *   - `dtype` selects the element type of the "act" tensors: HSPEC_F32
  *     (float) or HSPEC_BF16 (bfloat16 bits).  Accumulation is always fp32.
  *   - Shapes are row-major, last index fastest; "act" tensors are contiguous
