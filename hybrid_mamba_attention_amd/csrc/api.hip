@@ -170,12 +170,13 @@ int run_attn(hipStream_t st, int dtype, int C, int K, int Hq, int Hkv, int D, co
   return status_of(launch_block_attn(st, dtype, a));
 }
 
-// Workspace of the Mamba-2 block: fp32 projection, scan inputs and output,
-// the normalised activations, and split-K partials of either projection.
+// Workspace of the Mamba-2 block: the fp32 projection (which the scan reads
+// through its fused convolution), the scan output, the normalised
+// activations, and split-K partials of either projection.
 struct BlockPlan {
   int T, d_inner, conv_dim, d_proj, ngN;
   GemmPlan in_p, out_p;
-  size_t zx_off, x_off, b_off, c_off, dt_off, y_off, n_off, part_off, total;
+  size_t zx_off, y_off, n_off, part_off, total;
 };
 
 BlockPlan block_plan(const hspec_mamba_args* a) {
@@ -191,10 +192,6 @@ BlockPlan block_plan(const hspec_mamba_args* a) {
   auto take = [&](size_t bytes) { const size_t o = off; off += align256(bytes); return o; };
   const size_t T = size_t(p.T);
   p.zx_off = take(T * p.d_proj * 4);
-  p.x_off = take(T * p.d_inner * 4);
-  p.b_off = take(T * p.ngN * 4);
-  p.c_off = take(T * p.ngN * 4);
-  p.dt_off = take(T * a->H * 4);
   p.y_off = take(T * p.d_inner * 4);
   p.n_off = take(T * p.d_inner * esize(a->dtype));
   p.part_off = take(std::max(p.in_p.part_floats, p.out_p.part_floats) * 4);
@@ -226,10 +223,6 @@ int check_block(const hspec_mamba_args* a) {
 int run_block(hipStream_t s, const hspec_mamba_args* a, const BlockPlan& p) {
   unsigned char* ws = static_cast<unsigned char*>(a->workspace);
   float* zx = reinterpret_cast<float*>(ws + p.zx_off);
-  float* xs = reinterpret_cast<float*>(ws + p.x_off);
-  float* bs = reinterpret_cast<float*>(ws + p.b_off);
-  float* cs = reinterpret_cast<float*>(ws + p.c_off);
-  float* dt = reinterpret_cast<float*>(ws + p.dt_off);
   float* y = reinterpret_cast<float*>(ws + p.y_off);
   void* normed = ws + p.n_off;
   float* part = reinterpret_cast<float*>(ws + p.part_off);
@@ -239,12 +232,9 @@ int run_block(hipStream_t s, const hspec_mamba_args* a, const BlockPlan& p) {
   gi.lda = a->d_model; gi.ldb = a->d_model; gi.ldc = p.d_proj;
   int st = status_of(launch_gemm_tn(s, a->dtype, 1, gi, p.in_p));
   if (st != HSPEC_OK) return st;
-  ConvActArgs ca{zx, a->conv_w, a->conv_b, a->dt_bias, xs, bs, cs, dt,
-                 a->C, a->K, p.d_inner, p.ngN, a->H, p.d_proj};
-  st = status_of(launch_conv_act(s, ca));
-  if (st != HSPEC_OK) return st;
-  SsdArgs sa{xs, dt, a->A, bs, cs, a->Dskip, a->h0, y, a->h_final,
-             a->C, a->K, a->H, a->P, a->ng, a->N, a->chunk};
+  SsdArgs sa{nullptr, nullptr, a->A, nullptr, nullptr, a->Dskip, a->h0, y, a->h_final,
+             a->C, a->K, a->H, a->P, a->ng, a->N, a->chunk,
+             zx, a->conv_w, a->conv_b, a->dt_bias, p.d_proj, p.d_inner};
   st = status_of(launch_ssd_scan(s, HSPEC_F32, sa));
   if (st != HSPEC_OK) return st;
   GateNormArgs gn{y, zx, a->norm_w, a->norm_eps, normed, p.T, p.d_inner, p.d_proj};

@@ -143,6 +143,11 @@ __device__ __forceinline__ float wave_xor_sum(float v, int m) { return v + __shf
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+__device__ __forceinline__ float silu_f(float v) { return v / (1.f + __expf(-v)); }
+
+// log(1 + e^v); above 20 the correction is below fp32 resolution.
+__device__ __forceinline__ float softplus_f(float v) { return v > 20.f ? v : log1pf(__expf(v)); }
+
 constexpr float kLog2e = 1.4426950408889634f;
 
 }  // namespace hspec

@@ -47,6 +47,15 @@ struct SsdArgs {
   float* y;
   float* h_final;
   int C, K, H, P, ng, N, chunk;
+  // Fused front of the Mamba-2 block (zx set; x, delta, B, Cm unused): the
+  // scan reads the raw projection rows zx [C*K, d_proj] (z | x | B | C | dt)
+  // and applies the width-4 causal convolution + SiLU and the softplus step
+  // itself; fp32 only.
+  const float* zx;
+  const float* conv_w;   // [d_inner + 2*ng*N, 4]
+  const float* conv_b;   // same channels, or null
+  const float* dt_bias;  // [H]
+  int d_proj, d_inner;
 };
 hipError_t launch_ssd_scan(hipStream_t st, int dtype, const SsdArgs& a);
 
@@ -94,19 +103,6 @@ struct GemmPlan {
 GemmPlan gemm_plan(int dtype, int M, int N, int K);
 // out_f32: store fp32 (else the activation type of dtype)
 hipError_t launch_gemm_tn(hipStream_t st, int dtype, int out_f32, const GemmArgs& g, const GemmPlan& p);
-
-struct ConvActArgs {
-  const float* zx;      // fp32 [C*K, d_proj]: z | x | B | C | dt
-  const float* conv_w;  // fp32 [conv_dim, 4]
-  const float* conv_b;  // fp32 [conv_dim] or null
-  const float* dt_bias; // fp32 [H]
-  float* x;             // fp32 [C*K, d_inner]
-  float* B;             // fp32 [C*K, ngN]
-  float* Cm;            // fp32 [C*K, ngN]
-  float* delta;         // fp32 [C*K, H]
-  int C, K, d_inner, ngN, H, d_proj;
-};
-hipError_t launch_conv_act(hipStream_t st, const ConvActArgs& c);
 
 struct GateNormArgs {
   const float* y;       // fp32 [T, d_inner]

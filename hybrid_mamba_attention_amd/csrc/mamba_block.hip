@@ -2,9 +2,9 @@
 // Abstract, builds its drafter from Mamba-2 modules):
 //
 //   zxbcdt = hidden . W_in^T                  k_gemm_tn      (+ k_splitk_sum)
-//   x, B, C = SiLU(causal conv4(xBC)),        k_conv_act
-//   delta = softplus(dt_raw + dt_bias)
-//   y = SSD scan from h0 (+ D x)               k_ssd_scan     (ssd.hip, fp32 inputs)
+//   x, B, C = SiLU(causal conv4(xBC)),        k_ssd_scan     (ssd.hip: the scan reads the
+//   delta = softplus(dt_raw + dt_bias),                       raw rows and applies the
+//   y = SSD scan from h0 (+ D x)                              convolution in its loads)
 //   normed = RMSNorm(y * SiLU(z)) * w_norm     k_gate_norm
 //   out = normed . W_out^T                     k_gemm_tn      (+ k_splitk_sum)
 //
@@ -15,59 +15,6 @@
 #include "kernels.h"
 
 namespace hspec {
-
-namespace {
-
-__device__ __forceinline__ float silu_f(float v) { return v / (1.f + __expf(-v)); }
-
-// log(1 + e^v); above 20 the correction is below fp32 resolution.
-__device__ __forceinline__ float softplus_f(float v) { return v > 20.f ? v : log1pf(__expf(v)); }
-
-}  // namespace
-
-// ---------------------------------------------------------------------------
-// convolution, activations and step sizes
-// ---------------------------------------------------------------------------
-
-// One thread per (request, channel): channels [0, conv_dim) are x | B | C
-// (width-4 causal convolution from the block start, then SiLU); channels
-// [conv_dim, conv_dim + H) are the step sizes.  Loads of one position are
-// coalesced across the channels of a workgroup.
-__global__ __launch_bounds__(256) void k_conv_act(ConvActArgs c) {
-  const int ch = blockIdx.x * 256 + threadIdx.x, b = blockIdx.y;
-  const int conv_dim = c.d_inner + 2 * c.ngN;
-  const float* zx = c.zx + size_t(b) * c.K * c.d_proj + c.d_inner + ch;
-  if (ch < conv_dim) {
-    const float4 w = reinterpret_cast<const float4*>(c.conv_w)[ch];
-    const float bias = c.conv_b ? c.conv_b[ch] : 0.f;
-    float* dst;
-    int stride;
-    if (ch < c.d_inner) {
-      dst = c.x + size_t(b) * c.K * c.d_inner + ch;
-      stride = c.d_inner;
-    } else if (ch < c.d_inner + c.ngN) {
-      dst = c.B + size_t(b) * c.K * c.ngN + (ch - c.d_inner);
-      stride = c.ngN;
-    } else {
-      dst = c.Cm + size_t(b) * c.K * c.ngN + (ch - c.d_inner - c.ngN);
-      stride = c.ngN;
-    }
-    float x1 = 0.f, x2 = 0.f, x3 = 0.f;    // raw values 1, 2, 3 positions back
-    for (int t = 0; t < c.K; ++t) {
-      const float r = zx[size_t(t) * c.d_proj];
-      const float v = fmaf(w.w, r, fmaf(w.z, x1, fmaf(w.y, x2, fmaf(w.x, x3, bias))));
-      dst[size_t(t) * stride] = silu_f(v);
-      x3 = x2;
-      x2 = x1;
-      x1 = r;
-    }
-  } else if (ch < conv_dim + c.H) {
-    const int h = ch - conv_dim;
-    const float bias = c.dt_bias[h];
-    for (int t = 0; t < c.K; ++t)
-      c.delta[(size_t(b) * c.K + t) * c.H + h] = softplus_f(zx[size_t(t) * c.d_proj] + bias);
-  }
-}
 
 // ---------------------------------------------------------------------------
 // gated RMS normalisation
@@ -127,12 +74,6 @@ __global__ __launch_bounds__(256) void k_gate_norm_v4(GateNormArgs a) {
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
-
-hipError_t launch_conv_act(hipStream_t st, const ConvActArgs& c) {
-  const int ch = c.d_inner + 2 * c.ngN + c.H;
-  hipLaunchKernelGGL(k_conv_act, dim3((ch + 255) / 256, c.C), dim3(256), 0, st, c);
-  return hipGetLastError();
-}
 
 template <int NV>
 static void launch_gate_norm_v4(hipStream_t st, int dtype, const GateNormArgs& a, dim3 grid) {

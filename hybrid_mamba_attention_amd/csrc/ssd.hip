@@ -55,7 +55,12 @@ __host__ __device__ inline int ssd_heads_per_block(int H, int ng, int P) {
 // global load of a chunk is issued before the first wait, with clamped
 // indices and selects instead of per-element branches (a load under a branch
 // gets its own wait, which would serialize the loads' memory latencies).
-template <typename T, int NMAX, bool V4>
+// CONV: the inputs are the Mamba-2 block's raw projection rows; the lane
+// loads the Q + 3 raw values of its channel that its chunk's convolution
+// reads (zero before the block), each thread the four raw positions of its B
+// and Cm entries, and the conv + SiLU and softplus run after all of them are
+// issued.
+template <typename T, int NMAX, bool V4, bool CONV>
 __global__ __launch_bounds__(256) void k_ssd_scan(SsdArgs a) {
   using L = SsdLds<NMAX>;
   constexpr int Q = kSsdQ, LDB = L::LDB;
@@ -87,7 +92,7 @@ __global__ __launch_bounds__(256) void k_ssd_scan(SsdArgs a) {
   const float Ah = a.A[h];
   const float Dh = a.Dskip ? a.Dskip[h] : 0.f;
   const size_t HP = size_t(H) * P;
-  const T* __restrict__ xrow = static_cast<const T*>(a.x) + (size_t(b) * K * H + h) * P + pc;
+  const T* __restrict__ xrow = static_cast<const T*>(a.x) + (CONV ? 0 : (size_t(b) * K * H + h) * P + pc);
   float* __restrict__ yrow = a.y + (size_t(b) * K * H + h) * P + p;
 
   // the lane's state row H[p, 0..N), zero past N (and for idle lanes)
@@ -113,17 +118,60 @@ __global__ __launch_bounds__(256) void k_ssd_scan(SsdArgs a) {
     const int q = min(QC, K - c0);
     // issue: the lane's x[c0 + s, p], this thread's B / Cm entries, the lane's delta
     float xs[Q];
-#pragma unroll
-    for (int s = 0; s < Q; ++s) xs[s] = to_f32(xrow[size_t(min(c0 + s, K - 1)) * HP]);
     float bv[E], cv[E];
+    float dv;
+    if constexpr (CONV) {
+      // raw rows of request b: column d_inner + ch is conv channel ch; the
+      // step sizes follow the conv channels
+      const int ngN = a.ng * N, dpj = a.d_proj;
+      const float* zb = a.zx + size_t(b) * K * dpj + a.d_inner;
+      auto raw_at = [&](int t, int ch) { return zb[size_t(min(max(t, 0), K - 1)) * dpj + ch]; };
+      const int cx = h * P + pc;
+      float rx[Q + 3];
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const int i = tid + 256 * e, t = i / NMAX, n = i % NMAX;
-      const size_t src = ((size_t(b) * K + min(c0 + t, K - 1)) * a.ng + grp) * N + min(n, N - 1);
-      bv[e] = to_f32(Bm[src]);
-      cv[e] = to_f32(Cm[src]);
+      for (int s = 0; s < Q + 3; ++s) rx[s] = raw_at(c0 - 3 + s, cx);
+      float rb[E][4], rc[E][4];
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const int i = tid + 256 * e, t = i / NMAX, n = min(i % NMAX, N - 1);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          rb[e][j] = raw_at(c0 + t - 3 + j, a.d_inner + grp * N + n);
+          rc[e][j] = raw_at(c0 + t - 3 + j, a.d_inner + ngN + grp * N + n);
+        }
+      }
+      const float rdt = raw_at(c0 + lane, a.d_inner + 2 * ngN + h);
+      // positions before the block start are zero
+      auto conv = [&](int ch, int t_last, const float* r) {
+        const float4 w = reinterpret_cast<const float4*>(a.conv_w)[ch];
+        float v = a.conv_b ? a.conv_b[ch] : 0.f;
+        v = fmaf(w.x, t_last - 3 >= 0 ? r[0] : 0.f, v);
+        v = fmaf(w.y, t_last - 2 >= 0 ? r[1] : 0.f, v);
+        v = fmaf(w.z, t_last - 1 >= 0 ? r[2] : 0.f, v);
+        v = fmaf(w.w, r[3], v);
+        return silu_f(v);
+      };
+#pragma unroll
+      for (int s = 0; s < Q; ++s) xs[s] = conv(cx, c0 + s, rx + s);
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const int i = tid + 256 * e, t = i / NMAX, n = min(i % NMAX, N - 1);
+        bv[e] = conv(a.d_inner + grp * N + n, c0 + t, rb[e]);
+        cv[e] = conv(a.d_inner + ngN + grp * N + n, c0 + t, rc[e]);
+      }
+      dv = softplus_f(rdt + a.dt_bias[h]);
+    } else {
+#pragma unroll
+      for (int s = 0; s < Q; ++s) xs[s] = to_f32(xrow[size_t(min(c0 + s, K - 1)) * HP]);
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const int i = tid + 256 * e, t = i / NMAX, n = i % NMAX;
+        const size_t src = ((size_t(b) * K + min(c0 + t, K - 1)) * a.ng + grp) * N + min(n, N - 1);
+        bv[e] = to_f32(Bm[src]);
+        cv[e] = to_f32(Cm[src]);
+      }
+      dv = a.delta[(size_t(b) * K + min(c0 + lane, K - 1)) * H + h];
     }
-    const float dv = a.delta[(size_t(b) * K + min(c0 + lane, K - 1)) * H + h];
     if (!hmasked) {
 #pragma unroll
       for (int k = 0; k < NMAX; ++k) Hs[k] = (own && k < N) ? Hs[k] : 0.f;
@@ -263,10 +311,19 @@ template <typename T, int NMAX>
 static hipError_t launch_n(hipStream_t st, const SsdArgs& a) {
   const int hpw = ssd_heads_per_block(a.H, a.ng, a.P);
   const dim3 grid(a.C * (a.H / hpw)), block(256);
+  if constexpr (std::is_same<T, float>::value) {
+    if (a.zx) {
+      if (a.N % 4 == 0)
+        hipLaunchKernelGGL((k_ssd_scan<T, NMAX, true, true>), grid, block, 0, st, a);
+      else
+        hipLaunchKernelGGL((k_ssd_scan<T, NMAX, false, true>), grid, block, 0, st, a);
+      return hipGetLastError();
+    }
+  }
   if (a.N % 4 == 0)
-    hipLaunchKernelGGL((k_ssd_scan<T, NMAX, true>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((k_ssd_scan<T, NMAX, true, false>), grid, block, 0, st, a);
   else
-    hipLaunchKernelGGL((k_ssd_scan<T, NMAX, false>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((k_ssd_scan<T, NMAX, false, false>), grid, block, 0, st, a);
   return hipGetLastError();
 }
 
