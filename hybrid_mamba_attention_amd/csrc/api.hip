@@ -22,6 +22,9 @@ using namespace hspec;
 namespace {
 
 constexpr size_t kMaxLds = 160 * 1024;
+// GEMM operands up to 2^40 output elements (tile counts stay ints); no
+// projection that fits in device memory comes near it
+constexpr int64_t kMaxGemmOut = int64_t(1) << 40;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -34,7 +37,9 @@ int check_init(int dtype, int C, int d, int S, const void* u, const void* w, con
   if (!u || !w || !h0) return HSPEC_ERR_INVALID_ARG;
   if (!aligned(u, 16) || !aligned(w, 16) || !aligned(h0, 16)) return HSPEC_ERR_INVALID_ARG;
   if (d % 32 || S % 64) return HSPEC_ERR_UNSUPPORTED;
-  if (int64_t(S) / 64 > 0x7fffffff) return HSPEC_ERR_UNSUPPORTED;
+  // a lane's W row offsets within a 32-row k-step are 32-bit byte offsets,
+  // and the grid holds (S / 128) * ceil(C / 32) workgroups
+  if (S > (1 << 25) || C > (1 << 16)) return HSPEC_ERR_UNSUPPORTED;
   return HSPEC_OK;
 }
 
@@ -123,6 +128,8 @@ int check_attn(int dtype, int C, int K, int Hq, int Hkv, int D, const void* q, c
   const int e = esize(dtype);
   const int vec = 16 / e;
   if (ps <= 0 || ts <= 0 || hs <= 0 || ps % vec || ts % vec || hs % vec) return HSPEC_ERR_INVALID_ARG;
+  // the loader's offsets of a slab's 16 rows are 32-bit byte offsets
+  if (ts * e > (int64_t(1) << 27)) return HSPEC_ERR_UNSUPPORTED;
   for (const void* p : {q, kb, vb, kc, vc, out})
     if (!aligned(p, 16)) return HSPEC_ERR_INVALID_ARG;
   if (!aligned(pt, 4) || !aligned(ctx, 4)) return HSPEC_ERR_INVALID_ARG;
@@ -215,8 +222,9 @@ int check_block(const hspec_mamba_args* a) {
   const int64_t d_proj = 2 * d_inner + 2 * int64_t(a->ng) * a->N + a->H;
   const int64_t T = int64_t(a->C) * a->K;
   if (a->d_model % 8 || d_inner % 8) return HSPEC_ERR_UNSUPPORTED;
-  // row and column counts stay ints; requests index grid.y of the conv kernel
-  if (T > (1 << 30) || d_proj > (1 << 30) || a->C > 65535) return HSPEC_ERR_UNSUPPORTED;
+  // row and column counts stay ints, and so do the projections' tile counts
+  if (T > (1 << 30) || d_proj > (1 << 30)) return HSPEC_ERR_UNSUPPORTED;
+  if (T * std::max<int64_t>(d_proj, a->d_model) > kMaxGemmOut) return HSPEC_ERR_UNSUPPORTED;
   return HSPEC_OK;
 }
 
@@ -261,6 +269,7 @@ int check_inject(int dtype, int C, int n_new, int d, int Hkv, int D, const void*
   if (page_shift(page_size) < 0) return HSPEC_ERR_UNSUPPORTED;
   if (d % 8) return HSPEC_ERR_UNSUPPORTED;
   if (int64_t(C) * n_new > (1 << 30) || int64_t(Hkv) * D > (1 << 28)) return HSPEC_ERR_UNSUPPORTED;
+  if (int64_t(C) * n_new * 2 * Hkv * D > kMaxGemmOut) return HSPEC_ERR_UNSUPPORTED;
   return HSPEC_OK;
 }
 
@@ -326,6 +335,8 @@ int check_stack(const hspec_stack_args* a) {
   if (!(a->eps >= 0.f) || !std::isfinite(a->eps)) return HSPEC_ERR_INVALID_ARG;
   if (a->d_model % 8) return HSPEC_ERR_UNSUPPORTED;
   if (int64_t(a->C) * a->K > (1 << 30) || int64_t(a->Hq) * a->D > (1 << 28)) return HSPEC_ERR_UNSUPPORTED;
+  if (int64_t(a->C) * a->K * std::max<int64_t>(int64_t(a->Hq) * a->D, a->d_model) > kMaxGemmOut)
+    return HSPEC_ERR_UNSUPPORTED;
   for (int l = 0; l < a->n_layers; ++l) {
     const hspec_stack_layer& L = a->layers[l];
     if (!L.pre_norm_w || !aligned(L.pre_norm_w, 16)) return HSPEC_ERR_INVALID_ARG;

@@ -73,7 +73,8 @@ int hspec_abi_version(void);
  *   u       act  [C, d_model]      last-token hidden state per request
  *   w_init  act  [d_model, S]      projection weight, S = H*P*N
  *   h0      fp32 [C, S]            output (overwritten)
- * Limits: C >= 1, d_model % 32 == 0, S % 64 == 0 (else UNSUPPORTED).
+ * Limits: 1 <= C <= 65536, d_model % 32 == 0, S % 64 == 0, S <= 2^25 (else
+ * UNSUPPORTED).
  * Runs on bf16 (or fp32) matrix cores with fp32 accumulation.
  */
 int hspec_init_state(void* stream, int dtype, int C, int d_model, int S,
@@ -154,7 +155,8 @@ int hspec_ssd_scan(void* stream, int dtype, int C, int K, int H, int P, int ng, 
  *       with splits_b = max(1, ceil(ceil(ctx_b/16) / slabs_per_split)) and
  *       M = C * max(1, ceil(ceil(max_ctx/16) / slabs_per_split)); the rest
  *       holds fp32 split partials (slabs per split is a multiple of P/16).
- * Limits: D in {64, 128}; 1 <= K <= 64; Hq % Hkv == 0; (Hq/Hkv)*K <= 256.
+ * Limits: D in {64, 128}; 1 <= K <= 64; Hq % Hkv == 0; (Hq/Hkv)*K <= 256;
+ * token_stride times the element size <= 2^27 bytes (else UNSUPPORTED).
  */
 int hspec_block_attn_inplace(void* stream, int dtype, int C, int K, int Hq, int Hkv, int D,
                              const void* q, const void* k_blk, const void* v_blk,
@@ -246,9 +248,10 @@ int hspec_draft_layer_graph(const hspec_layer_args* a, hspec_graph* out);
  * normalised activations are rounded to the activation type before the
  * output projection.  `workspace` == NULL is a size query as for a3
  * (256-byte aligned device memory otherwise).
- * Limits: d_model % 8 == 0, d_inner % 8 == 0, the scan limits of a2
- * (else UNSUPPORTED); hidden, w_in, w_out, out, conv_w and norm_w 16-byte
- * aligned (else INVALID_ARG).
+ * Limits: d_model % 8 == 0, d_inner % 8 == 0, the scan limits of a2,
+ * C*K <= 2^30 and C*K * max(d_in_proj, d_model) <= 2^40 (else UNSUPPORTED);
+ * hidden, w_in, w_out, out, conv_w and norm_w 16-byte aligned (else
+ * INVALID_ARG).
  */
 typedef struct hspec_mamba_args {
   int dtype;
@@ -292,7 +295,8 @@ int hspec_mamba_block(void* stream, const hspec_mamba_args* a, size_t* required_
  * own distinct pages: writes to one slot from two requests race.
  * Runs on bf16 matrix cores (fp32 FMA for fp32), fp32 accumulation.
  * `workspace` == NULL is a size query as for a3 (split-K partials).
- * Limits: d_model % 8 == 0 (else UNSUPPORTED); hidden, w_kv 16-byte aligned.
+ * Limits: d_model % 8 == 0, C*n_new <= 2^30, Hkv*D <= 2^28 and
+ * C*n_new * 2*Hkv*D <= 2^40 (else UNSUPPORTED); hidden, w_kv 16-byte aligned.
  */
 int hspec_kv_inject(void* stream, int dtype, int C, int n_new, int d_model, int Hkv, int D,
                     const void* hidden, const void* w_kv, void* k_cache, void* v_cache,
@@ -327,7 +331,8 @@ int hspec_kv_inject(void* stream, int dtype, int C, int n_new, int d_model, int 
  *   layers     host array [n_layers]; the pointers inside are device memory
  *   workspace  as for a3: NULL = size query into *required_bytes
  * Limits: those of a1 (d_model % 32, S % 64), of the Mamba-2 block and of
- * a3; d_model % 8 == 0; pre_norm_w 16-byte aligned.
+ * a3; d_model % 8 == 0; C*K * max(Hq*D, d_model) <= 2^40; pre_norm_w 16-byte
+ * aligned.
  */
 typedef struct hspec_stack_layer {
   const float* pre_norm_w;      /* [d_model] */

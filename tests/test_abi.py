@@ -48,6 +48,9 @@ def _init(**kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(dtype=7), INVALID), (dict(C=0), INVALID), (dict(u=None), INVALID),
     (dict(h0=FAKE + 4), INVALID), (dict(d=100), UNSUPPORTED), (dict(S=100), UNSUPPORTED),
+    # the kernels' 32-bit row offsets and grid size bound S and C (a valid
+    # shape would launch: this entry point has no size query)
+    (dict(S=(1 << 25) + 64), UNSUPPORTED), (dict(C=(1 << 16) + 1), UNSUPPORTED),
 ])
 def test_init_state_validation(kw, code):
     assert _init(**kw) == code
@@ -89,6 +92,8 @@ def _attn(ws=None, nbytes=0, **kw):
     (dict(page=0), INVALID), (dict(page=48), UNSUPPORTED), (dict(page=8), UNSUPPORTED),
     (dict(page=512), UNSUPPORTED), (dict(page=32, max_pages=31), INVALID),
     (dict(D=96), UNSUPPORTED), (dict(K=65), UNSUPPORTED), (dict(Hq=64, Hkv=2, K=16), UNSUPPORTED),
+    # a slab's 16 row offsets are 32-bit byte offsets
+    (dict(ts=1 << 26), OK), (dict(ts=(1 << 26) + 8), UNSUPPORTED),
 ])
 def test_attention_validation(kw, code):
     assert _attn(**kw)[0] == code
@@ -178,6 +183,9 @@ def test_mamba_block_validation_and_workspace():
     assert _block(d_model=4100)[0] == UNSUPPORTED          # d_model % 8
     assert _block(P=128 + 8)[0] == UNSUPPORTED             # scan limit P <= 128
     assert _block(chunk=32)[0] == UNSUPPORTED
+    assert _block(C=(1 << 26) + 1, K=16)[0] == UNSUPPORTED  # C*K over 2^30 rows
+    assert _block(C=1 << 25, K=16)[0] == UNSUPPORTED        # 2^29 rows x 4096 columns > 2^40
+    assert _block(C=1 << 24, K=16)[0] == OK                 # 2^28 x 4096 = 2^40 (size query only)
     assert _block(workspace=FAKE, workspace_bytes=n - 1)[0] == WORKSPACE
     assert _block(workspace=FAKE + 16, workspace_bytes=n)[0] == WORKSPACE
     assert ops.lib().hspec_mamba_block(None, None, None) == INVALID
@@ -205,6 +213,8 @@ def test_kv_inject_validation_and_workspace():
     assert _inject(num_pages=0)[0] == INVALID
     assert _inject(d=4100)[0] == UNSUPPORTED
     assert _inject(page=24)[0] == UNSUPPORTED
+    assert _inject(C=1 << 26, n=16)[0] == UNSUPPORTED      # 2^30 rows x 2048 columns > 2^40
+    assert _inject(C=1 << 25, n=16)[0] == OK               # 2^29 x 2048 = 2^40 (size query only)
     assert _inject(ws=FAKE, nbytes=n1 - 1, C=1)[0] == WORKSPACE
 
 
@@ -260,6 +270,7 @@ def test_stack_validation_and_workspace():
     assert _stack(hidden_out=None)[0] == INVALID
     assert _stack(eps=-1.0)[0] == INVALID
     assert _stack(d_model=4100)[0] == UNSUPPORTED
+    assert _stack(C=1 << 25)[0] == UNSUPPORTED              # 2^29 rows x 4096 columns > 2^40
     assert _stack(mutate=lambda L: setattr(L[1], "wk", None))[0] == INVALID   # half without a weight
     assert _stack(mutate=lambda L: setattr(L[0], "pre_norm_w", FAKE + 4))[0] == INVALID
     assert _stack(mutate=lambda L: setattr(L[0], "w_init", None))[0] == INVALID
