@@ -12,8 +12,10 @@
 //     row pieces for the stage PF ahead into a register ring; a stage is then
 //     written to one of two LDS buffers, one barrier, and the waves run their
 //     MFMAs on it.  LDS rows are 128 bytes with the 16-byte piece index XORed
-//     by (row % 8), so both the stores and the operand reads are free of bank
-//     conflicts.
+//     by ((row / 2) % 8): 16 lanes of a 16-byte read (32 consecutive rows per
+//     half-wave) then cover the 64 banks once, and so do the stores (two rows
+//     of eight pieces).  XOR by (row % 8) suits 32 banks and measured 2-way
+//     conflicts on every operand read here.
 //   * Rows of A or B past M or N repeat the last row (their results are never
 //     stored); contraction indices past K load zeros.
 //   * Split-K: blockIdx.y takes one slice of K.  With more than one slice the
@@ -86,7 +88,7 @@ __global__ __launch_bounds__(256) void k_gemm_tn(GemmArgs g) {
 #pragma unroll
   for (int i = 0; i < (LA > LB ? LA : LB); ++i) {
     const int r = lr + 32 * i;
-    wpos[i] = r * 128 + ((lc ^ (r & 7)) << 4);
+    wpos[i] = r * 128 + ((lc ^ ((r >> 1) & 7)) << 4);
   }
 
   // Loads go out unconditionally (a piece past K reads an in-range address);
@@ -122,8 +124,11 @@ __global__ __launch_bounds__(256) void k_gemm_tn(GemmArgs g) {
   // operand rows of this lane (row l%32 of each 32-row tile; piece half l/32)
   const int orow = lane & 31, ohalf = lane >> 5;
   // The operands of k-step ks+1 are read from LDS before the MFMAs of k-step
-  // ks are issued, so LDS latency hides behind matrix work.
-  auto compute = [&](int buf) __attribute__((always_inline)) {
+  // ks are issued, so LDS latency hides behind matrix work.  `mid` (the next
+  // stage's LDS write and loads) runs after the third k-step's MFMAs, where
+  // its instructions interleave with the remaining matrix work instead of
+  // following it with the matrix pipe idle.
+  auto compute = [&](int buf, auto&& mid) __attribute__((always_inline)) {
     const unsigned char* ta = sA + buf * TA;
     const unsigned char* tb = sB + buf * TB;
     Vec8<bf16_t> ao[2][WM], bo[2][WN];
@@ -132,12 +137,12 @@ __global__ __launch_bounds__(256) void k_gemm_tn(GemmArgs g) {
 #pragma unroll
       for (int i = 0; i < WM; ++i) {
         const int r = wr * 32 * WM + 32 * i + orow;
-        a[i].v = *reinterpret_cast<const uint4*>(ta + r * 128 + ((pc ^ (r & 7)) << 4));
+        a[i].v = *reinterpret_cast<const uint4*>(ta + r * 128 + ((pc ^ ((r >> 1) & 7)) << 4));
       }
 #pragma unroll
       for (int j = 0; j < WN; ++j) {
         const int r = wc * 32 * WN + 32 * j + orow;
-        b[j].v = *reinterpret_cast<const uint4*>(tb + r * 128 + ((pc ^ (r & 7)) << 4));
+        b[j].v = *reinterpret_cast<const uint4*>(tb + r * 128 + ((pc ^ ((r >> 1) & 7)) << 4));
       }
     };
     read(0, ao[0], bo[0]);
@@ -149,14 +154,15 @@ __global__ __launch_bounds__(256) void k_gemm_tn(GemmArgs g) {
       for (int i = 0; i < WM; ++i)
 #pragma unroll
         for (int j = 0; j < WN; ++j) acc[i][j] = mma32(ao[ks & 1][i], bo[ks & 1][j], acc[i][j]);
+      if constexpr (ks == 2) mid();
     });
   };
 
-  // Stage st: barrier, MFMAs on LDS buffer st&1, then stage st+1 goes from
-  // its register slot into buffer (st+1)&1 (last read by stage st-1, which
-  // every wave finished before this barrier) and stage st+1+PF is issued
-  // into the freed slot.  The wait for stage st+1's loads thus comes after
-  // stage st's MFMAs are queued.  Every slot issues its loads, also past the
+  // Stage st: barrier, MFMAs on LDS buffer st&1; during its last k-steps,
+  // stage st+1 goes from its register slot into buffer (st+1)&1 (last read by
+  // stage st-1, which every wave finished before this barrier) and stage
+  // st+1+PF is issued into the freed slot.  The wait for stage st+1's loads
+  // thus comes after most of stage st's MFMAs are queued.  Every slot issues its loads, also past the
   // last stage (an in-range, already cached piece that is never used), and
   // stage nst is written to the idle buffer: with no path that skips a load,
   // each wait counts exactly the PF-1 newer stages still in flight.
@@ -172,10 +178,10 @@ __global__ __launch_bounds__(256) void k_gemm_tn(GemmArgs g) {
       constexpr int pp = decltype(P)::value;
       constexpr int nx = (pp + 1) % PF;
       __syncthreads();
-      compute(pp & 1);
-      __builtin_amdgcn_sched_barrier(0);   // the loads' wait stays behind the queued MFMAs
-      commit(st0 + pp + 1, (pp + 1) & 1, ra[nx], rb[nx]);
-      issue(st0 + pp + 1 + PF, ra[nx], rb[nx]);
+      compute(pp & 1, [&]() __attribute__((always_inline)) {
+        commit(st0 + pp + 1, (pp + 1) & 1, ra[nx], rb[nx]);
+        issue(st0 + pp + 1 + PF, ra[nx], rb[nx]);
+      });
     });
   }
   static_for<0, PF - 1>([&](auto P) __attribute__((always_inline)) {
@@ -183,7 +189,7 @@ __global__ __launch_bounds__(256) void k_gemm_tn(GemmArgs g) {
     constexpr int nx = (pp + 1) % PF;
     if (nfull + pp < nst) {   // uniform over the workgroup
       __syncthreads();
-      compute(pp & 1);
+      compute(pp & 1, [] {});
       commit(nfull + pp + 1, (pp + 1) & 1, ra[nx], rb[nx]);
     }
   });
