@@ -252,15 +252,17 @@ __global__ __launch_bounds__(256) void k_init_wide(InitArgs a) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) roff[e] = uint32_t((g * 8 + e) * S + 2 * c) * 2;
   // u pieces: piece q = row * 8 + slot holds the 16 bytes of logical segment
-  // slot ^ (row & 7) of that row's 64-wide slice (XOR swizzle: the A-operand
-  // reads of 8 consecutive rows then hit 8 different bank groups)
+  // slot ^ ((row / 2) & 7) of that row's 64-wide slice.  16-byte LDS reads are
+  // served as 64 banks: the 16 A-operand reads of 16 consecutive rows (two
+  // rows per 256 bytes) then hit 16 different bank groups; XOR by (row & 7)
+  // put rows r and r + 8 on the same banks.
   const bf16_t* usrc[Cfg::NU];
   uint32_t udst[Cfg::NU];
 #pragma unroll
   for (int t = 0; t < Cfg::NU; ++t) {
     const int q = int(threadIdx.x) + 256 * t;
     const int row = q >> 3, slot = q & 7;
-    usrc[t] = u + size_t(min(m0 + row, C - 1)) * d + 8 * (slot ^ (row & 7));
+    usrc[t] = u + size_t(min(m0 + row, C - 1)) * d + 8 * (slot ^ ((row >> 1) & 7));
     udst[t] = uint32_t(q) * 16;
   }
   // A operand of m-tile m, k-half h: row 32m + c, logical segment kh*4 + 2h + g
@@ -269,7 +271,7 @@ __global__ __launch_bounds__(256) void k_init_wide(InitArgs a) {
   for (int m = 0; m < MT; ++m)
 #pragma unroll
     for (int h = 0; h < 2; ++h)
-      aoff[m][h] = uint32_t(m * 32 + c) * 128 + uint32_t(((kh * 4 + 2 * h + g) ^ (c & 7)) << 4);
+      aoff[m][h] = uint32_t(m * 32 + c) * 128 + uint32_t(((kh * 4 + 2 * h + g) ^ ((c >> 1) & 7)) << 4);
 
   uint32_t ring[PF][16];  // k-step rows 8g+e (e < 8) and 16+8g+e (e >= 8), columns 2c, 2c+1
   u32x4 uring[PF][Cfg::NU];
