@@ -26,6 +26,7 @@
 // row m = request b * n_new + i is written as K | V rows of token position
 // start[b] + i into paged pools through the page table.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 #include "kernels.h"
@@ -292,19 +293,50 @@ __global__ __launch_bounds__(256) void k_gemm_tn_f32(GemmArgs g) {
   }
 }
 
-// Sum of the split-K partials in slice order.
-template <typename OutT>
+// Sum of the split-K partials in slice order, V consecutive columns per
+// thread (V = 4 needs N % 4 == 0; the head size, a multiple of 8, keeps four
+// scatter columns in one head).  The slices are loaded eight at a time, all
+// issued before the first add (clamped slice index; the sum skips the
+// repeats): a load per loop trip would wait out one memory round trip per
+// slice, which dominated this kernel at small M.
+template <typename OutT, int V>
 __global__ __launch_bounds__(256) void k_splitk_sum(GemmArgs g) {
+  using VecF = typename std::conditional<V == 4, float4, float>::type;
   const size_t mn = size_t(g.M) * g.N;
-  for (size_t e = size_t(blockIdx.x) * 256 + threadIdx.x; e < mn; e += size_t(gridDim.x) * 256) {
-    float s = 0.f;
-    for (int z = 0; z < g.splits; ++z) s += g.part[z * mn + e];
+  const size_t nq = mn / V;
+  const int ns = g.splits;
+  for (size_t q = size_t(blockIdx.x) * 256 + threadIdx.x; q < nq; q += size_t(gridDim.x) * 256) {
+    const size_t e = q * V;
+    float s[V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) s[v] = 0.f;
+    for (int z0 = 0; z0 < ns; z0 += 8) {
+      VecF x[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        x[u] = *reinterpret_cast<const VecF*>(g.part + size_t(min(z0 + u, ns - 1)) * mn + e);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (z0 + u < ns) {   // uniform
+          const float* xv = reinterpret_cast<const float*>(&x[u]);
+#pragma unroll
+          for (int v = 0; v < V; ++v) s[v] += xv[v];
+        }
+      }
+    }
     const size_t m = e / g.N, n = e % g.N;
+    OutT* dst;
     if (g.scatter) {
       const int64_t ro = scatter_row(g.sc, int(m));
-      if (ro >= 0) store_out(scatter_col<OutT>(g.sc, int(n)) + ro, s);
+      if (ro < 0) continue;
+      dst = scatter_col<OutT>(g.sc, int(n)) + ro;
     } else {
-      store_out(static_cast<OutT*>(g.c) + m * g.ldc + n, s);
+      dst = static_cast<OutT*>(g.c) + m * g.ldc + n;
+    }
+    if constexpr (V == 4) {
+      store_out4(dst, make_float4(s[0], s[1], s[2], s[3]));
+    } else {
+      store_out(dst, s[0]);
     }
   }
 }
@@ -392,9 +424,19 @@ static hipError_t launch_gemm_part(hipStream_t st, GemmArgs g, const GemmPart& p
     default: hipLaunchKernelGGL((k_gemm_tn_f32<OutT>), grid, dim3(256), 0, st, g); break;
   }
   if (p.splits > 1) {
-    const size_t mn = size_t(g.M) * g.N;
-    const unsigned blocks = unsigned(std::min<size_t>((mn + 255) / 256, 4096));
-    hipLaunchKernelGGL((k_splitk_sum<OutT>), dim3(blocks), dim3(256), 0, st, g);
+    // four columns per thread: whole 16-byte partial pieces, and output
+    // columns that stay in one row (or one head of one pool) at 4-element
+    // aligned addresses
+    auto al16 = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; };
+    const bool v4 = g.N % 4 == 0 &&
+                    (g.scatter ? g.sc.D % 4 == 0 && al16(g.sc.k_cache) && al16(g.sc.v_cache)
+                               : g.ldc % 4 == 0 && al16(g.c));
+    const size_t nq = size_t(g.M) * g.N / (v4 ? 4 : 1);
+    const unsigned blocks = unsigned(std::min<size_t>((nq + 255) / 256, 4096));
+    if (v4)
+      hipLaunchKernelGGL((k_splitk_sum<OutT, 4>), dim3(blocks), dim3(256), 0, st, g);
+    else
+      hipLaunchKernelGGL((k_splitk_sum<OutT, 1>), dim3(blocks), dim3(256), 0, st, g);
   }
   return hipGetLastError();
 }
