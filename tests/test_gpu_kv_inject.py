@@ -28,10 +28,22 @@ def written_mask(a, n_new):
     return m
 
 
-def run_and_check(w, n_new, starts, layout="NHD", page_size=16):
+def shifted(t, elems):
+    """A contiguous copy of t whose data starts `elems` elements past an
+    allocation's (aligned) start."""
+    flat = torch.empty(t.numel() + elems, dtype=t.dtype, device=t.device)
+    v = flat[elems:].view(t.shape)
+    v.copy_(t)
+    return v
+
+
+def run_and_check(w, n_new, starts, layout="NHD", page_size=16, pool_offset=0):
     a = wl.make_inject_inputs(w, n_new, ctx_lens=starts, page_size=page_size)
     dt = w.dtype
     kc, vc = to_dev(a["k_cache"], dt), to_dev(a["v_cache"], dt)
+    if pool_offset:
+        kc, vc = shifted(kc, pool_offset), shifted(vc, pool_offset)
+        assert kc.data_ptr() % 16 and vc.data_ptr() % 16
     if layout == "HND":
         kc, vc = kc.permute(0, 2, 1, 3).contiguous(), vc.permute(0, 2, 1, 3).contiguous()
     ops.kv_inject(to_dev(a["hidden"], dt), to_dev(a["w_kv"], dt), kc, vc, to_dev(a["page_table"], dt),
@@ -91,3 +103,10 @@ def test_kv_inject_skips_positions_outside_the_table():
     third = a["page_table"][1, 2]
     assert torch.equal(kc.view(torch.int16)[third], before[third])           # positions 32..35 skipped
     assert not torch.equal(kc.view(torch.int16)[pt[1, 1]], before[pt[1, 1]])  # 20..31 written
+
+
+def test_kv_inject_pools_off_16_byte_alignment():
+    """Pools 8 bytes off a 16-byte boundary: the split-K sum (C = 2) writes
+    the paged rows one element at a time instead of four."""
+    w = replace(wl.WORKLOADS[1], name="inject-misaligned", C=2)
+    run_and_check(w, 16, [5, 40], pool_offset=4)
