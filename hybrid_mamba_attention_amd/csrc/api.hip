@@ -149,14 +149,16 @@ int check_attn(int dtype, int C, int K, int Hq, int Hkv, int D, const void* q, c
   return HSPEC_OK;
 }
 
-int run_attn(hipStream_t st, int dtype, int C, int K, int Hq, int Hkv, int D, const void* q,
-             const void* kb, const void* vb, const void* kc, const void* vc, int64_t ps, int64_t ts,
-             int64_t hs, int num_pages, int page_size, const int32_t* pt, int max_pages,
-             const int32_t* ctx, int max_ctx, int kv_split_pages, float scale, int block_causal,
-             void* out, void* ws, size_t ws_bytes) {
+// The kernel arguments of a3 (arguments validated by check_attn); WORKSPACE
+// when `ws` cannot hold the plan and partials.
+int attn_args(AttnArgs& a, int C, int K, int Hq, int Hkv, int D, const void* q, const void* kb,
+              const void* vb, const void* kc, const void* vc, int64_t ps, int64_t ts, int64_t hs,
+              int num_pages, int page_size, const int32_t* pt, int max_pages, const int32_t* ctx,
+              int max_ctx, int kv_split_pages, float scale, int block_causal, void* out, void* ws,
+              size_t ws_bytes) {
   const AttnPlanShape p = plan_shape(C, K, Hq, Hkv, D, max_ctx, kv_split_pages, page_size);
   if (!ws || !aligned(ws, 256) || ws_bytes < p.total) return HSPEC_ERR_WORKSPACE;
-  AttnArgs a{};
+  a = AttnArgs{};
   a.q = q; a.k_blk = kb; a.v_blk = vb; a.k_cache = kc; a.v_cache = vc;
   a.page_stride = ps; a.token_stride = ts; a.head_stride = hs;
   a.num_pages = num_pages; a.page_table = pt; a.max_pages = max_pages;
@@ -174,6 +176,18 @@ int run_attn(hipStream_t st, int dtype, int C, int K, int Hq, int Hkv, int D, co
   a.max_splits = p.MS;
   a.block_causal = block_causal;
   a.lsp = page_shift(page_size);
+  return HSPEC_OK;
+}
+
+int run_attn(hipStream_t st, int dtype, int C, int K, int Hq, int Hkv, int D, const void* q,
+             const void* kb, const void* vb, const void* kc, const void* vc, int64_t ps, int64_t ts,
+             int64_t hs, int num_pages, int page_size, const int32_t* pt, int max_pages,
+             const int32_t* ctx, int max_ctx, int kv_split_pages, float scale, int block_causal,
+             void* out, void* ws, size_t ws_bytes) {
+  AttnArgs a;
+  const int st_ = attn_args(a, C, K, Hq, Hkv, D, q, kb, vb, kc, vc, ps, ts, hs, num_pages, page_size, pt,
+                            max_pages, ctx, max_ctx, kv_split_pages, scale, block_causal, out, ws, ws_bytes);
+  if (st_ != HSPEC_OK) return st_;
   return status_of(launch_block_attn(st, dtype, a));
 }
 
@@ -449,29 +463,28 @@ int check_layer(const hspec_layer_args* a, size_t* need) {
   return HSPEC_OK;
 }
 
-// The layer: attention half (a0/a3/a4) on s0; Mamba half (a1 -> a2) after it
-// on the same stream, or, with ev (2 events), forked onto s1 and joined.
-int enqueue_layer(const hspec_layer_args* a, hipStream_t s0, hipStream_t s1, hipEvent_t* ev) {
+// The layer on one stream: the attention (a0/a3; a4 too unless it joins the
+// scan), the state projection (a1), then the scan (a2) and, when some request
+// has several splits, the merge of the attention's partials (a4) in one
+// launch, so that those two small latency-bound kernels overlap.
+int enqueue_layer(const hspec_layer_args* a, hipStream_t s) {
   const bool no_init = !a->u && !a->w_init;
-  if (ev && (hipEventRecord(ev[0], s0) != hipSuccess || hipStreamWaitEvent(s1, ev[0], 0) != hipSuccess))
-    return HSPEC_ERR_HIP;
-  int st = run_attn(s0, a->dtype, a->C, a->K, a->Hq, a->Hkv, a->D, a->q, a->k_blk, a->v_blk, a->k_cache,
-                    a->v_cache, a->page_stride, a->token_stride, a->head_stride, a->num_pages,
-                    a->page_size, a->page_table, a->max_pages, a->ctx_lens, a->max_ctx, a->kv_split_pages,
-                    a->scale, a->block_causal, a->out, a->workspace, a->workspace_bytes);
-  if (st != HSPEC_OK) return st;
-  if (!no_init) {
-    InitArgs ia{a->u, a->w_init, a->h0, a->C, a->d_model, a->H * a->P * a->N};
-    st = status_of(launch_init_state(s1, a->dtype, ia));
-    if (st != HSPEC_OK) return st;
-  }
   SsdArgs sa{a->x, a->delta, a->A, a->B, a->Cm, a->Dskip, no_init ? nullptr : a->h0, a->y, a->h_final,
              a->C, a->K, a->H, a->P, a->ng, a->N, a->chunk};
-  st = status_of(launch_ssd_scan(s1, a->dtype, sa));
+  AttnArgs m;
+  int st = attn_args(m, a->C, a->K, a->Hq, a->Hkv, a->D, a->q, a->k_blk, a->v_blk, a->k_cache, a->v_cache,
+                     a->page_stride, a->token_stride, a->head_stride, a->num_pages, a->page_size,
+                     a->page_table, a->max_pages, a->ctx_lens, a->max_ctx, a->kv_split_pages, a->scale,
+                     a->block_causal, a->out, a->workspace, a->workspace_bytes);
   if (st != HSPEC_OK) return st;
-  if (ev && (hipEventRecord(ev[1], s1) != hipSuccess || hipStreamWaitEvent(s0, ev[1], 0) != hipSuccess))
-    return HSPEC_ERR_HIP;
-  return HSPEC_OK;
+  const bool fused = scan_merge_fits(a->dtype, sa, m);
+  st = status_of(launch_block_attn(s, a->dtype, m, !fused));
+  if (st == HSPEC_OK && !no_init) {
+    InitArgs ia{a->u, a->w_init, a->h0, a->C, a->d_model, a->H * a->P * a->N};
+    st = status_of(launch_init_state(s, a->dtype, ia));
+  }
+  if (st != HSPEC_OK) return st;
+  return status_of(fused ? launch_scan_merge(s, sa, m) : launch_ssd_scan(s, a->dtype, sa));
 }
 
 }  // namespace
@@ -579,7 +592,7 @@ int hspec_draft_layer(void* stream, const hspec_layer_args* a, size_t* required_
   if (required_bytes) *required_bytes = need;
   if (!a->workspace) return required_bytes ? HSPEC_OK : HSPEC_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  return enqueue_layer(a, s, s, nullptr);
+  return enqueue_layer(a, s);
 }
 
 int hspec_draft_layer_graph(const hspec_layer_args* a, hspec_graph* out) {
@@ -593,7 +606,7 @@ int hspec_draft_layer_graph(const hspec_layer_args* a, hspec_graph* out) {
   // slower at every C (C = 1: 88 vs 75 us; C = 128: 841 vs 767 us) -- both
   // halves are HBM-bound, so running them together only interferes.
   return capture_graph(0, [&](hipStream_t s0, hipStream_t, hipEvent_t*) {
-    return enqueue_layer(a, s0, s0, nullptr);
+    return enqueue_layer(a, s0);
   }, out);
 }
 

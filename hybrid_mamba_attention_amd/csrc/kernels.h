@@ -31,8 +31,8 @@ struct AttnArgs {
   int lsp;                        // log2(page size / 16)
 };
 
-// a0 + a3 + a4 on `st`.
-hipError_t launch_block_attn(hipStream_t st, int dtype, const AttnArgs& a);
+// a0 + a3 + a4 on `st` (merge = false: a4 is left to launch_scan_merge).
+hipError_t launch_block_attn(hipStream_t st, int dtype, const AttnArgs& a, bool merge = true);
 // dynamic LDS bytes of the attention kernel for a shape (host planning only)
 size_t attn_lds_bytes(int dtype, int D, int rows, int K);
 
@@ -58,6 +58,12 @@ struct SsdArgs {
   int d_proj, d_inner;
 };
 hipError_t launch_ssd_scan(hipStream_t st, int dtype, const SsdArgs& a);
+// The drafter layer's last launch at small C: a2's scan and a4's merge of the
+// attention's split partials in one grid (scan workgroups first).  Only for
+// bf16 activations, N % 4 == 0, D = 128 and no fused convolution (scan_merge_fits);
+// otherwise the two kernels run one after the other.
+bool scan_merge_fits(int dtype, const SsdArgs& s, const AttnArgs& m);
+hipError_t launch_scan_merge(hipStream_t st, const SsdArgs& s, const AttnArgs& m);
 
 struct InitArgs {
   const void* u;

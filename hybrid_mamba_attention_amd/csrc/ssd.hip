@@ -22,6 +22,7 @@
 // cumulative sum runs across one wave's lanes with shuffles.
 #include "common.h"
 #include "kernels.h"
+#include "merge.h"
 
 namespace hspec {
 
@@ -60,8 +61,10 @@ __host__ __device__ inline int ssd_heads_per_block(int H, int ng, int P) {
 // reads (zero before the block), each thread the four raw positions of its B
 // and Cm entries, and the conv + SiLU and softplus run after all of them are
 // issued.
+// The scan of workgroup `bid` (a device function so that the drafter layer's
+// combined scan + merge launch runs the same code).
 template <typename T, int NMAX, bool V4, bool CONV>
-__global__ __launch_bounds__(256) void k_ssd_scan(SsdArgs a) {
+__device__ __forceinline__ void ssd_scan_block(const SsdArgs& a, int bid) {
   using L = SsdLds<NMAX>;
   constexpr int Q = kSsdQ, LDB = L::LDB;
   constexpr int E = Q * NMAX / 256;  // B and Cm entries staged per thread
@@ -70,7 +73,7 @@ __global__ __launch_bounds__(256) void k_ssd_scan(SsdArgs a) {
   const int RB = (P + 63) >> 6;
   const int HPW = ssd_heads_per_block(H, a.ng, P);
   const int hblocks = H / HPW;
-  const int b = blockIdx.x / hblocks, hfirst = (blockIdx.x % hblocks) * HPW;
+  const int b = bid / hblocks, hfirst = (bid % hblocks) * HPW;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const bool active = wave < HPW * RB;
   const int h = min(hfirst + wave / RB, H - 1), p = (wave % RB) * 64 + lane;
@@ -298,6 +301,26 @@ __global__ __launch_bounds__(256) void k_ssd_scan(SsdArgs a) {
   }
 }
 
+template <typename T, int NMAX, bool V4, bool CONV>
+__global__ __launch_bounds__(256) void k_ssd_scan(SsdArgs a) {
+  ssd_scan_block<T, NMAX, V4, CONV>(a, blockIdx.x);
+}
+
+// Workgroups [0, n_scan) run the scan, the rest the merge of the attention's
+// split partials (grid (C * Hkv) x slabs, flattened request-major).  The two
+// are independent: the scan needs the projected state, the merge the
+// attention's partials, both written by earlier launches on the stream.
+template <int NMAX, int LPO, int U>
+__global__ __launch_bounds__(256) void k_scan_merge(SsdArgs s, AttnArgs m, int n_scan) {
+  const int bid = blockIdx.x;
+  if (bid < n_scan) {
+    ssd_scan_block<bf16_t, NMAX, true, false>(s, bid);
+  } else {
+    const int r = bid - n_scan, ch = m.C * m.Hkv;
+    attn_merge_block<bf16_t, 128, LPO, U>(m, r % ch, r / ch);
+  }
+}
+
 size_t ssd_lds_bytes(int P, int N, int Q) {
   (void)P;
   (void)Q;
@@ -337,6 +360,38 @@ static hipError_t launch_t(hipStream_t st, const SsdArgs& a) {
 
 hipError_t launch_ssd_scan(hipStream_t st, int dtype, const SsdArgs& a) {
   return dtype == 1 ? launch_t<bf16_t>(st, a) : launch_t<float>(st, a);
+}
+
+bool scan_merge_fits(int dtype, const SsdArgs& s, const AttnArgs& m) {
+  return dtype == 1 && !s.zx && s.N % 4 == 0 && m.D == 128 && m.max_items > m.C;
+}
+
+// The merge part takes the configuration k_attn_merge would (LPO lanes per
+// output quad, U splits per round of loads, by the largest split count).
+template <int NMAX, int LPO, int U>
+static hipError_t launch_scan_merge_cfg(hipStream_t st, const SsdArgs& s, const AttnArgs& m) {
+  const int n_scan = s.C * (s.H / ssd_heads_per_block(s.H, s.ng, s.P));
+  constexpr int OPB = 256 / LPO;
+  const int slabs = (m.rows * (128 / 4) + OPB - 1) / OPB;
+  const dim3 grid(n_scan + m.C * m.Hkv * slabs), block(256);
+  hipLaunchKernelGGL((k_scan_merge<NMAX, LPO, U>), grid, block, 0, st, s, m, n_scan);
+  return hipGetLastError();
+}
+
+template <int NMAX>
+static hipError_t launch_scan_merge_n(hipStream_t st, const SsdArgs& s, const AttnArgs& m) {
+  const int ms = m.max_splits;
+  if (ms <= 4) return launch_scan_merge_cfg<NMAX, 1, 4>(st, s, m);
+  if (ms <= 8) return launch_scan_merge_cfg<NMAX, 1, 8>(st, s, m);
+  if (ms <= 16) return launch_scan_merge_cfg<NMAX, 4, 4>(st, s, m);
+  return launch_scan_merge_cfg<NMAX, 4, 8>(st, s, m);
+}
+
+hipError_t launch_scan_merge(hipStream_t st, const SsdArgs& s, const AttnArgs& m) {
+  if (s.N <= 16) return launch_scan_merge_n<16>(st, s, m);
+  if (s.N <= 32) return launch_scan_merge_n<32>(st, s, m);
+  if (s.N <= 64) return launch_scan_merge_n<64>(st, s, m);
+  return launch_scan_merge_n<128>(st, s, m);
 }
 
 }  // namespace hspec
