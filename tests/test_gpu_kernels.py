@@ -348,8 +348,8 @@ def test_layer_block_causal_and_direct_reuse_ablation():
 
 
 def test_layer_graph_replays_match_eager():
-    """The layer's HIP graph (Mamba half on its own branch) against the eager
-    layer, bit for bit, over replays with eager work in between."""
+    """The layer's HIP graph (captured on one stream) against the eager layer,
+    bit for bit, over replays with eager work in between."""
     from helpers import layer_from_inputs
     w = wl.sweep_workload(4)
     w = replace_workload(w, ctx=("uniform", 100, 3000), seed=4545)
@@ -367,6 +367,31 @@ def test_layer_graph_replays_match_eager():
                                want.view(torch.int16) if want.dtype == torch.bfloat16 else want), rep
         torch.randn(1 << 18, device="cuda").sum()
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("C,ctx", [(4, ("uniform", 100, 3000)), (1, ("fixed", 8192))], ids=["c4-ragged-splits", "c1-32-splits"])
+def test_layer_equals_its_entry_points_bitwise(C, ctx):
+    """With several splits per request the layer runs the scan and the
+    attention's merge in one launch; its outputs must be the bits of the
+    separate entry points (a1, a2, a3 + a4) on the same inputs."""
+    from helpers import layer_from_inputs
+    from hybrid_mamba_attention_amd import ops
+    w = replace_workload(wl.sweep_workload(C), ctx=ctx, seed=4646 + C)
+    inp = wl.make_inputs(w)
+    layer = layer_from_inputs(inp)
+    assert int(layer.plan()[0]) > C, "the case must split requests"
+    a, dt = inp.arrays, w.dtype
+    h0 = ops.init_state(to_dev(a["u"], dt), to_dev(a["w_init"], dt))
+    y, hf = ops.ssd_scan(to_dev(a["x"], dt), to_dev(a["delta"], dt), to_dev(a["A"], dt), to_dev(a["B"], dt),
+                         to_dev(a["Cm"], dt), chunk=w.chunk, h0=h0, want_final=True)
+    out, _ = ops.block_attn_inplace(to_dev(a["q"], dt), to_dev(a["k_blk"], dt), to_dev(a["v_blk"], dt),
+                                    to_dev(a["k_cache"], dt), to_dev(a["v_cache"], dt),
+                                    to_dev(inp.page_table, dt), to_dev(inp.ctx_lens, dt), max_ctx=inp.max_ctx)
+    torch.cuda.synchronize()
+    assert torch.equal(layer.h0, h0)
+    assert torch.equal(layer.y, y)
+    assert torch.equal(layer.h_final, hf)
+    assert torch.equal(layer.out.view(torch.int16), out.view(torch.int16))
 
 
 def replace_workload(w, **kw):
