@@ -15,9 +15,11 @@ extern "C" {
 
 /*
  * Streaming read of `bytes` bytes at device pointer `buf` (16-byte aligned,
- * bytes a multiple of 16) with nontemporal 16-byte loads, 16384 workgroups
- * of 256 threads, four loads in flight per thread -- the best of the shapes
- * measured on MI355X for a 4 GiB buffer.  The data are XOR-folded and `sink`
+ * bytes a multiple of 16) with nontemporal 16-byte loads: 512 workgroups of
+ * 256 threads, each reading its own contiguous slice with eight loads in
+ * flight per thread -- the best of the shapes measured on MI355X for a 4 GiB
+ * buffer (7.0-7.2 TB/s; a grid-strided read of the same buffer, 6.6-6.7
+ * TB/s).  The data are XOR-folded and `sink`
  * (one device uint32) is written only if the fold hits a fixed value, so the
  * loads cannot be elided; the caller times the call.  Enqueues on `stream`
  * and returns HSPEC_OK (0), HSPEC_ERR_INVALID_ARG (-1) or HSPEC_ERR_HIP (-4).
