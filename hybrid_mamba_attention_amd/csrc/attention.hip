@@ -34,6 +34,8 @@
 //   * Each wave owns its rows across all the item's tokens, so nothing is
 //     merged inside the workgroup: a single-split request writes its
 //     normalised output, otherwise fp32 (m, l, O) partials go to the workspace.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 #include "merge.h"
@@ -200,9 +202,15 @@ template <typename T, int D> struct AttnLds {
 // accumulators are rescaled rarely.
 constexpr float kRescaleLog2 = 8.f;
 
-template <typename T, int D, int RT, int NW, int PF>
+template <typename T, int D, int RT, int NW, int PF, int HP>
 __global__ __launch_bounds__(64 * NW) void k_block_attn(AttnArgs a) {
-  using Gm = StageGeom<T, D>;
+  // HP kv heads per workgroup (1 or 2): with 2, heads j0 and j0+1 are
+  // adjacent in every token row (head stride D), so a stage's rows are 2D
+  // elements (one 512-byte piece per token for bf16, D = 128) and the waves
+  // split by head, NW/2 per head.
+  using Gm = StageGeom<T, HP * D>;
+  constexpr int WPH = NW / HP;  // waves per head
+  static_assert(HP == 1 || HP == 2, "one or two kv heads per workgroup");
   constexpr int NT = 64 * NW;
   constexpr int DS = D / 32, DPL = D / 16, EPC = Gm::EPC, CPR = Gm::CPR;
   constexpr int RPP = (NT / CPR) < 16 ? (NT / CPR) : 16;  // page rows one load round covers
@@ -214,7 +222,9 @@ __global__ __launch_bounds__(64 * NW) void k_block_attn(AttnArgs a) {
   const int li = lane & 15, lg = lane >> 4;
 
   const int Hkv = a.Hkv;
-  const int item = blockIdx.x / Hkv, j = blockIdx.x % Hkv;
+  const int item = blockIdx.x / (Hkv / HP), j0 = (blockIdx.x % (Hkv / HP)) * HP;
+  // this wave's kv head and its first row tile among that head's G*K rows
+  const int hl = wave / WPH, j = j0 + hl, wt = (wave % WPH) * RT;
   const int K = a.K, G = a.G, rows = a.rows;
   const int pps = a.pps;
   const int b = item / a.max_splits, split = item % a.max_splits;
@@ -229,7 +239,7 @@ __global__ __launch_bounds__(64 * NW) void k_block_attn(AttnArgs a) {
   Vec8<T> qv[RT][DS];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
-    const int row = min((wave * RT + rt) * 16 + li, rows - 1);
+    const int row = min((wt + rt) * 16 + li, rows - 1);
     const int t = row / G, gg = row % G;
     const T* qp = q + ((size_t(b) * K + t) * a.Hq + j * G + gg) * D;
 #pragma unroll
@@ -279,15 +289,15 @@ __global__ __launch_bounds__(64 * NW) void k_block_attn(AttnArgs a) {
   }
   const float c2 = a.scale_log2;
 
-  // ---- page descriptors (uniform): byte bases of K and V rows of kv head j
-  const int64_t head_off = int64_t(j) * a.head_stride * int64_t(sizeof(T));
+  // ---- page descriptors (uniform): byte bases of K and V rows of kv head j0
+  const int64_t head_off = int64_t(j0) * a.head_stride * int64_t(sizeof(T));
   const char* __restrict__ kcj = static_cast<const char*>(a.k_cache) + head_off;
   const char* __restrict__ vcj = static_cast<const char*>(a.v_cache) + head_off;
   const int64_t page_b = a.page_stride * int64_t(sizeof(T));
   const int64_t slab_b = 16 * a.token_stride * int64_t(sizeof(T));
   const int last_phys = a.num_pages - 1;
-  const char* kblk = static_cast<const char*>(a.k_blk) + ((size_t(b) * K) * Hkv + j) * D * sizeof(T);
-  const char* vblk = static_cast<const char*>(a.v_blk) + ((size_t(b) * K) * Hkv + j) * D * sizeof(T);
+  const char* kblk = static_cast<const char*>(a.k_blk) + ((size_t(b) * K) * Hkv + j0) * D * sizeof(T);
+  const char* vblk = static_cast<const char*>(a.v_blk) + ((size_t(b) * K) * Hkv + j0) * D * sizeof(T);
   const size_t blk_page_b = size_t(16) * Hkv * D * sizeof(T);
   // Stages [0, nhot) are two full context pages each: the hot path.  The rest
   // (a partial last page, the block's own keys) take the general path.
@@ -412,12 +422,14 @@ __global__ __launch_bounds__(64 * NW) void k_block_attn(AttnArgs a) {
     }
   };
 
-  // ---- consumer geometry (compile-time buffer offsets added per stage)
+  // ---- consumer geometry (compile-time buffer offsets added per stage); the
+  // wave's head starts hl*D elements into a stage row
+  const int hchunk = hl * (D / EPC);
   uint32_t kpos[DS][8 / EPC];   // row li (page 0), d group lg + 4*ds
 #pragma unroll
   for (int ds = 0; ds < DS; ++ds)
 #pragma unroll
-    for (int h = 0; h < 8 / EPC; ++h) kpos[ds][h] = Gm::pos(li, (lg + 4 * ds) * 8 / EPC + h) * 16;
+    for (int h = 0; h < 8 / EPC; ++h) kpos[ds][h] = Gm::pos(li, hchunk + (lg + 4 * ds) * 8 / EPC + h) * 16;
   // V rows: token 4*lg + e of page 0 (page 1 is +16 rows), elements li*DPL ..
   uint32_t vpos[4][DPL * sizeof(T) > 16 ? 2 : 1];
   constexpr int VCH = DPL * sizeof(T) > 16 ? 2 : 1;
@@ -426,7 +438,7 @@ __global__ __launch_bounds__(64 * NW) void k_block_attn(AttnArgs a) {
 #pragma unroll
     for (int h = 0; h < VCH; ++h) {
       const int row = 4 * lg + e;
-      const int e0 = li * DPL + h * EPC;  // first element of this chunk piece
+      const int e0 = hl * D + li * DPL + h * EPC;  // first element of this chunk piece
       vpos[e][h] = Gm::pos(row, e0 / EPC) * 16 + (e0 % EPC) * sizeof(T);
     }
 
@@ -434,7 +446,7 @@ __global__ __launch_bounds__(64 * NW) void k_block_attn(AttnArgs a) {
   // the last row, as the query loads do).
   int tq[RT];
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) tq[rt] = min((wave * RT + rt) * 16 + li, rows - 1) / G;
+  for (int rt = 0; rt < RT; ++rt) tq[rt] = min((wt + rt) * 16 + li, rows - 1) / G;
 
   auto compute = [&](int buf, const int (&nv)[2]) __attribute__((always_inline)) {
     const unsigned char* tk = sK + buf * TILE_B;
@@ -598,7 +610,7 @@ __global__ __launch_bounds__(64 * NW) void k_block_attn(AttnArgs a) {
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     const float lsum = group4_sum(acc.l[rt]);
-    const int row = (wave * RT + rt) * 16 + li;
+    const int row = (wt + rt) * 16 + li;
     if (row >= rows || nstage == 0) continue;  // nstage == 0: no such split
     if (nsplit == 1) {
       const int t = row / G, gg = row % G;
@@ -670,11 +682,11 @@ constexpr int kPrefetch = HSPEC_ATTN_PREFETCH;
 
 // (RT row tiles per wave, NW waves) for a query-row count: every wave reads the
 // whole stage from LDS, so fewer, wider waves cut LDS traffic per HBM byte.
-template <typename T, int D, int RT, int NW>
+template <typename T, int D, int RT, int NW, int HP = 1>
 static hipError_t launch_attn_cfg(hipStream_t st, const AttnArgs& a) {
-  const size_t lds = AttnLds<T, D>::bytes;
-  auto kern = k_block_attn<T, D, RT, NW, kPrefetch>;
-  hipLaunchKernelGGL(kern, dim3(a.max_items * a.Hkv), dim3(64 * NW), lds, st, a);
+  const size_t lds = AttnLds<T, HP * D>::bytes;
+  auto kern = k_block_attn<T, D, RT, NW, kPrefetch, HP>;
+  hipLaunchKernelGGL(kern, dim3(a.max_items * (a.Hkv / HP)), dim3(64 * NW), lds, st, a);
   return hipGetLastError();
 }
 
@@ -682,10 +694,23 @@ static hipError_t launch_attn_cfg(hipStream_t st, const AttnArgs& a) {
 #define HSPEC_ATTN_RT64 1  // row tiles per wave for 33..64 query rows (waves = 4 / this)
 #endif
 
+#ifndef HSPEC_ATTN_HEAD_PAIR
+#define HSPEC_ATTN_HEAD_PAIR 1
+#endif
 template <typename T, int D>
 static hipError_t launch_attn_d(hipStream_t st, const AttnArgs& a) {
   if (a.rows <= 16) return launch_attn_cfg<T, D, 1, 1>(st, a);
   if (a.rows <= 32) return launch_attn_cfg<T, D, 1, 2>(st, a);
+  // Two adjacent kv heads per workgroup (bf16, D = 128, 33..64 rows per head,
+  // splits of at least 128 slabs): each stage row is then one 512-byte piece
+  // of the token's K (V) instead of two 256-byte pieces read by two
+  // workgroups, which a read probe of the pattern measures at 7.1-7.2 TB/s
+  // against 6.6 TB/s (C = 128: 687 -> 651 us).  With short splits (small C)
+  // halving the workgroup count costs more than the pieces gain.
+  if constexpr (std::is_same<T, bf16_t>::value && D == 128) {
+    if (HSPEC_ATTN_HEAD_PAIR && a.rows <= 64 && a.Hkv % 2 == 0 && a.head_stride == D && a.pps >= 128)
+      return launch_attn_cfg<T, D, 1, 8, 2>(st, a);
+  }
   if (a.rows <= 64) return launch_attn_cfg<T, D, HSPEC_ATTN_RT64, 4 / HSPEC_ATTN_RT64>(st, a);
   if (a.rows <= 128) return launch_attn_cfg<T, D, 2, 4>(st, a);
   return launch_attn_cfg<T, D, 4, 4>(st, a);

@@ -207,6 +207,20 @@ def test_hnd_pool_layout_is_bit_identical():
     assert_close(to_host64(oh), oracle_attn(case), "bf16", "HND")
 
 
+@pytest.mark.parametrize("causal", [False, True], ids=["mask-free", "block-causal"])
+def test_head_pair_workgroups_match_single_heads(causal):
+    """Splits of at least 2048 tokens over NHD pools (adjacent kv heads) take
+    two heads per workgroup; the HND layout of the same pools keeps one head
+    per workgroup.  Same bits, and the oracle within tolerance (ragged
+    contexts, one split and 2048-token splits with a merge, the block keys)."""
+    case = make_attn_case(960, [2100, 4000, 2048, 3000], 16, 32, 8, 128, "bf16")
+    for split in (10 ** 6, 128):
+        on, _, _ = run_attn(case, split=split, layout="NHD", causal=causal)
+        oh, _, _ = run_attn(case, split=split, layout="HND", causal=causal)
+        assert torch.equal(on.view(torch.int16), oh.view(torch.int16)), split
+        assert_close(to_host64(on), oracle_attn(case, causal=causal), "bf16", f"head pair split={split}")
+
+
 def test_kv_pool_untouched_and_output_bounded():
     case = make_attn_case(13, [400, 3], 16, 32, 8, 128, "bf16")
     dt = case["dtype"]
