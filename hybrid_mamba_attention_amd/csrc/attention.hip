@@ -202,8 +202,11 @@ template <typename T, int D> struct AttnLds {
 // accumulators are rescaled rarely.
 constexpr float kRescaleLog2 = 8.f;
 
+// bf16 with two row tiles per wave (128 query rows per head) is held to two
+// waves per SIMD: it needs 259 registers unbounded, 256 with three spilled
+// (workload 4: 665 -> 559 us).  fp32 would spill hundreds, so it is not bound.
 template <typename T, int D, int RT, int NW, int PF, int HP>
-__global__ __launch_bounds__(64 * NW) void k_block_attn(AttnArgs a) {
+__global__ __launch_bounds__(64 * NW, (RT == 2 && sizeof(T) == 2) ? 2 : 1) void k_block_attn(AttnArgs a) {
   // HP kv heads per workgroup (1 or 2): with 2, heads j0 and j0+1 are
   // adjacent in every token row (head stride D), so a stage's rows are 2D
   // elements (one 512-byte piece per token for bf16, D = 128) and the waves
