@@ -2,8 +2,9 @@
 // in place (H-Spec, Abstract: attention modules reuse the target KV where it
 // lies; there is no drafter-side KV cache).
 //
-// a3  k_block_attn       one workgroup per (work item = request x split, kv head);
-//                        workgroup 0 also writes the int32 split plan (a0)
+// a3  k_block_attn       one workgroup per (work item = request x split, kv head),
+//                        or per (work item, pair of adjacent kv heads) with long
+//                        splits; workgroup 0 also writes the int32 split plan (a0)
 // a4  k_attn_merge       log-sum-exp merge of the splits of multi-split requests
 //
 // Work items are numbered request * max_splits + split, so every kernel finds
@@ -11,16 +12,19 @@
 // request's own split count exit at once.  The plan in the workspace lists the
 // same decomposition (compacted, in request order) for callers and tests.
 //
-// k_block_attn, per workgroup of NW waves (one work item, one kv head j):
+// k_block_attn, per workgroup of NW waves (one work item, HP = 1 or 2 kv heads):
 //   * The G*K query rows of kv head j (row r -> block position r / G, head
-//     j*G + r % G) are split over the waves, RT tiles of 16 rows each, and
-//     held in registers as matrix-core operands for the whole kernel.
+//     j*G + r % G) are split over NW/HP waves, RT tiles of 16 rows each, and
+//     held in registers as matrix-core operands for the whole kernel.  With
+//     HP = 2 (NHD pools, splits of 2048+ tokens) a stage row is the 2D-wide
+//     piece of both heads, 512 bytes for bf16 D = 128, and each half of the
+//     waves computes on its own head's columns.
 //   * The item's pages stream through LDS 32 tokens (two pages) at a time:
 //     every thread loads 16-byte pieces of K and V rows for the next stage
-//     (16 threads cover a 256-byte row, the physical page comes from the page
-//     table) while the waves compute on the current stage; one barrier per
-//     stage.  LDS rows are XOR-swizzled by 16-byte chunk so that operand reads
-//     are bank-conflict free.
+//     (16 threads cover a 256-byte row, 32 a 512-byte head-pair row; the
+//     physical page comes from the page table) while the waves compute on the
+//     current stage; one barrier per stage.  LDS rows are XOR-swizzled by
+//     16-byte chunk so that operand reads are bank-conflict free.
 //   * The draft block's own K keys and values ("transient intra-block KV")
 //     are the last stages of the last split: they pass through the same LDS
 //     buffers and are never written anywhere.  With the block-causal mask,
@@ -679,8 +683,9 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
 // Stages of K/V loads in flight per workgroup.  With nontemporal loads two
 // stages keep pace with four at 64 query rows (C = 128: 707 vs 729 us) and
 // leave the 128-row tiles at two waves per SIMD instead of one (workload 4:
-// 660 vs 771 us).  (Those figures predate the hot loop below; with it, depth
-// 2 runs at 96% of a plain streaming read, and depth 4 does not compile.)
+// 660 vs 771 us).  (Those figures predate the hot loop below.  With it,
+// depth 4 compiles for the bf16 64-row form, 235 registers, and measured 2-7%
+// slower at every C; the fp32 128-row form does not compile at depth 4.)
 constexpr int kPrefetch = HSPEC_ATTN_PREFETCH;
 
 // (RT row tiles per wave, NW waves) for a query-row count: every wave reads the
