@@ -1,0 +1,33 @@
+"""The bench line's host-side contract (no GPU): the committed HBM-traffic
+record belongs to the attention sources as they stand, and the multi-GPU flag
+is refused with a message."""
+import importlib.util
+import json
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def load_bench():
+    spec = importlib.util.spec_from_file_location("bench_under_test", os.path.join(ROOT, "bench.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def test_traffic_record_matches_the_attention_sources():
+    """bench.py reports `traffic` only while the attention kernel's sources
+    hash to the value stored with the counter runs in profiles/."""
+    bench = load_bench()
+    rec = json.load(open(os.path.join(ROOT, "profiles", "k_block_attn_llama8b-bf16-c128-ctx8192_traffic.json")))
+    assert rec["source_hash"] == bench.kernel_source_hash(), "attention sources changed: re-take the counters"
+    assert bench.traffic_from_profile("llama8b-bf16-c128-ctx8192") == rec["hbm_bytes_per_launch"]
+    assert 0.99 < rec["hbm_bytes_per_launch"] / rec["kernels"]["k_block_attn"]["algorithmic_bytes"] < 1.1
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120, cwd=ROOT)
+    assert r.returncode != 0 and "one GPU" in (r.stdout + r.stderr)
