@@ -207,14 +207,16 @@ def test_hnd_pool_layout_is_bit_identical():
     assert_close(to_host64(oh), oracle_attn(case), "bf16", "HND")
 
 
+@pytest.mark.parametrize("page", [16, 64])
 @pytest.mark.parametrize("causal", [False, True], ids=["mask-free", "block-causal"])
-def test_head_pair_workgroups_match_single_heads(causal):
+def test_head_pair_workgroups_match_single_heads(causal, page):
     """Splits of at least 2048 tokens over NHD pools (adjacent kv heads) take
     two heads per workgroup; the HND layout of the same pools keeps one head
     per workgroup.  Same bits, and the oracle within tolerance (ragged
-    contexts, one split and 2048-token splits with a merge, the block keys)."""
-    case = make_attn_case(960, [2100, 4000, 2048, 3000], 16, 32, 8, 128, "bf16")
-    for split in (10 ** 6, 128):
+    contexts, one split and 2048-token splits with a merge, the block keys,
+    16- and 64-token pages)."""
+    case = make_attn_case(960, [2100, 4000, 2048, 3000], 16, 32, 8, 128, "bf16", page=page)
+    for split in (10 ** 6, 2048 // page):
         on, _, _ = run_attn(case, split=split, layout="NHD", causal=causal)
         oh, _, _ = run_attn(case, split=split, layout="HND", causal=causal)
         assert torch.equal(on.view(torch.int16), oh.view(torch.int16)), split
