@@ -145,7 +145,7 @@ int check_attn(int dtype, int C, int K, int Hq, int Hkv, int D, const void* q, c
   if (int64_t(Hq / Hkv) * K > 256) return HSPEC_ERR_UNSUPPORTED;
   if (attn_lds_bytes(dtype, D, (Hq / Hkv) * K, K) > kMaxLds) return HSPEC_ERR_UNSUPPORTED;
   const AttnPlanShape p = plan_shape(C, K, Hq, Hkv, D, max_ctx, kv_split_pages, page_size);
-  if (int64_t(C) * p.MS * Hkv > 0x7fffffff) return HSPEC_ERR_UNSUPPORTED;
+  if (int64_t(C) * p.MS * Hkv >= 0x7fffffff) return HSPEC_ERR_UNSUPPORTED;  // + the plan workgroup
   return HSPEC_OK;
 }
 

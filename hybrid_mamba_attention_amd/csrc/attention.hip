@@ -4,7 +4,7 @@
 //
 // a3  k_block_attn       one workgroup per (work item = request x split, kv head),
 //                        or per (work item, pair of adjacent kv heads) with long
-//                        splits; workgroup 0 also writes the int32 split plan (a0)
+//                        splits; one more workgroup writes the int32 split plan (a0)
 // a4  k_attn_merge       log-sum-exp merge of the splits of multi-split requests
 //
 // Work items are numbered request * max_splits + split, so every kernel finds
@@ -56,7 +56,7 @@ __device__ __forceinline__ uint4 ld_stream(const char* p) {
 }
 
 // ---------------------------------------------------------------------------
-// a0: split plan, written by workgroup 0 of k_block_attn after its own item
+// a0: split plan, written by the last workgroup of k_block_attn (no other work)
 // (NT threads, `scan` = NT + 1 ints of LDS).  Layout documented in
 // include/hspec.h: splits_b = max(1, ceil(ceil(ctx_b / 16) / pps)), items
 // listed request by request.
@@ -228,6 +228,15 @@ __global__ __launch_bounds__(64 * NW, (RT == 2 && sizeof(T) == 2) ? 2 : 1) void 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int li = lane & 15, lg = lane >> 4;
 
+  extern __shared__ __align__(16) unsigned char smem[];
+  // The grid's last workgroup writes the split plan (a0) and nothing else, so
+  // the plan runs beside the work items instead of after one of them (it was
+  // ~3 us of the kernel at C = 1 when workgroup 0 wrote it after its item).
+  if (blockIdx.x == gridDim.x - 1) {
+    write_split_plan<NT>(a, reinterpret_cast<int*>(smem));
+    return;
+  }
+
   const int Hkv = a.Hkv;
   const int item = blockIdx.x / (Hkv / HP), j0 = (blockIdx.x % (Hkv / HP)) * HP;
   // this wave's kv head and its first row tile among that head's G*K rows
@@ -282,7 +291,6 @@ __global__ __launch_bounds__(64 * NW, (RT == 2 && sizeof(T) == 2) ? 2 : 1) void 
   const int nvp = ncache + nblk;
   const int nstage = (nvp + 1) >> 1;
 
-  extern __shared__ __align__(16) unsigned char smem[];
   unsigned char* sK = smem;                    // [2][TILE_B]
   unsigned char* sV = smem + 2 * TILE_B;       // [2][TILE_B]
 
@@ -662,7 +670,6 @@ __global__ __launch_bounds__(64 * NW, (RT == 2 && sizeof(T) == 2) ? 2 : 1) void 
       if (lg == 0) *reinterpret_cast<float2*>(a.part_ml + prow * 2) = make_float2(acc.m2[rt], lsum);
     }
   }
-  if (blockIdx.x == 0) write_split_plan<NT>(a, reinterpret_cast<int*>(smem));
 }
 
 // ---------------------------------------------------------------------------
@@ -694,7 +701,8 @@ template <typename T, int D, int RT, int NW, int HP = 1>
 static hipError_t launch_attn_cfg(hipStream_t st, const AttnArgs& a) {
   const size_t lds = AttnLds<T, HP * D>::bytes;
   auto kern = k_block_attn<T, D, RT, NW, kPrefetch, HP>;
-  hipLaunchKernelGGL(kern, dim3(a.max_items * (a.Hkv / HP)), dim3(64 * NW), lds, st, a);
+  // one workgroup per (item, head group), plus the plan writer
+  hipLaunchKernelGGL(kern, dim3(a.max_items * (a.Hkv / HP) + 1), dim3(64 * NW), lds, st, a);
   return hipGetLastError();
 }
 

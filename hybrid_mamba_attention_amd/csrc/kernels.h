@@ -22,7 +22,7 @@ struct AttnArgs {
   int C, K, Hq, Hkv, G, D, rows;  // rows = G * K query rows per kv head
   float scale_log2;               // softmax scale * log2(e)
   void* out;
-  int32_t* plan;                  // workspace head: the split plan (written by block 0)
+  int32_t* plan;                  // workspace head: the split plan (written by the last block)
   float* part_o;                  // [max_items, Hkv, rows, D], item = request * max_splits + split
   float* part_ml;                 // [max_items, Hkv, rows, 2]
   int max_items;                  // C * max_splits
