@@ -571,21 +571,39 @@ __global__ __launch_bounds__(64 * NW, (RT == 2 && sizeof(T) == 2) ? 2 : 1) void 
   if (kHot && nhot >= 2 * PF) {  // uniform over the workgroup
     // Hot loop: every stage it issues is two full context pages, so every
     // slot issues its loads on every path and each wait before a commit
-    // counts exactly the newer stage in flight.  The page-table window is
-    // refreshed once per 64 stages with an explicit full wait, so the page
-    // numbers read by every issue are never a pending load.
+    // counts exactly the newer stage in flight.  The next page-table window
+    // is loaded into (pnlo, pnhi) just before the last stage of the current
+    // one is issued; at the window's first stage an explicit wait for all
+    // but that stage's loads makes it current.  The page numbers read by
+    // every issue are thus never a pending load, and the K/V stream never
+    // drains for them (a full wait there cost one round trip per 64 stages).
+    // vmcnt(2 * NLD): one stage's loads may stay pending (count bits 3:0 and 15:14)
+    static_assert(2 * NLD < 64, "vmcnt field");
+    constexpr int kWinWait = 0x0F70 | ((2 * NLD) & 15) | (((2 * NLD) >> 4) << 14);
+    const int wmask = (64 << lsp) - 1;
+    int pnlo = 0, pnhi = 0;
+    // The first PF stages go out strictly in slot order.  Interleaved by the
+    // scheduler, the loop's wait bookkeeping at its header must assume slot 0
+    // may be the newest load, and it then waits for every load in flight
+    // before each slot-0 issue, every PF stages of the whole loop.
     static_for<0, PF>([&](auto P) __attribute__((always_inline)) {
       constexpr int pp = decltype(P)::value;
       issue_hot(pp, stk[pp], stv[pp]);
+      __builtin_amdgcn_sched_barrier(0);
     });
     for (; st0 + 2 * PF <= nhot; st0 += PF) {
       static_for<0, PF>([&](auto P) __attribute__((always_inline)) {
         constexpr int pp = decltype(P)::value;
         const int sn = st0 + pp + PF;   // < nhot
         commit(pp & 1, stk[pp], stv[pp]);
-        if ((sn & ((64 << lsp) - 1)) == 0) {   // first stage of a 128-page window
-          load_window(sn >> (6 + lsp));
-          __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+        if ((sn & wmask) == 0) {   // first stage of a 128-page window, loaded one step ago
+          __builtin_amdgcn_s_waitcnt(kWinWait);
+          pwlo = pnlo;
+          pwhi = pnhi;
+        } else if (((sn + 1) & wmask) == 0) {   // last stage of this window: fetch the next
+          const int base = (p_lo >> lsp) + 128 * ((sn + 1) >> (6 + lsp));
+          pnlo = pt[min(base + lane, a.max_pages - 1)];
+          pnhi = pt[min(base + 64 + lane, a.max_pages - 1)];
         }
         issue_hot(sn, stk[pp], stv[pp]);
         __syncthreads();
