@@ -194,9 +194,10 @@ __global__ __launch_bounds__(256) void k_init_state(InitArgs a) {
 // rows 8g .. 8g+7 and 16+8g .. 16+8g+7 of those two columns as one dword per
 // row: 128 contiguous bytes per row across the 32 lanes of a half-wave.
 //
-// Per step j: barrier; read the A operands of step j from the LDS slice
-// buffer j & 1; MFMAs; issue the W rows and u slice of step j+PF into the
-// register ring slot just freed; write the u slice of step j+1 into LDS
+// Per step j: barrier; build the B operands of step j; read its A operands
+// from the LDS slice buffer j & 1; MFMAs; issue the W rows and u slice of
+// step j+PF into the register ring slot just freed (before the MFMAs at 128
+// rows, see EARLY below); write the u slice of step j+1 into LDS
 // buffer (j+1) & 1.  The u slice is loaded PF steps ahead like W, because
 // loads retire in order and waiting on a later-issued u load would also wait
 // on every W load issued before it.
@@ -209,7 +210,11 @@ struct WideCfg {
   static constexpr int LDS = 2 * TILE > RED ? 2 * TILE : RED;
 };
 
-template <int MT, int PF>
+// EARLY: a step issues the loads of step j+PF as soon as the B operands of
+// step j are built, before its MFMAs.  At 128 rows a wave's 16 MFMAs would
+// otherwise hold the next loads back by ~500 cycles every step (C = 128:
+// 60-63 -> 57.5 us); at 32 and 64 rows issuing after the MFMAs is faster.
+template <int MT, int PF, bool EARLY>
 __global__ __launch_bounds__(256) void k_init_wide(InitArgs a) {
   using Cfg = WideCfg<MT>;
   static_assert(PF >= 2, "the u slice of step j+1 must already be in flight");
@@ -291,9 +296,8 @@ __global__ __launch_bounds__(256) void k_init_wide(InitArgs a) {
 #pragma unroll
     for (int t = 0; t < Cfg::NU; ++t) *reinterpret_cast<u32x4*>(lds + buf * Cfg::TILE + udst[t]) = ud[t];
   };
-  auto mfmas = [&](int buf, const uint32_t (&w)[16]) __attribute__((always_inline)) {
+  auto bops = [&](const uint32_t (&w)[16], Vec8<bf16_t> (&bop)[2][2]) __attribute__((always_inline)) {
     // B operand (k-half h, n-tile t): element e = W[16h + 8g + e][n0 + 2c + t]
-    Vec8<bf16_t> bop[2][2];
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -305,6 +309,8 @@ __global__ __launch_bounds__(256) void k_init_wide(InitArgs a) {
         bop[h][t].v.z = __builtin_amdgcn_perm(r[5], r[4], sel);
         bop[h][t].v.w = __builtin_amdgcn_perm(r[7], r[6], sel);
       }
+  };
+  auto mmas = [&](int buf, const Vec8<bf16_t> (&bop)[2][2]) __attribute__((always_inline)) {
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
@@ -315,7 +321,6 @@ __global__ __launch_bounds__(256) void k_init_wide(InitArgs a) {
         for (int t = 0; t < 2; ++t) acc[m][t] = mma32(ap, bop[h][t], acc[m][t]);
       }
   };
-
   static_for<0, PF>([&](auto P) __attribute__((always_inline)) {
     issue(decltype(P)::value, ring[decltype(P)::value], uring[decltype(P)::value]);
   });
@@ -325,8 +330,16 @@ __global__ __launch_bounds__(256) void k_init_wide(InitArgs a) {
   auto step = [&](int j, auto P) __attribute__((always_inline)) {
     constexpr int p = decltype(P)::value;
     __syncthreads();
-    mfmas(j & 1, ring[p]);
-    issue(j + PF, ring[p], uring[p]);
+    Vec8<bf16_t> bop[2][2];
+    bops(ring[p], bop);
+    if constexpr (EARLY) {
+      issue(j + PF, ring[p], uring[p]);
+      __builtin_amdgcn_sched_barrier(0);
+      mmas(j & 1, bop);
+    } else {
+      mmas(j & 1, bop);
+      issue(j + PF, ring[p], uring[p]);
+    }
     put_u((j + 1) & 1, uring[(p + 1) % PF]);
   };
   const int nfull = ns - ns % PF;
@@ -371,7 +384,7 @@ static hipError_t launch_cfg(hipStream_t st, const InitArgs& a) {
 template <int MT, int PF>
 static hipError_t launch_wide(hipStream_t st, const InitArgs& a) {
   const int mb = (a.C + 32 * MT - 1) / (32 * MT);
-  hipLaunchKernelGGL((k_init_wide<MT, PF>), dim3((a.S / 128) * mb), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((k_init_wide<MT, PF, (MT >= 4)>), dim3((a.S / 128) * mb), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
