@@ -223,6 +223,27 @@ def test_head_pair_workgroups_match_single_heads(causal, page):
         assert_close(to_host64(on), oracle_attn(case, causal=causal), "bf16", f"head pair split={split}")
 
 
+@pytest.mark.parametrize("page", [16, 32, 64])
+def test_contexts_across_page_table_windows(page):
+    """One split per request over contexts that span the kernel's 128-page
+    windows of the page table: a window starting at the last stage of full
+    pages (fetched during the loop over full pages, made current by the stages
+    after it) or right after them, and two window crossings.  NHD pools (two
+    heads per workgroup) and HND pools (one head) agree bit for bit, and both
+    match the oracle."""
+    flush(f"[attn windows page {page}]")
+    w = 64 * (page // 16)                 # stages (two 16-token slabs each) per window
+    ctx = [16 * (2 * w + 2) + 5,          # full-page stages end one past the first window start
+           16 * (2 * w) + 2,              # they end right before it
+           16 * (4 * w + 2) + 9]          # two window crossings
+    case = make_attn_case(970 + page, ctx, 16, 32, 8, 128, "bf16", page=page)
+    want = oracle_attn(case)
+    on, _, _ = run_attn(case, split=10 ** 6, layout="NHD")
+    oh, _, _ = run_attn(case, split=10 ** 6, layout="HND")
+    assert torch.equal(on.view(torch.int16), oh.view(torch.int16)), page
+    assert_close(to_host64(on), want, "bf16", f"windows page {page}")
+
+
 def test_kv_pool_untouched_and_output_bounded():
     case = make_attn_case(13, [400, 3], 16, 32, 8, 128, "bf16")
     dt = case["dtype"]
