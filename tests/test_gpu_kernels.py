@@ -406,17 +406,21 @@ def test_layer_graph_replays_match_eager():
         torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("C,ctx", [(4, ("uniform", 100, 3000)), (1, ("fixed", 8192))], ids=["c4-ragged-splits", "c1-32-splits"])
-def test_layer_equals_its_entry_points_bitwise(C, ctx):
+@pytest.mark.parametrize("C,ctx,split", [(4, ("uniform", 100, 3000), True), (1, ("fixed", 8192), True),
+                                         (64, ("fixed", 2048), False), (96, ("uniform", 2048, 3000), False)],
+                         ids=["c4-ragged-splits", "c1-32-splits", "c64-one-split", "c96-ragged-one-split"])
+def test_layer_equals_its_entry_points_bitwise(C, ctx, split):
     """With several splits per request the layer runs the scan and the
-    attention's merge in one launch; its outputs must be the bits of the
-    separate entry points (a1, a2, a3 + a4) on the same inputs."""
+    attention's merge in one launch; with one split per request (two kv heads
+    per attention workgroup) there is no merge.  Either way its outputs must be
+    the bits of the separate entry points (a1, a2, a3 + a4) on the same inputs."""
     from helpers import layer_from_inputs
     from hybrid_mamba_attention_amd import ops
+    flush(f"[layer vs entry points C={C} ctx={ctx}]")
     w = replace_workload(wl.sweep_workload(C), ctx=ctx, seed=4646 + C)
     inp = wl.make_inputs(w)
     layer = layer_from_inputs(inp)
-    assert int(layer.plan()[0]) > C, "the case must split requests"
+    assert (int(layer.plan()[0]) > C) == split, "the case must (not) split requests"
     a, dt = inp.arrays, w.dtype
     h0 = ops.init_state(to_dev(a["u"], dt), to_dev(a["w_init"], dt))
     y, hf = ops.ssd_scan(to_dev(a["x"], dt), to_dev(a["delta"], dt), to_dev(a["A"], dt), to_dev(a["B"], dt),
