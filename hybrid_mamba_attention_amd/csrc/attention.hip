@@ -708,9 +708,10 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
 // Stages of K/V loads in flight per workgroup.  With nontemporal loads two
 // stages keep pace with four at 64 query rows (C = 128: 707 vs 729 us) and
 // leave the 128-row tiles at two waves per SIMD instead of one (workload 4:
-// 660 vs 771 us).  (Those figures predate the hot loop below.  With it,
-// depth 4 compiles for the bf16 64-row form, 235 registers, and measured 2-7%
-// slower at every C; the fp32 128-row form does not compile at depth 4.)
+// 660 vs 771 us).  (Those figures predate the hot loop below.  With it and
+// its loads issued in slot order, depth 4 compiles for the bf16 64-row and
+// head-pair forms, 235-237 registers, and is no faster at any C (C = 128:
+// 656 vs 650 us); the 128-row forms spill hundreds of registers at depth 4.)
 constexpr int kPrefetch = HSPEC_ATTN_PREFETCH;
 
 // (RT row tiles per wave, NW waves) for a query-row count: every wave reads the
