@@ -702,9 +702,6 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
 // ---------------------------------------------------------------------------
 // host launcher
 // ---------------------------------------------------------------------------
-#ifndef HSPEC_ATTN_PREFETCH
-#define HSPEC_ATTN_PREFETCH 2
-#endif
 // Stages of K/V loads in flight per workgroup.  With nontemporal loads two
 // stages keep pace with four at 64 query rows (C = 128: 707 vs 729 us) and
 // leave the 128-row tiles at two waves per SIMD instead of one (workload 4:
@@ -712,7 +709,7 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
 // its loads issued in slot order, depth 4 compiles for the bf16 64-row and
 // head-pair forms, 235-237 registers, and is no faster at any C (C = 128:
 // 656 vs 650 us); the 128-row forms spill hundreds of registers at depth 4.)
-constexpr int kPrefetch = HSPEC_ATTN_PREFETCH;
+constexpr int kPrefetch = 2;
 
 // (RT row tiles per wave, NW waves) for a query-row count: every wave reads the
 // whole stage from LDS, so fewer, wider waves cut LDS traffic per HBM byte.
@@ -725,13 +722,6 @@ static hipError_t launch_attn_cfg(hipStream_t st, const AttnArgs& a) {
   return hipGetLastError();
 }
 
-#ifndef HSPEC_ATTN_RT64
-#define HSPEC_ATTN_RT64 1  // row tiles per wave for 33..64 query rows (waves = 4 / this)
-#endif
-
-#ifndef HSPEC_ATTN_HEAD_PAIR
-#define HSPEC_ATTN_HEAD_PAIR 1
-#endif
 template <typename T, int D>
 static hipError_t launch_attn_d(hipStream_t st, const AttnArgs& a) {
   if (a.rows <= 16) return launch_attn_cfg<T, D, 1, 1>(st, a);
@@ -743,10 +733,10 @@ static hipError_t launch_attn_d(hipStream_t st, const AttnArgs& a) {
   // against 6.6 TB/s (C = 128: 687 -> 651 us).  With short splits (small C)
   // halving the workgroup count costs more than the pieces gain.
   if constexpr (std::is_same<T, bf16_t>::value && D == 128) {
-    if (HSPEC_ATTN_HEAD_PAIR && a.rows <= 64 && a.Hkv % 2 == 0 && a.head_stride == D && a.pps >= 128)
+    if (a.rows <= 64 && a.Hkv % 2 == 0 && a.head_stride == D && a.pps >= 128)
       return launch_attn_cfg<T, D, 1, 8, 2>(st, a);
   }
-  if (a.rows <= 64) return launch_attn_cfg<T, D, HSPEC_ATTN_RT64, 4 / HSPEC_ATTN_RT64>(st, a);
+  if (a.rows <= 64) return launch_attn_cfg<T, D, 1, 4>(st, a);
   if (a.rows <= 128) return launch_attn_cfg<T, D, 2, 4>(st, a);
   return launch_attn_cfg<T, D, 4, 4>(st, a);
 }

@@ -31,10 +31,6 @@
 #include "common.h"
 #include "kernels.h"
 
-#ifndef HSPEC_GEMM_PF
-#define HSPEC_GEMM_PF 2
-#endif
-
 namespace hspec {
 
 // Paged destination of output row m (-1: the position has no page, so the
@@ -46,8 +42,10 @@ __device__ __forceinline__ int64_t scatter_row(const KvScatter& s, int m) {
   if (page < 0 || page >= s.num_pages) return -1;
   return int64_t(page) * s.ps + int64_t(p & ((1 << s.lpt) - 1)) * s.ts;
 }
+// n: column of this launch (the projection column is s.col0 + n)
 template <typename OutT>
 __device__ __forceinline__ OutT* scatter_col(const KvScatter& s, int n) {
+  n += s.col0;
   const bool v = n >= s.HD;
   const int nn = v ? n - s.HD : n;
   return static_cast<OutT*>(v ? s.v_cache : s.k_cache) + int64_t(nn / s.D) * s.hs + nn % s.D;
@@ -345,10 +343,9 @@ __global__ __launch_bounds__(256) void k_splitk_sum(GemmArgs g) {
 // host side
 // ---------------------------------------------------------------------------
 
-#ifndef HSPEC_GEMM_FORCE_CFG
-#define HSPEC_GEMM_FORCE_CFG -1
-#endif
-constexpr int kGemmPf = HSPEC_GEMM_PF;
+// Stages of loads in flight per thread.  Four (checked in the ISA: the
+// steady loop then waits at vmcnt(24)) measured no faster than two.
+constexpr int kGemmPf = 2;
 
 // bf16 tile shapes (WM, WN): cfg 0 = 64 x 128, 1 = 128 x 128, 3 = 64 x 64,
 // 4 = 128 x 256, 5 = 256 x 128; cfg 2 is the fp32 kernel.
@@ -364,7 +361,6 @@ static GemmPart gemm_part(int dtype, int M, int n0, int n, int K) {
   p.n = n;
   if (dtype == 1) {
     p.cfg = M <= 64 ? 0 : 1;                 // 64 x 128 or 128 x 128 tiles
-    if (HSPEC_GEMM_FORCE_CFG >= 0) p.cfg = HSPEC_GEMM_FORCE_CFG;
     cfg_tile(p.cfg, p.bm, p.bn);
   } else {
     p.cfg = 2;
@@ -410,6 +406,7 @@ template <typename OutT>
 static hipError_t launch_gemm_part(hipStream_t st, GemmArgs g, const GemmPart& p) {
   g.b = static_cast<const char*>(g.b) + size_t(p.n0) * g.ldb * (p.cfg == 2 ? 4 : 2);
   g.c = static_cast<OutT*>(g.c) + p.n0;
+  g.sc.col0 = p.n0;   // scatter targets are looked up by projection column
   g.N = p.n;
   g.tiles_m = p.tiles_m;
   g.splits = p.splits;

@@ -75,7 +75,10 @@ hipError_t launch_init_state(hipStream_t st, int dtype, const InitArgs& a);
 
 // Paged destination of a KV-injection GEMM: output row m = b * n_new + i is
 // token position start[b] + i of request b; columns [0, HD) are its K row,
-// [HD, 2*HD) its V row (head h at h*D .. h*D + D - 1).
+// [HD, 2*HD) its V row (head h at h*D .. h*D + D - 1).  A launch over the
+// columns [col0, col0 + n) of the projection (a ragged tail launched on its
+// own) numbers its columns from 0, so `col0` is added back before the
+// column's pool and offset are looked up.
 struct KvScatter {
   const int32_t* page_table;  // [C, max_pages]
   const int32_t* start;       // [C]
@@ -84,6 +87,7 @@ struct KvScatter {
   int64_t ps, ts, hs;         // page, token, head strides in elements
   int n_new, max_pages, num_pages, HD, D;
   int lpt;                    // log2(tokens per page)
+  int col0;                   // first projection column of this launch
 };
 
 // C[M, N] = A[M, K] . B[N, K]^T (row strides in elements); K % 8 == 0.

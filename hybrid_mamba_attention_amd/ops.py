@@ -167,15 +167,67 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _addr(t):
+    """Device address of a tensor already checked by _checked (None stays None)."""
+    return None if t is None else t.data_ptr()
+
+
+def _checked(specs, act=None):
+    """Check tensors before any of their addresses reaches the library.
+
+    specs: (name, tensor, kind, shape, optional) with kind "act" (the
+    activation type `act`), "f32", "i32" or "pool" (activation type, strides
+    allowed); shape None skips the shape check.  Type, shape and layout are
+    checked first, then that every tensor lives on the GPU -- all on one
+    device -- so a host tensor or a wrong element type raises here instead of
+    handing the kernels a pointer they would misread.  Returns the device."""
+    want = {"f32": torch.float32, "i32": torch.int32}
+    if act is not None and act not in (torch.float32, torch.bfloat16):
+        raise TypeError(f"activation tensors must be float32 or bfloat16, got {act}")
+    for name, t, kind, shape, optional in specs:
+        if t is None:
+            if optional:
+                continue
+            raise ValueError(f"{name} is required")
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch tensor")
+        dt = act if kind in ("act", "pool") else want[kind]
+        if t.dtype != dt:
+            raise TypeError(f"{name} must be {dt}, got {t.dtype}")
+        if shape is not None and tuple(t.shape) != tuple(int(x) for x in shape):
+            raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+        if kind != "pool" and not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    dev = None
+    for name, t, *_ in specs:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"{name} must live on the GPU, not {t.device}")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"{name} lives on {t.device}, the other tensors on {dev}")
+    return dev
+
+
+def _pool_geometry(k_cache, v_cache, layout):
+    """(Hkv, D, (page, token, head) strides) of a K/V pool pair, which must
+    agree in shape and strides."""
+    if k_cache.dim() != 4:
+        raise ValueError("KV pools are 4-D: [pages, P, Hkv, D] (NHD) or [pages, Hkv, P, D] (HND)")
+    if tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("K and V pools must have the same shape")
+    ps = kv_strides(k_cache, layout)
+    if kv_strides(v_cache, layout) != ps:
+        raise ValueError("K and V pools must share strides")
+    Hkv = k_cache.shape[2] if layout == "NHD" else k_cache.shape[1]
+    return int(Hkv), int(k_cache.shape[3]), ps
+
+
 def _stream(stream) -> ctypes.c_void_p:
     s = torch.cuda.current_stream() if stream is None else stream
     return ctypes.c_void_p(s.cuda_stream)
-
-
-def _contig(*ts):
-    for t in ts:
-        if t is not None and not t.is_contiguous():
-            raise ValueError("tensor must be contiguous")
 
 
 # ---------------------------------------------------------------------------
@@ -185,13 +237,16 @@ def _contig(*ts):
 def init_state(u: torch.Tensor, w_init: torch.Tensor, h0: torch.Tensor | None = None,
                stream=None) -> torch.Tensor:
     """h0[C, S] (fp32) = u[C, d] . w_init[d, S]."""
-    _contig(u, w_init, h0)
+    if u.dim() != 2 or w_init.dim() != 2:
+        raise ValueError("u is [C, d_model], w_init [d_model, S]")
     C, d = u.shape
     S = w_init.shape[1]
+    dev = _checked([("u", u, "act", None, False), ("w_init", w_init, "act", (d, S), False),
+                    ("h0", h0, "f32", (C, S), True)], u.dtype)
     if h0 is None:
-        h0 = torch.empty((C, S), dtype=torch.float32, device=u.device)
+        h0 = torch.empty((C, S), dtype=torch.float32, device=dev)
     _check("hspec_init_state", lib().hspec_init_state(
-        _stream(stream), _dtype_code(u), C, d, S, _ptr(u), _ptr(w_init), _ptr(h0)))
+        _stream(stream), _dtype_code(u), C, d, S, _addr(u), _addr(w_init), _addr(h0)))
     return h0
 
 
@@ -202,17 +257,26 @@ def init_state(u: torch.Tensor, w_init: torch.Tensor, h0: torch.Tensor | None = 
 def ssd_scan(x, delta, A, B, Cm, *, chunk: int, h0=None, Dskip=None, y=None, h_final=None,
              want_final: bool = False, stream=None):
     """y[C,K,H,P] (fp32) and optionally h_final[C,H,P,N] of the chunked SSD scan."""
-    _contig(x, delta, A, B, Cm, h0, Dskip, y, h_final)
+    if x.dim() != 4 or B.dim() != 4:
+        raise ValueError("x is [C, K, H, P], B [C, K, ng, N]")
     C, K, H, P = x.shape
     ng, N = B.shape[2], B.shape[3]
+    # the state may also come flat, as the projection writes it: [C, H*P*N]
+    if h0 is not None and tuple(h0.shape) == (C, H * P * N):
+        h0 = h0.view(C, H, P, N)
+    dev = _checked([("x", x, "act", None, False), ("delta", delta, "f32", (C, K, H), False),
+                    ("A", A, "f32", (H,), False), ("B", B, "act", None, False),
+                    ("Cm", Cm, "act", (C, K, ng, N), False), ("h0", h0, "f32", (C, H, P, N), True),
+                    ("Dskip", Dskip, "f32", (H,), True), ("y", y, "f32", (C, K, H, P), True),
+                    ("h_final", h_final, "f32", (C, H, P, N), True)], x.dtype)
     if y is None:
-        y = torch.empty((C, K, H, P), dtype=torch.float32, device=x.device)
+        y = torch.empty((C, K, H, P), dtype=torch.float32, device=dev)
     if h_final is None and want_final:
-        h_final = torch.empty((C, H, P, N), dtype=torch.float32, device=x.device)
+        h_final = torch.empty((C, H, P, N), dtype=torch.float32, device=dev)
     _check("hspec_ssd_scan", lib().hspec_ssd_scan(
         _stream(stream), _dtype_code(x), C, K, H, P, ng, N, chunk,
-        _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(Cm), _ptr(Dskip), _ptr(h0), _ptr(y),
-        _ptr(h_final)))
+        _addr(x), _addr(delta), _addr(A), _addr(B), _addr(Cm), _addr(Dskip), _addr(h0), _addr(y),
+        _addr(h_final)))
     return y, h_final
 
 
@@ -241,25 +305,32 @@ def kv_strides(k_cache: torch.Tensor, layout: str = "NHD"):
 
 def _attn_call(L, stream, q, k_blk, v_blk, k_cache, v_cache, page_table, ctx_lens, max_ctx,
                kv_split_pages, scale, block_causal, out, ws, ws_bytes, layout):
+    """out None: a size query (the library then only reads the sizes)."""
+    if q.dim() != 4 or k_blk.dim() != 4 or page_table.dim() != 2:
+        raise ValueError("q and k_blk are 4-D, page_table [C, max_pages]")
     C, K, Hq, D = q.shape
     Hkv = k_blk.shape[2]
-    ps, ts, hs = kv_strides(k_cache, layout)
-    if kv_strides(v_cache, layout) != (ps, ts, hs):
-        raise ValueError("K and V pools must share strides")
+    pool_hkv, pool_d, (ps, ts, hs) = _pool_geometry(k_cache, v_cache, layout)
+    if (pool_hkv, pool_d) != (Hkv, D):
+        raise ValueError(f"KV pools hold {pool_hkv} heads of {pool_d}, the block {Hkv} of {D}")
+    _checked([("q", q, "act", None, False), ("k_blk", k_blk, "act", (C, K, Hkv, D), False),
+              ("v_blk", v_blk, "act", (C, K, Hkv, D), False), ("k_cache", k_cache, "pool", None, False),
+              ("v_cache", v_cache, "pool", None, False),
+              ("page_table", page_table, "i32", (C, page_table.shape[1]), False),
+              ("ctx_lens", ctx_lens, "i32", (C,), False), ("out", out, "act", (C, K, Hq, D), True)], q.dtype)
     return L.hspec_block_attn_inplace(
-        stream, _dtype_code(q), C, K, Hq, Hkv, D, _ptr(q), _ptr(k_blk), _ptr(v_blk),
-        _ptr(k_cache), _ptr(v_cache), ps, ts, hs, k_cache.shape[0], page_size_of(k_cache, layout),
-        _ptr(page_table), page_table.shape[1], _ptr(ctx_lens), int(max_ctx), int(kv_split_pages), float(scale),
-        int(bool(block_causal)), _ptr(out), ws, ctypes.byref(ws_bytes))
+        _stream(stream), _dtype_code(q), C, K, Hq, Hkv, D, _addr(q), _addr(k_blk), _addr(v_blk),
+        _addr(k_cache), _addr(v_cache), ps, ts, hs, k_cache.shape[0], page_size_of(k_cache, layout),
+        _addr(page_table), page_table.shape[1], _addr(ctx_lens), int(max_ctx), int(kv_split_pages), float(scale),
+        int(bool(block_causal)), _addr(out if out is not None else q), ws, ctypes.byref(ws_bytes))
 
 
 def attn_workspace_bytes(q, k_blk, v_blk, k_cache, v_cache, page_table, ctx_lens, *, max_ctx,
                          kv_split_pages=0, scale=0.0, block_causal=False, layout="NHD") -> int:
     n = _sz(0)
-    out = torch.empty(1, dtype=q.dtype, device=q.device)  # never written by a size query
     _check("hspec_block_attn_inplace", _attn_call(
-        lib(), _stream(None), q, k_blk, v_blk, k_cache, v_cache, page_table, ctx_lens, max_ctx,
-        kv_split_pages, scale, block_causal, out, None, n, layout))
+        lib(), None, q, k_blk, v_blk, k_cache, v_cache, page_table, ctx_lens, max_ctx,
+        kv_split_pages, scale, block_causal, None, None, n, layout))
     return n.value
 
 
@@ -271,9 +342,6 @@ def block_attn_inplace(q, k_blk, v_blk, k_cache, v_cache, page_table, ctx_lens, 
     block_causal: block query t sees block keys s <= t only (context keys all).
     workspace: a uint8 CUDA tensor of at least attn_workspace_bytes(...) bytes
     (allocated here if None).  Returns (out, workspace)."""
-    _contig(q, k_blk, v_blk, page_table, ctx_lens, out)
-    if page_table.dtype != torch.int32 or ctx_lens.dtype != torch.int32:
-        raise TypeError("page_table and ctx_lens must be int32")
     L = lib()
     if out is None:
         out = torch.empty_like(q)
@@ -284,7 +352,7 @@ def block_attn_inplace(q, k_blk, v_blk, k_cache, v_cache, page_table, ctx_lens, 
         workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q.device)
     n = _sz(workspace.numel())
     _check("hspec_block_attn_inplace", _attn_call(
-        L, _stream(stream), q, k_blk, v_blk, k_cache, v_cache, page_table, ctx_lens, max_ctx,
+        L, stream, q, k_blk, v_blk, k_cache, v_cache, page_table, ctx_lens, max_ctx,
         kv_split_pages, scale, block_causal, out, _ptr(workspace), n, layout))
     return out, workspace
 
@@ -303,44 +371,59 @@ class DraftLayer:
     def __init__(self, *, u, w_init, x, delta, A, B, Cm, chunk, q, k_blk, v_blk, k_cache, v_cache,
                  page_table, ctx_lens, max_ctx, kv_split_pages=0, scale=0.0, block_causal=False,
                  Dskip=None, want_final=False, layout="NHD"):
-        _contig(u, w_init, x, delta, A, B, Cm, q, k_blk, v_blk, page_table, ctx_lens, Dskip)
         if (u is None) != (w_init is None):
             raise ValueError("u and w_init are given together (or both None for the ablation)")
-        dev = x.device
+        if x.dim() != 4 or B.dim() != 4 or q.dim() != 4 or k_blk.dim() != 4:
+            raise ValueError("x, B, q and k_blk are 4-D")
         C, K, H, P = x.shape
-        d = u.shape[1] if u is not None else 0
         ng, N = B.shape[2], B.shape[3]
-        _, _, Hq, D = q.shape
+        Hq, D = q.shape[2], q.shape[3]
         Hkv = k_blk.shape[2]
+        d = u.shape[-1] if u is not None else 0
+        act = x.dtype
+        pool_hkv, pool_d, (ps, ts, hs) = _pool_geometry(k_cache, v_cache, layout)
+        if (pool_hkv, pool_d) != (Hkv, D):
+            raise ValueError(f"KV pools hold {pool_hkv} heads of {pool_d}, the block {Hkv} of {D}")
+        if page_table.dim() != 2:
+            raise ValueError("page_table is [C, max_pages]")
+        dev = _checked([
+            ("u", u, "act", (C, d), True), ("w_init", w_init, "act", (d, H * P * N), True),
+            ("x", x, "act", None, False), ("delta", delta, "f32", (C, K, H), False),
+            ("A", A, "f32", (H,), False), ("B", B, "act", (C, K, ng, N), False),
+            ("Cm", Cm, "act", (C, K, ng, N), False), ("Dskip", Dskip, "f32", (H,), True),
+            ("q", q, "act", (C, K, Hq, D), False), ("k_blk", k_blk, "act", (C, K, Hkv, D), False),
+            ("v_blk", v_blk, "act", (C, K, Hkv, D), False),
+            ("k_cache", k_cache, "pool", None, False), ("v_cache", v_cache, "pool", None, False),
+            ("page_table", page_table, "i32", (C, page_table.shape[1]), False),
+            ("ctx_lens", ctx_lens, "i32", (C,), False),
+        ], act)
         self.h0 = (torch.empty((C, H * P * N), dtype=torch.float32, device=dev)
                    if u is not None else None)
         self.y = torch.empty((C, K, H, P), dtype=torch.float32, device=dev)
         self.h_final = (torch.empty((C, H, P, N), dtype=torch.float32, device=dev)
                         if want_final else None)
         self.out = torch.empty_like(q)
-        ps, ts, hs = kv_strides(k_cache, layout)
         a = LayerArgs()
         a.dtype = _dtype_code(x)
         a.C, a.K = C, K
         a.d_model, a.H, a.P, a.ng, a.N, a.chunk = d, H, P, ng, N, chunk
-        if u is not None:
-            a.u, a.w_init, a.h0 = u.data_ptr(), w_init.data_ptr(), self.h0.data_ptr()
-        a.x, a.delta, a.A = x.data_ptr(), delta.data_ptr(), A.data_ptr()
-        a.B, a.Cm = B.data_ptr(), Cm.data_ptr()
-        a.Dskip = Dskip.data_ptr() if Dskip is not None else None
-        a.y = self.y.data_ptr()
-        a.h_final = self.h_final.data_ptr() if self.h_final is not None else None
+        a.u, a.w_init, a.h0 = _addr(u), _addr(w_init), _addr(self.h0)
+        a.x, a.delta, a.A = _addr(x), _addr(delta), _addr(A)
+        a.B, a.Cm = _addr(B), _addr(Cm)
+        a.Dskip = _addr(Dskip)
+        a.y = _addr(self.y)
+        a.h_final = _addr(self.h_final)
         a.Hq, a.Hkv, a.D = Hq, Hkv, D
-        a.q, a.k_blk, a.v_blk = q.data_ptr(), k_blk.data_ptr(), v_blk.data_ptr()
-        a.k_cache, a.v_cache = k_cache.data_ptr(), v_cache.data_ptr()
+        a.q, a.k_blk, a.v_blk = _addr(q), _addr(k_blk), _addr(v_blk)
+        a.k_cache, a.v_cache = _addr(k_cache), _addr(v_cache)
         a.page_stride, a.token_stride, a.head_stride = ps, ts, hs
         a.num_pages = k_cache.shape[0]
         a.page_size = page_size_of(k_cache, layout)
-        a.page_table, a.max_pages = page_table.data_ptr(), page_table.shape[1]
-        a.ctx_lens, a.max_ctx = ctx_lens.data_ptr(), int(max_ctx)
+        a.page_table, a.max_pages = _addr(page_table), page_table.shape[1]
+        a.ctx_lens, a.max_ctx = _addr(ctx_lens), int(max_ctx)
         a.kv_split_pages, a.scale = int(kv_split_pages), float(scale)
         a.block_causal = int(bool(block_causal))
-        a.out = self.out.data_ptr()
+        a.out = _addr(self.out)
         a.workspace, a.workspace_bytes = None, 0
         need = _sz(0)
         _check("hspec_draft_layer", lib().hspec_draft_layer(None, ctypes.byref(a), ctypes.byref(need)))
@@ -399,22 +482,31 @@ class MambaBlock:
 
     def __init__(self, *, hidden, w_in, conv_w, dt_bias, A, norm_w, w_out, H, P, N, chunk, ng=1,
                  conv_b=None, Dskip=None, h0=None, eps=1e-5, want_final=False):
-        _contig(hidden, w_in, conv_w, conv_b, dt_bias, A, Dskip, h0, norm_w, w_out)
-        dev = hidden.device
+        if hidden.dim() != 3:
+            raise ValueError("hidden is [C, K, d_model]")
         C, K, d = hidden.shape
+        d_inner = H * P
+        conv_dim = d_inner + 2 * ng * N
+        d_proj = 2 * d_inner + 2 * ng * N + H
+        dev = _checked([
+            ("hidden", hidden, "act", None, False), ("w_in", w_in, "act", (d_proj, d), False),
+            ("conv_w", conv_w, "f32", (conv_dim, 4), False), ("conv_b", conv_b, "f32", (conv_dim,), True),
+            ("dt_bias", dt_bias, "f32", (H,), False), ("A", A, "f32", (H,), False),
+            ("Dskip", Dskip, "f32", (H,), True), ("h0", h0, "f32", (C, H, P, N), True),
+            ("norm_w", norm_w, "f32", (d_inner,), False), ("w_out", w_out, "act", (d, d_inner), False),
+        ], hidden.dtype)
         self.out = torch.empty_like(hidden)
         self.h_final = (torch.empty((C, H, P, N), dtype=torch.float32, device=dev)
                         if want_final else None)
         a = MambaArgs()
         a.dtype = _dtype_code(hidden)
         a.C, a.K, a.d_model, a.H, a.P, a.ng, a.N, a.chunk = C, K, d, H, P, ng, N, chunk
-        ptr = lambda t: t.data_ptr() if t is not None else None
-        a.hidden, a.w_in = ptr(hidden), ptr(w_in)
-        a.conv_w, a.conv_b, a.dt_bias = ptr(conv_w), ptr(conv_b), ptr(dt_bias)
-        a.A, a.Dskip, a.h0 = ptr(A), ptr(Dskip), ptr(h0)
-        a.norm_w, a.norm_eps = ptr(norm_w), float(eps)
-        a.w_out = ptr(w_out)
-        a.out, a.h_final = ptr(self.out), ptr(self.h_final)
+        a.hidden, a.w_in = _addr(hidden), _addr(w_in)
+        a.conv_w, a.conv_b, a.dt_bias = _addr(conv_w), _addr(conv_b), _addr(dt_bias)
+        a.A, a.Dskip, a.h0 = _addr(A), _addr(Dskip), _addr(h0)
+        a.norm_w, a.norm_eps = _addr(norm_w), float(eps)
+        a.w_out = _addr(w_out)
+        a.out, a.h_final = _addr(self.out), _addr(self.h_final)
         a.workspace, a.workspace_bytes = None, 0
         need = _sz(0)
         _check("hspec_mamba_block", lib().hspec_mamba_block(None, ctypes.byref(a), ctypes.byref(need)))
@@ -452,33 +544,66 @@ class DraftStack:
 
     def __init__(self, *, hidden_in, u, layers, page_table, ctx_lens, max_ctx, H, P, N, chunk, Hq, Hkv, D,
                  ng=1, eps=1e-5, kv_split_pages=0, scale=0.0, layout="NHD"):
-        _contig(hidden_in, u, page_table, ctx_lens)
-        dev = hidden_in.device
+        if hidden_in.dim() != 3 or page_table.dim() != 2 or not layers:
+            raise ValueError("hidden_in is [C, K, d_model], page_table [C, max_pages], layers non-empty")
         C, K, d = hidden_in.shape
-        self.hidden_out = torch.empty((C, K, d), dtype=torch.float32, device=dev)
-        arr = (StackLayer * len(layers))()
+        act = hidden_in.dtype
+        d_inner = H * P
+        conv_dim = d_inner + 2 * ng * N
+        d_proj = 2 * d_inner + 2 * ng * N + H
+        specs = [("hidden_in", hidden_in, "act", None, False), ("u", u, "act", (C, d), False),
+                 ("page_table", page_table, "i32", (C, page_table.shape[1]), False),
+                 ("ctx_lens", ctx_lens, "i32", (C,), False)]
+        # every attention half shares the one set of pool strides and the
+        # page table, so all layers' pools must agree in shape and strides
         pools = None
         for l, Ld in enumerate(layers):
-            ptr = lambda k: Ld[k].data_ptr() if Ld.get(k) is not None else None
-            arr[l].pre_norm_w = ptr("pre_norm_w")
+            unknown = set(Ld) - {"pre_norm_w", *_MAMBA_KEYS, *_ATTN_KEYS}
+            if unknown:
+                raise ValueError(f"layer {l}: unknown keys {sorted(unknown)}")
+            specs.append((f"layers[{l}].pre_norm_w", Ld.get("pre_norm_w"), "f32", (d,), False))
+            if Ld.get("w_in") is not None:
+                mshape = dict(w_init=("act", (d, H * P * N), False), w_in=("act", (d_proj, d), False),
+                              conv_w=("f32", (conv_dim, 4), False), conv_b=("f32", (conv_dim,), True),
+                              dt_bias=("f32", (H,), False), A=("f32", (H,), False),
+                              Dskip=("f32", (H,), True), norm_w=("f32", (d_inner,), False),
+                              w_out=("act", (d, d_inner), False))
+                specs += [(f"layers[{l}].{k}", Ld.get(k), kind, shp, opt) for k, (kind, shp, opt) in mshape.items()]
+            if Ld.get("wq") is not None:
+                ashape = dict(wq=(Hq * D, d), wk=(Hkv * D, d), wv=(Hkv * D, d), wo=(d, Hq * D))
+                specs += [(f"layers[{l}].{k}", Ld.get(k), "act", shp, False) for k, shp in ashape.items()]
+                kc, vc = Ld.get("k_cache"), Ld.get("v_cache")
+                if kc is None or vc is None:
+                    raise ValueError(f"layer {l}: an attention half needs k_cache and v_cache")
+                geo = _pool_geometry(kc, vc, layout)
+                if geo[:2] != (Hkv, D):
+                    raise ValueError(f"layer {l}: KV pools hold {geo[0]} heads of {geo[1]}, not {Hkv} of {D}")
+                if pools is not None and (geo[2] != pools[0] or kc.shape != pools[1]):
+                    raise ValueError(f"layer {l}: KV pools differ in shape or strides from an earlier layer's")
+                pools = (geo[2], kc.shape, kc)
+                specs += [(f"layers[{l}].k_cache", kc, "pool", None, False),
+                          (f"layers[{l}].v_cache", vc, "pool", None, False)]
+        dev = _checked(specs, act)
+        self.hidden_out = torch.empty((C, K, d), dtype=torch.float32, device=dev)
+        arr = (StackLayer * len(layers))()
+        for l, Ld in enumerate(layers):
+            arr[l].pre_norm_w = _addr(Ld.get("pre_norm_w"))
             for k in _MAMBA_KEYS + _ATTN_KEYS:
-                setattr(arr[l], k, ptr(k))
-            if Ld.get("k_cache") is not None:
-                pools = Ld["k_cache"]
+                setattr(arr[l], k, _addr(Ld.get(k)))
         a = StackArgs()
         a.dtype = _dtype_code(hidden_in)
         a.C, a.K, a.d_model, a.n_layers = C, K, d, len(layers)
         a.H, a.P, a.ng, a.N, a.chunk, a.eps = H, P, ng, N, chunk, float(eps)
         a.Hq, a.Hkv, a.D = Hq, Hkv, D
         if pools is not None:
-            a.page_stride, a.token_stride, a.head_stride = kv_strides(pools, layout)
-            a.num_pages, a.page_size = pools.shape[0], page_size_of(pools, layout)
+            a.page_stride, a.token_stride, a.head_stride = pools[0]
+            a.num_pages, a.page_size = pools[2].shape[0], page_size_of(pools[2], layout)
         else:
             a.page_stride, a.token_stride, a.head_stride, a.num_pages, a.page_size = 8, 8, 8, 1, 16
-        a.page_table, a.max_pages = page_table.data_ptr(), page_table.shape[1]
-        a.ctx_lens, a.max_ctx = ctx_lens.data_ptr(), int(max_ctx)
+        a.page_table, a.max_pages = _addr(page_table), page_table.shape[1]
+        a.ctx_lens, a.max_ctx = _addr(ctx_lens), int(max_ctx)
         a.kv_split_pages, a.scale = int(kv_split_pages), float(scale)
-        a.hidden_in, a.u, a.hidden_out = hidden_in.data_ptr(), u.data_ptr(), self.hidden_out.data_ptr()
+        a.hidden_in, a.u, a.hidden_out = _addr(hidden_in), _addr(u), _addr(self.hidden_out)
         a.layers = arr
         need = _sz(0)
         _check("hspec_draft_stack", lib().hspec_draft_stack(None, ctypes.byref(a), ctypes.byref(need)))
@@ -517,33 +642,31 @@ class DraftStack:
 # ---------------------------------------------------------------------------
 
 def _inject_call(stream, hidden, w_kv, k_cache, v_cache, page_table, start_pos, ws, n, layout):
+    if hidden.dim() != 3 or page_table.dim() != 2:
+        raise ValueError("hidden is [C, n_new, d_model], page_table [C, max_pages]")
     C, n_new, d = hidden.shape
-    Hkv, D = (k_cache.shape[2], k_cache.shape[3]) if layout == "NHD" else (k_cache.shape[1], k_cache.shape[3])
-    if w_kv.shape != (2 * Hkv * D, d):
-        raise ValueError("w_kv must be [2*Hkv*D, d_model]")
-    ps, ts, hs = kv_strides(k_cache, layout)
-    if kv_strides(v_cache, layout) != (ps, ts, hs):
-        raise ValueError("K and V pools must share strides")
+    Hkv, D, (ps, ts, hs) = _pool_geometry(k_cache, v_cache, layout)
+    _checked([("hidden", hidden, "act", None, False), ("w_kv", w_kv, "act", (2 * Hkv * D, d), False),
+              ("k_cache", k_cache, "pool", None, False), ("v_cache", v_cache, "pool", None, False),
+              ("page_table", page_table, "i32", (C, page_table.shape[1]), False),
+              ("start_pos", start_pos, "i32", (C,), False)], hidden.dtype)
     return lib().hspec_kv_inject(
-        stream, _dtype_code(hidden), C, n_new, d, Hkv, D, _ptr(hidden), _ptr(w_kv), _ptr(k_cache),
-        _ptr(v_cache), ps, ts, hs, k_cache.shape[0], page_size_of(k_cache, layout), _ptr(page_table),
-        page_table.shape[1], _ptr(start_pos), ws, ctypes.byref(n))
+        _stream(stream), _dtype_code(hidden), C, n_new, d, Hkv, D, _addr(hidden), _addr(w_kv), _addr(k_cache),
+        _addr(v_cache), ps, ts, hs, k_cache.shape[0], page_size_of(k_cache, layout), _addr(page_table),
+        page_table.shape[1], _addr(start_pos), ws, ctypes.byref(n))
 
 
 def kv_inject(hidden, w_kv, k_cache, v_cache, page_table, start_pos, *, workspace=None, layout="NHD",
               stream=None):
     """Write w_kv . hidden[b, i] as K | V rows of positions start_pos[b] + i into
     the paged pools (in place).  Returns the workspace."""
-    _contig(hidden, w_kv, page_table, start_pos)
-    if page_table.dtype != torch.int32 or start_pos.dtype != torch.int32:
-        raise TypeError("page_table and start_pos must be int32")
     if workspace is None:
         n = _sz(0)
-        _check("hspec_kv_inject", _inject_call(_stream(stream), hidden, w_kv, k_cache, v_cache, page_table,
+        _check("hspec_kv_inject", _inject_call(stream, hidden, w_kv, k_cache, v_cache, page_table,
                                                start_pos, None, n, layout))
         workspace = torch.empty(max(n.value, 256), dtype=torch.uint8, device=hidden.device)
     n = _sz(workspace.numel())
-    _check("hspec_kv_inject", _inject_call(_stream(stream), hidden, w_kv, k_cache, v_cache, page_table,
+    _check("hspec_kv_inject", _inject_call(stream, hidden, w_kv, k_cache, v_cache, page_table,
                                            start_pos, _ptr(workspace), n, layout))
     return workspace
 

@@ -5,6 +5,14 @@ Tolerances (per output tensor, over all compared elements):
   fp32 workloads:  relative L2 error <= 1e-5
   bf16 workloads:  relative L2 error <= 1e-2 and max |error| <= 3e-2
 (bf16 inputs, fp32 accumulation; the attention output is itself bf16).
+
+Attention outputs are also compared row by row (one row = one request, block
+position and query head, D values): every row's relative L2 error must stay
+within ROW_REL.  |o| is only ~0.02-0.2, so one wrong row (a wrong page, head
+or split) could hide under the whole-tensor bounds, but not under this one.
+The bf16 bound, 2e-2, is twice the tensor bound: a row's error is the bf16
+rounding of its D outputs and of the probabilities (~2^-9 relative each),
+measured at ~2e-3 over whole tensors.
 """
 import numpy as np
 import torch
@@ -12,6 +20,7 @@ import torch
 import oracle
 
 TOL = {"f32": dict(rel=1e-5, abs=None), "bf16": dict(rel=1e-2, abs=3e-2)}
+ROW_REL = {"f32": 1e-4, "bf16": 2e-2}
 
 
 def flush(msg: str):
@@ -48,6 +57,27 @@ def assert_close(got, want, dtype: str, what: str):
     assert np.isfinite(np.asarray(got, np.float64)).all(), f"{what}: non-finite output"
     assert ok, f"{what}: rel-L2 {rel:.3e} max-abs {mx:.3e} exceeds {t}"
     return rel, mx
+
+
+def row_errors(got, want):
+    """Relative L2 error of every row (last axis) and the row index of the worst."""
+    got = np.asarray(got, np.float64)
+    want = np.asarray(want, np.float64)
+    num = np.linalg.norm(got - want, axis=-1)
+    den = np.linalg.norm(want, axis=-1)
+    rel = num / np.maximum(den, 1e-30)
+    worst = np.unravel_index(int(np.argmax(rel)), rel.shape) if rel.size else ()
+    return rel, worst
+
+
+def assert_attn_close(got, want, dtype: str, what: str):
+    """assert_close over the whole tensor, then every row [..., D] on its own."""
+    res = assert_close(got, want, dtype, what)
+    rel, worst = row_errors(got, want)
+    if rel.size:
+        assert rel.max() <= ROW_REL[dtype], (
+            f"{what}: row {tuple(int(i) for i in worst)} rel-L2 {rel.max():.3e} exceeds {ROW_REL[dtype]}")
+    return res
 
 
 def layer_from_inputs(inp, *, kv_split_pages=0, want_final=True, with_dskip=False,

@@ -21,7 +21,7 @@ import oracle
 from hybrid_mamba_attention_amd import ops
 from hybrid_mamba_attention_amd import workloads as wl
 
-from helpers import assert_close, flush, to_dev, to_host64
+from helpers import assert_attn_close, assert_close, flush, to_dev, to_host64
 
 pytestmark = pytest.mark.gpu
 PAGE = 16
@@ -105,7 +105,7 @@ def test_attention_shapes(name, ctx, K, Hq, Hkv, D, dtype):
     want = oracle_attn(case)
     for split in (0, 1, 3):
         o, _, _ = run_attn(case, split=split)
-        assert_close(to_host64(o), want, dtype, f"{name} split={split}")
+        assert_attn_close(to_host64(o), want, dtype, f"{name} split={split}")
 
 
 CAUSAL_CASES = [
@@ -127,7 +127,7 @@ def test_attention_block_causal(name, ctx, K, Hq, Hkv, D, dtype):
     want = oracle_attn(case, causal=True)
     for split in (0, 1, 3):
         o, _, _ = run_attn(case, split=split, causal=True)
-        assert_close(to_host64(o), want, dtype, f"{name} causal split={split}")
+        assert_attn_close(to_host64(o), want, dtype, f"{name} causal split={split}")
 
 
 def test_block_causal_edges():
@@ -142,7 +142,7 @@ def test_block_causal_edges():
     oc, _, _ = run_attn(c, causal=True)
     of, _, _ = run_attn(c, causal=False)
     oc, of = to_host64(oc), to_host64(of)
-    assert_close(oc[:, -1], of[:, -1], "bf16", "last block position")
+    assert_attn_close(oc[:, -1], of[:, -1], "bf16", "last block position")
     assert np.abs(oc[:, 0] - of[:, 0]).max() > 0.05
 
 
@@ -158,12 +158,12 @@ def test_bigger_pages(P):
     want = oracle_attn(case)
     for split in (0, 1, 3):
         o, _, _ = run_attn(case, split=split)
-        assert_close(to_host64(o), want, "bf16", f"page {P} split={split}")
+        assert_attn_close(to_host64(o), want, "bf16", f"page {P} split={split}")
         if split:
             o16, _, _ = run_attn(ref16, split=split * (P // 16))
             assert torch.equal(o.view(torch.int16), o16.view(torch.int16)), f"page {P} split={split}"
     oc, _, _ = run_attn(case, split=1, causal=True)
-    assert_close(to_host64(oc), oracle_attn(case, causal=True), "bf16", f"page {P} causal")
+    assert_attn_close(to_host64(oc), oracle_attn(case, causal=True), "bf16", f"page {P} causal")
 
 
 def test_bigger_pages_hnd():
@@ -171,7 +171,7 @@ def test_bigger_pages_hnd():
     on, _, _ = run_attn(case, layout="NHD")
     oh, _, _ = run_attn(case, layout="HND")
     assert torch.equal(on.view(torch.int16), oh.view(torch.int16))
-    assert_close(to_host64(oh), oracle_attn(case), "bf16", "HND page 64")
+    assert_attn_close(to_host64(oh), oracle_attn(case), "bf16", "HND page 64")
 
 
 def test_split_invariance_and_repeatability():
@@ -181,7 +181,7 @@ def test_split_invariance_and_repeatability():
         o1, ws, _ = run_attn(case, split=split)
         o2, _, _ = run_attn(case, split=split)
         assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)), f"split={split} not repeatable"
-        assert_close(to_host64(o1), want, "bf16", f"split={split}")
+        assert_attn_close(to_host64(o1), want, "bf16", f"split={split}")
         plan = ws[:4 * 4].view(torch.int32).cpu().numpy()
         M = int(plan[3])
         plan = ws[:4 * (4 + 2 * 4 + 2 * M)].view(torch.int32).cpu().numpy()
@@ -204,7 +204,7 @@ def test_hnd_pool_layout_is_bit_identical():
     oh, _, (kc, _) = run_attn(case, layout="HND")
     assert kc.shape[1] == 2 and ops.kv_strides(kc, "HND") == (16 * 2 * 128, 128, 16 * 128)
     assert torch.equal(on.view(torch.int16), oh.view(torch.int16))
-    assert_close(to_host64(oh), oracle_attn(case), "bf16", "HND")
+    assert_attn_close(to_host64(oh), oracle_attn(case), "bf16", "HND")
 
 
 @pytest.mark.parametrize("page", [16, 64])
@@ -220,7 +220,7 @@ def test_head_pair_workgroups_match_single_heads(causal, page):
         on, _, _ = run_attn(case, split=split, layout="NHD", causal=causal)
         oh, _, _ = run_attn(case, split=split, layout="HND", causal=causal)
         assert torch.equal(on.view(torch.int16), oh.view(torch.int16)), split
-        assert_close(to_host64(on), oracle_attn(case, causal=causal), "bf16", f"head pair split={split}")
+        assert_attn_close(to_host64(on), oracle_attn(case, causal=causal), "bf16", f"head pair split={split}")
 
 
 @pytest.mark.parametrize("page", [16, 32, 64])
@@ -241,7 +241,7 @@ def test_contexts_across_page_table_windows(page):
     on, _, _ = run_attn(case, split=10 ** 6, layout="NHD")
     oh, _, _ = run_attn(case, split=10 ** 6, layout="HND")
     assert torch.equal(on.view(torch.int16), oh.view(torch.int16)), page
-    assert_close(to_host64(on), want, "bf16", f"windows page {page}")
+    assert_attn_close(to_host64(on), want, "bf16", f"windows page {page}")
 
 
 def test_kv_pool_untouched_and_output_bounded():
@@ -262,7 +262,7 @@ def test_kv_pool_untouched_and_output_bounded():
         assert torch.equal(x, y), "an input buffer was written"
     assert (canary[q.numel():] == 12345).all(), "wrote past the output tensor"
     assert torch.isfinite(out.float()).all()
-    assert_close(to_host64(out), oracle_attn(case), dt, "canary case")
+    assert_attn_close(to_host64(out), oracle_attn(case), dt, "canary case")
 
 
 def test_peaked_logits():
@@ -271,7 +271,7 @@ def test_peaked_logits():
     want = oracle_attn(case)
     for split in (0, 8):
         o, _, _ = run_attn(case, split=split)
-        assert_close(to_host64(o), want, "bf16", f"peaked split={split}")
+        assert_attn_close(to_host64(o), want, "bf16", f"peaked split={split}")
 
 
 # ----------------------------------------------------------------------------
@@ -372,7 +372,7 @@ def test_layer_block_causal_and_direct_reuse_ablation():
                 H=4, N=32, seed=4343)
     inp = wl.make_inputs(w)
     full = layer_from_inputs(inp, block_causal=True)
-    assert_close(to_host64(full.out), oracle_attn_inp(inp, block_causal=True), "bf16", "causal out")
+    assert_attn_close(to_host64(full.out), oracle_attn_inp(inp, block_causal=True), "bf16", "causal out")
     y, hf = oracle_scan(inp, oracle_h0(inp))
     assert_close(to_host64(full.y), y, "bf16", "y")
     abl = layer_from_inputs(inp, no_init=True)
@@ -380,7 +380,7 @@ def test_layer_block_causal_and_direct_reuse_ablation():
     y0, hf0 = oracle_scan(inp, np.zeros((w.C, w.S)))
     assert_close(to_host64(abl.y), y0, "bf16", "y from the zero state")
     assert_close(to_host64(abl.h_final), hf0, "bf16", "h_final from the zero state")
-    assert_close(to_host64(abl.out), oracle_attn_inp(inp), "bf16", "ablation out")
+    assert_attn_close(to_host64(abl.out), oracle_attn_inp(inp), "bf16", "ablation out")
     assert np.abs(to_host64(abl.y) - y).max() > 1e-3, "the projected state must matter"
 
 

@@ -69,6 +69,10 @@ CASES = [
     ("n7-cross-page-d200", 3, 7, 200, 2, 128, "bf16", [14, 0, 31]),
     ("d64-hkv4-n21", 5, 21, 512, 4, 64, "bf16", [5, 16, 33, 0, 70]),
     ("f32-small", 2, 5, 64, 2, 64, "f32", [3, 15]),
+    # 2*Hkv*D = 192 columns: 128-column tiles leave a 64-column tail, and at
+    # 25600 rows (200 row tiles) that tail is launched on its own so the
+    # whole tiles fill one round; its V columns must land in V, not in K
+    ("tail-launch-hkv1-d96-25600rows", 100, 256, 64, 1, 96, "bf16", None),
 ]
 
 
