@@ -8,6 +8,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "../../include/hspec.h"
@@ -489,6 +490,35 @@ int enqueue_layer(const hspec_layer_args* a, hipStream_t s) {
 
 }  // namespace
 
+// Workspace of hspec_draft_layer_noalloc: one static array per GPU, so that
+// entry point allocates nothing.  In host code `scratch` names only a host
+// stand-in for the device array: its device address comes from
+// hipGetSymbolAddress, once per device, and only that address is ever passed
+// to kernels.
+static __device__ __align__(256) unsigned char scratch[HSPEC_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices] = {};
+
+// Device address of `scratch` on the calling thread's current device.
+int scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return HSPEC_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return HSPEC_ERR_HIP;
+    g_scratch_addr[dev] = p;
+  }
+  *out = g_scratch_addr[dev];
+  return HSPEC_OK;
+}
+
+}  // namespace
+
 struct hspec_graph_s {
   hipGraph_t graph;
   hipGraphExec_t exec;
@@ -539,6 +569,7 @@ const char* hspec_status_string(int status) {
     case HSPEC_ERR_UNSUPPORTED: return "HSPEC_ERR_UNSUPPORTED";
     case HSPEC_ERR_WORKSPACE: return "HSPEC_ERR_WORKSPACE";
     case HSPEC_ERR_HIP: return "HSPEC_ERR_HIP";
+    case HSPEC_ERR_SCRATCH: return "HSPEC_ERR_SCRATCH";
     default: return "HSPEC_UNKNOWN_STATUS";
   }
 }
@@ -593,6 +624,22 @@ int hspec_draft_layer(void* stream, const hspec_layer_args* a, size_t* required_
   if (!a->workspace) return required_bytes ? HSPEC_OK : HSPEC_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   return enqueue_layer(a, s);
+}
+
+int hspec_draft_layer_noalloc(void* stream, const hspec_layer_args* a) {
+  if (!a) return HSPEC_ERR_INVALID_ARG;
+  if (a->workspace || a->workspace_bytes) return HSPEC_ERR_INVALID_ARG;
+  size_t need = 0;
+  int st = check_layer(a, &need);
+  if (st != HSPEC_OK) return st;
+  if (need > HSPEC_NOALLOC_SCRATCH_BYTES) return HSPEC_ERR_SCRATCH;
+  void* ws = nullptr;
+  st = scratch_address(&ws);
+  if (st != HSPEC_OK) return st;
+  hspec_layer_args b = *a;
+  b.workspace = ws;
+  b.workspace_bytes = HSPEC_NOALLOC_SCRATCH_BYTES;
+  return enqueue_layer(&b, static_cast<hipStream_t>(stream));
 }
 
 int hspec_draft_layer_graph(const hspec_layer_args* a, hspec_graph* out) {

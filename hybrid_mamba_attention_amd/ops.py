@@ -17,7 +17,8 @@ LIB_PATH = os.path.join(_HERE, "libhspec.so")
 
 F32, BF16 = 0, 1
 _STATUS = {0: "HSPEC_OK", -1: "HSPEC_ERR_INVALID_ARG", -2: "HSPEC_ERR_UNSUPPORTED",
-           -3: "HSPEC_ERR_WORKSPACE", -4: "HSPEC_ERR_HIP"}
+           -3: "HSPEC_ERR_WORKSPACE", -4: "HSPEC_ERR_HIP", -5: "HSPEC_ERR_SCRATCH"}
+ABI_VERSION = 7
 
 _vp, _i, _i64, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
 
@@ -107,6 +108,8 @@ def lib() -> ctypes.CDLL:
                                             _vp, _vp, ctypes.POINTER(_sz)])
     L.hspec_draft_layer.restype = _i
     L.hspec_draft_layer.argtypes = [_vp, ctypes.POINTER(LayerArgs), ctypes.POINTER(_sz)]
+    L.hspec_draft_layer_noalloc.restype = _i
+    L.hspec_draft_layer_noalloc.argtypes = [_vp, ctypes.POINTER(LayerArgs)]
     L.hspec_mamba_args_size.restype = _sz
     L.hspec_mamba_block.restype = _i
     L.hspec_mamba_block.argtypes = [_vp, ctypes.POINTER(MambaArgs), ctypes.POINTER(_sz)]
@@ -124,7 +127,7 @@ def lib() -> ctypes.CDLL:
     L.hspec_graph_launch.argtypes = [_vp, _vp]
     L.hspec_graph_destroy.restype = _i
     L.hspec_graph_destroy.argtypes = [_vp]
-    if L.hspec_abi_version() != 6:
+    if L.hspec_abi_version() != ABI_VERSION:
         raise RuntimeError("libhspec.so ABI version mismatch")
     if L.hspec_layer_args_size() != ctypes.sizeof(LayerArgs):
         raise RuntimeError("hspec_layer_args layout mismatch between library and binding")
@@ -435,6 +438,14 @@ class DraftLayer:
 
     def __call__(self, stream=None):
         _check("hspec_draft_layer", lib().hspec_draft_layer(_stream(stream), ctypes.byref(self._args), None))
+        return self
+
+    def noalloc(self, stream=None):
+        """The same layer through hspec_draft_layer_noalloc: the library's static
+        scratch instead of this object's workspace (nothing is allocated)."""
+        a = LayerArgs.from_buffer_copy(self._args)
+        a.workspace, a.workspace_bytes = None, 0
+        _check("hspec_draft_layer_noalloc", lib().hspec_draft_layer_noalloc(_stream(stream), ctypes.byref(a)))
         return self
 
     def graph(self):

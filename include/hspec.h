@@ -12,7 +12,7 @@
  * Entry points
  *   hspec_init_state, hspec_ssd_scan,       the layer's steps (a1, a2, a0+a3+a4)
  *   hspec_block_attn_inplace
- *   hspec_draft_layer (+ _graph)            the layer (a5)
+ *   hspec_draft_layer (+ _graph, _noalloc)  the layer (a5)
  *   hspec_mamba_block                       the Mamba-2 block around the scan
  *   hspec_draft_stack (+ _graph)            a stack of hybrid layers
  *   hspec_kv_inject                         contrast workload: the drafter-side
@@ -28,9 +28,10 @@
  *   - All pointers except the integer metadata noted below are device
  *     pointers.  The caller owns every buffer; the library allocates no
  *     device memory and keeps no state between calls (the _graph forms create
- *     host-side HIP graph objects, freed by hspec_graph_destroy), so calls on
- *     different streams may run concurrently as long as their output and
- *     workspace buffers differ.
+ *     host-side HIP graph objects, freed by hspec_graph_destroy; the static
+ *     scratch of hspec_draft_layer_noalloc and its per-device address live
+ *     until the process ends), so calls on different streams may run
+ *     concurrently as long as their output and workspace buffers differ.
  *   - `dtype` selects the element type of the "act" tensors: HSPEC_F32
  *     (float) or HSPEC_BF16 (bfloat16 bits).  Accumulation is always fp32.
  *   - Shapes are row-major, last index fastest; "act" tensors are contiguous
@@ -53,14 +54,16 @@ typedef enum {
   HSPEC_ERR_INVALID_ARG = -1,   /* a size, pointer or stride breaks the contract      */
   HSPEC_ERR_UNSUPPORTED = -2,   /* legal but outside the shapes these kernels handle  */
   HSPEC_ERR_WORKSPACE = -3,     /* workspace pointer missing or smaller than required */
-  HSPEC_ERR_HIP = -4            /* the HIP runtime refused a launch                   */
+  HSPEC_ERR_HIP = -4,           /* the HIP runtime refused a launch                   */
+  HSPEC_ERR_SCRATCH = -5        /* hspec_draft_layer_noalloc: the call needs more
+                                   than HSPEC_NOALLOC_SCRATCH_BYTES of scratch       */
 } hspec_status;
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* hspec_status_string(int status);
 
 /* ABI version of this header; bumped on any incompatible change. */
-#define HSPEC_ABI_VERSION 6
+#define HSPEC_ABI_VERSION 7
 int hspec_abi_version(void);
 
 /*
@@ -205,6 +208,27 @@ size_t hspec_layer_args_size(void);
 /* `required_bytes` receives the workspace size a5 needs (may be NULL when
  * a->workspace is set). */
 int hspec_draft_layer(void* stream, const hspec_layer_args* a, size_t* required_bytes);
+
+/*
+ * a5 for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * kernels as hspec_draft_layer, but its workspace (the split plan and the
+ * attention's split partials) is a static device array of the library,
+ * HSPEC_NOALLOC_SCRATCH_BYTES long, instead of a caller's buffer.
+ *   a->workspace must be NULL and a->workspace_bytes 0 (else INVALID_ARG).
+ *   A call whose workspace (the size hspec_draft_layer would report) exceeds
+ *   HSPEC_NOALLOC_SCRATCH_BYTES returns HSPEC_ERR_SCRATCH and launches
+ *   nothing.
+ * The array exists once per GPU (on the calling thread's current device,
+ * which must be the stream's device) and is held until the process ends; its
+ * address is looked up on the first call on each device.  Nothing is
+ * allocated and nothing needs clearing: every byte a call reads from it was
+ * written earlier in the same call.  All calls on one GPU share the array,
+ * so calls that overlap in time on one GPU (concurrent streams, or two
+ * threads) race: serialise them.
+ */
+#define HSPEC_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int hspec_draft_layer_noalloc(void* stream, const hspec_layer_args* a);
 
 /* Executable HIP graph of a layer or a stack (see hspec_draft_stack_graph). */
 typedef struct hspec_graph_s* hspec_graph;
