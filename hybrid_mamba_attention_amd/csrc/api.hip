@@ -64,10 +64,20 @@ int check_ssd(int dtype, int C, int K, int H, int P, int ng, int N, int chunk, c
   return HSPEC_OK;
 }
 
+// Host side of the attention's work plan (the device derives the same plan
+// from ctx_lens; include/hspec.h documents it).  The host knows only bounds:
+// w_max, the most ranges the plan can use, sizes the grid and the workspace.
 struct AttnPlanShape {
-  int pps, M, MS;  // 16-token slabs per split, C * MS work items, splits of a max_ctx request
+  int w_max, gran, range_gran, min_gran, nbk, head_pair;
   size_t plan_bytes, part_o_off, part_ml_off, total;
 };
+
+// Workgroups the automatic plan aims at: two per CU, one resident round of
+// the one-head forms at their occupancy (measured at 8192-token contexts,
+// C = 2..64: 512 work units beat both 256, too little in flight, and 1024,
+// twice the per-unit prologue and fp32 partials).  The head-pair form holds
+// one workgroup per CU and takes twice the ranges (two rounds).
+constexpr int kTargetGroups = 512;
 
 // log2(page_size / 16) for a supported page size, else -1
 int page_shift(int page_size) {
@@ -76,42 +86,39 @@ int page_shift(int page_size) {
   return -1;
 }
 
-// Slabs (16 tokens) per split; splits start on page boundaries, so the result
-// is a multiple of the page's slab count spp.
-int auto_pages_per_split(int C, int Hkv, int max_ctx, int spp) {
-  const int max_pages = (max_ctx + 15) / 16;
-  if (max_pages <= 0) return 16;
-  const int64_t base = int64_t(C) * Hkv;
-  // Aim at about 512 work items -- two per CU, one resident round at the
-  // attention kernel's occupancy: measured at 8192-token contexts, C = 2..64,
-  // 512 items beat both 256 (too little in flight) and 1024 (twice the
-  // per-item prologue and fp32 partials: G*K rows x (D+2) written and read
-  // back by the merge).  Past 512 (request, kv head) pairs nothing is split.
-  const int64_t target = 512;
-  if (base >= target) return (max_pages + spp - 1) / spp * spp;
-  const int64_t splits = (target + base - 1) / base;
-  int64_t pps = (max_pages + splits - 1) / splits;
-  if (pps < 16) pps = 16;    // >= 256 tokens per item: partials stay small next to the KV they summarise
-  const int64_t m = std::max(8, spp);
-  return int((pps + m - 1) / m * m);
-}
-
-AttnPlanShape plan_shape(int C, int K, int Hq, int Hkv, int D, int max_ctx, int kv_split_pages,
-                         int page_size) {
+AttnPlanShape plan_shape(int dtype, int C, int K, int Hq, int Hkv, int D, int64_t head_stride, int max_ctx,
+                         int kv_split_pages, int page_size) {
   AttnPlanShape p{};
   const int spp = page_size / 16;
-  p.pps = kv_split_pages > 0 ? kv_split_pages * spp : auto_pages_per_split(C, Hkv, max_ctx, spp);
-  const int64_t max_pages = (int64_t(max_ctx) + 15) / 16;
-  const int64_t max_splits = std::max<int64_t>(1, (max_pages + p.pps - 1) / p.pps);
-  p.MS = int(std::min<int64_t>(max_splits, 0x7fffffff));
-  p.M = int(std::min<int64_t>(int64_t(C) * max_splits, 0x7fffffff));
+  p.gran = std::max(2, spp);
+  p.nbk = (K + 15) / 16;
+  p.min_gran = (16 + p.gran - 1) / p.gran;   // ranges of >= 16 slabs when the batch allows
+  // granules of a max_ctx request, and of the batch at most
+  const int64_t gmax = ((int64_t(max_ctx) + 15) / 16 + p.nbk + p.gran - 1) / p.gran;
+  const int64_t tmax = int64_t(C) * gmax;
+  const bool hp_ok = head_pair_fits((Hq / Hkv) * K, Hkv, head_stride, dtype, D);
+  int64_t w_max;
+  if (kv_split_pages > 0) {
+    p.range_gran = int(std::max<int64_t>(1, (int64_t(kv_split_pages) * spp + p.gran - 1) / p.gran));
+    w_max = (tmax + p.range_gran - 1) / p.range_gran;
+    p.head_pair = hp_ok && int64_t(p.range_gran) * p.gran >= 128;
+  } else {
+    p.range_gran = 0;
+    // two heads per workgroup when the batch at its bound gives ranges of
+    // 128+ slabs with the head pair's range count
+    const int64_t w_hp = std::max<int64_t>(1, 2 * kTargetGroups / Hkv);
+    p.head_pair = hp_ok && tmax * p.gran >= 128 * std::min(w_hp, tmax);
+    w_max = std::max<int64_t>(1, (p.head_pair ? 2 : 1) * kTargetGroups / Hkv);
+  }
+  w_max = std::max<int64_t>(1, std::min(w_max, tmax));   // a range holds at least one granule
+  p.w_max = int(std::min<int64_t>(w_max, 0x7fffffff));
   const size_t rows = size_t(Hq / Hkv) * K;
-  p.plan_bytes = align256(size_t(4 + 2 * size_t(C) + 2 * size_t(p.M)) * 4);
+  p.plan_bytes = align256((4 + 3 * size_t(C) + size_t(p.w_max) + 1) * 4);
   p.part_o_off = p.plan_bytes;
   size_t po = 0, pml = 0;
-  if (p.M > C) {  // only then can a request have more than one split
-    po = align256(size_t(p.M) * Hkv * rows * D * 4);
-    pml = align256(size_t(p.M) * Hkv * rows * 2 * 4);
+  if (p.w_max > 1) {  // only then can a request span several ranges
+    po = align256(2 * size_t(p.w_max) * Hkv * rows * D * 4);
+    pml = align256(2 * size_t(p.w_max) * Hkv * rows * 2 * 4);
   }
   p.part_ml_off = p.part_o_off + po;
   p.total = p.part_ml_off + pml;
@@ -145,19 +152,24 @@ int check_attn(int dtype, int C, int K, int Hq, int Hkv, int D, const void* q, c
   if (K > 64) return HSPEC_ERR_UNSUPPORTED;
   if (int64_t(Hq / Hkv) * K > 256) return HSPEC_ERR_UNSUPPORTED;
   if (attn_lds_bytes(dtype, D, (Hq / Hkv) * K, K) > kMaxLds) return HSPEC_ERR_UNSUPPORTED;
-  const AttnPlanShape p = plan_shape(C, K, Hq, Hkv, D, max_ctx, kv_split_pages, page_size);
-  if (int64_t(C) * p.MS * Hkv >= 0x7fffffff) return HSPEC_ERR_UNSUPPORTED;  // + the plan workgroup
+  // the kernels count the batch's keys in 32-bit slabs (granules times
+  // slabs per granule) and launch w_max workgroups per kv head group, + 1
+  const int spp = page_size / 16, gran = std::max(2, spp);
+  const int64_t gmax = ((int64_t(max_ctx) + 15) / 16 + (K + 15) / 16 + gran - 1) / gran;
+  if (int64_t(C) * gmax * gran >= 0x7fffffff) return HSPEC_ERR_UNSUPPORTED;
+  const AttnPlanShape p = plan_shape(dtype, C, K, Hq, Hkv, D, hs, max_ctx, kv_split_pages, page_size);
+  if (int64_t(p.w_max) * Hkv >= 0x7fffffff) return HSPEC_ERR_UNSUPPORTED;
   return HSPEC_OK;
 }
 
 // The kernel arguments of a3 (arguments validated by check_attn); WORKSPACE
 // when `ws` cannot hold the plan and partials.
-int attn_args(AttnArgs& a, int C, int K, int Hq, int Hkv, int D, const void* q, const void* kb,
+int attn_args(AttnArgs& a, int dtype, int C, int K, int Hq, int Hkv, int D, const void* q, const void* kb,
               const void* vb, const void* kc, const void* vc, int64_t ps, int64_t ts, int64_t hs,
               int num_pages, int page_size, const int32_t* pt, int max_pages, const int32_t* ctx,
               int max_ctx, int kv_split_pages, float scale, int block_causal, void* out, void* ws,
               size_t ws_bytes) {
-  const AttnPlanShape p = plan_shape(C, K, Hq, Hkv, D, max_ctx, kv_split_pages, page_size);
+  const AttnPlanShape p = plan_shape(dtype, C, K, Hq, Hkv, D, hs, max_ctx, kv_split_pages, page_size);
   if (!ws || !aligned(ws, 256) || ws_bytes < p.total) return HSPEC_ERR_WORKSPACE;
   a = AttnArgs{};
   a.q = q; a.k_blk = kb; a.v_blk = vb; a.k_cache = kc; a.v_cache = vc;
@@ -172,9 +184,12 @@ int attn_args(AttnArgs& a, int C, int K, int Hq, int Hkv, int D, const void* q, 
   a.plan = reinterpret_cast<int32_t*>(base);
   a.part_o = reinterpret_cast<float*>(base + p.part_o_off);
   a.part_ml = reinterpret_cast<float*>(base + p.part_ml_off);
-  a.max_items = p.M;
-  a.pps = p.pps;
-  a.max_splits = p.MS;
+  a.w_max = p.w_max;
+  a.gran = p.gran;
+  a.range_gran = p.range_gran;
+  a.min_gran = p.min_gran;
+  a.nbk = p.nbk;
+  a.head_pair = p.head_pair;
   a.block_causal = block_causal;
   a.lsp = page_shift(page_size);
   return HSPEC_OK;
@@ -186,7 +201,7 @@ int run_attn(hipStream_t st, int dtype, int C, int K, int Hq, int Hkv, int D, co
              const int32_t* ctx, int max_ctx, int kv_split_pages, float scale, int block_causal,
              void* out, void* ws, size_t ws_bytes) {
   AttnArgs a;
-  const int st_ = attn_args(a, C, K, Hq, Hkv, D, q, kb, vb, kc, vc, ps, ts, hs, num_pages, page_size, pt,
+  const int st_ = attn_args(a, dtype, C, K, Hq, Hkv, D, q, kb, vb, kc, vc, ps, ts, hs, num_pages, page_size, pt,
                             max_pages, ctx, max_ctx, kv_split_pages, scale, block_causal, out, ws, ws_bytes);
   if (st_ != HSPEC_OK) return st_;
   return status_of(launch_block_attn(st, dtype, a));
@@ -318,7 +333,8 @@ StackPlan stack_plan(const hspec_stack_args* a) {
   const hspec_stack_layer L{};
   const hspec_mamba_args m = block_args_of(a, L, nullptr, nullptr, nullptr, nullptr, 0);
   p.bp = block_plan(&m);
-  p.ap = plan_shape(a->C, a->K, a->Hq, a->Hkv, a->D, a->max_ctx, a->kv_split_pages, a->page_size);
+  p.ap = plan_shape(a->dtype, a->C, a->K, a->Hq, a->Hkv, a->D, a->head_stride, a->max_ctx, a->kv_split_pages,
+                    a->page_size);
   p.gq = gemm_plan(a->dtype, p.T, a->Hq * a->D, a->d_model);
   p.gkv = gemm_plan(a->dtype, p.T, a->Hkv * a->D, a->d_model);
   p.go = gemm_plan(a->dtype, p.T, a->d_model, a->Hq * a->D);
@@ -460,7 +476,8 @@ int check_layer(const hspec_layer_args* a, size_t* need) {
                   a->page_size, a->page_table, a->max_pages, a->ctx_lens, a->max_ctx, a->kv_split_pages,
                   a->scale, a->block_causal, a->out, &dummy);
   if (st != HSPEC_OK) return st;
-  *need = plan_shape(a->C, a->K, a->Hq, a->Hkv, a->D, a->max_ctx, a->kv_split_pages, a->page_size).total;
+  *need = plan_shape(a->dtype, a->C, a->K, a->Hq, a->Hkv, a->D, a->head_stride, a->max_ctx, a->kv_split_pages,
+                     a->page_size).total;
   return HSPEC_OK;
 }
 
@@ -473,7 +490,7 @@ int enqueue_layer(const hspec_layer_args* a, hipStream_t s) {
   SsdArgs sa{a->x, a->delta, a->A, a->B, a->Cm, a->Dskip, no_init ? nullptr : a->h0, a->y, a->h_final,
              a->C, a->K, a->H, a->P, a->ng, a->N, a->chunk};
   AttnArgs m;
-  int st = attn_args(m, a->C, a->K, a->Hq, a->Hkv, a->D, a->q, a->k_blk, a->v_blk, a->k_cache, a->v_cache,
+  int st = attn_args(m, a->dtype, a->C, a->K, a->Hq, a->Hkv, a->D, a->q, a->k_blk, a->v_blk, a->k_cache, a->v_cache,
                      a->page_stride, a->token_stride, a->head_stride, a->num_pages, a->page_size,
                      a->page_table, a->max_pages, a->ctx_lens, a->max_ctx, a->kv_split_pages, a->scale,
                      a->block_causal, a->out, a->workspace, a->workspace_bytes);
@@ -607,7 +624,7 @@ int hspec_block_attn_inplace(void* stream, int dtype, int C, int K, int Hq, int 
                             ctx_lens, max_ctx, kv_split_pages, scale, block_causal, out, workspace_bytes);
   if (st != HSPEC_OK) return st;
   if (!workspace) {
-    *workspace_bytes = plan_shape(C, K, Hq, Hkv, D, max_ctx, kv_split_pages, page_size).total;
+    *workspace_bytes = plan_shape(dtype, C, K, Hq, Hkv, D, head_stride, max_ctx, kv_split_pages, page_size).total;
     return HSPEC_OK;
   }
   return run_attn(static_cast<hipStream_t>(stream), dtype, C, K, Hq, Hkv, D, q, k_blk, v_blk,

@@ -2,31 +2,43 @@
 // in place (H-Spec, Abstract: attention modules reuse the target KV where it
 // lies; there is no drafter-side KV cache).
 //
-// a3  k_block_attn       one workgroup per (work item = request x split, kv head),
-//                        or per (work item, pair of adjacent kv heads) with long
-//                        splits; one more workgroup writes the int32 split plan (a0)
-// a4  k_attn_merge       log-sum-exp merge of the splits of multi-split requests
+// a3  k_block_attn       one workgroup per (work range, kv head), or per (work
+//                        range, pair of adjacent kv heads) with long ranges;
+//                        one more workgroup writes the int32 work plan (a0)
+// a4  k_attn_merge       log-sum-exp merge of the pieces of requests that
+//                        span more than one range
 //
-// Work items are numbered request * max_splits + split, so every kernel finds
-// its request and split from its block index and ctx_lens alone; items past a
-// request's own split count exit at once.  The plan in the workspace lists the
-// same decomposition (compacted, in request order) for callers and tests.
+// Work plan (a0).  Each request's keys are its context, in slabs of 16
+// tokens, followed by its K block keys (nbk slabs), counted in granules of
+// `gran` slabs (max(2, slabs per page), from the request's start, so a
+// granule boundary starts a page and an even slab).  The batch's granules,
+// request after request, are cut into W nearly equal ranges (B_w =
+// floor(w * T / W)); a workgroup takes its range's slabs request by request
+// (segments).  Long and short requests thus cost the same wall time: ragged
+// batches keep every workgroup busy for the same number of slabs.  Every
+// workgroup derives the plan from ctx_lens itself (a block scan over the
+// requests); a segment that is a whole request writes its normalised output,
+// one that is a piece of a longer request writes fp32 (m, l, O) to slot
+// 2w + k of the workspace (k = 0 for the segment starting at the range's
+// first granule, 1 for the one starting later), and k_attn_merge combines
+// the pieces.  The plan in the workspace lists the same decomposition for
+// the merge, callers and tests.
 //
-// k_block_attn, per workgroup of NW waves (one work item, HP = 1 or 2 kv heads):
+// k_block_attn, per workgroup of NW waves (one range, HP = 1 or 2 kv heads):
 //   * The G*K query rows of kv head j (row r -> block position r / G, head
 //     j*G + r % G) are split over NW/HP waves, RT tiles of 16 rows each, and
-//     held in registers as matrix-core operands for the whole kernel.  With
-//     HP = 2 (NHD pools, splits of 2048+ tokens) a stage row is the 2D-wide
+//     held in registers as matrix-core operands for a whole segment.  With
+//     HP = 2 (NHD pools, ranges of 2048+ tokens) a stage row is the 2D-wide
 //     piece of both heads, 512 bytes for bf16 D = 128, and each half of the
 //     waves computes on its own head's columns.
-//   * The item's pages stream through LDS 32 tokens (two pages) at a time:
+//   * A segment's slabs stream through LDS 32 tokens (two slabs) at a time:
 //     every thread loads 16-byte pieces of K and V rows for the next stage
 //     (16 threads cover a 256-byte row, 32 a 512-byte head-pair row; the
 //     physical page comes from the page table) while the waves compute on the
 //     current stage; one barrier per stage.  LDS rows are XOR-swizzled by
 //     16-byte chunk so that operand reads are bank-conflict free.
 //   * The draft block's own K keys and values ("transient intra-block KV")
-//     are the last stages of the last split: they pass through the same LDS
+//     are the last slabs of a request's keys: they pass through the same LDS
 //     buffers and are never written anywhere.  With the block-causal mask,
 //     those stages also drop block key s for query rows at block position
 //     t < s; context pages are never masked.
@@ -35,9 +47,8 @@
 //     in the lane (two xor-shuffles give the row max, the sum is deferred).
 //   * O^T += V^T . P^T on MFMA: each lane reads 8 token rows x D/16 values of
 //     V and transposes them in registers; P^T is the lane's own probabilities.
-//   * Each wave owns its rows across all the item's tokens, so nothing is
-//     merged inside the workgroup: a single-split request writes its
-//     normalised output, otherwise fp32 (m, l, O) partials go to the workspace.
+//   * Each wave owns its rows across all of a segment's tokens, so nothing is
+//     merged inside the workgroup.
 #include <type_traits>
 
 #include "common.h"
@@ -56,61 +67,150 @@ __device__ __forceinline__ uint4 ld_stream(const char* p) {
 }
 
 // ---------------------------------------------------------------------------
-// a0: split plan, written by the last workgroup of k_block_attn (no other work)
-// (NT threads, `scan` = NT + 1 ints of LDS).  Layout documented in
-// include/hspec.h: splits_b = max(1, ceil(ceil(ctx_b / 16) / pps)), items
-// listed request by request.
+// a0: the work plan (include/hspec.h documents the layout)
 // ---------------------------------------------------------------------------
+
+__device__ __forceinline__ int ctx_of(const AttnArgs& a, int b) { return min(max(a.ctx_lens[b], 0), a.max_ctx); }
+
+// Granules of a request's keys: ceil(ctx / 16) context slabs, then the block's.
+__device__ __forceinline__ int req_granules(const AttnArgs& a, int ctx) {
+  return (((ctx + 15) >> 4) + a.nbk + a.gran - 1) / a.gran;
+}
+
+// Ranges for a batch of T granules (T >= C >= 1, so W <= T: no range is
+// empty): fixed ranges of range_gran granules (the last one shorter), or W
+// nearly equal ranges.  The host sizes w_max for the fixed form's count.
+__device__ __forceinline__ int range_count(const AttnArgs& a, int T) {
+  const int W = a.range_gran > 0 ? (T + a.range_gran - 1) / a.range_gran : (T + a.min_gran - 1) / a.min_gran;
+  return max(1, min(W, a.w_max));
+}
+// B_w, the first granule of range w (B_W = T)
+__device__ __forceinline__ int range_bound(const AttnArgs& a, int w, int T, int W) {
+  return a.range_gran > 0 ? int(min(int64_t(w) * a.range_gran, int64_t(T))) : int(int64_t(w) * T / W);
+}
+// The range holding granule x < T: the largest w with B_w <= x.
+__device__ __forceinline__ int range_of(const AttnArgs& a, int x, int T, int W) {
+  if (a.range_gran > 0) return x / a.range_gran;
+  return int((int64_t(x + 1) * W + T - 1) / T) - 1;   // floor(w*T/W) <= x  <=>  w < (x+1)*W/T
+}
+
+// Inclusive prefix sum of v over the workgroup's NT threads (NT / 64 waves;
+// lds[0 .. NT/64) is scratch); *total receives the sum.  Every thread calls it.
 template <int NT>
-__device__ void write_split_plan(const AttnArgs& a, int* scan) {
-  const int tid = threadIdx.x;
-  const int C = a.C, M = a.max_items, pps = a.pps;
+__device__ __forceinline__ int block_incl_scan(int v, int* lds, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) lds[wave] = x;
+  __syncthreads();
+  int before = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < NT / 64; ++i) {
+    const int t = lds[i];
+    before += i < wave ? t : 0;
+    tot += t;
+  }
+  __syncthreads();
+  *total = tot;
+  return x + before;
+}
+
+// The batch's total granules T (every thread; lds as block_incl_scan).  g0
+// receives this thread's request granules of the first chunk (requests
+// 0 .. NT-1), which a second pass over a batch of C <= NT then reuses.
+template <int NT>
+__device__ __forceinline__ int batch_granules(const AttnArgs& a, int* lds, int* g0) {
+  int part = 0;
+  *g0 = 0;
+  for (int base = 0; base < a.C; base += NT) {
+    const int b = base + int(threadIdx.x);
+    const int gb = b < a.C ? req_granules(a, ctx_of(a, b)) : 0;
+    if (base == 0) *g0 = gb;
+    part += gb;
+  }
+  int T;
+  block_incl_scan<NT>(part, lds, &T);
+  return T;
+}
+
+// Written by the grid's last workgroup, which does nothing else: W, the
+// request starts S_b, each request's first range and piece count, and the
+// range bounds B_0 .. B_W (-1 past W up to the capacity).
+template <int NT>
+__device__ void write_plan(const AttnArgs& a, int* lds) {
+  const int tid = threadIdx.x, C = a.C;
   int32_t* plan = a.plan;
-  int32_t* n_splits = plan + 4;
-  int32_t* first = plan + 4 + C;
-  int32_t* req = plan + 4 + 2 * C;
-  int32_t* spl = req + M;
+  int g0;
+  const int T = batch_granules<NT>(a, lds, &g0);
+  const int W = range_count(a, T);
   int carry = 0;
   for (int base = 0; base < C; base += NT) {
     const int b = base + tid;
-    int ns = 0;
+    const int gb = base == 0 ? g0 : (b < C ? req_granules(a, ctx_of(a, b)) : 0);
+    int tot;
+    const int incl = carry + block_incl_scan<NT>(gb, lds, &tot);
     if (b < C) {
-      const int ctx = min(max(a.ctx_lens[b], 0), a.max_ctx);
-      ns = max(1, (((ctx + 15) >> 4) + pps - 1) / pps);
+      const int S = incl - gb;
+      const int wf = range_of(a, S, T, W), wl = range_of(a, incl - 1, T, W);
+      plan[4 + b] = S;
+      plan[4 + C + b] = wf;
+      plan[4 + 2 * C + b] = wl - wf + 1;
     }
-    __syncthreads();
-    scan[tid] = ns;
-    __syncthreads();
-    for (int off = 1; off < NT; off <<= 1) {
-      const int v = tid >= off ? scan[tid - off] : 0;
-      __syncthreads();
-      scan[tid] += v;
-      __syncthreads();
-    }
-    const int excl = carry + scan[tid] - ns;
-    if (b < C) {
-      n_splits[b] = ns;
-      first[b] = excl;
-      for (int s = 0; s < ns; ++s) {
-        if (excl + s < M) {
-          req[excl + s] = b;
-          spl[excl + s] = s;
-        }
-      }
-    }
-    carry += scan[NT - 1];
+    carry += tot;
   }
-  const int total = min(carry, M);
-  for (int i = total + tid; i < M; i += NT) {
-    req[i] = -1;
-    spl[i] = -1;
-  }
+  int32_t* bounds = plan + 4 + 3 * C;
+  for (int w = tid; w <= a.w_max; w += NT) bounds[w] = w <= W ? range_bound(a, w, T, W) : -1;
   if (tid == 0) {
-    plan[0] = total;
-    plan[1] = pps;
+    plan[0] = W;
+    plan[1] = a.gran;
     plan[2] = C;
-    plan[3] = M;
+    plan[3] = a.w_max;
   }
+}
+
+// Where range w starts: the request b holding its first granule B0 and that
+// request's first granule S (uniform over the workgroup; b = -1 when w >= W).
+struct RangeStart {
+  int W, T, B0, B1, b, S;
+};
+template <int NT>
+__device__ RangeStart find_range(const AttnArgs& a, int w, int* lds) {
+  const int tid = threadIdx.x, C = a.C;
+  RangeStart r;
+  int g0;
+  r.T = batch_granules<NT>(a, lds, &g0);
+  r.W = range_count(a, r.T);
+  r.b = -1;
+  r.S = 0;
+  if (w >= r.W) return r;
+  r.B0 = range_bound(a, w, r.T, r.W);
+  r.B1 = range_bound(a, w + 1, r.T, r.W);
+  int* found = lds + 16;   // past block_incl_scan's scratch
+  if (tid == 0) found[0] = -1;
+  int carry = 0;
+  for (int base = 0; base < C; base += NT) {
+    const int b = base + tid;
+    const int gb = base == 0 ? g0 : (b < C ? req_granules(a, ctx_of(a, b)) : 0);
+    int tot;
+    const int incl = carry + block_incl_scan<NT>(gb, lds, &tot);  // (its barriers order found[0] = -1)
+    if (b < C && incl - gb <= r.B0 && r.B0 < incl) {   // exactly one thread of the batch
+      found[0] = b;
+      found[1] = incl - gb;
+    }
+    __syncthreads();
+    const int fb = found[0];
+    if (fb >= 0) {
+      r.b = __builtin_amdgcn_readfirstlane(fb);
+      r.S = __builtin_amdgcn_readfirstlane(found[1]);
+      break;
+    }
+    carry += tot;
+  }
+  return r;
 }
 
 // ---------------------------------------------------------------------------
@@ -229,79 +329,28 @@ __global__ __launch_bounds__(64 * NW, (RT == 2 && sizeof(T) == 2) ? 2 : 1) void 
   const int li = lane & 15, lg = lane >> 4;
 
   extern __shared__ __align__(16) unsigned char smem[];
-  // The grid's last workgroup writes the split plan (a0) and nothing else, so
-  // the plan runs beside the work items instead of after one of them (it was
-  // ~3 us of the kernel at C = 1 when workgroup 0 wrote it after its item).
+  // The grid's last workgroup writes the work plan (a0) and nothing else, so
+  // the plan runs beside the ranges instead of after one of them.
   if (blockIdx.x == gridDim.x - 1) {
-    write_split_plan<NT>(a, reinterpret_cast<int*>(smem));
+    write_plan<NT>(a, reinterpret_cast<int*>(smem));
     return;
   }
 
   const int Hkv = a.Hkv;
-  const int item = blockIdx.x / (Hkv / HP), j0 = (blockIdx.x % (Hkv / HP)) * HP;
+  const int w = blockIdx.x / (Hkv / HP), j0 = (blockIdx.x % (Hkv / HP)) * HP;
   // this wave's kv head and its first row tile among that head's G*K rows
   const int hl = wave / WPH, j = j0 + hl, wt = (wave % WPH) * RT;
   const int K = a.K, G = a.G, rows = a.rows;
-  const int pps = a.pps;
-  const int b = item / a.max_splits, split = item % a.max_splits;
-  const int p_lo = split * pps;
+  const RangeStart rs = find_range<NT>(a, w, reinterpret_cast<int*>(smem));
+  if (rs.b < 0) return;   // no such range for this batch (uniform)
 
-  // Loads that depend only on the block index go out before ctx_lens[b]
-  // comes back, so their round trips overlap: the query rows and the first
-  // page-table window.
-  // This wave's query rows as B operands (row li of tile rt, d group lg + 4*ds);
-  // rows past G*K repeat the last row (their outputs are never stored).
-  const T* __restrict__ q = static_cast<const T*>(a.q);
-  Vec8<T> qv[RT][DS];
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    const int row = min((wt + rt) * 16 + li, rows - 1);
-    const int t = row / G, gg = row % G;
-    const T* qp = q + ((size_t(b) * K + t) * a.Hq + j * G + gg) * D;
-#pragma unroll
-    for (int ds = 0; ds < DS; ++ds) load8(qv[rt][ds], qp + (lg + 4 * ds) * 8);
-  }
-  const int32_t* __restrict__ pt = a.page_table + size_t(b) * a.max_pages;
-  // The kernel walks the context in slabs of 16 tokens; a page holds
+  // The kernel walks a request's keys in slabs of 16 tokens; a page holds
   // 2^lsp slabs (page size 16 << lsp), so slab q lies in page q >> lsp at
-  // token offset 16 * (q & (2^lsp - 1)).  Splits start on page boundaries.
+  // token offset 16 * (q & (2^lsp - 1)).  Segments start on granule
+  // boundaries, which start a page and an even slab.
   const int lsp = a.lsp, smask = (1 << lsp) - 1;
-  // Page-table window of the hot path: lane l holds the item's entries
-  // pg_lo + 128*w + l and pg_lo + 128*w + 64 + l of the current window w
-  // (pg_lo = the split's first page), and a stage takes its entries with
-  // v_readlane.  The window is one vector load per 128 pages (a scalar read
-  // waited on at every issue, missing the scalar cache every 8 stages, cost
-  // ~4% at 256 stages per item).  Entries past the table row are clamped into
-  // it.
-  int pwlo = 0, pwhi = 0;
-  auto load_window = [&](int w) __attribute__((always_inline)) {
-    const int base = (p_lo >> lsp) + 128 * w;
-    pwlo = pt[min(base + lane, a.max_pages - 1)];
-    pwhi = pt[min(base + 64 + lane, a.max_pages - 1)];
-  };
-  load_window(0);
-
-  const int ctx = min(max(a.ctx_lens[b], 0), a.max_ctx);
-  const int npages = (ctx + 15) >> 4;
-  const int nsplit = max(1, (npages + pps - 1) / pps);
-  // Items past the request's own split count (split >= nsplit) get no pages
-  // and no stages and store nothing; item 0 always exists.
-  const int ncache = max(0, min(npages, p_lo + pps) - p_lo);
-  const int nblk = (split == nsplit - 1) ? (K + 15) >> 4 : 0;
-  const int nvp = ncache + nblk;
-  const int nstage = (nvp + 1) >> 1;
-
   unsigned char* sK = smem;                    // [2][TILE_B]
   unsigned char* sV = smem + 2 * TILE_B;       // [2][TILE_B]
-
-  Acc<T, D, RT> acc;
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    acc.m2[rt] = -INFINITY;
-    acc.l[rt] = 0.f;
-#pragma unroll
-    for (int cc = 0; cc < DPL; ++cc) acc.o[rt][cc] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
   const float c2 = a.scale_log2;
 
   // ---- page descriptors (uniform): byte bases of K and V rows of kv head j0
@@ -311,41 +360,7 @@ __global__ __launch_bounds__(64 * NW, (RT == 2 && sizeof(T) == 2) ? 2 : 1) void 
   const int64_t page_b = a.page_stride * int64_t(sizeof(T));
   const int64_t slab_b = 16 * a.token_stride * int64_t(sizeof(T));
   const int last_phys = a.num_pages - 1;
-  const char* kblk = static_cast<const char*>(a.k_blk) + ((size_t(b) * K) * Hkv + j0) * D * sizeof(T);
-  const char* vblk = static_cast<const char*>(a.v_blk) + ((size_t(b) * K) * Hkv + j0) * D * sizeof(T);
   const size_t blk_page_b = size_t(16) * Hkv * D * sizeof(T);
-  // Stages [0, nhot) are two full context pages each: the hot path.  The rest
-  // (a partial last page, the block's own keys) take the general path.
-  const int nfull = max(0, min(ctx >> 4, p_lo + pps) - p_lo);
-  const int nhot = nfull >> 1;
-  struct Page {
-    const char* k;
-    const char* v;
-    int n;     // valid tokens (0 = absent)
-    bool blk;  // block page (token stride Hkv*D)
-    int cb;    // block-causal block page: 1 + its index among the block pages, else 0
-  };
-  auto page = [&](int vp) __attribute__((always_inline)) -> Page {
-    Page pg{kcj, vcj, 0, false, 0};
-    if (vp < ncache) {
-      const int lp = p_lo + vp;
-      const int phys = pt[lp >> lsp];
-      if (phys >= 0 && phys <= last_phys) {
-        const int64_t off = int64_t(phys) * page_b + int64_t(lp & smask) * slab_b;
-        pg.k = kcj + off;
-        pg.v = vcj + off;
-        pg.n = min(16, ctx - lp * 16);
-      }
-    } else if (vp < nvp) {
-      const int bp = vp - ncache;
-      pg.k = kblk + bp * blk_page_b;
-      pg.v = vblk + bp * blk_page_b;
-      pg.n = min(16, K - bp * 16);
-      pg.blk = true;
-      pg.cb = a.block_causal ? bp + 1 : 0;
-    }
-    return pg;
-  };
 
   // ---- loader geometry: thread -> (page row trow + q*RPP, 16-byte chunk tchunk)
   const int tchunk = threadIdx.x % CPR;
@@ -362,80 +377,6 @@ __global__ __launch_bounds__(64 * NW, (RT == 2 && sizeof(T) == 2) ? 2 : 1) void 
     for (int tt = 0; tt < 2; ++tt) wpos[tt * RND + qq] = Gm::pos(tt * 16 + slot, tchunk) * 16;
   }
 
-
-  // Two full context pages (stage st < nhot): page numbers from the window,
-  // unpredicated loads off scalar page bases (entries clamped into the pool:
-  // never a stray read).
-  constexpr bool kHot = RPP * CPR == NT;
-  auto issue_hot = [&](int st, uint4 (&stk)[NLD], uint4 (&stv)[NLD]) __attribute__((always_inline)) {
-    // slabs 2st and 2st+1 of the split: window entries o0, o1 (the same page
-    // unless pages are 16 tokens; an even o0 keeps both in one lane half)
-    const int q0 = 2 * st, o0 = (q0 >> lsp) & 127, o1 = ((q0 + 1) >> lsp) & 127;
-    const int v = (o0 >> 6) ? pwhi : pwlo;
-    const int ph0 = min(max(__builtin_amdgcn_readlane(v, o0 & 63), 0), last_phys);
-    const int ph1 = min(max(__builtin_amdgcn_readlane(v, o1 & 63), 0), last_phys);
-    const int64_t off0 = int64_t(ph0) * page_b + int64_t(q0 & smask) * slab_b;
-    const int64_t off1 = int64_t(ph1) * page_b + int64_t((q0 + 1) & smask) * slab_b;
-    const char* k0 = kcj + off0;
-    const char* v0 = vcj + off0;
-    const char* k1 = kcj + off1;
-    const char* v1 = vcj + off1;
-#pragma unroll
-    for (int qq = 0; qq < RND; ++qq) {
-      stk[qq] = ld_stream(k0 + coff[qq]);
-      stv[qq] = ld_stream(v0 + coff[qq]);
-      stk[RND + qq] = ld_stream(k1 + coff[qq]);
-      stv[RND + qq] = ld_stream(v1 + coff[qq]);
-    }
-  };
-  auto issue = [&](int st, uint4 (&stk)[NLD], uint4 (&stv)[NLD], int (&nv)[2]) __attribute__((always_inline)) {
-    if (kHot && st < nhot) {
-      issue_hot(st, stk, stv);
-      nv[0] = 16;
-      nv[1] = 16;
-      return;
-    }
-    const Page p0 = page(2 * st), p1 = page(2 * st + 1);
-    // valid-token count, with the block-causal page index above bit 8: a
-    // stage is on the unmasked fast path exactly when both words equal 16
-    nv[0] = p0.n | (p0.cb << 8);
-    nv[1] = p1.n | (p1.cb << 8);
-    // (each page spelled out: selecting between the two by reference would
-    // keep the staging registers from being promoted out of memory)
-#pragma unroll
-    for (int qq = 0; qq < RND; ++qq) {
-      const int slot = trow + qq * RPP;
-      const uint32_t off = p0.blk ? uint32_t(slot) * bts_b + tchunk * 16 : coff[qq];
-      uint4 kx = make_uint4(0, 0, 0, 0), vx = make_uint4(0, 0, 0, 0);  // absent tokens: V must be 0, not NaN
-      if (lactive && slot < p0.n) {
-        kx = *reinterpret_cast<const uint4*>(p0.k + off);
-        vx = *reinterpret_cast<const uint4*>(p0.v + off);
-      }
-      stk[qq] = kx;
-      stv[qq] = vx;
-    }
-#pragma unroll
-    for (int qq = 0; qq < RND; ++qq) {
-      const int slot = trow + qq * RPP;
-      const uint32_t off = p1.blk ? uint32_t(slot) * bts_b + tchunk * 16 : coff[qq];
-      uint4 kx = make_uint4(0, 0, 0, 0), vx = make_uint4(0, 0, 0, 0);
-      if (lactive && slot < p1.n) {
-        kx = *reinterpret_cast<const uint4*>(p1.k + off);
-        vx = *reinterpret_cast<const uint4*>(p1.v + off);
-      }
-      stk[RND + qq] = kx;
-      stv[RND + qq] = vx;
-    }
-  };
-  auto commit = [&](int buf, const uint4 (&stk)[NLD], const uint4 (&stv)[NLD]) __attribute__((always_inline)) {
-    if (lactive) {
-#pragma unroll
-      for (int i = 0; i < NLD; ++i) {
-        *reinterpret_cast<uint4*>(sK + buf * TILE_B + wpos[i]) = stk[i];
-        *reinterpret_cast<uint4*>(sV + buf * TILE_B + wpos[i]) = stv[i];
-      }
-    }
-  };
 
   // ---- consumer geometry (compile-time buffer offsets added per stage); the
   // wave's head starts hl*D elements into a stage row
@@ -457,236 +398,409 @@ __global__ __launch_bounds__(64 * NW, (RT == 2 && sizeof(T) == 2) ? 2 : 1) void 
       vpos[e][h] = Gm::pos(row, e0 / EPC) * 16 + (e0 % EPC) * sizeof(T);
     }
 
+
   // Block position of each query row this lane scores (rows past G*K repeat
   // the last row, as the query loads do).
   int tq[RT];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) tq[rt] = min((wt + rt) * 16 + li, rows - 1) / G;
+  const T* __restrict__ q = static_cast<const T*>(a.q);
 
-  auto compute = [&](int buf, const int (&nv)[2]) __attribute__((always_inline)) {
-    const unsigned char* tk = sK + buf * TILE_B;
-    const unsigned char* tv = sV + buf * TILE_B;
-    const bool partial = nv[0] != 16 || nv[1] != 16;
-    Vec8<T> kop[2][DS];
+  // ---- the range's segments: request b from slab p_lo to p_hi of its keys
+  int b = rs.b, S = rs.S;
+  while (S < rs.B1) {   // uniform
+    const int ctx = ctx_of(a, b);
+    const int npages = (ctx + 15) >> 4;          // context slabs
+    const int L = npages + a.nbk;                // the request's keys, in slabs
+    const int Gb = (L + a.gran - 1) / a.gran;
+    const int p_lo = max(rs.B0 - S, 0) * a.gran;
+    const int p_hi = min((rs.B1 - S) * a.gran, L);
+    // a whole request writes its output; a piece goes to slot 2w + k
+    const bool whole = p_lo == 0 && p_hi == L;
+    const int pslot = 2 * w + (S > rs.B0 ? 1 : 0);
+
+    // This wave's query rows as B operands (row li of tile rt, d group lg + 4*ds);
+    // rows past G*K repeat the last row (their outputs are never stored).
+    Vec8<T> qv[RT][DS];
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
+    for (int rt = 0; rt < RT; ++rt) {
+      const int row = min((wt + rt) * 16 + li, rows - 1);
+      const int t = row / G, gg = row % G;
+      const T* qp = q + ((size_t(b) * K + t) * a.Hq + j * G + gg) * D;
 #pragma unroll
-      for (int ds = 0; ds < DS; ++ds) {
-        if constexpr (sizeof(T) == 2) {
-          kop[tt][ds].v = *reinterpret_cast<const uint4*>(tk + tt * 16 * CPR * 16 + kpos[ds][0]);
+      for (int ds = 0; ds < DS; ++ds) load8(qv[rt][ds], qp + (lg + 4 * ds) * 8);
+    }
+    const int32_t* __restrict__ pt = a.page_table + size_t(b) * a.max_pages;
+    // Page-table window of the hot path: lane l holds the segment's entries
+    // pg_lo + 128*w + l and pg_lo + 128*w + 64 + l of the current window w
+    // (pg_lo = the segment's first page), and a stage takes its entries with
+    // v_readlane.  The window is one vector load per 128 pages (a scalar read
+    // waited on at every issue, missing the scalar cache every 8 stages, cost
+    // ~4% at 256 stages per item).  Entries past the table row are clamped
+    // into it.
+    int pwlo = 0, pwhi = 0;
+    auto load_window = [&](int wi) __attribute__((always_inline)) {
+      const int base = (p_lo >> lsp) + 128 * wi;
+      pwlo = pt[min(base + lane, a.max_pages - 1)];
+      pwhi = pt[min(base + 64 + lane, a.max_pages - 1)];
+    };
+    load_window(0);
+
+    // context slabs, then block slabs from block slab bofs on
+    const int ncache = max(0, min(npages, p_hi) - p_lo);
+    const int bofs = max(p_lo, npages) - npages;
+    const int nblk = max(0, p_hi - max(p_lo, npages));
+    const int nvp = ncache + nblk;
+    const int nstage = (nvp + 1) >> 1;
+
+    Acc<T, D, RT> acc;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      acc.m2[rt] = -INFINITY;
+      acc.l[rt] = 0.f;
+#pragma unroll
+      for (int cc = 0; cc < DPL; ++cc) acc.o[rt][cc] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    const char* kblk = static_cast<const char*>(a.k_blk) + ((size_t(b) * K) * Hkv + j0) * D * sizeof(T);
+    const char* vblk = static_cast<const char*>(a.v_blk) + ((size_t(b) * K) * Hkv + j0) * D * sizeof(T);
+    // Stages [0, nhot) are two full context pages each: the hot path.  The rest
+    // (a partial last page, the block's own keys) take the general path.
+    const int nfull = max(0, min(ctx >> 4, p_hi) - p_lo);
+    const int nhot = nfull >> 1;
+    struct Page {
+      const char* k;
+      const char* v;
+      int n;     // valid tokens (0 = absent)
+      bool blk;  // block page (token stride Hkv*D)
+      int cb;    // block-causal block page: 1 + its index among the block pages, else 0
+    };
+    auto page = [&](int vp) __attribute__((always_inline)) -> Page {
+      Page pg{kcj, vcj, 0, false, 0};
+      if (vp < ncache) {
+        const int lp = p_lo + vp;
+        const int phys = pt[lp >> lsp];
+        if (phys >= 0 && phys <= last_phys) {
+          const int64_t off = int64_t(phys) * page_b + int64_t(lp & smask) * slab_b;
+          pg.k = kcj + off;
+          pg.v = vcj + off;
+          pg.n = min(16, ctx - lp * 16);
+        }
+      } else if (vp < nvp) {
+        const int bp = bofs + vp - ncache;
+        pg.k = kblk + bp * blk_page_b;
+        pg.v = vblk + bp * blk_page_b;
+        pg.n = min(16, K - bp * 16);
+        pg.blk = true;
+        pg.cb = a.block_causal ? bp + 1 : 0;
+      }
+      return pg;
+    };
+
+    // Two full context pages (stage st < nhot): page numbers from the window,
+    // unpredicated loads off scalar page bases (entries clamped into the pool:
+    // never a stray read).
+    constexpr bool kHot = RPP * CPR == NT;
+    auto issue_hot = [&](int st, uint4 (&stk)[NLD], uint4 (&stv)[NLD]) __attribute__((always_inline)) {
+      // slabs 2st and 2st+1 of the split: window entries o0, o1 (the same page
+      // unless pages are 16 tokens; an even o0 keeps both in one lane half)
+      const int q0 = 2 * st, o0 = (q0 >> lsp) & 127, o1 = ((q0 + 1) >> lsp) & 127;
+      const int v = (o0 >> 6) ? pwhi : pwlo;
+      const int ph0 = min(max(__builtin_amdgcn_readlane(v, o0 & 63), 0), last_phys);
+      const int ph1 = min(max(__builtin_amdgcn_readlane(v, o1 & 63), 0), last_phys);
+      const int64_t off0 = int64_t(ph0) * page_b + int64_t(q0 & smask) * slab_b;
+      const int64_t off1 = int64_t(ph1) * page_b + int64_t((q0 + 1) & smask) * slab_b;
+      const char* k0 = kcj + off0;
+      const char* v0 = vcj + off0;
+      const char* k1 = kcj + off1;
+      const char* v1 = vcj + off1;
+#pragma unroll
+      for (int qq = 0; qq < RND; ++qq) {
+        stk[qq] = ld_stream(k0 + coff[qq]);
+        stv[qq] = ld_stream(v0 + coff[qq]);
+        stk[RND + qq] = ld_stream(k1 + coff[qq]);
+        stv[RND + qq] = ld_stream(v1 + coff[qq]);
+      }
+    };
+    auto issue = [&](int st, uint4 (&stk)[NLD], uint4 (&stv)[NLD], int (&nv)[2]) __attribute__((always_inline)) {
+      if (kHot && st < nhot) {
+        issue_hot(st, stk, stv);
+        nv[0] = 16;
+        nv[1] = 16;
+        return;
+      }
+      const Page p0 = page(2 * st), p1 = page(2 * st + 1);
+      // valid-token count, with the block-causal page index above bit 8: a
+      // stage is on the unmasked fast path exactly when both words equal 16
+      nv[0] = p0.n | (p0.cb << 8);
+      nv[1] = p1.n | (p1.cb << 8);
+      // (each page spelled out: selecting between the two by reference would
+      // keep the staging registers from being promoted out of memory)
+#pragma unroll
+      for (int qq = 0; qq < RND; ++qq) {
+        const int slot = trow + qq * RPP;
+        const uint32_t off = p0.blk ? uint32_t(slot) * bts_b + tchunk * 16 : coff[qq];
+        uint4 kx = make_uint4(0, 0, 0, 0), vx = make_uint4(0, 0, 0, 0);  // absent tokens: V must be 0, not NaN
+        if (lactive && slot < p0.n) {
+          kx = *reinterpret_cast<const uint4*>(p0.k + off);
+          vx = *reinterpret_cast<const uint4*>(p0.v + off);
+        }
+        stk[qq] = kx;
+        stv[qq] = vx;
+      }
+#pragma unroll
+      for (int qq = 0; qq < RND; ++qq) {
+        const int slot = trow + qq * RPP;
+        const uint32_t off = p1.blk ? uint32_t(slot) * bts_b + tchunk * 16 : coff[qq];
+        uint4 kx = make_uint4(0, 0, 0, 0), vx = make_uint4(0, 0, 0, 0);
+        if (lactive && slot < p1.n) {
+          kx = *reinterpret_cast<const uint4*>(p1.k + off);
+          vx = *reinterpret_cast<const uint4*>(p1.v + off);
+        }
+        stk[RND + qq] = kx;
+        stv[RND + qq] = vx;
+      }
+    };
+    auto commit = [&](int buf, const uint4 (&stk)[NLD], const uint4 (&stv)[NLD]) __attribute__((always_inline)) {
+      if (lactive) {
+#pragma unroll
+        for (int i = 0; i < NLD; ++i) {
+          *reinterpret_cast<uint4*>(sK + buf * TILE_B + wpos[i]) = stk[i];
+          *reinterpret_cast<uint4*>(sV + buf * TILE_B + wpos[i]) = stv[i];
+        }
+      }
+    };
+
+    auto compute = [&](int buf, const int (&nv)[2]) __attribute__((always_inline)) {
+      const unsigned char* tk = sK + buf * TILE_B;
+      const unsigned char* tv = sV + buf * TILE_B;
+      const bool partial = nv[0] != 16 || nv[1] != 16;
+      Vec8<T> kop[2][DS];
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int ds = 0; ds < DS; ++ds) {
+          if constexpr (sizeof(T) == 2) {
+            kop[tt][ds].v = *reinterpret_cast<const uint4*>(tk + tt * 16 * CPR * 16 + kpos[ds][0]);
+          } else {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              const uint4 x = *reinterpret_cast<const uint4*>(tk + tt * 16 * CPR * 16 + kpos[ds][h]);
+              kop[tt][ds].v[4 * h + 0] = __uint_as_float(x.x);
+              kop[tt][ds].v[4 * h + 1] = __uint_as_float(x.y);
+              kop[tt][ds].v[4 * h + 2] = __uint_as_float(x.z);
+              kop[tt][ds].v[4 * h + 3] = __uint_as_float(x.w);
+            }
+          }
+        }
+      float p[RT][8];
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int ds = 0; ds < DS; ++ds)
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt) sacc[tt] = mma8(kop[tt][ds], qv[rt][ds], sacc[tt]);
+        float sv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sv[e] = sacc[e >> 2][e & 3];
+        if (partial) {
+          // token 4*lg + (e&3) of page e>>2 is kept when it is one of the page's
+          // valid tokens and, on a block-causal block page with index cb-1, its
+          // block position 16*(cb-1) + token is at most this row's position
+          int lim[2];
+#pragma unroll
+          for (int pg = 0; pg < 2; ++pg) {
+            const int n = nv[pg] & 255, cb = nv[pg] >> 8;
+            lim[pg] = cb ? min(n, tq[rt] - 16 * (cb - 1) + 1) : n;
+          }
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (4 * lg + (e & 3) >= lim[e >> 2]) sv[e] = -INFINITY;
+        }
+        const float mx = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), sv[2]),
+                               fmaxf(fmaxf(sv[3], sv[4]), fmaxf(fmaxf(sv[5], sv[6]), sv[7])));
+        const float mx2 = group4_max(mx) * c2;
+        const bool need = mx2 > acc.m2[rt] + kRescaleLog2;
+        if (__any(need)) {
+          if (need) {
+            const float alpha = fast_exp2(acc.m2[rt] - mx2);
+            acc.l[rt] *= alpha;
+#pragma unroll
+            for (int cc = 0; cc < DPL; ++cc) acc.o[rt][cc] *= alpha;
+            acc.m2[rt] = mx2;
+          }
+        }
+        const float nb = acc.m2[rt] == -INFINITY ? 0.f : -acc.m2[rt];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) p[rt][e] = fast_exp2(fmaf(sv[e], c2, nb));
+        acc.l[rt] += ((p[rt][0] + p[rt][1]) + (p[rt][2] + p[rt][3])) +
+                     ((p[rt][4] + p[rt][5]) + (p[rt][6] + p[rt][7]));
+      }
+      // O^T += V^T . P^T: lane reads 8 token rows x D/16 values, transposes in registers
+      VRow<T, DPL> vr[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const unsigned char* base = tv + (e >> 2) * 16 * CPR * 16;
+        if constexpr (sizeof(T) == 2 && DPL == 8) {
+          vr[e].v = *reinterpret_cast<const uint4*>(base + vpos[e & 3][0]);
+        } else if constexpr (sizeof(T) == 2) {
+          vr[e].v = *reinterpret_cast<const uint2*>(base + vpos[e & 3][0]);
         } else {
 #pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const uint4 x = *reinterpret_cast<const uint4*>(tk + tt * 16 * CPR * 16 + kpos[ds][h]);
-            kop[tt][ds].v[4 * h + 0] = __uint_as_float(x.x);
-            kop[tt][ds].v[4 * h + 1] = __uint_as_float(x.y);
-            kop[tt][ds].v[4 * h + 2] = __uint_as_float(x.z);
-            kop[tt][ds].v[4 * h + 3] = __uint_as_float(x.w);
+          for (int h = 0; h < DPL / 4; ++h) {
+            const uint4 x = *reinterpret_cast<const uint4*>(base + vpos[e & 3][h]);
+            vr[e].v[4 * h + 0] = __uint_as_float(x.x);
+            vr[e].v[4 * h + 1] = __uint_as_float(x.y);
+            vr[e].v[4 * h + 2] = __uint_as_float(x.z);
+            vr[e].v[4 * h + 3] = __uint_as_float(x.w);
           }
         }
       }
-    float p[RT][8];
+      Vec8<T> vt[DPL];
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+      for (int cc = 0; cc < DPL; ++cc) vtrans<DPL>(vt[cc], vr, cc);
 #pragma unroll
-      for (int ds = 0; ds < DS; ++ds)
+      for (int rt = 0; rt < RT; ++rt) {
+        Vec8<T> pv;
+        pack_p(pv, p[rt]);
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt) sacc[tt] = mma8(kop[tt][ds], qv[rt][ds], sacc[tt]);
-      float sv[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) sv[e] = sacc[e >> 2][e & 3];
-      if (partial) {
-        // token 4*lg + (e&3) of page e>>2 is kept when it is one of the page's
-        // valid tokens and, on a block-causal block page with index cb-1, its
-        // block position 16*(cb-1) + token is at most this row's position
-        int lim[2];
-#pragma unroll
-        for (int pg = 0; pg < 2; ++pg) {
-          const int n = nv[pg] & 255, cb = nv[pg] >> 8;
-          lim[pg] = cb ? min(n, tq[rt] - 16 * (cb - 1) + 1) : n;
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (4 * lg + (e & 3) >= lim[e >> 2]) sv[e] = -INFINITY;
+        for (int cc = 0; cc < DPL; ++cc) acc.o[rt][cc] = mma8(vt[cc], pv, acc.o[rt][cc]);
       }
-      const float mx = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), sv[2]),
-                             fmaxf(fmaxf(sv[3], sv[4]), fmaxf(fmaxf(sv[5], sv[6]), sv[7])));
-      const float mx2 = group4_max(mx) * c2;
-      const bool need = mx2 > acc.m2[rt] + kRescaleLog2;
-      if (__any(need)) {
-        if (need) {
-          const float alpha = fast_exp2(acc.m2[rt] - mx2);
-          acc.l[rt] *= alpha;
-#pragma unroll
-          for (int cc = 0; cc < DPL; ++cc) acc.o[rt][cc] *= alpha;
-          acc.m2[rt] = mx2;
-        }
-      }
-      const float nb = acc.m2[rt] == -INFINITY ? 0.f : -acc.m2[rt];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) p[rt][e] = fast_exp2(fmaf(sv[e], c2, nb));
-      acc.l[rt] += ((p[rt][0] + p[rt][1]) + (p[rt][2] + p[rt][3])) +
-                   ((p[rt][4] + p[rt][5]) + (p[rt][6] + p[rt][7]));
-    }
-    // O^T += V^T . P^T: lane reads 8 token rows x D/16 values, transposes in registers
-    VRow<T, DPL> vr[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const unsigned char* base = tv + (e >> 2) * 16 * CPR * 16;
-      if constexpr (sizeof(T) == 2 && DPL == 8) {
-        vr[e].v = *reinterpret_cast<const uint4*>(base + vpos[e & 3][0]);
-      } else if constexpr (sizeof(T) == 2) {
-        vr[e].v = *reinterpret_cast<const uint2*>(base + vpos[e & 3][0]);
-      } else {
-#pragma unroll
-        for (int h = 0; h < DPL / 4; ++h) {
-          const uint4 x = *reinterpret_cast<const uint4*>(base + vpos[e & 3][h]);
-          vr[e].v[4 * h + 0] = __uint_as_float(x.x);
-          vr[e].v[4 * h + 1] = __uint_as_float(x.y);
-          vr[e].v[4 * h + 2] = __uint_as_float(x.z);
-          vr[e].v[4 * h + 3] = __uint_as_float(x.w);
-        }
-      }
-    }
-    Vec8<T> vt[DPL];
-#pragma unroll
-    for (int cc = 0; cc < DPL; ++cc) vtrans<DPL>(vt[cc], vr, cc);
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      Vec8<T> pv;
-      pack_p(pv, p[rt]);
-#pragma unroll
-      for (int cc = 0; cc < DPL; ++cc) acc.o[rt][cc] = mma8(vt[cc], pv, acc.o[rt][cc]);
-    }
-  };
+    };
 
-  // Software pipeline: PF stages of loads in flight in registers, two LDS
-  // buffers.  Stage st goes to LDS buffer st&1 (last read by stage st-2, which
-  // every wave finished before the previous barrier); stage st+PF is then
-  // issued into the registers just freed; one barrier; then the math.
-  uint4 stk[PF][NLD], stv[PF][NLD];
-  int nv[PF][2];
-  int st0 = 0;
-  if (kHot && nhot >= 2 * PF) {  // uniform over the workgroup
-    // Hot loop: every stage it issues is two full context pages, so every
-    // slot issues its loads on every path and each wait before a commit
-    // counts exactly the newer stage in flight.  The next page-table window
-    // is loaded into (pnlo, pnhi) just before the last stage of the current
-    // one is issued; at the window's first stage an explicit wait for all
-    // but that stage's loads makes it current.  The page numbers read by
-    // every issue are thus never a pending load, and the K/V stream never
-    // drains for them (a full wait there cost one round trip per 64 stages).
-    // vmcnt(2 * NLD): one stage's loads may stay pending (count bits 3:0 and 15:14)
-    static_assert(2 * NLD < 64, "vmcnt field");
-    constexpr int kWinWait = 0x0F70 | ((2 * NLD) & 15) | (((2 * NLD) >> 4) << 14);
-    const int wmask = (64 << lsp) - 1;
-    int pnlo = 0, pnhi = 0;
-    // The first PF stages go out strictly in slot order.  Interleaved by the
-    // scheduler, the loop's wait bookkeeping at its header must assume slot 0
-    // may be the newest load, and it then waits for every load in flight
-    // before each slot-0 issue, every PF stages of the whole loop.
-    static_for<0, PF>([&](auto P) __attribute__((always_inline)) {
-      constexpr int pp = decltype(P)::value;
-      issue_hot(pp, stk[pp], stv[pp]);
-      __builtin_amdgcn_sched_barrier(0);
-    });
-    for (; st0 + 2 * PF <= nhot; st0 += PF) {
+    // Software pipeline: PF stages of loads in flight in registers, two LDS
+    // buffers.  Stage st goes to LDS buffer st&1 (last read by stage st-2, which
+    // every wave finished before the previous barrier); stage st+PF is then
+    // issued into the registers just freed; one barrier; then the math.
+    uint4 stk[PF][NLD], stv[PF][NLD];
+    int nv[PF][2];
+    int st0 = 0;
+    if (kHot && nhot >= 2 * PF) {  // uniform over the workgroup
+      // Hot loop: every stage it issues is two full context pages, so every
+      // slot issues its loads on every path and each wait before a commit
+      // counts exactly the newer stage in flight.  The next page-table window
+      // is loaded into (pnlo, pnhi) just before the last stage of the current
+      // one is issued; at the window's first stage an explicit wait for all
+      // but that stage's loads makes it current.  The page numbers read by
+      // every issue are thus never a pending load, and the K/V stream never
+      // drains for them (a full wait there cost one round trip per 64 stages).
+      // vmcnt(2 * NLD): one stage's loads may stay pending (count bits 3:0 and 15:14)
+      static_assert(2 * NLD < 64, "vmcnt field");
+      constexpr int kWinWait = 0x0F70 | ((2 * NLD) & 15) | (((2 * NLD) >> 4) << 14);
+      const int wmask = (64 << lsp) - 1;
+      int pnlo = 0, pnhi = 0;
+      // The first PF stages go out strictly in slot order.  Interleaved by the
+      // scheduler, the loop's wait bookkeeping at its header must assume slot 0
+      // may be the newest load, and it then waits for every load in flight
+      // before each slot-0 issue, every PF stages of the whole loop.
       static_for<0, PF>([&](auto P) __attribute__((always_inline)) {
         constexpr int pp = decltype(P)::value;
-        const int sn = st0 + pp + PF;   // < nhot
-        commit(pp & 1, stk[pp], stv[pp]);
-        if ((sn & wmask) == 0) {   // first stage of a 128-page window, loaded one step ago
-          __builtin_amdgcn_s_waitcnt(kWinWait);
-          pwlo = pnlo;
-          pwhi = pnhi;
-        } else if (((sn + 1) & wmask) == 0) {   // last stage of this window: fetch the next
-          const int base = (p_lo >> lsp) + 128 * ((sn + 1) >> (6 + lsp));
-          pnlo = pt[min(base + lane, a.max_pages - 1)];
-          pnhi = pt[min(base + 64 + lane, a.max_pages - 1)];
+        issue_hot(pp, stk[pp], stv[pp]);
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      __syncthreads();   // LDS free: the previous segment's last stage (or the plan scan) is done
+      for (; st0 + 2 * PF <= nhot; st0 += PF) {
+        static_for<0, PF>([&](auto P) __attribute__((always_inline)) {
+          constexpr int pp = decltype(P)::value;
+          const int sn = st0 + pp + PF;   // < nhot
+          commit(pp & 1, stk[pp], stv[pp]);
+          if ((sn & wmask) == 0) {   // first stage of a 128-page window, loaded one step ago
+            __builtin_amdgcn_s_waitcnt(kWinWait);
+            pwlo = pnlo;
+            pwhi = pnhi;
+          } else if (((sn + 1) & wmask) == 0) {   // last stage of this window: fetch the next
+            const int base = (p_lo >> lsp) + 128 * ((sn + 1) >> (6 + lsp));
+            pnlo = pt[min(base + lane, a.max_pages - 1)];
+            pnhi = pt[min(base + 64 + lane, a.max_pages - 1)];
+          }
+          issue_hot(sn, stk[pp], stv[pp]);
+          __syncthreads();
+          const int full[2] = {16, 16};
+          compute(pp & 1, full);
+        });
+      }
+#pragma unroll
+      for (int pp = 0; pp < PF; ++pp) nv[pp][0] = nv[pp][1] = 16;
+    } else {
+      static_for<0, PF>([&](auto P) __attribute__((always_inline)) {
+        constexpr int pp = decltype(P)::value;
+        if (pp < nstage) issue(pp, stk[pp], stv[pp], nv[pp]);
+      });
+      __syncthreads();   // LDS free: the previous segment's last stage (or the plan scan) is done
+    }
+    // the remaining stages: the hot tail, a partial last page, the block's keys
+    for (; st0 < nstage; st0 += PF) {
+      static_for<0, PF>([&](auto P) __attribute__((always_inline)) {
+        constexpr int pp = decltype(P)::value;
+        const int st = st0 + pp;
+        if (st < nstage) {  // uniform over the workgroup
+          commit(pp & 1, stk[pp], stv[pp]);
+          const int n0 = nv[pp][0], n1 = nv[pp][1];
+          if (st + PF < nstage) {
+            const int sn = st + PF;
+            if ((sn & ((64 << lsp) - 1)) == 0 && sn < nhot) load_window(sn >> (6 + lsp));  // next window
+            issue(sn, stk[pp], stv[pp], nv[pp]);
+          }
+          __syncthreads();
+          const int nn[2] = {n0, n1};
+          compute(pp & 1, nn);
         }
-        issue_hot(sn, stk[pp], stv[pp]);
-        __syncthreads();
-        const int full[2] = {16, 16};
-        compute(pp & 1, full);
       });
     }
-#pragma unroll
-    for (int pp = 0; pp < PF; ++pp) nv[pp][0] = nv[pp][1] = 16;
-  } else {
-    static_for<0, PF>([&](auto P) __attribute__((always_inline)) {
-      constexpr int pp = decltype(P)::value;
-      if (pp < nstage) issue(pp, stk[pp], stv[pp], nv[pp]);
-    });
-  }
-  // the remaining stages: the hot tail, a partial last page, the block's keys
-  for (; st0 < nstage; st0 += PF) {
-    static_for<0, PF>([&](auto P) __attribute__((always_inline)) {
-      constexpr int pp = decltype(P)::value;
-      const int st = st0 + pp;
-      if (st < nstage) {  // uniform over the workgroup
-        commit(pp & 1, stk[pp], stv[pp]);
-        const int n0 = nv[pp][0], n1 = nv[pp][1];
-        if (st + PF < nstage) {
-          const int sn = st + PF;
-          if ((sn & ((64 << lsp) - 1)) == 0 && sn < nhot) load_window(sn >> (6 + lsp));  // next window
-          issue(sn, stk[pp], stv[pp], nv[pp]);
-        }
-        __syncthreads();
-        const int nn[2] = {n0, n1};
-        compute(pp & 1, nn);
-      }
-    });
-  }
 
-  // store: lane holds row li of each tile and d = (4*lg + r)*DPL + cc
+    // store: lane holds row li of each tile and d = (4*lg + r)*DPL + cc
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    const float lsum = group4_sum(acc.l[rt]);
-    const int row = (wt + rt) * 16 + li;
-    if (row >= rows || nstage == 0) continue;  // nstage == 0: no such split
-    if (nsplit == 1) {
-      const int t = row / G, gg = row % G;
-      T* o = static_cast<T*>(a.out) + ((size_t(b) * K + t) * a.Hq + j * G + gg) * D;
-      const float inv = 1.f / lsum;
+    for (int rt = 0; rt < RT; ++rt) {
+      const float lsum = group4_sum(acc.l[rt]);
+      const int row = (wt + rt) * 16 + li;
+      if (row >= rows || nstage == 0) continue;
+      if (whole) {
+        const int t = row / G, gg = row % G;
+        T* o = static_cast<T*>(a.out) + ((size_t(b) * K + t) * a.Hq + j * G + gg) * D;
+        const float inv = 1.f / lsum;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        T* dst = o + (4 * lg + r) * DPL;
-        if constexpr (sizeof(T) == 2) {
-          if constexpr (DPL == 8) {
-            uint4 w;
-            w.x = pack_bf16x2(acc.o[rt][0][r] * inv, acc.o[rt][1][r] * inv);
-            w.y = pack_bf16x2(acc.o[rt][2][r] * inv, acc.o[rt][3][r] * inv);
-            w.z = pack_bf16x2(acc.o[rt][4][r] * inv, acc.o[rt][5][r] * inv);
-            w.w = pack_bf16x2(acc.o[rt][6][r] * inv, acc.o[rt][7][r] * inv);
-            *reinterpret_cast<uint4*>(dst) = w;
+        for (int r = 0; r < 4; ++r) {
+          T* dst = o + (4 * lg + r) * DPL;
+          if constexpr (sizeof(T) == 2) {
+            if constexpr (DPL == 8) {
+              uint4 pk;
+              pk.x = pack_bf16x2(acc.o[rt][0][r] * inv, acc.o[rt][1][r] * inv);
+              pk.y = pack_bf16x2(acc.o[rt][2][r] * inv, acc.o[rt][3][r] * inv);
+              pk.z = pack_bf16x2(acc.o[rt][4][r] * inv, acc.o[rt][5][r] * inv);
+              pk.w = pack_bf16x2(acc.o[rt][6][r] * inv, acc.o[rt][7][r] * inv);
+              *reinterpret_cast<uint4*>(dst) = pk;
+            } else {
+              uint2 pk;
+              pk.x = pack_bf16x2(acc.o[rt][0][r] * inv, acc.o[rt][1][r] * inv);
+              pk.y = pack_bf16x2(acc.o[rt][2][r] * inv, acc.o[rt][3][r] * inv);
+              *reinterpret_cast<uint2*>(dst) = pk;
+            }
           } else {
-            uint2 w;
-            w.x = pack_bf16x2(acc.o[rt][0][r] * inv, acc.o[rt][1][r] * inv);
-            w.y = pack_bf16x2(acc.o[rt][2][r] * inv, acc.o[rt][3][r] * inv);
-            *reinterpret_cast<uint2*>(dst) = w;
+#pragma unroll
+            for (int cc = 0; cc < DPL; cc += 4)
+              *reinterpret_cast<float4*>(reinterpret_cast<float*>(dst) + cc) =
+                  make_float4(acc.o[rt][cc][r] * inv, acc.o[rt][cc + 1][r] * inv,
+                              acc.o[rt][cc + 2][r] * inv, acc.o[rt][cc + 3][r] * inv);
           }
-        } else {
+        }
+      } else {
+        const size_t prow = (size_t(pslot) * Hkv + j) * rows + row;
+        float* po = a.part_o + prow * D;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float* dst = po + (4 * lg + r) * DPL;
 #pragma unroll
           for (int cc = 0; cc < DPL; cc += 4)
-            *reinterpret_cast<float4*>(reinterpret_cast<float*>(dst) + cc) =
-                make_float4(acc.o[rt][cc][r] * inv, acc.o[rt][cc + 1][r] * inv,
-                            acc.o[rt][cc + 2][r] * inv, acc.o[rt][cc + 3][r] * inv);
+            *reinterpret_cast<float4*>(dst + cc) =
+                make_float4(acc.o[rt][cc][r], acc.o[rt][cc + 1][r], acc.o[rt][cc + 2][r], acc.o[rt][cc + 3][r]);
         }
+        if (lg == 0) *reinterpret_cast<float2*>(a.part_ml + prow * 2) = make_float2(acc.m2[rt], lsum);
       }
-    } else {
-      const size_t prow = (size_t(item) * Hkv + j) * rows + row;
-      float* po = a.part_o + prow * D;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float* dst = po + (4 * lg + r) * DPL;
-#pragma unroll
-        for (int cc = 0; cc < DPL; cc += 4)
-          *reinterpret_cast<float4*>(dst + cc) =
-              make_float4(acc.o[rt][cc][r], acc.o[rt][cc + 1][r], acc.o[rt][cc + 2][r], acc.o[rt][cc + 3][r]);
-      }
-      if (lg == 0) *reinterpret_cast<float2*>(a.part_ml + prow * 2) = make_float2(acc.m2[rt], lsum);
     }
+
+    S += Gb;
+    ++b;
   }
 }
 
@@ -717,8 +831,8 @@ template <typename T, int D, int RT, int NW, int HP = 1>
 static hipError_t launch_attn_cfg(hipStream_t st, const AttnArgs& a) {
   const size_t lds = AttnLds<T, HP * D>::bytes;
   auto kern = k_block_attn<T, D, RT, NW, kPrefetch, HP>;
-  // one workgroup per (item, head group), plus the plan writer
-  hipLaunchKernelGGL(kern, dim3(a.max_items * (a.Hkv / HP) + 1), dim3(64 * NW), lds, st, a);
+  // one workgroup per (range, head group), plus the plan writer
+  hipLaunchKernelGGL(kern, dim3(a.w_max * (a.Hkv / HP) + 1), dim3(64 * NW), lds, st, a);
   return hipGetLastError();
 }
 
@@ -727,18 +841,19 @@ static hipError_t launch_attn_d(hipStream_t st, const AttnArgs& a) {
   if (a.rows <= 16) return launch_attn_cfg<T, D, 1, 1>(st, a);
   if (a.rows <= 32) return launch_attn_cfg<T, D, 1, 2>(st, a);
   // Two adjacent kv heads per workgroup (bf16, D = 128, 33..64 rows per head,
-  // splits of at least 128 slabs): each stage row is then one 512-byte piece
-  // of the token's K (V) instead of two 256-byte pieces read by two
-  // workgroups, which a read probe of the pattern measures at 7.1-7.2 TB/s
-  // against 6.6 TB/s (C = 128: 687 -> 651 us).  With short splits (small C)
-  // halving the workgroup count costs more than the pieces gain.
+  // ranges of about 128 slabs or more, as the host planned): each stage row is
+  // then one 512-byte piece of the token's K (V) instead of two 256-byte
+  // pieces read by two workgroups, which a read probe of the pattern measures
+  // at 7.1-7.2 TB/s against 6.6 TB/s (C = 128: 687 -> 651 us).  With short
+  // ranges (small C) halving the workgroup count costs more than the pieces
+  // gain.
   if constexpr (std::is_same<T, bf16_t>::value && D == 128) {
-    if (a.rows <= 64 && a.Hkv % 2 == 0 && a.head_stride == D && a.pps >= 128)
+    if (a.head_pair && head_pair_fits(a.rows, a.Hkv, a.head_stride, 1, D))
       return launch_attn_cfg<T, D, 1, 8, 2>(st, a);
   }
   if (a.rows <= 64) return launch_attn_cfg<T, D, 1, 4>(st, a);
   if (a.rows <= 128) return launch_attn_cfg<T, D, 2, 4>(st, a);
-  return launch_attn_cfg<T, D, 4, 4>(st, a);
+  return launch_attn_cfg<T, D, 2, 8>(st, a);
 }
 
 size_t attn_lds_bytes(int dtype, int D, int rows, int K) {
@@ -748,6 +863,10 @@ size_t attn_lds_bytes(int dtype, int D, int rows, int K) {
   return D == 64 ? AttnLds<float, 64>::bytes : AttnLds<float, 128>::bytes;
 }
 
+bool head_pair_fits(int rows, int Hkv, int64_t head_stride, int dtype, int D) {
+  return dtype == 1 && D == 128 && rows > 32 && rows <= 64 && Hkv % 2 == 0 && head_stride == D;
+}
+
 template <typename T, int D, int LPO, int U>
 static hipError_t launch_merge_cfg(hipStream_t st, const AttnArgs& a) {
   const dim3 mg(a.C * a.Hkv, (a.rows * (D / 4) + 256 / LPO - 1) / (256 / LPO));
@@ -755,9 +874,10 @@ static hipError_t launch_merge_cfg(hipStream_t st, const AttnArgs& a) {
   return hipGetLastError();
 }
 
+// LPO and U by the most pieces a request can have (one per range).
 template <typename T, int D>
 static hipError_t launch_merge(hipStream_t st, const AttnArgs& a) {
-  const int ms = a.max_splits;
+  const int ms = a.w_max;
   if (ms <= 4) return launch_merge_cfg<T, D, 1, 4>(st, a);
   if (ms <= 8) return launch_merge_cfg<T, D, 1, 8>(st, a);
   if (ms <= 16) return launch_merge_cfg<T, D, 4, 4>(st, a);
@@ -772,7 +892,7 @@ hipError_t launch_block_attn(hipStream_t st, int dtype, const AttnArgs& a, bool 
     e = a.D == 64 ? launch_attn_d<float, 64>(st, a) : launch_attn_d<float, 128>(st, a);
   }
   if (e != hipSuccess) return e;
-  if (merge && a.max_items > a.C) {  // some request may have several splits
+  if (merge && a.w_max > 1) {  // some request may span several ranges
     if (dtype == 1) {
       e = a.D == 64 ? launch_merge<bf16_t, 64>(st, a) : launch_merge<bf16_t, 128>(st, a);
     } else {

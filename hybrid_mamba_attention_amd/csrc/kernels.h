@@ -22,11 +22,20 @@ struct AttnArgs {
   int C, K, Hq, Hkv, G, D, rows;  // rows = G * K query rows per kv head
   float scale_log2;               // softmax scale * log2(e)
   void* out;
-  int32_t* plan;                  // workspace head: the split plan (written by the last block)
-  float* part_o;                  // [max_items, Hkv, rows, D], item = request * max_splits + split
-  float* part_ml;                 // [max_items, Hkv, rows, 2]
-  int max_items;                  // C * max_splits
-  int pps, max_splits;            // 16-token slabs per split; splits of a max_ctx request
+  int32_t* plan;                  // workspace head: the work plan (written by the last block)
+  float* part_o;                  // [2 * w_max, Hkv, rows, D]: piece of range w's segment k at slot 2w + k
+  float* part_ml;                 // [2 * w_max, Hkv, rows, 2]
+  // Work plan: each request's keys are its context slabs (16 tokens) then
+  // nbk block slabs, counted in granules of `gran` slabs; the batch's
+  // granules are cut into W <= w_max equal ranges, one workgroup per (range,
+  // kv head group).  W = ceil(T / range_gran) for fixed ranges, else
+  // min(w_max, ceil(T / min_gran)) (T = the batch's granules).
+  int w_max;
+  int gran;
+  int range_gran;                 // 0 = automatic
+  int min_gran;
+  int nbk;
+  int head_pair;                  // 1: two kv heads per workgroup when the shape allows (long ranges)
   int block_causal;               // 1: block query t sees block keys s <= t only
   int lsp;                        // log2(page size / 16)
 };
@@ -35,6 +44,8 @@ struct AttnArgs {
 hipError_t launch_block_attn(hipStream_t st, int dtype, const AttnArgs& a, bool merge = true);
 // dynamic LDS bytes of the attention kernel for a shape (host planning only)
 size_t attn_lds_bytes(int dtype, int D, int rows, int K);
+// whether the two-heads-per-workgroup form exists for a shape
+bool head_pair_fits(int rows, int Hkv, int64_t head_stride, int dtype, int D);
 
 struct SsdArgs {
   const void* x;

@@ -1,7 +1,7 @@
-// a4: the log-sum-exp merge of a request's split partials, one (request, kv
-// head) and one slab of output columns per workgroup.  A device function so
-// that k_attn_merge and the drafter layer's combined scan + merge launch
-// (ssd.hip) run the same code.
+// a4: the log-sum-exp merge of a request's pieces (the partials its work
+// ranges left), one (request, kv head) and one slab of output columns per
+// workgroup.  A device function so that k_attn_merge and the drafter layer's
+// combined scan + merge launch (ssd.hip) run the same code.
 #pragma once
 
 #include "common.h"
@@ -10,27 +10,34 @@
 namespace hspec {
 
 // LPO lanes (1 or 4) per (row, 4 output columns), in log2 units like the
-// partials: lane q takes splits q, q+LPO, ..., loading U of them at a time
+// partials: lane q takes pieces q, q+LPO, ..., loading U of them at a time
 // (clamped indices, no data-dependent branches) and keeping a running
 // maximum; with LPO = 4 the quad then combines its four (m, l, O) with two
-// xor-shuffles.  A request with up to LPO*U splits costs one round of
-// independent loads; LPO and U are sized to the largest split count at launch
-// so few loads are clamped repeats and few lanes idle.
+// xor-shuffles.  A request with up to LPO*U pieces costs one round of
+// independent loads; LPO and U are sized to the most pieces a request can
+// have at launch, so few loads are clamped repeats and few lanes idle.
+// The request's pieces come from the work plan the attention grid wrote:
+// piece i sits in slot 2*(w_first + i) (+1 for the first piece when the
+// request starts after its first range's first granule).
 // (bx, by): the merge grid's block index (request * Hkv + kv head, column slab).
 template <typename T, int D, int LPO, int U>
 __device__ __forceinline__ void attn_merge_block(const AttnArgs& a, int bx, int by) {
   constexpr int OPB = 256 / LPO;  // outputs per block
-  const int Hkv = a.Hkv;
+  const int Hkv = a.Hkv, C = a.C;
   const int b = bx / Hkv, j = bx % Hkv;
-  const int ctx = min(max(a.ctx_lens[b], 0), a.max_ctx);
-  const int ns = max(1, (((ctx + 15) >> 4) + a.pps - 1) / a.pps);
-  if (ns <= 1) return;
+  const int32_t* plan = a.plan;
+  const int ns = plan[4 + 2 * C + b];
+  if (ns <= 1) return;   // finished by its one range
+  const int wf = plan[4 + C + b];
+  const int k0 = plan[4 + 3 * C + wf] < plan[4 + b] ? 1 : 0;
   const int rows = a.rows, G = a.G, K = a.K;
   const int idx = by * OPB + int(threadIdx.x) / LPO, q = int(threadIdx.x) % LPO;
   const bool live = idx < rows * (D / 4);  // whole quads agree
   const int row = min(idx / (D / 4), rows - 1), d4 = idx % (D / 4);
-  const size_t stride = size_t(Hkv) * rows;  // partial rows between consecutive splits
-  const size_t p0 = (size_t(b) * a.max_splits * Hkv + j) * rows + row;
+  auto prow = [&](int i) -> size_t {     // partial row of piece i
+    const int slot = 2 * (wf + i) + (i == 0 ? k0 : 0);
+    return (size_t(slot) * Hkv + j) * rows + row;
+  };
   float M = -INFINITY, Ls = 0.f;
   float4 acc = make_float4(0, 0, 0, 0);
   for (int s0 = q; s0 < ns; s0 += LPO * U) {
@@ -38,11 +45,15 @@ __device__ __forceinline__ void attn_merge_block(const AttnArgs& a, int bx, int 
     float4 v[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const size_t pr = p0 + size_t(min(s0 + LPO * u, ns - 1)) * stride;
+      const size_t pr = prow(min(s0 + LPO * u, ns - 1));
       ml[u] = *reinterpret_cast<const float2*>(a.part_ml + pr * 2);
       v[u] = reinterpret_cast<const float4*>(a.part_o + pr * D)[d4];
     }
-    float mr = M;  // every split holds at least one token: its maximum is finite
+    // A piece's maximum is -inf when the block-causal mask hides all its keys
+    // from this row (a piece of block keys only); such a piece weighs 0.  The
+    // request's first piece always holds a key every row sees (its context or
+    // block key 0), so the total weight is positive.
+    float mr = M;
 #pragma unroll
     for (int u = 0; u < U; ++u)
       if (s0 + LPO * u < ns) mr = fmaxf(mr, ml[u].x);
@@ -51,13 +62,13 @@ __device__ __forceinline__ void attn_merge_block(const AttnArgs& a, int bx, int 
     Ls *= sc;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const float f = s0 + LPO * u < ns ? fast_exp2(ml[u].x - mr) : 0.f;
+      const float f = (s0 + LPO * u < ns && ml[u].x != -INFINITY) ? fast_exp2(ml[u].x - mr) : 0.f;
       acc.x += f * v[u].x; acc.y += f * v[u].y; acc.z += f * v[u].z; acc.w += f * v[u].w;
       Ls += f * ml[u].y;
     }
     M = mr;
   }
-  // combine the quad (a lane without splits has M = -inf, Ls = 0, acc = 0)
+  // combine the quad (a lane without pieces has M = -inf, Ls = 0, acc = 0)
 #pragma unroll
   for (int x = 1; x < LPO; x <<= 1) {
     const float Mo = __shfl_xor(M, x, 64), Lo = __shfl_xor(Ls, x, 64);

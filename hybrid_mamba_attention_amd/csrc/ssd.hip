@@ -307,7 +307,7 @@ __global__ __launch_bounds__(256) void k_ssd_scan(SsdArgs a) {
 }
 
 // Workgroups [0, n_scan) run the scan, the rest the merge of the attention's
-// split partials (grid (C * Hkv) x slabs, flattened request-major).  The two
+// partials (grid (C * Hkv) x slabs, flattened request-major).  The two
 // are independent: the scan needs the projected state, the merge the
 // attention's partials, both written by earlier launches on the stream.
 template <int NMAX, int LPO, int U>
@@ -363,11 +363,12 @@ hipError_t launch_ssd_scan(hipStream_t st, int dtype, const SsdArgs& a) {
 }
 
 bool scan_merge_fits(int dtype, const SsdArgs& s, const AttnArgs& m) {
-  return dtype == 1 && !s.zx && s.N % 4 == 0 && m.D == 128 && m.max_items > m.C;
+  return dtype == 1 && !s.zx && s.N % 4 == 0 && m.D == 128 && m.w_max > 1;
 }
 
 // The merge part takes the configuration k_attn_merge would (LPO lanes per
-// output quad, U splits per round of loads, by the largest split count).
+// output quad, U pieces per round of loads, by the most pieces a request can
+// have).
 template <int NMAX, int LPO, int U>
 static hipError_t launch_scan_merge_cfg(hipStream_t st, const SsdArgs& s, const AttnArgs& m) {
   const int n_scan = s.C * (s.H / ssd_heads_per_block(s.H, s.ng, s.P));
@@ -380,7 +381,7 @@ static hipError_t launch_scan_merge_cfg(hipStream_t st, const SsdArgs& s, const 
 
 template <int NMAX>
 static hipError_t launch_scan_merge_n(hipStream_t st, const SsdArgs& s, const AttnArgs& m) {
-  const int ms = m.max_splits;
+  const int ms = m.w_max;   // the most pieces a request can have
   if (ms <= 4) return launch_scan_merge_cfg<NMAX, 1, 4>(st, s, m);
   if (ms <= 8) return launch_scan_merge_cfg<NMAX, 1, 8>(st, s, m);
   if (ms <= 16) return launch_scan_merge_cfg<NMAX, 4, 4>(st, s, m);

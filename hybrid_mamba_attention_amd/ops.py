@@ -328,6 +328,13 @@ def _attn_call(L, stream, q, k_blk, v_blk, k_cache, v_cache, page_table, ctx_len
         int(bool(block_causal)), _addr(out if out is not None else q), ws, ctypes.byref(ws_bytes))
 
 
+def plan_of(workspace: torch.Tensor, C: int) -> torch.Tensor:
+    """The int32 work plan at the head of an attention workspace:
+    [W, granule slabs, C, w_max], S_b, first range, pieces (C each), B_0..B_w_max."""
+    w_max = int(workspace[12:16].view(torch.int32).item())
+    return workspace[:4 * (4 + 3 * C + w_max + 1)].view(torch.int32)
+
+
 def attn_workspace_bytes(q, k_blk, v_blk, k_cache, v_cache, page_table, ctx_lens, *, max_ctx,
                          kv_split_pages=0, scale=0.0, block_causal=False, layout="NHD") -> int:
     n = _sz(0)
@@ -468,11 +475,8 @@ class DraftLayer:
             self._graph = None
 
     def plan(self) -> torch.Tensor:
-        """The int32 split plan at the head of the workspace (see include/hspec.h)."""
-        w = self.workspace
-        C = self._args.C
-        M = int(w[12:16].view(torch.int32).item())
-        return w[:4 * (4 + 2 * C + 2 * M)].view(torch.int32)
+        """The int32 work plan at the head of the workspace (see include/hspec.h)."""
+        return plan_of(self.workspace, self._args.C)
 
 
 def draft_layer(**kw):

@@ -227,7 +227,7 @@ int hspec_draft_layer(void* stream, const hspec_layer_args* a, size_t* required_
  * so calls that overlap in time on one GPU (concurrent streams, or two
  * threads) race: serialise them.
  */
-#define HSPEC_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+#define HSPEC_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
 int hspec_draft_layer_noalloc(void* stream, const hspec_layer_args* a);
 
 /* Executable HIP graph of a layer or a stack (see hspec_draft_stack_graph). */

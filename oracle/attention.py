@@ -25,9 +25,9 @@ Block-causal variant (block_causal=True): block query t sees every context
 key and the block keys s <= t only (mask inside the block); the no-mask form
 above is the default reading.
 
-block_attention is the definition.  block_attention_splits restates it as
-split-KV: each split of the plan yields a partial (running max m, sum l,
-unnormalised output); partials merge as
+block_attention is the definition.  block_attention_ranges restates it as
+split-KV over the work plan of plan.py: each piece of a request's keys yields
+a partial (running max m, sum l, unnormalised output); partials merge as
     M = max_s m_s,   o = sum_s e^(m_s - M) O_s / sum_s e^(m_s - M) l_s,
 with an empty split contributing m = -inf, l = 0, O = 0.
 """
@@ -142,23 +142,37 @@ def merge_partials(parts):
     return num / den[:, None]
 
 
-def block_attention_splits(q, k_blk, v_blk, k_cache, v_cache, page_table, ctx_lens, pps, *,
-                           dtype: str, scale=None, requests=None, block_causal=False) -> np.ndarray:
-    """Split-KV restatement of block_attention: pps context pages per split,
-    block keys in the last split, partials merged as in the module docstring."""
+def key_index(v: int, ctx: int, K: int) -> int:
+    """Position in the concatenated key sequence (context, then block keys) of
+    slab boundary v: context slab v starts at token 16v, block slab v - n_b
+    (n_b = ceil(ctx/16)) at key ctx + 16 (v - n_b)."""
+    n = -(-ctx // PAGE)
+    return min(PAGE * v, ctx) if v <= n else ctx + min(PAGE * (v - n), K)
+
+
+def block_attention_ranges(q, k_blk, v_blk, k_cache, v_cache, page_table, ctx_lens, *, w_max: int,
+                           range_pages: int = 0, dtype: str, scale=None, requests=None,
+                           block_causal=False) -> np.ndarray:
+    """Split-KV restatement of block_attention over the work plan of plan.py:
+    each request's keys are cut where the batch's ranges cut them; every
+    piece yields a partial (m, l, O), and the pieces merge as in the module
+    docstring.  A request inside one range is a single piece."""
+    from .plan import range_plan, request_pieces
     C, K, Hq, D = q.shape
     Hkv = k_blk.shape[2]
     G = Hq // Hkv
     sc = _scale(D, scale)
+    P = k_cache.shape[1]
+    plan = range_plan(ctx_lens, K=K, w_max=w_max, page_size=P, range_pages=range_pages)
     out = np.zeros((C, K, Hq, D))
     reqs = range(C) if requests is None else requests
     for b in reqs:
         ctx = int(ctx_lens[b])
-        n_pages = -(-ctx // PAGE)
-        n_splits = max(1, -(-n_pages // pps))
-        bounds = [(s * pps * PAGE, min(ctx, (s + 1) * pps * PAGE)) for s in range(n_splits)]
-        lo_last = bounds[-1][0]
-        bounds[-1] = (lo_last, ctx + K)                                 # block keys join the last split
+        L = -(-ctx // PAGE) + -(-K // PAGE)
+        bounds = [(key_index(lo, ctx, K), key_index(hi, ctx, K))
+                  for _, _, lo, hi in request_pieces(plan, C, b, L)]
+        assert bounds[0][0] == 0 and bounds[-1][1] == ctx + K
+        assert all(bounds[i][1] == bounds[i + 1][0] for i in range(len(bounds) - 1))
         qb = decode(q[b], dtype)
         kb = decode(k_blk[b], dtype)
         vb = decode(v_blk[b], dtype)

@@ -1,63 +1,139 @@
-"""a0: the integer split plan for split-KV attention (oracle side).
+"""a0: the integer work plan of the in-place block attention (oracle side).
 
-The target context of request b spans n_b = ceil(ctx_b / 16) pages.  Its
-pages are cut into splits of a fixed number of pages `pps`; the draft block's
-own K keys belong to the last split.  A request with no context still has one
-split (block keys only):
+H-Spec's attention modules read every request's target KV in place (Abstract;
+review page, "Key claims under review": concurrent serving at C = 8-128, with
+ragged contexts).  The pages give no work decomposition; the reading here
+spreads the whole batch's keys evenly over a fixed number of work ranges, so
+that long and short requests cost the same wall time:
 
-    n_splits_b = max(1, ceil(n_b / pps))
+  * Request b's key sequence is its context, in slabs of 16 tokens
+    (n_b = ceil(ctx_b / 16)), followed by its K block keys (nbk =
+    ceil(K / 16) slabs): L_b = n_b + nbk slabs.
+  * Slabs are grouped into granules of g = max(2, P/16) slabs (P = tokens per
+    page), counted from each request's start, so every granule boundary
+    starts a page and an even slab.  Request b holds G_b = ceil(L_b / g)
+    granules; the batch holds T = sum_b G_b, request b starting at granule
+    S_b = sum_{b' < b} G_b' of the concatenation.
+  * The concatenation is cut into W ranges, range w holding granules
+    [B_w, B_{w+1}):
+      - automatic (range_pages = 0): W = min(w_max, max(1, ceil(T / r_min))),
+        r_min = ceil(16 / g) granules (a range holds >= 16 slabs when the
+        batch is large enough), and B_w = floor(w * T / W): nearly equal
+        ranges;
+      - fixed (range_pages > 0): ranges of exactly R = max(1,
+        ceil(range_pages * (P/16) / g)) granules, the last one shorter:
+        W = ceil(T / R), B_w = min(w * R, T).
+    In both cases W <= T, so no range is empty.
+  * Request b's pieces are the ranges it overlaps: w_first_b (the range
+    holding granule S_b) through the range holding granule S_b + G_b - 1.
+    A request inside one range (one piece) is finished by that range; the
+    pieces of a longer request are merged by log-sum-exp (E5).
+  * A piece's partial result goes to slot 2*w + k of its range w: k = 0 for
+    the segment that starts at the range's first granule, k = 1 for a segment
+    that starts later in the range (which, when it is a piece, must run to
+    the range's end).  Piece i of request b therefore sits in slot
+    2*(w_first_b + i) + (1 if i == 0 and B_{w_first_b} < S_b else 0).
 
-Work items are the (request, split) pairs, request-major.  The plan is laid
-out as one int32 array (the same layout the library writes at the start of
-its attention workspace, so the two can be compared bit for bit):
+The plan is one int32 array, laid out as the library writes it at the start
+of its attention workspace (so the two can be compared bit for bit):
 
-    [0] total items      [1] pps      [2] C      [3] capacity M
-    [4 : 4+C]            n_splits_b
-    [4+C : 4+2C]         index of request b's first item (exclusive prefix sum)
-    [4+2C : 4+2C+M]      request of item i, or -1 for i >= total
-    [4+2C+M : 4+2C+2M]   split of item i,   or -1 for i >= total
+    [0] W     [1] g     [2] C     [3] w_max
+    [4 : 4+C]            S_b        (first granule of request b)
+    [4+C : 4+2C]         w_first_b  (range holding request b's first granule)
+    [4+2C : 4+3C]        pieces_b   (ranges request b overlaps)
+    [4+3C : 4+3C+w_max+1]  B_w for w = 0..W (B_W = T), then -1 up to the capacity
 
-Capacity M = C * max(1, ceil(ceil(max_ctx / 16) / pps)), where max_ctx is the
-caller's upper bound on the context lengths.
+w_max (the capacity) is the caller's bound on W: the library sizes its grid
+and workspace by it.
 """
 import numpy as np
 
-PAGE = 16
+SLAB = 16
 
 
-def max_items_for(C: int, max_ctx: int, pps: int) -> int:
-    max_pages = -(-int(max_ctx) // PAGE)
-    return int(C) * max(1, -(-max_pages // int(pps)))
+def granule_slabs(page_size: int) -> int:
+    if page_size < SLAB or page_size % SLAB or (page_size // SLAB) & (page_size // SLAB - 1):
+        raise ValueError("page size must be 16 tokens times a power of two")
+    return max(2, page_size // SLAB)
 
 
-def plan_len(C: int, max_items: int) -> int:
-    return 4 + 2 * int(C) + 2 * int(max_items)
-
-
-def split_plan(ctx_lens, pps: int, max_ctx: int | None = None) -> np.ndarray:
+def request_granules(ctx_lens, K: int, page_size: int = 16) -> np.ndarray:
+    """G_b: granules of request b's key sequence (context slabs, then block slabs)."""
     ctx = np.asarray(ctx_lens, dtype=np.int64)
-    if pps <= 0:
-        raise ValueError("pages per split must be positive")
-    if max_ctx is None:
-        max_ctx = int(ctx.max()) if len(ctx) else 0
-    if len(ctx) and int(ctx.max()) > max_ctx:
-        raise ValueError("a context length exceeds max_ctx")
     if (ctx < 0).any():
         raise ValueError("negative context length")
-    C = len(ctx)
-    M = max_items_for(C, max_ctx, pps)
-    n_pages = (ctx + PAGE - 1) // PAGE
-    n_splits = np.maximum(1, (n_pages + pps - 1) // pps)
-    first = np.concatenate([[0], np.cumsum(n_splits)[:-1]]) if C else np.zeros(0, np.int64)
-    total = int(n_splits.sum())
-    item_req = np.full(M, -1, dtype=np.int64)
-    item_split = np.full(M, -1, dtype=np.int64)
-    i = 0
+    if K < 1:
+        raise ValueError("the draft block holds at least one key")
+    g = granule_slabs(page_size)
+    L = (ctx + SLAB - 1) // SLAB + (K + SLAB - 1) // SLAB
+    return (L + g - 1) // g
+
+
+def range_count(T: int, *, w_max: int, page_size: int = 16, range_pages: int = 0) -> int:
+    g = granule_slabs(page_size)
+    if range_pages < 0 or w_max < 1:
+        raise ValueError("range_pages >= 0 and w_max >= 1")
+    if range_pages == 0:
+        r_min = -(-SLAB // g)
+        return int(min(w_max, max(1, -(-T // r_min))))
+    R = max(1, -(-(range_pages * (page_size // SLAB)) // g))
+    W = -(-T // R)
+    if W > w_max:
+        raise ValueError("fixed ranges exceed the capacity w_max")
+    return int(W)
+
+
+def plan_len(C: int, w_max: int) -> int:
+    return 4 + 3 * int(C) + int(w_max) + 1
+
+
+def range_plan(ctx_lens, *, K: int, w_max: int, page_size: int = 16, range_pages: int = 0) -> np.ndarray:
+    """The int32 plan laid out as in the module docstring."""
+    G = request_granules(ctx_lens, K, page_size)
+    C = len(G)
+    if C < 1:
+        raise ValueError("at least one request")
+    T = int(G.sum())
+    W = range_count(T, w_max=w_max, page_size=page_size, range_pages=range_pages)
+    assert 1 <= W <= T
+    if range_pages == 0:
+        B = [w * T // W for w in range(W + 1)]
+    else:
+        R = max(1, -(-(range_pages * (page_size // SLAB)) // granule_slabs(page_size)))
+        B = [min(w * R, T) for w in range(W + 1)]
+    S = np.concatenate([[0], np.cumsum(G)[:-1]])
+    w_first = np.zeros(C, np.int64)
+    pieces = np.zeros(C, np.int64)
     for b in range(C):
-        for s in range(int(n_splits[b])):
-            item_req[i] = b
-            item_split[i] = s
-            i += 1
-    assert i == total <= M
-    out = np.concatenate([[total, pps, C, M], n_splits, first, item_req, item_split])
+        first, last = int(S[b]), int(S[b] + G[b] - 1)
+        wf = max(w for w in range(W) if B[w] <= first)
+        wl = max(w for w in range(W) if B[w] <= last)
+        w_first[b], pieces[b] = wf, wl - wf + 1
+    bounds = np.full(w_max + 1, -1, np.int64)
+    bounds[:W + 1] = B
+    out = np.concatenate([[W, granule_slabs(page_size), C, w_max], S, w_first, pieces, bounds])
     return out.astype(np.int32)
+
+
+def unpack(plan, C: int) -> dict:
+    """The fields of a plan array (by name)."""
+    p = np.asarray(plan, np.int64)
+    W = int(p[0])
+    B = p[4 + 3 * C:4 + 3 * C + W + 1]
+    return dict(W=W, g=int(p[1]), C=int(p[2]), w_max=int(p[3]), T=int(B[-1]), S=p[4:4 + C],
+                w_first=p[4 + C:4 + 2 * C], pieces=p[4 + 2 * C:4 + 3 * C], B=B)
+
+
+def request_pieces(plan, C: int, b: int, L_b: int):
+    """Request b's pieces as (range w, slot, first slab, end slab) of its key
+    sequence (L_b slabs), in order."""
+    f = unpack(plan, C)
+    g, S, B = f["g"], int(f["S"][b]), f["B"]
+    out = []
+    for i in range(int(f["pieces"][b])):
+        w = int(f["w_first"][b]) + i
+        lo = max(int(B[w]) - S, 0) * g
+        hi = min((int(B[w + 1]) - S) * g, L_b)
+        k = 1 if (i == 0 and int(B[w]) < S) else 0
+        out.append((w, 2 * w + k, lo, hi))
+    return out

@@ -99,16 +99,25 @@ def test_attention_validation(kw, code):
     assert _attn(**kw)[0] == code
 
 
+def _ws_expect(C, w_max, rows, Hkv=8, D=128):
+    up = lambda x: -(-x // 256) * 256
+    plan = up((4 + 3 * C + w_max + 1) * 4)
+    if w_max == 1:
+        return plan
+    return plan + up(2 * w_max * Hkv * rows * D * 4) + up(2 * w_max * Hkv * rows * 2 * 4)
+
+
 def test_attention_workspace_query():
-    code, n = _attn(split=32)
-    assert code == OK
-    C, M = 4, 4 * 2                                  # ceil(ceil(1000/16)/32) = 2 splits max
-    plan = (4 + 2 * C + 2 * M) * 4
-    rows = 4 * 16
-    expect = -(-plan // 256) * 256 + -(-(M * 8 * rows * 128 * 4) // 256) * 256 + -(-(M * 8 * rows * 2 * 4) // 256) * 256
-    assert n == expect
-    code1, n1 = _attn(split=1000)                      # one split per request: no partials
-    assert code1 == OK and n1 == 256
+    """The workspace holds the int32 plan (4 + 3C + w_max + 1 entries) and,
+    when a request can span ranges, fp32 partials for two slots per range.
+    C = 4, K = 16, max_ctx = 1000: a request's keys are 63 + 1 slabs, 32
+    granules of 2 slabs; the batch at most 128 granules."""
+    code, n = _attn(split=32)                           # 32 pages = 16 granules per range: 8 ranges
+    assert code == OK and n == _ws_expect(4, 8, 64)
+    code0, n0 = _attn(split=0)                          # automatic: 512 / Hkv = 64 ranges at most
+    assert code0 == OK and n0 == _ws_expect(4, 64, 64)
+    code1, n1 = _attn(split=1000)                       # one range for the whole batch: no partials
+    assert code1 == OK and n1 == _ws_expect(4, 1, 64)
     # a real (non-NULL) workspace that is too small is refused before any launch
     assert _attn(ws=FAKE, nbytes=n - 1, split=32)[0] == WORKSPACE
 
@@ -219,19 +228,17 @@ def test_kv_inject_validation_and_workspace():
 
 
 def test_attention_workspace_with_bigger_pages():
-    """Splits are counted in 16-token slabs and start on page boundaries."""
+    """Ranges are counted in granules of max(2, page / 16) slabs, so they
+    start on page boundaries."""
     code, n16 = _attn(split=0, page=16, max_pages=64)
     assert code == OK
     for P in (32, 64, 128, 256):
         code, n = _attn(split=0, page=P, max_pages=-(-1000 // P))
         assert code == OK and n > 0
-    # a user split of 4 pages of 64 tokens is 16 slabs: ceil(63 / 16) = 4 splits per request
+    # 64-token pages: granules of 4 slabs, a request at most 16 of them (63 + 1
+    # slabs); a range of 4 pages is 16 slabs = 4 granules: 64 / 4 = 16 ranges
     code, n = _attn(split=4, page=64, max_pages=16)
-    C, M = 4, 4 * 4
-    plan = (4 + 2 * C + 2 * M) * 4
-    rows = 4 * 16
-    expect = -(-plan // 256) * 256 + -(-(M * 8 * rows * 128 * 4) // 256) * 256 + -(-(M * 8 * rows * 2 * 4) // 256) * 256
-    assert code == OK and n == expect
+    assert code == OK and n == _ws_expect(4, 16, 64)
 
 
 def _stack(kinds=("MA", "MA"), mutate=None, **kw):

@@ -148,20 +148,26 @@ def test_block_causal_edges():
 
 @pytest.mark.parametrize("P", [32, 64, 128, 256])
 def test_bigger_pages(P):
-    """Pages of P tokens: parity with the oracle at several splits, and the
-    same bits as the 16-token layout of the same context at the same split
-    (in slabs), since the kernel walks both in the same 16-token slabs."""
+    """Pages of P tokens: parity with the oracle at several range sizes; and,
+    for contexts whose keys (context slabs + the block slab) fill whole pages,
+    the same bits as the 16-token layout of the same context with ranges of
+    the same length in slabs: the kernel walks both in the same 16-token
+    slabs and cuts them at the same slabs, only the slab addresses differ."""
     flush(f"[attn page {P}]")
     ctx = [0, 1, P - 1, P, P + 1, 1000, 3000]
     case = make_attn_case(900 + P, ctx, 16, 32, 8, 128, "bf16", page=P)
-    ref16 = make_attn_case(900 + P, ctx, 16, 32, 8, 128, "bf16", page=16)
     want = oracle_attn(case)
     for split in (0, 1, 3):
         o, _, _ = run_attn(case, split=split)
         assert_attn_close(to_host64(o), want, "bf16", f"page {P} split={split}")
-        if split:
-            o16, _, _ = run_attn(ref16, split=split * (P // 16))
-            assert torch.equal(o.view(torch.int16), o16.view(torch.int16)), f"page {P} split={split}"
+    spp = P // 16
+    aligned = [16 * (m * spp - 1) - r for m, r in ((1, 0), (2, 5), (3, 15), (9, 1))]
+    case = make_attn_case(910 + P, aligned, 16, 32, 8, 128, "bf16", page=P)
+    ref16 = make_attn_case(910 + P, aligned, 16, 32, 8, 128, "bf16", page=16)
+    for split in (1, 3):
+        o, _, _ = run_attn(case, split=split)
+        o16, _, _ = run_attn(ref16, split=split * spp)
+        assert torch.equal(o.view(torch.int16), o16.view(torch.int16)), f"page {P} split={split}"
     oc, _, _ = run_attn(case, split=1, causal=True)
     assert_attn_close(to_host64(oc), oracle_attn(case, causal=True), "bf16", f"page {P} causal")
 
@@ -182,10 +188,9 @@ def test_split_invariance_and_repeatability():
         o2, _, _ = run_attn(case, split=split)
         assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)), f"split={split} not repeatable"
         assert_attn_close(to_host64(o1), want, "bf16", f"split={split}")
-        plan = ws[:4 * 4].view(torch.int32).cpu().numpy()
-        M = int(plan[3])
-        plan = ws[:4 * (4 + 2 * 4 + 2 * M)].view(torch.int32).cpu().numpy()
-        assert np.array_equal(plan, oracle.split_plan(case["ctx_lens"], int(plan[1]), 1000)), split
+        plan = ops.plan_of(ws, len(case["ctx_lens"])).cpu().numpy()
+        want_plan = oracle.range_plan(case["ctx_lens"], K=16, w_max=int(plan[3]), range_pages=split)
+        assert np.array_equal(plan, want_plan), split
 
 
 def test_scrambled_page_table_is_bit_identical():
@@ -407,20 +412,25 @@ def test_layer_graph_replays_match_eager():
 
 
 @pytest.mark.parametrize("C,ctx,split", [(4, ("uniform", 100, 3000), True), (1, ("fixed", 8192), True),
-                                         (64, ("fixed", 2048), False), (96, ("uniform", 2048, 3000), False)],
-                         ids=["c4-ragged-splits", "c1-32-splits", "c64-one-split", "c96-ragged-one-split"])
+                                         (64, ("fixed", 2048), False), (96, ("uniform", 2048, 3000), True),
+                                         (128, ("fixed", 8192), False)],
+                         ids=["c4-ragged-pieces", "c1-33-pieces", "c64-whole", "c96-ragged-pieces",
+                              "c128-whole-head-pair"])
 def test_layer_equals_its_entry_points_bitwise(C, ctx, split):
-    """With several splits per request the layer runs the scan and the
-    attention's merge in one launch; with one split per request (two kv heads
-    per attention workgroup) there is no merge.  Either way its outputs must be
-    the bits of the separate entry points (a1, a2, a3 + a4) on the same inputs."""
+    """When some request spans several ranges the layer runs the scan and the
+    attention's merge in one launch; when every range holds whole requests
+    (C = 64 at 2048 tokens: one request per range; C = 128 at 8192: two kv
+    heads per workgroup) the merge finds nothing to do.  Either way its outputs
+    must be the bits of the separate entry points (a1, a2, a3 + a4) on the
+    same inputs."""
     from helpers import layer_from_inputs
     from hybrid_mamba_attention_amd import ops
     flush(f"[layer vs entry points C={C} ctx={ctx}]")
     w = replace_workload(wl.sweep_workload(C), ctx=ctx, seed=4646 + C)
     inp = wl.make_inputs(w)
     layer = layer_from_inputs(inp)
-    assert (int(layer.plan()[0]) > C) == split, "the case must (not) split requests"
+    plan = layer.plan().cpu().numpy()
+    assert (plan[4 + 2 * C:4 + 3 * C].max() > 1) == split, "the case must (not) cut requests into pieces"
     a, dt = inp.arrays, w.dtype
     h0 = ops.init_state(to_dev(a["u"], dt), to_dev(a["w_init"], dt))
     y, hf = ops.ssd_scan(to_dev(a["x"], dt), to_dev(a["delta"], dt), to_dev(a["A"], dt), to_dev(a["B"], dt),

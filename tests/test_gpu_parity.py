@@ -37,10 +37,11 @@ def _check_layer(idx, sample_requests=None):
     res["out"] = assert_attn_close(got, o, w.dtype, f"w{idx} attention out")
     flush(f"[parity] workload {idx}: " + ", ".join(f"{k} rel-L2 {v[0]:.2e} max-abs {v[1]:.2e}"
                                                    for k, v in res.items()))
-    # the int32 split plan at the head of the workspace, bit for bit
+    # the int32 work plan at the head of the workspace, bit for bit (the
+    # capacity w_max is the host's sizing bound, read from the plan)
     plan = layer.plan().cpu().numpy()
-    want = oracle.split_plan(inp.ctx_lens, int(plan[1]), inp.max_ctx)
-    assert np.array_equal(plan, want), "split plan differs from the oracle planner"
+    want = oracle.range_plan(inp.ctx_lens, K=w.K, w_max=int(plan[3]))
+    assert np.array_equal(plan, want), "work plan differs from the oracle planner"
     flush(f"[parity] workload {idx}: ok")
 
 

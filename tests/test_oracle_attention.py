@@ -68,9 +68,11 @@ def test_golden_hand(golden_dir):
                                np.array(g["v_blk"], np.float32), kc, vc, pt, np.array([g["ctx_len"]]),
                                dtype="f32", scale=math.log(3.0))
     _close(o, g["o"], 1e-14)
-    o2 = oracle.block_attention_splits(np.array(g["q"], np.float32), np.array(g["k_blk"], np.float32),
+    # one-granule ranges: the context token and the block token in one piece
+    o2 = oracle.block_attention_ranges(np.array(g["q"], np.float32), np.array(g["k_blk"], np.float32),
                                        np.array(g["v_blk"], np.float32), kc, vc, pt,
-                                       np.array([g["ctx_len"]]), 1, dtype="f32", scale=math.log(3.0))
+                                       np.array([g["ctx_len"]]), w_max=4, range_pages=1, dtype="f32",
+                                       scale=math.log(3.0))
     _close(o2, g["o"], 1e-14)
 
 
@@ -98,13 +100,35 @@ def test_scrambled_equals_identity_page_table():
     _close(_run(a), _run(b))
 
 
-@pytest.mark.parametrize("pps", [1, 2, 3, 7, 1000])
-def test_split_invariance(pps):
+@pytest.mark.parametrize("w_max,range_pages", [(64, 0), (3, 0), (1, 0), (1000, 1), (1000, 2), (1000, 7)])
+def test_split_invariance(w_max, range_pages):
+    """Cut where the batch's work ranges cut the keys (pieces of one or more
+    slabs, cuts inside a context and at the context / block boundary), the
+    merged partials equal the unsplit attention."""
     d = _paged([100, 0, 16, 17, 250], 2, 8, seed=4)
     ref = _run(d)
-    o = oracle.block_attention_splits(d["q"], d["k_blk"], d["v_blk"], d["k_cache"], d["v_cache"],
-                                      d["page_table"], d["ctx_lens"], pps, dtype="f32")
+    o = oracle.block_attention_ranges(d["q"], d["k_blk"], d["v_blk"], d["k_cache"], d["v_cache"],
+                                      d["page_table"], d["ctx_lens"], w_max=w_max, range_pages=range_pages,
+                                      dtype="f32")
     _close(o, ref)
+
+
+def test_ranges_cut_inside_the_block_keys():
+    """K = 40 (three block slabs) with one-granule ranges: pieces start and
+    end between block slabs, and the merge still gives the unsplit result."""
+    d = _paged([0, 37], 2, 8, seed=24, K=40)
+    plan = oracle.range_plan(d["ctx_lens"], K=40, w_max=64, range_pages=1)
+    ps = oracle.request_pieces(plan, 2, 0, 3)
+    assert [(lo, hi) for _, _, lo, hi in ps] == [(0, 2), (2, 3)]
+    o = oracle.block_attention_ranges(d["q"], d["k_blk"], d["v_blk"], d["k_cache"], d["v_cache"],
+                                      d["page_table"], d["ctx_lens"], w_max=64, range_pages=1, dtype="f32")
+    _close(o, _run(d))
+
+
+def test_key_index_of_slab_boundaries():
+    # context of 37 tokens (3 slabs) then K = 40 block keys (3 slabs)
+    assert [oracle.key_index(v, 37, 40) for v in range(7)] == [0, 16, 32, 37, 53, 69, 77]
+    assert [oracle.key_index(v, 0, 5) for v in range(2)] == [0, 5]
 
 
 def test_zero_query_is_mean_of_values():
@@ -250,12 +274,13 @@ def test_block_causal_ignores_later_block_keys():
     assert not np.allclose(_run(d)[:, :3], _run(e)[:, :3])  # the unmasked form does
 
 
-@pytest.mark.parametrize("pps", [1, 3, 1000])
-def test_block_causal_split_invariance(pps):
+@pytest.mark.parametrize("range_pages", [0, 1, 3])
+def test_block_causal_split_invariance(range_pages):
     d = _paged([100, 0, 16, 33], 2, 8, seed=14, K=6)
     ref = _run(d, block_causal=True)
-    o = oracle.block_attention_splits(d["q"], d["k_blk"], d["v_blk"], d["k_cache"], d["v_cache"],
-                                      d["page_table"], d["ctx_lens"], pps, dtype="f32", block_causal=True)
+    o = oracle.block_attention_ranges(d["q"], d["k_blk"], d["v_blk"], d["k_cache"], d["v_cache"],
+                                      d["page_table"], d["ctx_lens"], w_max=1000, range_pages=range_pages,
+                                      dtype="f32", block_causal=True)
     _close(o, ref)
 
 

@@ -43,39 +43,70 @@ def test_linear_no_bias():
 
 def test_plan_hand(golden_dir):
     g = json.load(open(os.path.join(golden_dir, "plan_hand.json")))
-    plan = oracle.split_plan(g["ctx"], g["pps"], g["max_ctx"])
-    assert plan.dtype == np.int32
-    assert plan.tolist() == g["plan"]
-    assert len(plan) == oracle.plan_len(len(g["ctx"]), plan[3])
+    for case in g["cases"]:
+        plan = oracle.range_plan(case["ctx"], K=case["K"], w_max=case["w_max"], page_size=case["page"],
+                                 range_pages=case["range_pages"])
+        assert plan.dtype == np.int32
+        head = case["plan_head"]
+        assert plan[:len(head)].tolist() == head
+        assert (plan[len(head):] == -1).all()
+        assert len(plan) == oracle.plan_len(len(case["ctx"]), case["w_max"])
+        C = len(case["ctx"])
+        for b, want in case.get("pieces_of_request", {}).items():
+            b = int(b)
+            L = -(-case["ctx"][b] // 16) + -(-case["K"] // 16)
+            assert [list(p) for p in oracle.request_pieces(plan, C, b, L)] == want
 
 
-@pytest.mark.parametrize("pps", [1, 3, 8, 64, 10 ** 6])
-def test_plan_invariants(pps):
-    ctx = np.random.default_rng(pps).integers(0, 700, size=23)
-    plan = oracle.split_plan(ctx, pps, max_ctx=800)
-    C = len(ctx)
-    total, p, c, M = plan[:4]
-    n_splits = plan[4:4 + C]
-    first = plan[4 + C:4 + 2 * C]
-    req = plan[4 + 2 * C:4 + 2 * C + M]
-    spl = plan[4 + 2 * C + M:]
-    assert p == pps and c == C and total == n_splits.sum() <= M
-    assert M == C * max(1, -(-(-(-800 // 16)) // pps))
-    pages = -(-ctx // 16)
-    # every context page is covered by exactly one split of its request
-    for b in range(C):
-        covered = []
-        for s in range(n_splits[b]):
-            i = first[b] + s
-            assert req[i] == b and spl[i] == s
-            covered += list(range(s * pps, min(pages[b], (s + 1) * pps)))
-        assert covered == list(range(pages[b]))
-        assert n_splits[b] >= 1
-    assert (req[total:] == -1).all() and (spl[total:] == -1).all()
+CASES = [(16, 64, 0), (16, 7, 0), (16, 64, 3), (32, 64, 0), (64, 16, 5), (256, 64, 0), (16, 3, 0)]
+
+
+@pytest.mark.parametrize("page,w_max,range_pages", CASES)
+def test_plan_invariants(page, w_max, range_pages):
+    """Every slab of every request lies in exactly one of its pieces, in
+    order; each range's segments tile it; slots of partial pieces are unique;
+    automatic ranges differ in size by at most one granule."""
+    rng = np.random.default_rng(page + w_max + range_pages)
+    for trial in range(20):
+        C = int(rng.integers(1, 30))
+        K = int(rng.integers(1, 65))
+        ctx = rng.integers(0, 3000, size=C) * (rng.random(C) < 0.9)
+        try:
+            plan = oracle.range_plan(ctx, K=K, w_max=w_max, page_size=page, range_pages=range_pages)
+        except ValueError:
+            assert range_pages > 0   # fixed ranges beyond the capacity are refused
+            continue
+        f = oracle.plan.unpack(plan, C)
+        W, T, g, B = f["W"], f["T"], f["g"], f["B"]
+        G = oracle.request_granules(ctx, K, page)
+        assert g == max(2, page // 16) and T == G.sum() and 1 <= W <= min(w_max, T)
+        assert B[0] == 0 and B[-1] == T and (np.diff(B) >= 1).all()
+        if range_pages == 0:
+            assert np.diff(B).max() - np.diff(B).min() <= 1
+        else:
+            R = max(1, -(-(range_pages * (page // 16)) // g))
+            assert (np.diff(B)[:-1] == R).all() and 1 <= np.diff(B)[-1] <= R
+        slots = []
+        for b in range(C):
+            L = -(-int(ctx[b]) // 16) + -(-K // 16)
+            ps = oracle.request_pieces(plan, C, b, L)
+            assert ps[0][2] == 0 and ps[-1][3] == L
+            for (w0, s0, lo0, hi0), (w1, s1, lo1, hi1) in zip(ps, ps[1:]):
+                assert hi0 == lo1 and w1 == w0 + 1
+            for w, slot, lo, hi in ps:
+                assert lo < hi and lo % g == 0 and slot // 2 == w
+                assert B[w] <= f["S"][b] + lo // g and f["S"][b] + (hi - 1) // g < B[w + 1]
+            if len(ps) > 1:
+                slots += [p[1] for p in ps]
+        assert len(slots) == len(set(slots))
 
 
 def test_plan_rejects_bad_args():
     with pytest.raises(ValueError):
-        oracle.split_plan([10], 0)
+        oracle.range_plan([10], K=0, w_max=4)
     with pytest.raises(ValueError):
-        oracle.split_plan([100], 4, max_ctx=50)
+        oracle.range_plan([-1], K=4, w_max=4)
+    with pytest.raises(ValueError):
+        oracle.range_plan([10], K=4, w_max=4, page_size=48)
+    with pytest.raises(ValueError):
+        oracle.range_plan([4000], K=4, w_max=4, range_pages=1)

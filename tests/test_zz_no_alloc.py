@@ -33,7 +33,8 @@ def _compare_entry_points(w, kv_split_pages=0):
     torch.cuda.synchronize()
     for k in OUTS:
         assert torch.equal(_bits(getattr(layer, k)), _bits(ref[k])), f"{w.name}: {k} differs"
-    return int(layer.plan()[0])
+    C = w.C
+    return int(layer.plan()[4 + 2 * C:4 + 3 * C].max())   # most pieces of one request
 
 
 def test_noalloc_matches_the_workspace_entry_point_twice():
@@ -43,18 +44,18 @@ def test_noalloc_matches_the_workspace_entry_point_twice():
     big = replace(wl.sweep_workload(4), name="noalloc-big", ctx=("uniform", 3000, 8192), seed=9001)
     small = replace(wl.sweep_workload(2), name="noalloc-small", ctx=("uniform", 1, 600), seed=9002)
     flush("[noalloc] big call")
-    items_big = _compare_entry_points(big)
-    assert items_big > big.C, "the first call must split requests (partials in the scratch)"
+    pieces = _compare_entry_points(big)
+    assert pieces > 1, "the first call must cut requests into pieces (partials in the scratch)"
     flush("[noalloc] smaller call")
     _compare_entry_points(small)
 
 
 def test_noalloc_refuses_more_than_the_scratch():
-    """One-page splits of 8192-token contexts need ~0.5 GB of partials."""
+    """One-page ranges of 8192-token contexts need ~0.5 GB of partial slots."""
     w = replace(wl.sweep_workload(4), name="noalloc-too-big", seed=9003)
     inp = wl.make_inputs(w, parts=("attn", "mamba"))
     layer = layer_from_inputs(inp, kv_split_pages=1)
-    assert layer.workspace.numel() > 64 << 20
+    assert layer.workspace.numel() > 128 << 20
     out_before = layer.out.clone()
     with pytest.raises(ops.HspecError) as e:
         layer.noalloc()
