@@ -79,9 +79,10 @@ __device__ __forceinline__ int req_granules(const AttnArgs& a, int ctx) {
 
 // Ranges for a batch of T granules (T >= C >= 1, so W <= T: no range is
 // empty): fixed ranges of range_gran granules (the last one shorter), or W
-// nearly equal ranges.  The host sizes w_max for the fixed form's count.
+// nearly equal ranges of at least min_gran granules each (one range when
+// the batch has fewer).  The host sizes w_max for the fixed form's count.
 __device__ __forceinline__ int range_count(const AttnArgs& a, int T) {
-  const int W = a.range_gran > 0 ? (T + a.range_gran - 1) / a.range_gran : (T + a.min_gran - 1) / a.min_gran;
+  const int W = a.range_gran > 0 ? (T + a.range_gran - 1) / a.range_gran : T / a.min_gran;
   return max(1, min(W, a.w_max));
 }
 // B_w, the first granule of range w (B_W = T)
@@ -172,15 +173,50 @@ __device__ void write_plan(const AttnArgs& a, int* lds) {
   }
 }
 
-// Where range w starts: the request b holding its first granule B0 and that
-// request's first granule S (uniform over the workgroup; b = -1 when w >= W).
+// Inclusive prefix sum over the 64 lanes of a wave (no LDS, no barrier).
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
+
+// Where range w starts: the request b holding its first granule B0, that
+// request's first granule S and its context length (uniform over the
+// workgroup; b = -1 when w >= W).
 struct RangeStart {
-  int W, T, B0, B1, b, S;
+  int W, T, B0, B1, b, S, ctx;
 };
 template <int NT>
 __device__ RangeStart find_range(const AttnArgs& a, int w, int* lds) {
   const int tid = threadIdx.x, C = a.C;
   RangeStart r;
+  if (C <= 64) {
+    // One wave holds the whole batch: every wave scans it on its own, with
+    // lane ops only, so no barrier and no LDS round trip delays the stream.
+    const int lane = tid & 63;
+    const int ctx = lane < C ? ctx_of(a, lane) : 0;
+    const int gb = lane < C ? req_granules(a, ctx) : 0;
+    const int incl = wave_incl_scan(gb);
+    r.T = __builtin_amdgcn_readlane(incl, 63);
+    r.W = range_count(a, r.T);
+    r.b = -1;
+    r.S = 0;
+    r.ctx = 0;
+    if (w >= r.W) return r;
+    r.B0 = range_bound(a, w, r.T, r.W);
+    r.B1 = range_bound(a, w + 1, r.T, r.W);
+    const uint64_t hit = __ballot(lane < C && incl - gb <= r.B0 && r.B0 < incl);
+    if (hit == 0) return r;   // cannot happen: B0 < T lies in some request
+    const int fb = __ffsll(static_cast<long long>(hit)) - 1;   // exactly one lane
+    r.b = fb;
+    r.S = __builtin_amdgcn_readlane(incl - gb, fb);
+    r.ctx = __builtin_amdgcn_readlane(ctx, fb);
+    return r;
+  }
   int g0;
   r.T = batch_granules<NT>(a, lds, &g0);
   r.W = range_count(a, r.T);
@@ -189,6 +225,7 @@ __device__ RangeStart find_range(const AttnArgs& a, int w, int* lds) {
   if (w >= r.W) return r;
   r.B0 = range_bound(a, w, r.T, r.W);
   r.B1 = range_bound(a, w + 1, r.T, r.W);
+  r.ctx = 0;
   int* found = lds + 16;   // past block_incl_scan's scratch
   if (tid == 0) found[0] = -1;
   int carry = 0;
@@ -210,6 +247,7 @@ __device__ RangeStart find_range(const AttnArgs& a, int w, int* lds) {
     }
     carry += tot;
   }
+  r.ctx = r.b >= 0 ? ctx_of(a, r.b) : 0;
   return r;
 }
 
@@ -341,6 +379,24 @@ __global__ __launch_bounds__(64 * NW, (RT == 2 && sizeof(T) == 2) ? 2 : 1) void 
   // this wave's kv head and its first row tile among that head's G*K rows
   const int hl = wave / WPH, j = j0 + hl, wt = (wave % WPH) * RT;
   const int K = a.K, G = a.G, rows = a.rows;
+  // This wave's query rows as B operands (row li of tile rt, d group lg + 4*ds);
+  // rows past G*K repeat the last row (their outputs are never stored).
+  const T* __restrict__ q = static_cast<const T*>(a.q);
+  Vec8<T> qv[RT][DS];
+  auto load_q = [&](int bq) __attribute__((always_inline)) {
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const int row = min((wt + rt) * 16 + li, rows - 1);
+      const int t = row / G, gg = row % G;
+      const T* qp = q + ((size_t(bq) * K + t) * a.Hq + j * G + gg) * D;
+#pragma unroll
+      for (int ds = 0; ds < DS; ++ds) load8(qv[rt][ds], qp + (lg + 4 * ds) * 8);
+    }
+  };
+  // With one request its query rows are known before the plan: their loads
+  // go out with the plan's, so the two round trips overlap.
+  const bool q_early = a.C == 1;
+  if (q_early) load_q(0);
   const RangeStart rs = find_range<NT>(a, w, reinterpret_cast<int*>(smem));
   if (rs.b < 0) return;   // no such range for this batch (uniform)
 
@@ -404,12 +460,11 @@ __global__ __launch_bounds__(64 * NW, (RT == 2 && sizeof(T) == 2) ? 2 : 1) void 
   int tq[RT];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) tq[rt] = min((wt + rt) * 16 + li, rows - 1) / G;
-  const T* __restrict__ q = static_cast<const T*>(a.q);
 
   // ---- the range's segments: request b from slab p_lo to p_hi of its keys
-  int b = rs.b, S = rs.S;
+  int b = rs.b, S = rs.S, ctx_next = rs.ctx;
   while (S < rs.B1) {   // uniform
-    const int ctx = ctx_of(a, b);
+    const int ctx = ctx_next;
     const int npages = (ctx + 15) >> 4;          // context slabs
     const int L = npages + a.nbk;                // the request's keys, in slabs
     const int Gb = (L + a.gran - 1) / a.gran;
@@ -419,17 +474,7 @@ __global__ __launch_bounds__(64 * NW, (RT == 2 && sizeof(T) == 2) ? 2 : 1) void 
     const bool whole = p_lo == 0 && p_hi == L;
     const int pslot = 2 * w + (S > rs.B0 ? 1 : 0);
 
-    // This wave's query rows as B operands (row li of tile rt, d group lg + 4*ds);
-    // rows past G*K repeat the last row (their outputs are never stored).
-    Vec8<T> qv[RT][DS];
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      const int row = min((wt + rt) * 16 + li, rows - 1);
-      const int t = row / G, gg = row % G;
-      const T* qp = q + ((size_t(b) * K + t) * a.Hq + j * G + gg) * D;
-#pragma unroll
-      for (int ds = 0; ds < DS; ++ds) load8(qv[rt][ds], qp + (lg + 4 * ds) * 8);
-    }
+    if (!q_early) load_q(b);
     const int32_t* __restrict__ pt = a.page_table + size_t(b) * a.max_pages;
     // Page-table window of the hot path: lane l holds the segment's entries
     // pg_lo + 128*w + l and pg_lo + 128*w + 64 + l of the current window w
@@ -801,6 +846,7 @@ __global__ __launch_bounds__(64 * NW, (RT == 2 && sizeof(T) == 2) ? 2 : 1) void 
 
     S += Gb;
     ++b;
+    if (S < rs.B1) ctx_next = ctx_of(a, b);
   }
 }
 
@@ -874,14 +920,17 @@ static hipError_t launch_merge_cfg(hipStream_t st, const AttnArgs& a) {
   return hipGetLastError();
 }
 
-// LPO and U by the most pieces a request can have (one per range).
+// Four lanes per output (LPO = 4, up to 16 pieces each per round) when the
+// plan has many ranges per request, i.e. few long requests cut into many
+// pieces (small C); otherwise one lane (up to 8 pieces per round), which
+// keeps the grid -- mostly workgroups of whole requests that exit at once --
+// four times smaller.
+bool merge_wide(const AttnArgs& a) { return a.w_max > 4 * a.C; }
+
 template <typename T, int D>
 static hipError_t launch_merge(hipStream_t st, const AttnArgs& a) {
-  const int ms = a.w_max;
-  if (ms <= 4) return launch_merge_cfg<T, D, 1, 4>(st, a);
-  if (ms <= 8) return launch_merge_cfg<T, D, 1, 8>(st, a);
-  if (ms <= 16) return launch_merge_cfg<T, D, 4, 4>(st, a);
-  return launch_merge_cfg<T, D, 4, 8>(st, a);
+  if (merge_wide(a)) return launch_merge_cfg<T, D, 4, 16>(st, a);
+  return launch_merge_cfg<T, D, 1, 8>(st, a);
 }
 
 hipError_t launch_block_attn(hipStream_t st, int dtype, const AttnArgs& a, bool merge) {

@@ -29,7 +29,7 @@ struct AttnArgs {
   // nbk block slabs, counted in granules of `gran` slabs; the batch's
   // granules are cut into W <= w_max equal ranges, one workgroup per (range,
   // kv head group).  W = ceil(T / range_gran) for fixed ranges, else
-  // min(w_max, ceil(T / min_gran)) (T = the batch's granules).
+  // min(w_max, max(1, floor(T / min_gran))) (T = the batch's granules).
   int w_max;
   int gran;
   int range_gran;                 // 0 = automatic
@@ -44,6 +44,8 @@ struct AttnArgs {
 hipError_t launch_block_attn(hipStream_t st, int dtype, const AttnArgs& a, bool merge = true);
 // dynamic LDS bytes of the attention kernel for a shape (host planning only)
 size_t attn_lds_bytes(int dtype, int D, int rows, int K);
+// the merge's lanes per output: 4 when ranges outnumber requests four to one
+bool merge_wide(const AttnArgs& a);
 // whether the two-heads-per-workgroup form exists for a shape
 bool head_pair_fits(int rows, int Hkv, int64_t head_stride, int dtype, int D);
 

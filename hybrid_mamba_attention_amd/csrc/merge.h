@@ -10,12 +10,13 @@
 namespace hspec {
 
 // LPO lanes (1 or 4) per (row, 4 output columns), in log2 units like the
-// partials: lane q takes pieces q, q+LPO, ..., loading U of them at a time
-// (clamped indices, no data-dependent branches) and keeping a running
-// maximum; with LPO = 4 the quad then combines its four (m, l, O) with two
-// xor-shuffles.  A request with up to LPO*U pieces costs one round of
-// independent loads; LPO and U are sized to the most pieces a request can
-// have at launch, so few loads are clamped repeats and few lanes idle.
+// partials: lane q takes pieces q, q+LPO, ..., loading up to U of them at a
+// time (clamped indices, no data-dependent branches inside a round) and
+// keeping a running maximum; with LPO = 4 the quad then combines its four
+// (m, l, O) with two xor-shuffles.  LPO and U are sized at launch to the
+// most pieces a request can have; the loads per round follow the request's
+// own count, so a request of up to LPO*U pieces costs one round of
+// independent loads with few clamped repeats.
 // The request's pieces come from the work plan the attention grid wrote:
 // piece i sits in slot 2*(w_first + i) (+1 for the first piece when the
 // request starts after its first range's first granule).
@@ -40,34 +41,47 @@ __device__ __forceinline__ void attn_merge_block(const AttnArgs& a, int bx, int 
   };
   float M = -INFINITY, Ls = 0.f;
   float4 acc = make_float4(0, 0, 0, 0);
-  for (int s0 = q; s0 < ns; s0 += LPO * U) {
-    float2 ml[U];
-    float4 v[U];
+  // Rounds of UU loads per lane, all issued before the first use.
+  auto rounds = [&](auto UC) __attribute__((always_inline)) {
+    constexpr int UU = decltype(UC)::value;
+    for (int s0 = q; s0 < ns; s0 += LPO * UU) {
+      float2 ml[UU];
+      float4 v[UU];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const size_t pr = prow(min(s0 + LPO * u, ns - 1));
-      ml[u] = *reinterpret_cast<const float2*>(a.part_ml + pr * 2);
-      v[u] = reinterpret_cast<const float4*>(a.part_o + pr * D)[d4];
+      for (int u = 0; u < UU; ++u) {
+        const size_t pr = prow(min(s0 + LPO * u, ns - 1));
+        ml[u] = *reinterpret_cast<const float2*>(a.part_ml + pr * 2);
+        v[u] = reinterpret_cast<const float4*>(a.part_o + pr * D)[d4];
+      }
+      // A piece's maximum is -inf when the block-causal mask hides all its
+      // keys from this row (a piece of block keys only); such a piece weighs
+      // 0.  The request's first piece always holds a key every row sees (its
+      // context or block key 0), so the total weight is positive.
+      float mr = M;
+#pragma unroll
+      for (int u = 0; u < UU; ++u)
+        if (s0 + LPO * u < ns) mr = fmaxf(mr, ml[u].x);
+      const float sc = M == -INFINITY ? 0.f : fast_exp2(M - mr);
+      acc.x *= sc; acc.y *= sc; acc.z *= sc; acc.w *= sc;
+      Ls *= sc;
+#pragma unroll
+      for (int u = 0; u < UU; ++u) {
+        const float f = (s0 + LPO * u < ns && ml[u].x != -INFINITY) ? fast_exp2(ml[u].x - mr) : 0.f;
+        acc.x += f * v[u].x; acc.y += f * v[u].y; acc.z += f * v[u].z; acc.w += f * v[u].w;
+        Ls += f * ml[u].y;
+      }
+      M = mr;
     }
-    // A piece's maximum is -inf when the block-causal mask hides all its keys
-    // from this row (a piece of block keys only); such a piece weighs 0.  The
-    // request's first piece always holds a key every row sees (its context or
-    // block key 0), so the total weight is positive.
-    float mr = M;
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-      if (s0 + LPO * u < ns) mr = fmaxf(mr, ml[u].x);
-    const float sc = M == -INFINITY ? 0.f : fast_exp2(M - mr);
-    acc.x *= sc; acc.y *= sc; acc.z *= sc; acc.w *= sc;
-    Ls *= sc;
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const float f = (s0 + LPO * u < ns && ml[u].x != -INFINITY) ? fast_exp2(ml[u].x - mr) : 0.f;
-      acc.x += f * v[u].x; acc.y += f * v[u].y; acc.z += f * v[u].z; acc.w += f * v[u].w;
-      Ls += f * ml[u].y;
-    }
-    M = mr;
-  }
+  };
+  // Loads per lane and round by the request's own piece count (uniform over
+  // the workgroup): sized by the most pieces any request could have, a
+  // request of two pieces would issue up to LPO * U clamped repeats per
+  // output, which dominated the merge when ranges cut most requests in two.
+  const int per_lane = (ns + LPO - 1) / LPO;
+  if (per_lane <= 1 || U == 1) rounds(std::integral_constant<int, 1>{});
+  else if (per_lane <= 2 || U == 2) rounds(std::integral_constant<int, 2>{});
+  else if (per_lane <= 4 || U == 4) rounds(std::integral_constant<int, 4>{});
+  else rounds(std::integral_constant<int, U>{});
   // combine the quad (a lane without pieces has M = -inf, Ls = 0, acc = 0)
 #pragma unroll
   for (int x = 1; x < LPO; x <<= 1) {

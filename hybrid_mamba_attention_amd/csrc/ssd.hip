@@ -367,8 +367,7 @@ bool scan_merge_fits(int dtype, const SsdArgs& s, const AttnArgs& m) {
 }
 
 // The merge part takes the configuration k_attn_merge would (LPO lanes per
-// output quad, U pieces per round of loads, by the most pieces a request can
-// have).
+// output quad and at most U pieces per lane and round of loads).
 template <int NMAX, int LPO, int U>
 static hipError_t launch_scan_merge_cfg(hipStream_t st, const SsdArgs& s, const AttnArgs& m) {
   const int n_scan = s.C * (s.H / ssd_heads_per_block(s.H, s.ng, s.P));
@@ -381,11 +380,8 @@ static hipError_t launch_scan_merge_cfg(hipStream_t st, const SsdArgs& s, const 
 
 template <int NMAX>
 static hipError_t launch_scan_merge_n(hipStream_t st, const SsdArgs& s, const AttnArgs& m) {
-  const int ms = m.w_max;   // the most pieces a request can have
-  if (ms <= 4) return launch_scan_merge_cfg<NMAX, 1, 4>(st, s, m);
-  if (ms <= 8) return launch_scan_merge_cfg<NMAX, 1, 8>(st, s, m);
-  if (ms <= 16) return launch_scan_merge_cfg<NMAX, 4, 4>(st, s, m);
-  return launch_scan_merge_cfg<NMAX, 4, 8>(st, s, m);
+  if (merge_wide(m)) return launch_scan_merge_cfg<NMAX, 4, 16>(st, s, m);
+  return launch_scan_merge_cfg<NMAX, 1, 8>(st, s, m);
 }
 
 hipError_t launch_scan_merge(hipStream_t st, const SsdArgs& s, const AttnArgs& m) {

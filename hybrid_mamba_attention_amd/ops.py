@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libhspec.so")
 F32, BF16 = 0, 1
 _STATUS = {0: "HSPEC_OK", -1: "HSPEC_ERR_INVALID_ARG", -2: "HSPEC_ERR_UNSUPPORTED",
            -3: "HSPEC_ERR_WORKSPACE", -4: "HSPEC_ERR_HIP", -5: "HSPEC_ERR_SCRATCH"}
-ABI_VERSION = 7
+ABI_VERSION = 8
 
 _vp, _i, _i64, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
 

@@ -63,7 +63,7 @@ typedef enum {
 const char* hspec_status_string(int status);
 
 /* ABI version of this header; bumped on any incompatible change. */
-#define HSPEC_ABI_VERSION 7
+#define HSPEC_ABI_VERSION 8
 int hspec_abi_version(void);
 
 /*
@@ -140,26 +140,40 @@ int hspec_ssd_scan(void* stream, int dtype, int C, int K, int H, int P, int ng, 
  *   ctx_lens     int32 [C] device; 0 <= ctx_lens[b] <= max_ctx
  *   max_ctx      host upper bound of ctx_lens (sizes the grid and workspace);
  *                max_pages >= ceil(max_ctx/P)
- *   kv_split_pages  context pages (of P tokens) per split-KV work item (0 =
- *                pick automatically); results do not depend on it beyond fp32
- *                rounding, and are bitwise repeatable for a fixed value
+ *   kv_split_pages  0 = automatic work ranges (below); otherwise ranges of
+ *                this many pages of P tokens each (the last one shorter).
+ *                Results do not depend on it beyond fp32 rounding, and are
+ *                bitwise repeatable for a fixed value
  *   scale        softmax scale; 0.f means 1/sqrt(D)
  *   out          act [C, K, Hq, D]
  *   workspace / workspace_bytes:
  *       workspace == NULL: size query -- *workspace_bytes receives the bytes
  *       this call needs; nothing is launched.  Otherwise *workspace_bytes is
  *       the capacity of `workspace` (device, 256-byte aligned), which must be
- *       at least the queried size.  The workspace starts with the int32 split
- *       plan:
- *         [0] items  [1] 16-token slabs per split  [2] C  [3] capacity M
- *         [4, 4+C) splits of request b    [4+C, 4+2C) first item of request b
- *         [4+2C, 4+2C+M) request of item i (-1 unused)
- *         [4+2C+M, 4+2C+2M) split of item i (-1 unused)
- *       with splits_b = max(1, ceil(ceil(ctx_b/16) / slabs_per_split)) and
- *       M = C * max(1, ceil(ceil(max_ctx/16) / slabs_per_split)); the rest
- *       holds fp32 split partials (slabs per split is a multiple of P/16).
+ *       at least the queried size.
+ * Work plan.  Request b's keys are its ceil(ctx_b/16) context slabs of 16
+ * tokens followed by its ceil(K/16) block slabs, counted in granules of
+ * g = max(2, P/16) slabs from the request's start (G_b granules).  The
+ * batch's T = sum G_b granules, request after request (request b from
+ * granule S_b), are cut into W ranges [B_w, B_{w+1}): automatically W =
+ * min(w_max, max(1, floor(T / ceil(16/g)))) nearly equal ranges, B_w =
+ * floor(w*T/W);
+ * with kv_split_pages, ranges of R = ceil(kv_split_pages*(P/16)/g)
+ * granules, B_w = min(w*R, T).  One workgroup per (range, kv head group)
+ * takes its range's slabs request by request; a request inside one range is
+ * finished there, a request spanning several ranges (its pieces) is merged
+ * by log-sum-exp.  w_max, a bound the host derives from C, max_ctx, K, Hkv
+ * and the page size, sizes the grid and the workspace.  The workspace
+ * starts with the int32 plan the kernels derive from ctx_lens:
+ *         [0] W  [1] g  [2] C  [3] w_max
+ *         [4, 4+C) S_b    [4+C, 4+2C) range of request b's first granule
+ *         [4+2C, 4+3C) ranges request b spans (its pieces)
+ *         [4+3C, 4+3C+w_max+1) B_0 .. B_W (B_W = T), then -1
+ *       followed, when w_max > 1, by fp32 partials of two slots per range.
  * Limits: D in {64, 128}; 1 <= K <= 64; Hq % Hkv == 0; (Hq/Hkv)*K <= 256;
- * token_stride times the element size <= 2^27 bytes (else UNSUPPORTED).
+ * token_stride times the element size <= 2^27 bytes; the batch's keys at
+ * their bound, C * g * ceil((ceil(max_ctx/16) + ceil(K/16)) / g) slabs,
+ * below 2^31 (else UNSUPPORTED).
  */
 int hspec_block_attn_inplace(void* stream, int dtype, int C, int K, int Hq, int Hkv, int D,
                              const void* q, const void* k_blk, const void* v_blk,

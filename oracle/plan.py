@@ -16,10 +16,9 @@ that long and short requests cost the same wall time:
     S_b = sum_{b' < b} G_b' of the concatenation.
   * The concatenation is cut into W ranges, range w holding granules
     [B_w, B_{w+1}):
-      - automatic (range_pages = 0): W = min(w_max, max(1, ceil(T / r_min))),
-        r_min = ceil(16 / g) granules (a range holds >= 16 slabs when the
-        batch is large enough), and B_w = floor(w * T / W): nearly equal
-        ranges;
+      - automatic (range_pages = 0): W = min(w_max, max(1, floor(T / r_min))),
+        r_min = ceil(16 / g) granules (every range holds >= 16 slabs when the
+        batch has them), and B_w = floor(w * T / W): nearly equal ranges;
       - fixed (range_pages > 0): ranges of exactly R = max(1,
         ceil(range_pages * (P/16) / g)) granules, the last one shorter:
         W = ceil(T / R), B_w = min(w * R, T).
@@ -75,7 +74,7 @@ def range_count(T: int, *, w_max: int, page_size: int = 16, range_pages: int = 0
         raise ValueError("range_pages >= 0 and w_max >= 1")
     if range_pages == 0:
         r_min = -(-SLAB // g)
-        return int(min(w_max, max(1, -(-T // r_min))))
+        return int(min(w_max, max(1, T // r_min)))
     R = max(1, -(-(range_pages * (page_size // SLAB)) // g))
     W = -(-T // R)
     if W > w_max:

@@ -32,7 +32,7 @@ def test_loads_and_exports_every_declared_symbol():
             "hspec_probe_stream_read"} <= set(names)
     for n in names:
         assert hasattr(L, n), f"{n} declared in hspec.h but not exported"
-    assert L.hspec_abi_version() == ops.ABI_VERSION == 7
+    assert L.hspec_abi_version() == ops.ABI_VERSION == 8
     assert L.hspec_layer_args_size() == ctypes.sizeof(ops.LayerArgs)
     assert L.hspec_mamba_args_size() == ctypes.sizeof(ops.MambaArgs)
     assert L.hspec_stack_args_size() == ctypes.sizeof(ops.StackArgs)
