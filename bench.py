@@ -33,6 +33,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor peak
 BF16_DENSE_TFLOPS = 2500.0     # MI355X dense bf16 matrix peak
+FP32_MATRIX_TFLOPS = 157.3     # MI355X dense fp32 matrix peak
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 
 
@@ -55,7 +56,13 @@ def parse():
                    help="skip the drafter-side KV injection contrast timings")
     p.add_argument("--no-stack", action="store_true",
                    help="skip the drafter-stack (eager vs HIP graph) timings")
+    p.add_argument("--no-configs", action="store_true",
+                   help="skip the per-workload table (all five workloads, one entry each)")
     p.add_argument("--sweep", default="1,2,4,8,16,32,64,128")
+    p.add_argument("--summarize-profiles", nargs="+", metavar="DIR",
+                   help="write the profiles/ records from rocprofv3 output directories (no GPU work): "
+                        "a --kernel-trace --stats run, FETCH_SIZE and WRITE_SIZE --pmc runs (with "
+                        "--calib-copy) and an MFMA --pmc run of this script")
     p.add_argument("--calib-copy", action="store_true",
                    help="also launch a plain 1 GiB device copy (counter calibration under rocprofv3)")
     return p.parse_args()
@@ -129,6 +136,14 @@ def ssd_bytes(w):
             + w.C * w.K * w.H * 4)
 
 
+def plan_summary(plan, C):
+    """The work plan's shape: ranges used and their capacity, requests cut
+    into pieces by range boundaries, and the pieces in all."""
+    pieces = plan[4 + 2 * C:4 + 3 * C]
+    return dict(ranges=int(plan[0]), range_capacity=int(plan[3]), granule_slabs=int(plan[1]),
+                requests_cut=int((pieces > 1).sum()), pieces=int(pieces.sum()))
+
+
 def measure(w, inp, args, torch, flush, with_parts=True):
     from hybrid_mamba_attention_amd import ops
     layer, t = build_layer(inp, args.kv_split_pages, torch)
@@ -152,10 +167,84 @@ def measure(w, inp, args, torch, flush, with_parts=True):
         res["ssd_scan"] = stats(timed(lambda: ops.ssd_scan(t["x"], t["delta"], t["A"], t["B"], t["Cm"],
                                                            chunk=w.chunk, h0=h0, y=y),
                                       args.steps, args.warmup, flush, torch))
-        res["plan"] = layer.plan().cpu().numpy()[:4].tolist()
+        res["plan"] = plan_summary(layer.plan().cpu().numpy(), w.C)
     del layer, t
     torch.cuda.empty_cache()
     return res
+
+
+def part_metrics(w, inp, r):
+    """Per-kernel figures of one measure() result: event times, algorithmic
+    bytes and their rate, and the projection's matrix-core share."""
+    from hybrid_mamba_attention_amd import workloads as wl
+    att_b = attention_bytes(w, inp.ctx_lens)
+    kv_b = wl.kv_bytes(w, inp.ctx_lens)
+    att_ms, init_ms, ssd_ms = r["attention"]["mean"], r["init_state"]["mean"], r["ssd_scan"]["mean"]
+    peak = BF16_DENSE_TFLOPS if w.dtype == "bf16" else FP32_MATRIX_TFLOPS
+    ib = init_bytes(w)
+    return {
+        "attention": dict(ms=att_ms, algorithmic_bytes=att_b, kv_bytes=kv_b,
+                          gbs=att_b / (att_ms * 1e-3) / 1e9, hbm_frac=att_b / (att_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                          kv_frac=kv_b / (att_ms * 1e-3) / 1e9 / HBM_PEAK_GBS),
+        "init_state": dict(ms=init_ms, algorithmic_bytes=ib, gbs=ib / (init_ms * 1e-3) / 1e9,
+                           hbm_frac=ib / (init_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                           mfma_frac=2.0 * w.C * w.d_model * w.S / (init_ms * 1e-3) / 1e12 / peak,
+                           mfma_peak_tflops=peak),
+        "ssd_scan": dict(ms=ssd_ms, algorithmic_bytes=ssd_bytes(w), gbs=ssd_bytes(w) / (ssd_ms * 1e-3) / 1e9),
+    }
+
+
+def measure_configs(args, torch, flush, main_idx, main_result, main_inp):
+    """All five workloads, one entry each: the layer step and its parts."""
+    from hybrid_mamba_attention_amd import workloads as wl
+    out = {}
+    for idx in sorted(wl.WORKLOADS):
+        w = wl.WORKLOADS[idx]
+        print(f"[bench] workload {idx} {w.name}", file=sys.stderr, flush=True)
+        inp = main_inp if idx == main_idx else wl.make_inputs(w)
+        r = main_result if idx == main_idx else measure(w, inp, args, torch, flush)
+        ms = r["step"]["mean"]
+        out[str(idx)] = dict(workload=w.name, C=w.C, K=w.K, ctx=list(w.ctx), dtype=w.dtype,
+                             ctx_tokens=int(inp.ctx_lens.sum()), ms_per_step=ms,
+                             ms_per_step_graph=r["step_graph"]["mean"],
+                             block_tokens_per_s=w.C * w.K / (ms * 1e-3), plan=r["plan"],
+                             kernels=part_metrics(w, inp, r))
+        if inp is not main_inp:
+            del inp
+        torch.cuda.empty_cache()
+    return out
+
+
+def host_metadata(torch):
+    """Where the line was measured: the host CPU and thread count the CPU
+    baseline runs on, NumPy and its BLAS, and the ROCm / HIP / torch builds."""
+    import platform
+    import numpy as np
+    cpu = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = []
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [dict(library=os.path.basename(i.get("filepath", "")), internal_api=i.get("internal_api"),
+                     version=i.get("version"), threads=i.get("num_threads"))
+                for i in threadpool_info() if i.get("user_api") == "blas"]
+    except Exception:  # pragma: no cover
+        pass
+    rocm = None
+    for f in ("/opt/rocm/.info/version", "/opt/rocm/.info/version-dev"):
+        if os.path.exists(f):
+            rocm = open(f).read().strip()
+            break
+    return dict(cpu_model=cpu, host_threads=len(os.sched_getaffinity(0)), python=platform.python_version(),
+                numpy=np.__version__, blas=blas, rocm=rocm, hip_runtime=torch.version.hip, torch=torch.__version__,
+                gpu=torch.cuda.get_device_name(0))
 
 
 def measure_variants(w, inp, args, torch, flush):
@@ -359,6 +448,31 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
+def mfma_source_hash():
+    """Hash of the matrix-core kernels' sources (the state projection and the
+    block GEMMs), so the committed MFMA counters are used only while they apply."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "hybrid_mamba_attention_amd", "csrc")
+    for f in ("init_state.hip", "gemm.hip", "common.h"):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def mfma_from_profile(workload_name):
+    """Matrix-core utilisation per kernel from the committed counter record
+    (rocprofv3: SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE x SIMDs), or
+    None once the kernels have changed since it was taken."""
+    path = os.path.join(PROFILE_DIR, f"mfma_{workload_name}_counters.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("source_hash") != mfma_source_hash():
+        return None
+    return {k: dict(mfma_util=v["mfma_util"], counted_flops=v["counted_flops"], avg_us=v["avg_us"])
+            for k, v in rec["kernels"].items()}
+
+
 def traffic_from_profile(workload_name):
     path = os.path.join(PROFILE_DIR, f"k_block_attn_{workload_name}_traffic.json")
     if not os.path.exists(path):
@@ -367,6 +481,128 @@ def traffic_from_profile(workload_name):
     if rec.get("source_hash") != kernel_source_hash():
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+# ----------------------------------------------------------------------------
+# profiles/ records from rocprofv3 output (no GPU work)
+# ----------------------------------------------------------------------------
+
+SIMDS = 256 * 4          # MI355X: 256 CUs x 4 SIMDs
+KERNEL_KEYS = ("k_block_attn", "k_attn_merge", "k_init_wide", "k_init_state", "k_ssd_scan", "k_scan_merge",
+               "k_gemm_tn", "k_splitk_sum", "k_gate_norm", "__amd_rocclr_copyBuffer")
+
+
+def _rocprof_csv(d, what):
+    import glob
+    hits = sorted(glob.glob(os.path.join(d, "**", f"*{what}.csv"), recursive=True))
+    if not hits:
+        return []
+    import csv
+    with open(hits[0]) as f:
+        return list(csv.DictReader(f))
+
+
+def _short(name):
+    for k in KERNEL_KEYS:
+        if k in name:
+            return k
+    return None
+
+
+def _counter_table(d):
+    """{(kernel, grid): {counter: [value per dispatch]}} of a --pmc run."""
+    import collections
+    per = collections.defaultdict(dict)
+    for r in _rocprof_csv(d, "counter_collection"):
+        k = _short(r["Kernel_Name"])
+        if k is None:
+            continue
+        key = (k, int(r["Grid_Size"]), r["Dispatch_Id"])
+        per[key][r["Counter_Name"]] = per[key].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        per[key]["_us"] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+    out = collections.defaultdict(lambda: collections.defaultdict(list))
+    for (k, grid, _), cs in per.items():
+        for c, v in cs.items():
+            out[(k, grid)][c].append(v)
+    return out
+
+
+def summarize_profiles(dirs, workload_idx):
+    """Write profiles/k_block_attn_<w>_traffic.{json,md} (FETCH_SIZE and
+    WRITE_SIZE runs with the calibration copy) and profiles/mfma_<w>_counters.
+    {json,md} (an SQ_VALU_MFMA_BUSY_CYCLES / SQ_INSTS_VALU_MFMA_MOPS_BF16 /
+    GRBM_GUI_ACTIVE run) from rocprofv3 csv directories."""
+    import numpy as np
+    from hybrid_mamba_attention_amd import workloads as wl
+    w = wl.WORKLOADS[workload_idx]
+    inp = wl.make_inputs(w, parts=())
+    alg = {"k_block_attn": attention_bytes(w, inp.ctx_lens), "k_init_wide": init_bytes(w),
+           "k_ssd_scan": ssd_bytes(w)}
+    tables = {d: _counter_table(d) for d in dirs}
+    trace = {}
+    for d in dirs:
+        for r in _rocprof_csv(d, "kernel_trace"):
+            k = _short(r["Kernel_Name"])
+            if k:
+                trace.setdefault(k, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+
+    def find(counter):
+        for d, t in tables.items():
+            if any(counter in cs for cs in t.values()):
+                return d, t
+        return None, None
+
+    def main_grid(t, k):
+        """The kernel's most frequent grid (the benchmarked workload's launch)."""
+        grids = [(len(cs.get("_us", [])), g) for (kk, g), cs in t.items() if kk == k]
+        return max(grids)[1] if grids else None
+
+    written = []
+    fd, ft = find("FETCH_SIZE")
+    wd, wt = find("WRITE_SIZE")
+    if ft and wt:
+        def calib(t, c):
+            v = [max(cs[c]) for (k, g), cs in t.items() if k == "__amd_rocclr_copyBuffer" and c in cs]
+            return max(v)
+        copy_bytes = float(1 << 30)
+        fetch_factor = copy_bytes / (calib(ft, "FETCH_SIZE") * 1024)
+        write_factor = copy_bytes / (calib(wt, "WRITE_SIZE") * 1024)
+        rec = dict(workload=w.name, source_hash=kernel_source_hash(), fetch_factor=fetch_factor,
+                   write_factor=write_factor, kernels={},
+                   fetch_command=f"rocprofv3 --pmc FETCH_SIZE ... -d {fd}", write_command=f"... -d {wd}")
+        for k in ("k_block_attn", "k_init_wide", "k_ssd_scan"):
+            g = main_grid(ft, k)
+            if g is None:
+                continue
+            fk = float(np.mean(ft[(k, g)]["FETCH_SIZE"]))
+            wk = float(np.mean(wt[(k, g)]["WRITE_SIZE"])) if (k, g) in wt else 0.0
+            hb = fk * 1024 * fetch_factor + wk * 1024 * write_factor
+            rec["kernels"][k] = dict(grid_threads=g, fetch_kib=fk, write_kib=wk, hbm_bytes=hb,
+                                     algorithmic_bytes=alg.get(k), ratio=hb / alg[k] if k in alg else None)
+        rec["hbm_bytes_per_launch"] = rec["kernels"]["k_block_attn"]["hbm_bytes"]
+        if "k_block_attn" in trace:
+            rec["k_block_attn_avg_us_kernel_trace"] = float(np.mean(trace["k_block_attn"]))
+        path = os.path.join(PROFILE_DIR, f"k_block_attn_{w.name}_traffic.json")
+        json.dump(rec, open(path, "w"), indent=1)
+        written.append(path)
+    md_, mt = find("SQ_VALU_MFMA_BUSY_CYCLES")
+    if mt:
+        rec = dict(workload=w.name, source_hash=mfma_source_hash(), simds=SIMDS, kernels={})
+        for (k, g), cs in sorted(mt.items()):
+            if k == "__amd_rocclr_copyBuffer" or "SQ_VALU_MFMA_BUSY_CYCLES" not in cs:
+                continue
+            busy = float(np.mean(cs["SQ_VALU_MFMA_BUSY_CYCLES"]))
+            gui = float(np.mean(cs["GRBM_GUI_ACTIVE"])) if "GRBM_GUI_ACTIVE" in cs else None
+            mops = float(np.mean(cs.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", [0.0])))
+            rec["kernels"][f"{k} grid {g}"] = dict(
+                dispatches=len(cs["SQ_VALU_MFMA_BUSY_CYCLES"]), avg_us=float(np.mean(cs["_us"])),
+                mfma_busy_cycles=busy, gui_active_cycles=gui,
+                mfma_util=busy / (gui * SIMDS) if gui else None, counted_flops=mops * 512)
+        path = os.path.join(PROFILE_DIR, f"mfma_{w.name}_counters.json")
+        json.dump(rec, open(path, "w"), indent=1)
+        written.append(path)
+    for p in written:
+        print(p)
 
 
 # ----------------------------------------------------------------------------
@@ -410,6 +646,9 @@ def cpu_baseline(w, inp, n_req, min_seconds=10.0, max_seconds=30.0):
 
 def main():
     args = parse()
+    if args.summarize_profiles:
+        summarize_profiles(args.summarize_profiles, args.workload)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the drafter layer shards by request across GPUs with no exchange).", file=sys.stderr)
@@ -446,20 +685,14 @@ def main():
     ms = r["step"]["mean"]
     tokens = w.C * w.K
     kv_b = wl.kv_bytes(w, inp.ctx_lens)
-    att_b = attention_bytes(w, inp.ctx_lens)
-    att_ms = r["attention"]["mean"]
-    init_ms = r["init_state"]["mean"]
-    achieved = att_b / (att_ms * 1e-3) / 1e9
+    parts = part_metrics(w, inp, r)
+    att = parts["attention"]
+    achieved = att["gbs"]
     traffic = traffic_from_profile(w.name)
     kernels = {
-        "attention (k_block_attn; k_attn_merge when split)": dict(ms=att_ms, algorithmic_bytes=att_b,
-                                                        gbs=achieved, hbm_frac=achieved / HBM_PEAK_GBS),
-        "init_state (k_init_wide)": dict(ms=init_ms, algorithmic_bytes=init_bytes(w),
-                                          gbs=init_bytes(w) / (init_ms * 1e-3) / 1e9,
-                                          hbm_frac=init_bytes(w) / (init_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                                          mfma_frac=2.0 * w.C * w.d_model * w.S / (init_ms * 1e-3) / 1e12 / BF16_DENSE_TFLOPS),
-        "ssd_scan (k_ssd_scan)": dict(ms=r["ssd_scan"]["mean"], algorithmic_bytes=ssd_bytes(w),
-                                      gbs=ssd_bytes(w) / (r["ssd_scan"]["mean"] * 1e-3) / 1e9),
+        "attention (k_block_attn; k_attn_merge when a request spans ranges)": att,
+        "init_state (k_init_wide)": parts["init_state"],
+        "ssd_scan (k_ssd_scan)": parts["ssd_scan"],
     }
     line = {
         "metric": "drafted block-tokens/sec per drafter layer",
@@ -471,16 +704,17 @@ def main():
         "config": {"workload": w.name, "C": w.C, "K": w.K, "ctx": list(w.ctx), "Hq": w.Hq, "Hkv": w.Hkv,
                    "D": w.D, "d_model": w.d_model, "mamba_H_P_N_chunk": [w.H, w.P, w.N, w.chunk],
                    "kv_bytes_in_place": kv_b, "w_init_bytes": wl.w_init_bytes(w),
-                   "kv_split_pages": r["plan"][1], "work_items": r["plan"][0],
-                   "cache_flush_between_steps": not args.no_flush},
+                   "work_plan": r["plan"], "cache_flush_between_steps": not args.no_flush},
         "step_ms": r["step"],
         "step_ms_graph": r["step_graph"],
         "kernels": kernels,
-        "kv_read_gbs": kv_b / (att_ms * 1e-3) / 1e9,
-        "kv_read_frac_of_peak": kv_b / (att_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "kv_read_gbs": kv_b / (att["ms"] * 1e-3) / 1e9,
+        "kv_read_frac_of_peak": att["kv_frac"],
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": "k_block_attn"},
+        "mfma_counters": mfma_from_profile(w.name),
+        "host": host_metadata(torch),
     }
     if probe is not None:
         line["stream_read_probe"] = dict(probe, attention_frac_of_probe=achieved / probe["gbs"])
@@ -517,6 +751,8 @@ def main():
             if si is not inp:
                 del si
         line["sweep_ctx8192"] = sweep
+    if not args.no_configs:
+        line["configs"] = measure_configs(args, torch, flush, args.workload, r, inp)
     if not args.no_cpu:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(w, inp, n_req=min(w.C, 64))

@@ -72,12 +72,15 @@ struct AttnPlanShape {
   size_t plan_bytes, part_o_off, part_ml_off, total;
 };
 
-// Workgroups the automatic plan aims at: two per CU, one resident round of
-// the one-head forms at their occupancy (measured at 8192-token contexts,
-// C = 2..64: 512 work units beat both 256, too little in flight, and 1024,
-// twice the per-unit prologue and fp32 partials).  The head-pair form holds
-// one workgroup per CU and takes twice the ranges (two rounds).
-constexpr int kTargetGroups = 512;
+// (range, kv head) units the automatic plan aims at: two per CU, one
+// resident round of the one-head forms at their occupancy (measured at
+// 8192-token contexts, C = 2..64: 512 units beat both 256, too little in
+// flight, and 1024, twice the per-unit prologue and fp32 partials).  The
+// head-pair form takes the same ranges in half the workgroups, one round at
+// one workgroup per CU.  (Twice the ranges for it -- two rounds -- cut every
+// request of a uniform batch in two: C = 32 and 64 at 8192 tokens took 12%
+// and 9% longer.)
+constexpr int kTargetUnits = 512;
 
 // log2(page_size / 16) for a supported page size, else -1
 int page_shift(int page_size) {
@@ -104,11 +107,10 @@ AttnPlanShape plan_shape(int dtype, int C, int K, int Hq, int Hkv, int D, int64_
     p.head_pair = hp_ok && int64_t(p.range_gran) * p.gran >= 128;
   } else {
     p.range_gran = 0;
+    w_max = std::max<int64_t>(1, kTargetUnits / Hkv);
     // two heads per workgroup when the batch at its bound gives ranges of
-    // 128+ slabs with the head pair's range count
-    const int64_t w_hp = std::max<int64_t>(1, 2 * kTargetGroups / Hkv);
-    p.head_pair = hp_ok && tmax * p.gran >= 128 * std::min(w_hp, tmax);
-    w_max = std::max<int64_t>(1, (p.head_pair ? 2 : 1) * kTargetGroups / Hkv);
+    // 128+ slabs
+    p.head_pair = hp_ok && tmax * p.gran >= 128 * std::min(w_max, tmax);
   }
   w_max = std::max<int64_t>(1, std::min(w_max, tmax));   // a range holds at least one granule
   p.w_max = int(std::min<int64_t>(w_max, 0x7fffffff));
