@@ -16,6 +16,7 @@
 
 namespace hspec {
 size_t ssd_lds_bytes(int P, int N, int Q);
+bool ssd_chunk_fits(int chunk, int N, bool conv);
 }
 
 using namespace hspec;
@@ -44,12 +45,14 @@ int check_init(int dtype, int C, int d, int S, const void* u, const void* w, con
   return HSPEC_OK;
 }
 
-// shape limits of the scan (pointers are checked by the callers)
-int check_ssd_shape(int dtype, int C, int K, int H, int P, int ng, int N, int chunk) {
+// shape limits of the scan (pointers are checked by the callers); conv: the
+// Mamba-2 block's scan with the convolution fused into its loads
+int check_ssd_shape(int dtype, int C, int K, int H, int P, int ng, int N, int chunk, bool conv = false) {
   if (!dtype_ok(dtype) || C < 1 || K < 1 || H < 1 || P < 1 || N < 1 || ng < 1 || chunk < 1)
     return HSPEC_ERR_INVALID_ARG;
   if (H % ng) return HSPEC_ERR_INVALID_ARG;
-  if (chunk > 16 || (chunk & (chunk - 1))) return HSPEC_ERR_UNSUPPORTED;
+  if (chunk > 64 || (chunk & (chunk - 1))) return HSPEC_ERR_UNSUPPORTED;
+  if (!ssd_chunk_fits(chunk, N, conv)) return HSPEC_ERR_UNSUPPORTED;
   if (P > 128 || N > 128) return HSPEC_ERR_UNSUPPORTED;
   if (ssd_lds_bytes(P, N, chunk) > kMaxLds) return HSPEC_ERR_UNSUPPORTED;
   if (int64_t(C) * H > 0x7fffffff) return HSPEC_ERR_UNSUPPORTED;
@@ -248,7 +251,7 @@ int check_block(const hspec_mamba_args* a) {
     if (!aligned(q, 16)) return HSPEC_ERR_INVALID_ARG;
   if (!(a->norm_eps >= 0.f) || !std::isfinite(a->norm_eps)) return HSPEC_ERR_INVALID_ARG;
   // the scan's own limits (its inputs are workspace buffers here)
-  const int st = check_ssd_shape(HSPEC_F32, a->C, a->K, a->H, a->P, a->ng, a->N, a->chunk);
+  const int st = check_ssd_shape(HSPEC_F32, a->C, a->K, a->H, a->P, a->ng, a->N, a->chunk, true);
   if (st != HSPEC_OK) return st;
   const int64_t d_inner = int64_t(a->H) * a->P;
   const int64_t d_proj = 2 * d_inner + 2 * int64_t(a->ng) * a->N + a->H;

@@ -71,10 +71,11 @@ struct SsdArgs {
   int d_proj, d_inner;
 };
 hipError_t launch_ssd_scan(hipStream_t st, int dtype, const SsdArgs& a);
-// The drafter layer's last launch at small C: a2's scan and a4's merge of the
-// attention's split partials in one grid (scan workgroups first).  Only for
-// bf16 activations, N % 4 == 0, D = 128 and no fused convolution (scan_merge_fits);
-// otherwise the two kernels run one after the other.
+// The drafter layer's last launch: a2's scan and a4's merge of the
+// attention's partials in one grid (scan workgroups first).  Only for bf16
+// activations, N % 4 == 0, chunks of at most 16, D = 128 and no fused
+// convolution (scan_merge_fits); otherwise the two kernels run one after the
+// other.
 bool scan_merge_fits(int dtype, const SsdArgs& s, const AttnArgs& m);
 hipError_t launch_scan_merge(hipStream_t st, const SsdArgs& s, const AttnArgs& m);
 

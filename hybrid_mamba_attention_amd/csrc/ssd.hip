@@ -26,20 +26,23 @@
 
 namespace hspec {
 
-constexpr int kSsdQ = 16;  // largest chunk (positions staged per pass)
-
-// Static LDS, in floats.  sB / sC rows are padded to NMAX + 4 so the
-// per-thread Cm.B^T dot products (rows t and s in different lanes) spread
-// over the banks; every other read is a wave-wide broadcast.
-template <int NMAX> struct SsdLds {
+// Static LDS, in floats, for chunks of up to QM positions (16, 32 or 64:
+// the whole chunk is staged at once, so the intra-chunk decay matrix spans
+// it).  sB / sC rows are padded to NMAX + 4 so the per-thread Cm.B^T dot
+// products (rows t and s in different lanes) spread over the banks; every
+// other read is a wave-wide broadcast.
+template <int NMAX, int QM> struct SsdLds {
   static constexpr int LDB = NMAX + 4;
-  static constexpr int oB = 0;                        // sB[Q][LDB]   B_s
-  static constexpr int oC = oB + kSsdQ * LDB;         // sC[Q][LDB]   Cm_t
-  static constexpr int oCB = oC + kSsdQ * LDB;        // sCB[Q][Q]    Cm_t . B_s at [t][s]
-  static constexpr int oWave = oCB + kSsdQ * kSsdQ;   // per wave: lam[Q], w[Q], dt[Q], pad[Q], M[Q][Q]
-  static constexpr int WAVE = 4 * kSsdQ + kSsdQ * kSsdQ;
+  static constexpr int oB = 0;                        // sB[QM][LDB]   B_s
+  static constexpr int oC = oB + QM * LDB;            // sC[QM][LDB]   Cm_t
+  static constexpr int oCB = oC + QM * LDB;           // sCB[QM][QM]   Cm_t . B_s at [t][s]
+  static constexpr int oWave = oCB + QM * QM;         // per wave: lam, w, dt, pad [QM]; M[QM][QM]
+  static constexpr int WAVE = 4 * QM + QM * QM;
   static constexpr int floats = oWave + 4 * WAVE;
 };
+
+// the smallest chunk capacity that holds a chunk
+inline int ssd_chunk_cap(int chunk) { return chunk <= 16 ? 16 : chunk <= 32 ? 32 : 64; }
 
 // Heads per workgroup: as many as fit in 4 waves and divide the heads of one
 // B/Cm group (so a workgroup never spans two groups).
@@ -63,11 +66,12 @@ __host__ __device__ inline int ssd_heads_per_block(int H, int ng, int P) {
 // issued.
 // The scan of workgroup `bid` (a device function so that the drafter layer's
 // combined scan + merge launch runs the same code).
-template <typename T, int NMAX, bool V4, bool CONV>
+template <typename T, int NMAX, int QM, bool V4, bool CONV>
 __device__ __forceinline__ void ssd_scan_block(const SsdArgs& a, int bid) {
-  using L = SsdLds<NMAX>;
-  constexpr int Q = kSsdQ, LDB = L::LDB;
+  using L = SsdLds<NMAX, QM>;
+  constexpr int Q = QM, LDB = L::LDB;
   constexpr int E = Q * NMAX / 256;  // B and Cm entries staged per thread
+  static_assert(Q * NMAX % 256 == 0 && Q <= 64, "whole staging rounds; one lane per chunk position");
   __shared__ __align__(16) float lds[L::floats];
   const int H = a.H, P = a.P, N = a.N, K = a.K, QC = a.chunk;
   const int RB = (P + 63) >> 6;
@@ -207,9 +211,10 @@ __device__ __forceinline__ void ssd_scan_block(const SsdArgs& a, int bid) {
       }
     }
     __syncthreads();
-    // head-independent Cm_t . B_s of the group (one entry per thread)
-    {
-      const int t = tid / Q, s = tid % Q;
+    // head-independent Cm_t . B_s of the group (Q*Q / 256 entries per thread)
+#pragma unroll
+    for (int i = tid; i < Q * Q; i += 256) {
+      const int t = i / Q, s = i % Q;
       const float* cr = sC + t * LDB;
       const float* br = sB + s * LDB;
       float d0 = 0.f, d1 = 0.f;
@@ -222,11 +227,11 @@ __device__ __forceinline__ void ssd_scan_block(const SsdArgs& a, int bid) {
         d0 = fmaf(c.z, bb.z, d0);
         d1 = fmaf(c.w, bb.w, d1);
       }
-      sCB[tid] = d0 + d1;
+      sCB[i] = d0 + d1;
     }
     __syncthreads();
     // this head's decay-weighted M, masked before the exponential
-#pragma unroll
+#pragma unroll 4
     for (int j = 0; j < Q * Q / 64; ++j) {
       const int i = lane + 64 * j;
       const int t = i / Q, s = i % Q;
@@ -236,7 +241,37 @@ __device__ __forceinline__ void ssd_scan_block(const SsdArgs& a, int bid) {
     }
     __syncthreads();
     // y[t, p] = exp(lam_t) H_in[p, :] . Cm_t + sum_{s <= t} M[t, s] x[s, p] + D x[t, p]
-    if (own) {
+    if (own && Q > 16) {
+      // Chunks of 32 or 64: one position per loop trip, the full row of M
+      // (zero past t) against the lane's x values, so the code grows with
+      // Q instead of Q^2 (the unrolled triangle took minutes to compile).
+#pragma unroll 1
+      for (int t = 0; t < q; ++t) {
+        const float* cr = sC + t * LDB;
+        float z0 = 0.f, z1 = 0.f;
+#pragma unroll
+        for (int n = 0; n < NMAX; n += 4) {
+          const float4 c = *reinterpret_cast<const float4*>(cr + n);
+          z0 = fmaf(Hs[n], c.x, z0);
+          z1 = fmaf(Hs[n + 1], c.y, z1);
+          z0 = fmaf(Hs[n + 2], c.z, z0);
+          z1 = fmaf(Hs[n + 3], c.w, z1);
+        }
+        float z = (z0 + z1) * __expf(slam[t]);
+        const float* mr = sM + t * Q;
+        float xt = 0.f;
+#pragma unroll
+        for (int s = 0; s < Q; s += 4) {
+          const float4 m = *reinterpret_cast<const float4*>(mr + s);
+          z = fmaf(m.x, xs[s], z);
+          z = fmaf(m.y, xs[s + 1], z);
+          z = fmaf(m.z, xs[s + 2], z);
+          z = fmaf(m.w, xs[s + 3], z);
+          xt = s == (t & ~3) ? ((t & 3) == 0 ? xs[s] : (t & 3) == 1 ? xs[s + 1] : (t & 3) == 2 ? xs[s + 2] : xs[s + 3]) : xt;
+        }
+        yrow[size_t(c0 + t) * HP] = fmaf(Dh, xt, z);
+      }
+    } else if (own) {
 #pragma unroll
       for (int t = 0; t < Q; ++t) {
         if (t < q) {
@@ -301,9 +336,9 @@ __device__ __forceinline__ void ssd_scan_block(const SsdArgs& a, int bid) {
   }
 }
 
-template <typename T, int NMAX, bool V4, bool CONV>
+template <typename T, int NMAX, int QM, bool V4, bool CONV>
 __global__ __launch_bounds__(256) void k_ssd_scan(SsdArgs a) {
-  ssd_scan_block<T, NMAX, V4, CONV>(a, blockIdx.x);
+  ssd_scan_block<T, NMAX, QM, V4, CONV>(a, blockIdx.x);
 }
 
 // Workgroups [0, n_scan) run the scan, the rest the merge of the attention's
@@ -314,7 +349,7 @@ template <int NMAX, int LPO, int U>
 __global__ __launch_bounds__(256) void k_scan_merge(SsdArgs s, AttnArgs m, int n_scan) {
   const int bid = blockIdx.x;
   if (bid < n_scan) {
-    ssd_scan_block<bf16_t, NMAX, true, false>(s, bid);
+    ssd_scan_block<bf16_t, NMAX, 16, true, false>(s, bid);
   } else {
     const int r = bid - n_scan, ch = m.C * m.Hkv;
     attn_merge_block<bf16_t, 128, LPO, U>(m, r % ch, r / ch);
@@ -323,11 +358,18 @@ __global__ __launch_bounds__(256) void k_scan_merge(SsdArgs s, AttnArgs m, int n
 
 size_t ssd_lds_bytes(int P, int N, int Q) {
   (void)P;
-  (void)Q;
-  if (N <= 16) return SsdLds<16>::floats * sizeof(float);
-  if (N <= 32) return SsdLds<32>::floats * sizeof(float);
-  if (N <= 64) return SsdLds<64>::floats * sizeof(float);
-  return SsdLds<128>::floats * sizeof(float);
+  const int qm = ssd_chunk_cap(Q);
+  auto by_n = [&](auto QC) -> size_t {
+    constexpr int QM = decltype(QC)::value;
+    if (N <= 16) return SsdLds<16, QM>::floats * sizeof(float);
+    if (N <= 32) return SsdLds<32, QM>::floats * sizeof(float);
+    if (N <= 64) return SsdLds<64, QM>::floats * sizeof(float);
+    return SsdLds<128, QM>::floats * sizeof(float);
+  };
+  if (qm == 16) return by_n(std::integral_constant<int, 16>{});
+  // chunks of 32 and 64 run with a state capacity of 64
+  if (qm == 32) return SsdLds<64, 32>::floats * sizeof(float);
+  return SsdLds<64, 64>::floats * sizeof(float);
 }
 
 template <typename T, int NMAX>
@@ -337,25 +379,44 @@ static hipError_t launch_n(hipStream_t st, const SsdArgs& a) {
   if constexpr (std::is_same<T, float>::value) {
     if (a.zx) {
       if (a.N % 4 == 0)
-        hipLaunchKernelGGL((k_ssd_scan<T, NMAX, true, true>), grid, block, 0, st, a);
+        hipLaunchKernelGGL((k_ssd_scan<T, NMAX, 16, true, true>), grid, block, 0, st, a);
       else
-        hipLaunchKernelGGL((k_ssd_scan<T, NMAX, false, true>), grid, block, 0, st, a);
+        hipLaunchKernelGGL((k_ssd_scan<T, NMAX, 16, false, true>), grid, block, 0, st, a);
       return hipGetLastError();
     }
   }
   if (a.N % 4 == 0)
-    hipLaunchKernelGGL((k_ssd_scan<T, NMAX, true, false>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((k_ssd_scan<T, NMAX, 16, true, false>), grid, block, 0, st, a);
   else
-    hipLaunchKernelGGL((k_ssd_scan<T, NMAX, false, false>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((k_ssd_scan<T, NMAX, 16, false, false>), grid, block, 0, st, a);
+  return hipGetLastError();
+}
+
+// Chunks of 32 or 64 positions: the plain scan (no fused convolution), with
+// N % 4 == 0 and N <= 64 (ssd_chunk_fits; the host refuses the rest).
+template <typename T, int QM>
+static hipError_t launch_big_chunk(hipStream_t st, const SsdArgs& a) {
+  const int hpw = ssd_heads_per_block(a.H, a.ng, a.P);
+  const dim3 grid(a.C * (a.H / hpw)), block(256);
+  // one state capacity (64) for all of them: each chunk size unrolls Q^2 / 2
+  // multiply-adds per lane, and more instantiations cost minutes of build
+  hipLaunchKernelGGL((k_ssd_scan<T, 64, QM, true, false>), grid, block, 0, st, a);
   return hipGetLastError();
 }
 
 template <typename T>
 static hipError_t launch_t(hipStream_t st, const SsdArgs& a) {
+  const int qm = ssd_chunk_cap(a.chunk);
+  if (qm == 32) return launch_big_chunk<T, 32>(st, a);
+  if (qm == 64) return launch_big_chunk<T, 64>(st, a);
   if (a.N <= 16) return launch_n<T, 16>(st, a);
   if (a.N <= 32) return launch_n<T, 32>(st, a);
   if (a.N <= 64) return launch_n<T, 64>(st, a);
   return launch_n<T, 128>(st, a);
+}
+
+bool ssd_chunk_fits(int chunk, int N, bool conv) {
+  return chunk <= 16 || (!conv && N % 4 == 0 && N <= 64);
 }
 
 hipError_t launch_ssd_scan(hipStream_t st, int dtype, const SsdArgs& a) {
@@ -363,7 +424,7 @@ hipError_t launch_ssd_scan(hipStream_t st, int dtype, const SsdArgs& a) {
 }
 
 bool scan_merge_fits(int dtype, const SsdArgs& s, const AttnArgs& m) {
-  return dtype == 1 && !s.zx && s.N % 4 == 0 && m.D == 128 && m.w_max > 1;
+  return dtype == 1 && !s.zx && s.N % 4 == 0 && s.chunk <= 16 && m.D == 128 && m.w_max > 1;
 }
 
 // The merge part takes the configuration k_attn_merge would (LPO lanes per

@@ -102,8 +102,10 @@ int hspec_init_state(void* stream, int dtype, int C, int d_model, int S,
  *   h0      fp32 [C, H, P, N] or NULL (NULL = zero state); the layout of a1's h0
  *   y       fp32 [C, K, H, P]     output
  *   h_final fp32 [C, H, P, N] or NULL: the state after the last block position
- * Limits: chunk in {1,2,4,8,16}; P <= 128; N <= 128; ng
- * divides H (else INVALID_ARG / UNSUPPORTED).
+ * Limits: chunk in {1, 2, 4, 8, 16, 32, 64} (the whole chunk is staged at
+ * once: its decay matrix spans all its positions); chunks of 32 and 64 take
+ * N <= 64 with N % 4 == 0; P <= 128; N <= 128; ng divides H (else
+ * INVALID_ARG / UNSUPPORTED).
  */
 int hspec_ssd_scan(void* stream, int dtype, int C, int K, int H, int P, int ng, int N, int chunk,
                    const void* x, const float* delta, const float* A,
@@ -286,7 +288,8 @@ int hspec_draft_layer_graph(const hspec_layer_args* a, hspec_graph* out);
  * normalised activations are rounded to the activation type before the
  * output projection.  `workspace` == NULL is a size query as for a3
  * (256-byte aligned device memory otherwise).
- * Limits: d_model % 8 == 0, d_inner % 8 == 0, the scan limits of a2,
+ * Limits: d_model % 8 == 0, d_inner % 8 == 0, the scan limits of a2 with
+ * chunk <= 16 (the convolution runs inside the scan's 16-position staging),
  * C*K <= 2^30 and C*K * max(d_in_proj, d_model) <= 2^40 (else UNSUPPORTED);
  * hidden, w_in, w_out, out, conv_w and norm_w 16-byte aligned (else
  * INVALID_ARG).

@@ -67,7 +67,9 @@ def _ssd(no_y=False, **kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(K=0), INVALID), (dict(ng=3), INVALID), (dict(no_y=True), INVALID),
-    (dict(chunk=12), UNSUPPORTED), (dict(chunk=32), UNSUPPORTED), (dict(P=256), UNSUPPORTED),
+    (dict(chunk=12), UNSUPPORTED), (dict(chunk=128), UNSUPPORTED), (dict(P=256), UNSUPPORTED),
+    # chunks of 32 and 64 take states of up to 64 with N % 4 == 0
+    (dict(chunk=32, N=128), UNSUPPORTED), (dict(chunk=64, N=66), UNSUPPORTED),
 ])
 def test_ssd_validation(kw, code):
     assert _ssd(**kw) == code

@@ -304,6 +304,13 @@ SSD_CASES = [
     # many chunks
     (2, 64, 4, 64, 1, 32, 16, "bf16", False, False),
     (1, 64, 4, 64, 1, 32, 1, "f32", True, False),
+    # chunks of 32 and 64: several chunks with a partial last one, a block
+    # shorter than one chunk, groups, the skip term, the largest state they take
+    (2, 80, 4, 64, 1, 32, 32, "bf16", True, False),
+    (3, 70, 8, 64, 2, 64, 64, "bf16", False, False),
+    (2, 40, 4, 64, 1, 16, 64, "f32", True, False),
+    (1, 33, 2, 128, 1, 8, 32, "f32", False, True),
+    (2, 128, 4, 64, 1, 32, 64, "bf16", True, False),
 ]
 
 
