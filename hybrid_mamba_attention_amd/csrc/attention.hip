@@ -334,6 +334,21 @@ template <typename T, int D> struct StageGeom {
   __host__ __device__ static constexpr int pos(int row, int chunk) { return row * CPR + (chunk ^ (row % SWZ)); }
 };
 
+// The 16-byte d-chunk of its head that V-operand lane li reads (bf16,
+// D = 128, where each lane reads one chunk of each token row).
+// ds_read_b128 serves a wave in four passes of 16 lanes: the lanes that share
+// bit 5 and the parity of bits 2..4 (lanes 0-3, 12-15, 20-23 and 24-27 form
+// one pass, as an LDS access-pattern probe of this GPU measures).  A V read
+// puts lane groups lg = 2m and 2m+1 (token rows 4lg + e) in each pass; with
+// chunk li, the row swizzle maps the two groups' lanes onto the same eight
+// bank groups (a 2-way conflict on every V read).  Here lanes 0-3 and 12-15
+// read chunks 0-7 and lanes 4-11 chunks 8-15, so the two groups of a pass
+// cover all sixteen bank groups.  The stage layout is unchanged; the output
+// rows follow the same permutation (d = vchunk(i) * 8 + cc).
+__host__ __device__ constexpr int vchunk(int i) {
+  return (i & 3) | ((((i >> 2) ^ (i >> 3)) & 1) << 3) | (((i >> 3) & 1) << 2);
+}
+
 template <typename T, int D> struct AttnLds {
   using G = StageGeom<T, D>;
   static constexpr size_t bytes = size_t(2) * 2 * G::TILE * 16;  // {K,V} x double buffer
@@ -442,7 +457,10 @@ __global__ __launch_bounds__(64 * NW, (RT == 2 && sizeof(T) == 2) ? 2 : 1) void 
   for (int ds = 0; ds < DS; ++ds)
 #pragma unroll
     for (int h = 0; h < 8 / EPC; ++h) kpos[ds][h] = Gm::pos(li, hchunk + (lg + 4 * ds) * 8 / EPC + h) * 16;
-  // V rows: token 4*lg + e of page 0 (page 1 is +16 rows), elements li*DPL ..
+  // V rows: token 4*lg + e of page 0 (page 1 is +16 rows), elements
+  // dch(li)*DPL .. (dch: vchunk for one 16-byte chunk per lane, else identity)
+  constexpr bool kVPerm = DPL * sizeof(T) == 16;
+  auto dch = [](int i) { return kVPerm ? vchunk(i) : i; };
   uint32_t vpos[4][DPL * sizeof(T) > 16 ? 2 : 1];
   constexpr int VCH = DPL * sizeof(T) > 16 ? 2 : 1;
 #pragma unroll
@@ -450,7 +468,7 @@ __global__ __launch_bounds__(64 * NW, (RT == 2 && sizeof(T) == 2) ? 2 : 1) void 
 #pragma unroll
     for (int h = 0; h < VCH; ++h) {
       const int row = 4 * lg + e;
-      const int e0 = hl * D + li * DPL + h * EPC;  // first element of this chunk piece
+      const int e0 = hl * D + dch(li) * DPL + h * EPC;  // first element of this chunk piece
       vpos[e][h] = Gm::pos(row, e0 / EPC) * 16 + (e0 % EPC) * sizeof(T);
     }
 
@@ -794,7 +812,7 @@ __global__ __launch_bounds__(64 * NW, (RT == 2 && sizeof(T) == 2) ? 2 : 1) void 
       });
     }
 
-    // store: lane holds row li of each tile and d = (4*lg + r)*DPL + cc
+    // store: lane holds row li of each tile and d = dch(4*lg + r)*DPL + cc
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
       const float lsum = group4_sum(acc.l[rt]);
@@ -806,7 +824,7 @@ __global__ __launch_bounds__(64 * NW, (RT == 2 && sizeof(T) == 2) ? 2 : 1) void 
         const float inv = 1.f / lsum;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          T* dst = o + (4 * lg + r) * DPL;
+          T* dst = o + dch(4 * lg + r) * DPL;
           if constexpr (sizeof(T) == 2) {
             if constexpr (DPL == 8) {
               uint4 pk;
@@ -834,7 +852,7 @@ __global__ __launch_bounds__(64 * NW, (RT == 2 && sizeof(T) == 2) ? 2 : 1) void 
         float* po = a.part_o + prow * D;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          float* dst = po + (4 * lg + r) * DPL;
+          float* dst = po + dch(4 * lg + r) * DPL;
 #pragma unroll
           for (int cc = 0; cc < DPL; cc += 4)
             *reinterpret_cast<float4*>(dst + cc) =

@@ -1,7 +1,9 @@
 /*
- * hspec_probe.h -- measurement aid of libhspec.so (not part of the drafter
+ * hspec_probe.h -- measurement aids of libhspec.so (not part of the drafter
  * layer): the HBM read bandwidth this GPU actually sustains, against which the
- * in-place KV attention's bandwidth is reported next to the vendor peak.
+ * in-place KV attention's bandwidth is reported next to the vendor peak; and
+ * the LDS cost of one wave-wide access pattern, with which the attention
+ * stage's LDS reads and writes are profiled one kind at a time.
  */
 #ifndef HSPEC_PROBE_H
 #define HSPEC_PROBE_H
@@ -25,6 +27,22 @@ extern "C" {
  * and returns HSPEC_OK (0), HSPEC_ERR_INVALID_ARG (-1) or HSPEC_ERR_HIP (-4).
  */
 int hspec_probe_stream_read(void* stream, const void* buf, size_t bytes, uint32_t* sink);
+
+/*
+ * LDS access-pattern probe: `grid` workgroups of four waves, each with 16 KiB
+ * of LDS, every wave repeating one access `iters` times (a multiple of 8, at
+ * most 2^20) with lane l at byte offset offsets[l] of the workgroup's LDS.
+ * kind 0: 16-byte read (ds_read_b128), 1: 16-byte write (ds_write_b128),
+ * 2: 8-byte read (ds_read_b64).  `offsets` is a HOST array of 64 entries, each
+ * aligned to the access size and inside the 16 KiB; the kernel touches no
+ * global memory except `sink` (one device uint32), written only if the
+ * folded data hit a fixed value.  Used under a counter profiler: per
+ * dispatch, SQ_LDS_BANK_CONFLICT over SQ_INSTS_LDS is the conflict cost of
+ * the pattern.  Enqueues on `stream`; returns HSPEC_OK (0),
+ * HSPEC_ERR_INVALID_ARG (-1) or HSPEC_ERR_HIP (-4).
+ */
+int hspec_probe_lds_pattern(void* stream, int kind, const uint32_t* offsets, int iters, int grid,
+                            uint32_t* sink);
 
 #ifdef __cplusplus
 }

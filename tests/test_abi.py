@@ -29,7 +29,7 @@ def test_loads_and_exports_every_declared_symbol():
     assert {"hspec_init_state", "hspec_ssd_scan", "hspec_block_attn_inplace",
             "hspec_draft_layer", "hspec_mamba_block", "hspec_kv_inject", "hspec_draft_stack",
             "hspec_draft_stack_graph", "hspec_graph_launch", "hspec_graph_destroy",
-            "hspec_probe_stream_read"} <= set(names)
+            "hspec_probe_stream_read", "hspec_probe_lds_pattern"} <= set(names)
     for n in names:
         assert hasattr(L, n), f"{n} declared in hspec.h but not exported"
     assert L.hspec_abi_version() == ops.ABI_VERSION == 8
@@ -132,6 +132,19 @@ def test_probe_validation():
     assert f(None, FAKE, 100, FAKE) == INVALID          # not a multiple of 16
     assert f(None, FAKE + 8, 1 << 20, FAKE) == INVALID  # misaligned
     assert f(None, None, 1 << 20, FAKE) == INVALID
+    g = ops.lib().hspec_probe_lds_pattern
+    g.restype = ctypes.c_int
+    g.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.POINTER(ctypes.c_uint32), ctypes.c_int, ctypes.c_int,
+                  ctypes.c_void_p]
+    good = (ctypes.c_uint32 * 64)(*[16 * l for l in range(64)])
+    bad_align = (ctypes.c_uint32 * 64)(*([8] + [16 * l for l in range(1, 64)]))
+    past_end = (ctypes.c_uint32 * 64)(*([16384] + [0] * 63))
+    assert g(None, 3, good, 64, 1, FAKE) == INVALID            # no such kind
+    assert g(None, 0, good, 12, 1, FAKE) == INVALID            # not a multiple of 8
+    assert g(None, 0, good, 64, 0, FAKE) == INVALID            # empty grid
+    assert g(None, 0, good, 64, 1, None) == INVALID            # no sink
+    assert g(None, 0, bad_align, 64, 1, FAKE) == INVALID       # 16-byte access at an 8-byte offset
+    assert g(None, 2, past_end, 64, 1, FAKE) == INVALID        # 8-byte read past the 16 KiB
 
 
 def _layer(**kw):
