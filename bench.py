@@ -488,8 +488,28 @@ def traffic_from_profile(workload_name):
 # ----------------------------------------------------------------------------
 
 SIMDS = 256 * 4          # MI355X: 256 CUs x 4 SIMDs
+XCDS = 8                 # GRBM_GUI_ACTIVE is reported summed over the 8 XCDs' instances
 KERNEL_KEYS = ("k_block_attn", "k_attn_merge", "k_init_wide", "k_init_state", "k_ssd_scan", "k_scan_merge",
                "k_gemm_tn", "k_splitk_sum", "k_gate_norm", "__amd_rocclr_copyBuffer")
+_BENCH = "python3 bench.py --steps {steps} --warmup {warmup} --no-sweep --no-cpu --no-variants --no-stack --no-configs"
+# The passes the profiles/ summaries come from, each a run of its own, from the
+# repository root on one MI355X with TMPDIR=/tmp (counters are never combined
+# with trace domains; each --pmc set fits one hardware pass).
+PROFILE_PASSES = {
+    "trace": "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof_trace -o run -- "
+             + _BENCH.format(steps=10, warmup=3) + " --calib-copy",
+    "fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/prof_fetch -o run -- "
+             + _BENCH.format(steps=3, warmup=1) + " --no-block --no-inject --no-probe --calib-copy",
+    "write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/prof_write -o run -- "
+             + _BENCH.format(steps=3, warmup=1) + " --no-block --no-inject --no-probe --calib-copy",
+    "mfma": "rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 GRBM_GUI_ACTIVE "
+            "--output-format csv -d gpurun_out/prof_mfma -o run -- "
+            + _BENCH.format(steps=3, warmup=1) + " --no-inject --no-probe",
+    "sq": "rocprofv3 --pmc SQ_WAVES SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_WAIT_INST_ANY SQ_ACTIVE_INST_VALU "
+          "SQ_ACTIVE_INST_LDS SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU GRBM_GUI_ACTIVE "
+          "--output-format csv -d gpurun_out/prof_sq -o run -- "
+          + _BENCH.format(steps=3, warmup=1) + " --no-block --no-inject --no-probe",
+}
 
 
 def _rocprof_csv(d, what):
@@ -509,8 +529,14 @@ def _short(name):
     return None
 
 
+def _instance(name):
+    """A kernel's name with its template arguments, without the parameter list."""
+    n = (name[5:] if name.startswith("void ") else name).replace("(anonymous namespace)::", "")
+    return n.split("(")[0]
+
+
 def _counter_table(d):
-    """{(kernel, grid): {counter: [value per dispatch]}} of a --pmc run."""
+    """{(kernel, grid): {counter: [value per dispatch], "_us": [...], "_name": [...]}} of a --pmc run."""
     import collections
     per = collections.defaultdict(dict)
     for r in _rocprof_csv(d, "counter_collection"):
@@ -520,6 +546,7 @@ def _counter_table(d):
         key = (k, int(r["Grid_Size"]), r["Dispatch_Id"])
         per[key][r["Counter_Name"]] = per[key].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
         per[key]["_us"] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        per[key]["_name"] = _instance(r["Kernel_Name"])
     out = collections.defaultdict(lambda: collections.defaultdict(list))
     for (k, grid, _), cs in per.items():
         for c, v in cs.items():
@@ -527,11 +554,39 @@ def _counter_table(d):
     return out
 
 
+def _write(path, text, written):
+    with open(path, "w") as fh:
+        fh.write(text)
+    written.append(path)
+
+
+def _stats_md(d, w, written):
+    """Kernel-time table of a --kernel-trace --stats run."""
+    rows = _rocprof_csv(d, "kernel_stats")
+    if not rows:
+        return
+    lines = [f"# Kernel time summary: drafter layer and Mamba-2 block, workload {w.name}", "",
+             "Command (from the repository root, on one MI355X; TMPDIR=/tmp):", "", "    " + PROFILE_PASSES["trace"], "",
+             "The run times 10 drafter-layer calls and 10 calls of each of its entry points alone, then the "
+             "Mamba-2 block (hspec_mamba_block) and the drafter-side KV-injection contrast at C = 4 ... 128, each "
+             "call after a 2 GiB read that evicts L2 and the Infinity Cache (the at::native reduce_kernel rows); "
+             "the 1 GiB __amd_rocclr_copyBuffer rows are the counter-calibration copy and the k_stream_read rows "
+             "the bandwidth probe.", "",
+             "| kernel | calls | avg us | min us | max us | share of GPU time |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        name = r["Name"] if "Name" in r else r.get("KernelName", "")
+        lines.append(f"| `{_instance(name)[:100]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f}% |")
+    _write(os.path.join(PROFILE_DIR, f"layer_and_block_{w.name}_kernel_stats.md"), "\n".join(lines) + "\n", written)
+
+
 def summarize_profiles(dirs, workload_idx):
-    """Write profiles/k_block_attn_<w>_traffic.{json,md} (FETCH_SIZE and
-    WRITE_SIZE runs with the calibration copy) and profiles/mfma_<w>_counters.
-    {json,md} (an SQ_VALU_MFMA_BUSY_CYCLES / SQ_INSTS_VALU_MFMA_MOPS_BF16 /
-    GRBM_GUI_ACTIVE run) from rocprofv3 csv directories."""
+    """Write the profiles/ records of the benchmarked workload from rocprofv3
+    csv directories (the PROFILE_PASSES runs): the kernel-time table of the
+    trace run; k_block_attn_<w>_traffic.{json,md} from the FETCH_SIZE and
+    WRITE_SIZE runs with their calibration copy; mfma_<w>_counters.{json,md}
+    (matrix-core busy share per kernel) and sq_<w>_counters.md (where the
+    waves of the main kernels spend their cycles)."""
     import numpy as np
     from hybrid_mamba_attention_amd import workloads as wl
     w = wl.WORKLOADS[workload_idx]
@@ -540,11 +595,13 @@ def summarize_profiles(dirs, workload_idx):
            "k_ssd_scan": ssd_bytes(w)}
     tables = {d: _counter_table(d) for d in dirs}
     trace = {}
+    written = []
     for d in dirs:
         for r in _rocprof_csv(d, "kernel_trace"):
             k = _short(r["Kernel_Name"])
             if k:
                 trace.setdefault(k, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        _stats_md(d, w, written)
 
     def find(counter):
         for d, t in tables.items():
@@ -557,7 +614,6 @@ def summarize_profiles(dirs, workload_idx):
         grids = [(len(cs.get("_us", [])), g) for (kk, g), cs in t.items() if kk == k]
         return max(grids)[1] if grids else None
 
-    written = []
     fd, ft = find("FETCH_SIZE")
     wd, wt = find("WRITE_SIZE")
     if ft and wt:
@@ -569,7 +625,7 @@ def summarize_profiles(dirs, workload_idx):
         write_factor = copy_bytes / (calib(wt, "WRITE_SIZE") * 1024)
         rec = dict(workload=w.name, source_hash=kernel_source_hash(), fetch_factor=fetch_factor,
                    write_factor=write_factor, kernels={},
-                   fetch_command=f"rocprofv3 --pmc FETCH_SIZE ... -d {fd}", write_command=f"... -d {wd}")
+                   fetch_command=PROFILE_PASSES["fetch"], write_command=PROFILE_PASSES["write"])
         for k in ("k_block_attn", "k_init_wide", "k_ssd_scan"):
             g = main_grid(ft, k)
             if g is None:
@@ -585,22 +641,78 @@ def summarize_profiles(dirs, workload_idx):
         path = os.path.join(PROFILE_DIR, f"k_block_attn_{w.name}_traffic.json")
         json.dump(rec, open(path, "w"), indent=1)
         written.append(path)
-    md_, mt = find("SQ_VALU_MFMA_BUSY_CYCLES")
+        lines = [f"# HBM traffic per launch: workload {w.name}", "",
+                 "Two counter passes, each in a run of its own (from the repository root, on one MI355X; TMPDIR=/tmp):",
+                 "", "    " + PROFILE_PASSES["fetch"], "    " + PROFILE_PASSES["write"], "",
+                 "Calibration: the same runs launch a plain 1 GiB device copy (__amd_rocclr_copyBuffer). "
+                 f"It reads {calib(ft, 'FETCH_SIZE'):.1f} KiB by FETCH_SIZE and writes {calib(wt, 'WRITE_SIZE'):.1f} KiB "
+                 f"by WRITE_SIZE per dispatch, so bytes = FETCH_SIZE x 1024 x {fetch_factor:.4f} and "
+                 f"WRITE_SIZE x 1024 x {write_factor:.4f} on this chip.", "",
+                 "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes (scaled) | algorithmic bytes | ratio |",
+                 "|---|---|---|---|---|---|"]
+        for k, v in rec["kernels"].items():
+            lines.append(f"| `{k}` | {v['fetch_kib']:.1f} | {v['write_kib']:.1f} | {v['hbm_bytes']:.4e} | "
+                         f"{v['algorithmic_bytes']:.4e} | {v['ratio']:.3f} |")
+        if "k_block_attn_avg_us_kernel_trace" in rec:
+            lines += ["", f"Average k_block_attn duration in the kernel-trace run ({PROFILE_PASSES['trace'].split(' -d ')[0]} ...): "
+                      f"{rec['k_block_attn_avg_us_kernel_trace']:.1f} us."]
+        lines += ["", f"Attention sources hash (bench.py kernel_source_hash): {rec['source_hash']}."]
+        _write(os.path.join(PROFILE_DIR, f"k_block_attn_{w.name}_traffic.md"), "\n".join(lines) + "\n", written)
+    md_, mt = find("SQ_INSTS_VALU_MFMA_MOPS_BF16")
     if mt:
-        rec = dict(workload=w.name, source_hash=mfma_source_hash(), simds=SIMDS, kernels={})
+        rec = dict(workload=w.name, source_hash=mfma_source_hash(), simds=SIMDS, xcds=XCDS,
+                   command=PROFILE_PASSES["mfma"], kernels={})
         for (k, g), cs in sorted(mt.items()):
             if k == "__amd_rocclr_copyBuffer" or "SQ_VALU_MFMA_BUSY_CYCLES" not in cs:
                 continue
             busy = float(np.mean(cs["SQ_VALU_MFMA_BUSY_CYCLES"]))
-            gui = float(np.mean(cs["GRBM_GUI_ACTIVE"])) if "GRBM_GUI_ACTIVE" in cs else None
+            gui = float(np.mean(cs["GRBM_GUI_ACTIVE"])) / XCDS if "GRBM_GUI_ACTIVE" in cs else None
             mops = float(np.mean(cs.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", [0.0])))
+            us = float(np.mean(cs["_us"]))
             rec["kernels"][f"{k} grid {g}"] = dict(
-                dispatches=len(cs["SQ_VALU_MFMA_BUSY_CYCLES"]), avg_us=float(np.mean(cs["_us"])),
-                mfma_busy_cycles=busy, gui_active_cycles=gui,
-                mfma_util=busy / (gui * SIMDS) if gui else None, counted_flops=mops * 512)
+                instance=cs["_name"][0], dispatches=len(cs["SQ_VALU_MFMA_BUSY_CYCLES"]), avg_us=us,
+                mfma_busy_cycles=busy, gui_active_cycles_per_xcd=gui,
+                mfma_util=busy / (gui * SIMDS) if gui else None, counted_flops=mops * 512,
+                counted_tflops=mops * 512 / (us * 1e-6) / 1e12 if us else None)
         path = os.path.join(PROFILE_DIR, f"mfma_{w.name}_counters.json")
         json.dump(rec, open(path, "w"), indent=1)
         written.append(path)
+        lines = [f"# Matrix-core utilisation per kernel: workload {w.name}", "",
+                 "Command (from the repository root, on one MI355X; TMPDIR=/tmp):", "", "    " + PROFILE_PASSES["mfma"], "",
+                 "Per dispatch, averaged per kernel and grid (threads). `MFMA busy` = SQ_VALU_MFMA_BUSY_CYCLES "
+                 f"/ (GRBM_GUI_ACTIVE of one XCD x {SIMDS} SIMDs): the csv gives GRBM_GUI_ACTIVE summed over the "
+                 f"{XCDS} XCDs, 8 x 2.4 GHz x the kernel's time.  `counted TFLOP/s` = SQ_INSTS_VALU_MFMA_MOPS_BF16 "
+                 "x 512 flop / kernel time (dense bf16 peak 2500).", "",
+                 "| kernel | grid | dispatches | avg us | MFMA busy | counted TFLOP/s |", "|---|---|---|---|---|---|"]
+        for key, v in rec["kernels"].items():
+            k, g = key.split(" grid ")
+            lines.append(f"| `{v['instance'][:80]}` | {g} | {v['dispatches']} | {v['avg_us']:.1f} | "
+                         f"{(v['mfma_util'] or 0) * 100:.1f}% | {(v['counted_tflops'] or 0):.0f} |")
+        lines += ["", f"Matrix-core sources hash (bench.py mfma_source_hash): {rec['source_hash']}."]
+        _write(os.path.join(PROFILE_DIR, f"mfma_{w.name}_counters.md"), "\n".join(lines) + "\n", written)
+    sd, st = find("SQ_WAIT_INST_ANY")
+    if st:
+        lines = [f"# Where the waves spend their cycles: workload {w.name}", "",
+                 "Command (from the repository root, on one MI355X; TMPDIR=/tmp):", "", "    " + PROFILE_PASSES["sq"], "",
+                 "Per dispatch of each kernel's benchmarked launch, chip sums averaged over the dispatches, as "
+                 "shares of SQ_WAVE_CYCLES (the cycles its waves were resident).  `MFMA busy` as in the "
+                 "matrix-core table; `VALU / SIMD-cycle` = SQ_INSTS_VALU / (GRBM_GUI_ACTIVE of one XCD x SIMDs).", "",
+                 "| kernel | dispatches | avg us | waiting (SQ_WAIT_INST_ANY) | VALU active | LDS active | "
+                 "MFMA busy | VALU / SIMD-cycle |", "|---|---|---|---|---|---|---|---|"]
+        for k in ("k_block_attn", "k_init_wide", "k_ssd_scan", "k_attn_merge", "k_scan_merge"):
+            g = main_grid(st, k)
+            if g is None:
+                continue
+            cs = st[(k, g)]
+            m = {c: float(np.mean(v)) for c, v in cs.items() if c != "_name"}
+            wc = m.get("SQ_WAVE_CYCLES", 0.0) or 1.0
+            gui = m.get("GRBM_GUI_ACTIVE", 0.0) / XCDS or 1.0
+            lines.append(f"| `{cs['_name'][0][:70]}` | {len(cs['_us'])} | {m['_us']:.1f} | "
+                         f"{100 * m.get('SQ_WAIT_INST_ANY', 0) / wc:.1f}% | {100 * m.get('SQ_ACTIVE_INST_VALU', 0) / wc:.1f}% | "
+                         f"{100 * m.get('SQ_ACTIVE_INST_LDS', 0) / wc:.1f}% | "
+                         f"{100 * m.get('SQ_VALU_MFMA_BUSY_CYCLES', 0) / (gui * SIMDS):.1f}% | "
+                         f"{m.get('SQ_INSTS_VALU', 0) / (gui * SIMDS):.3f} |")
+        _write(os.path.join(PROFILE_DIR, f"sq_{w.name}_counters.md"), "\n".join(lines) + "\n", written)
     for p in written:
         print(p)
 
