@@ -64,9 +64,17 @@ __host__ __device__ inline int ssd_heads_per_block(int H, int ng, int P) {
 // reads (zero before the block), each thread the four raw positions of its B
 // and Cm entries, and the conv + SiLU and softplus run after all of them are
 // issued.
+// TS = 4 (batches with few heads): the workgroup takes one head (P <= 64) and
+// its four waves share it, wave k forming y at positions k, k+4, ... of each
+// chunk and a quarter of the head's decay matrix.  Every wave keeps the whole
+// state row and updates it after each chunk but the last (the next chunk
+// reads all of it); after the last, whose update only feeds h_final, wave k
+// updates and writes state columns [k*NMAX/4, (k+1)*NMAX/4).  A position's sum runs over the full row of the masked matrix,
+// whose entries past the position are exact zeros, so y has the same bits as
+// with one wave per head.
 // The scan of workgroup `bid` (a device function so that the drafter layer's
 // combined scan + merge launch runs the same code).
-template <typename T, int NMAX, int QM, bool V4, bool CONV>
+template <typename T, int NMAX, int QM, bool V4, bool CONV, int TS = 1>
 __device__ __forceinline__ void ssd_scan_block(const SsdArgs& a, int bid) {
   using L = SsdLds<NMAX, QM>;
   constexpr int Q = QM, LDB = L::LDB;
@@ -74,13 +82,17 @@ __device__ __forceinline__ void ssd_scan_block(const SsdArgs& a, int bid) {
   static_assert(Q * NMAX % 256 == 0 && Q <= 64, "whole staging rounds; one lane per chunk position");
   __shared__ __align__(16) float lds[L::floats];
   const int H = a.H, P = a.P, N = a.N, K = a.K, QC = a.chunk;
+  static_assert(TS == 1 || TS == 4, "one wave per head row block, or four per head");
+  static_assert(TS == 1 || V4, "the column-split h_final store is the 16-byte one");
   const int RB = (P + 63) >> 6;
-  const int HPW = ssd_heads_per_block(H, a.ng, P);
+  const int HPW = TS == 1 ? ssd_heads_per_block(H, a.ng, P) : 1;
   const int hblocks = H / HPW;
   const int b = bid / hblocks, hfirst = (bid % hblocks) * HPW;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const bool active = wave < HPW * RB;
-  const int h = min(hfirst + wave / RB, H - 1), p = (wave % RB) * 64 + lane;
+  // (head, row block) of the wave; its position slice (wave-uniform, scalar)
+  const int hw = wave / TS, tsw = __builtin_amdgcn_readfirstlane(wave % TS);
+  const bool active = hw < HPW * RB;
+  const int h = min(hfirst + hw / RB, H - 1), p = (hw % RB) * 64 + lane;
   const bool own = active && p < P;
   const int pc = min(p, P - 1);
   const int grp = hfirst / (H / a.ng);
@@ -88,7 +100,7 @@ __device__ __forceinline__ void ssd_scan_block(const SsdArgs& a, int bid) {
   float* sB = lds + L::oB;
   float* sC = lds + L::oC;
   float* sCB = lds + L::oCB;
-  float* wl = lds + L::oWave + wave * L::WAVE;
+  float* wl = lds + L::oWave + hw * L::WAVE;
   float* slam = wl;
   float* sw = wl + Q;
   float* sdt = wl + 2 * Q;
@@ -204,7 +216,7 @@ __device__ __forceinline__ void ssd_scan_block(const SsdArgs& a, int bid) {
         if (lane >= off) v += u;
       }
       const float lend = __shfl(v, q - 1, 64);
-      if (lane < Q) {
+      if (lane < Q && tsw == 0) {
         slam[lane] = v;
         sdt[lane] = dt;
         sw[lane] = lane < q ? __expf(lend - v) * dt : 0.f;
@@ -230,10 +242,11 @@ __device__ __forceinline__ void ssd_scan_block(const SsdArgs& a, int bid) {
       sCB[i] = d0 + d1;
     }
     __syncthreads();
-    // this head's decay-weighted M, masked before the exponential
+    // this head's decay-weighted M, masked before the exponential (a quarter
+    // of it per wave with TS = 4)
 #pragma unroll 4
-    for (int j = 0; j < Q * Q / 64; ++j) {
-      const int i = lane + 64 * j;
+    for (int j = 0; j < Q * Q / 64 / TS; ++j) {
+      const int i = lane + 64 * (j * TS + tsw);
       const int t = i / Q, s = i % Q;
       float v = 0.f;
       if (s <= t && t < q) v = __expf(slam[t] - slam[s]) * sCB[i] * sdt[s];
@@ -246,7 +259,7 @@ __device__ __forceinline__ void ssd_scan_block(const SsdArgs& a, int bid) {
       // (zero past t) against the lane's x values, so the code grows with
       // Q instead of Q^2 (the unrolled triangle took minutes to compile).
 #pragma unroll 1
-      for (int t = 0; t < q; ++t) {
+      for (int t = tsw; t < q; t += TS) {
         const float* cr = sC + t * LDB;
         float z0 = 0.f, z1 = 0.f;
 #pragma unroll
@@ -273,7 +286,8 @@ __device__ __forceinline__ void ssd_scan_block(const SsdArgs& a, int bid) {
       }
     } else if (own) {
 #pragma unroll
-      for (int t = 0; t < Q; ++t) {
+      for (int jt = 0; jt < Q / TS; ++jt) {
+        const int t = jt * TS + tsw;
         if (t < q) {
           const float* cr = sC + t * LDB;
           float z0 = 0.f, z1 = 0.f;
@@ -287,24 +301,44 @@ __device__ __forceinline__ void ssd_scan_block(const SsdArgs& a, int bid) {
           }
           float z = (z0 + z1) * __expf(slam[t]);
           const float* mr = sM + t * Q;
+          if constexpr (TS == 1) {
 #pragma unroll
-          for (int s = 0; s <= t; s += 4) {
-            const float4 m = *reinterpret_cast<const float4*>(mr + s);
-            z = fmaf(m.x, xs[s], z);
-            if (s + 1 <= t) z = fmaf(m.y, xs[s + 1], z);
-            if (s + 2 <= t) z = fmaf(m.z, xs[s + 2], z);
-            if (s + 3 <= t) z = fmaf(m.w, xs[s + 3], z);
+            for (int s = 0; s <= t; s += 4) {
+              const float4 m = *reinterpret_cast<const float4*>(mr + s);
+              z = fmaf(m.x, xs[s], z);
+              if (s + 1 <= t) z = fmaf(m.y, xs[s + 1], z);
+              if (s + 2 <= t) z = fmaf(m.z, xs[s + 2], z);
+              if (s + 3 <= t) z = fmaf(m.w, xs[s + 3], z);
+            }
+            yrow[size_t(c0 + t) * HP] = fmaf(Dh, xs[t], z);
+          } else {
+            // the full row: M[t][s] is an exact zero for s > t
+#pragma unroll
+            for (int s = 0; s < Q; s += 4) {
+              const float4 m = *reinterpret_cast<const float4*>(mr + s);
+              z = fmaf(m.x, xs[s], z);
+              z = fmaf(m.y, xs[s + 1], z);
+              z = fmaf(m.z, xs[s + 2], z);
+              z = fmaf(m.w, xs[s + 3], z);
+            }
+            float xt = xs[jt * TS];
+#pragma unroll
+            for (int k = 1; k < TS; ++k) xt = tsw == k ? xs[jt * TS + k] : xt;
+            yrow[size_t(c0 + t) * HP] = fmaf(Dh, xt, z);
           }
-          yrow[size_t(c0 + t) * HP] = fmaf(Dh, xs[t], z);
         }
       }
     }
     // state passing: H_out[p, n] = exp(lam_end) H_in[p, n] + sum_s w_s x[s, p] B[s, n]
-    // (after the last chunk only h_final needs it)
+    // (after the last chunk only h_final needs it; with TS waves per head
+    // each then takes its quarter of the columns)
     if (c0 + QC >= K && !a.h_final) break;
+    const bool split_n = TS > 1 && c0 + QC >= K;
+    constexpr int NQ = NMAX / TS;
     const float dend = __expf(slam[q - 1]);
 #pragma unroll
-    for (int n = 0; n < NMAX; ++n) Hs[n] *= dend;
+    for (int n = 0; n < NMAX; ++n)
+      if (!split_n || n / NQ == tsw) Hs[n] *= dend;
 #pragma unroll
     for (int s = 0; s < Q; ++s) {
       if (s < q) {
@@ -312,6 +346,7 @@ __device__ __forceinline__ void ssd_scan_block(const SsdArgs& a, int bid) {
         const float* br = sB + s * LDB;
 #pragma unroll
         for (int n = 0; n < NMAX; n += 4) {
+          if (split_n && n / NQ != tsw) continue;
           const float4 bb = *reinterpret_cast<const float4*>(br + n);
           Hs[n] = fmaf(coef, bb.x, Hs[n]);
           Hs[n + 1] = fmaf(coef, bb.y, Hs[n + 1]);
@@ -327,7 +362,8 @@ __device__ __forceinline__ void ssd_scan_block(const SsdArgs& a, int bid) {
     if constexpr (V4) {
 #pragma unroll
       for (int k = 0; k < NMAX; k += 4)
-        if (k < N) *reinterpret_cast<float4*>(hf + k) = make_float4(Hs[k], Hs[k + 1], Hs[k + 2], Hs[k + 3]);
+        if (k < N && (TS == 1 || k / (NMAX / TS) == tsw))
+          *reinterpret_cast<float4*>(hf + k) = make_float4(Hs[k], Hs[k + 1], Hs[k + 2], Hs[k + 3]);
     } else {
 #pragma unroll
       for (int k = 0; k < NMAX; ++k)
@@ -336,20 +372,20 @@ __device__ __forceinline__ void ssd_scan_block(const SsdArgs& a, int bid) {
   }
 }
 
-template <typename T, int NMAX, int QM, bool V4, bool CONV>
+template <typename T, int NMAX, int QM, bool V4, bool CONV, int TS = 1>
 __global__ __launch_bounds__(256) void k_ssd_scan(SsdArgs a) {
-  ssd_scan_block<T, NMAX, QM, V4, CONV>(a, blockIdx.x);
+  ssd_scan_block<T, NMAX, QM, V4, CONV, TS>(a, blockIdx.x);
 }
 
 // Workgroups [0, n_scan) run the scan, the rest the merge of the attention's
 // partials (grid (C * Hkv) x slabs, flattened request-major).  The two
 // are independent: the scan needs the projected state, the merge the
 // attention's partials, both written by earlier launches on the stream.
-template <int NMAX, int LPO, int U>
+template <int NMAX, int LPO, int U, int TS>
 __global__ __launch_bounds__(256) void k_scan_merge(SsdArgs s, AttnArgs m, int n_scan) {
   const int bid = blockIdx.x;
   if (bid < n_scan) {
-    ssd_scan_block<bf16_t, NMAX, 16, true, false>(s, bid);
+    ssd_scan_block<bf16_t, NMAX, 16, true, false, TS>(s, bid);
   } else {
     const int r = bid - n_scan, ch = m.C * m.Hkv;
     attn_merge_block<bf16_t, 128, LPO, U>(m, r % ch, r / ch);
@@ -372,8 +408,23 @@ size_t ssd_lds_bytes(int P, int N, int Q) {
   return SsdLds<64, 64>::floats * sizeof(float);
 }
 
+// Four waves per head (TS = 4) when the batch has too few heads for the
+// four-heads form to give every CU a workgroup: at C = 1 (16 heads) that form
+// runs 16 waves on the whole chip, each a serial chain over its chunk's
+// positions.  States of 17..64 (the model shapes), plain inputs, N % 4 == 0.
+static bool ssd_split_positions(const SsdArgs& a) {
+  return !a.zx && a.P <= 64 && a.N > 16 && a.N <= 64 && a.N % 4 == 0 && a.chunk <= 16 &&
+         int64_t(a.C) * a.H < 1024;
+}
+
 template <typename T, int NMAX>
 static hipError_t launch_n(hipStream_t st, const SsdArgs& a) {
+  if constexpr (NMAX == 32 || NMAX == 64) {
+    if (ssd_split_positions(a)) {
+      hipLaunchKernelGGL((k_ssd_scan<T, NMAX, 16, true, false, 4>), dim3(a.C * a.H), dim3(256), 0, st, a);
+      return hipGetLastError();
+    }
+  }
   const int hpw = ssd_heads_per_block(a.H, a.ng, a.P);
   const dim3 grid(a.C * (a.H / hpw)), block(256);
   if constexpr (std::is_same<T, float>::value) {
@@ -431,11 +482,19 @@ bool scan_merge_fits(int dtype, const SsdArgs& s, const AttnArgs& m) {
 // output quad and at most U pieces per lane and round of loads).
 template <int NMAX, int LPO, int U>
 static hipError_t launch_scan_merge_cfg(hipStream_t st, const SsdArgs& s, const AttnArgs& m) {
-  const int n_scan = s.C * (s.H / ssd_heads_per_block(s.H, s.ng, s.P));
   constexpr int OPB = 256 / LPO;
   const int slabs = (m.rows * (128 / 4) + OPB - 1) / OPB;
+  if constexpr (NMAX == 32 || NMAX == 64) {
+    if (ssd_split_positions(s)) {
+      const int n_scan = s.C * s.H;
+      hipLaunchKernelGGL((k_scan_merge<NMAX, LPO, U, 4>), dim3(n_scan + m.C * m.Hkv * slabs), dim3(256), 0, st,
+                         s, m, n_scan);
+      return hipGetLastError();
+    }
+  }
+  const int n_scan = s.C * (s.H / ssd_heads_per_block(s.H, s.ng, s.P));
   const dim3 grid(n_scan + m.C * m.Hkv * slabs), block(256);
-  hipLaunchKernelGGL((k_scan_merge<NMAX, LPO, U>), grid, block, 0, st, s, m, n_scan);
+  hipLaunchKernelGGL((k_scan_merge<NMAX, LPO, U, 1>), grid, block, 0, st, s, m, n_scan);
   return hipGetLastError();
 }
 

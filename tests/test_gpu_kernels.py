@@ -336,6 +336,36 @@ def test_ssd_scan(C, K, H, P, ng, N, chunk, dtype, dskip, zero_state):
     assert_close(to_host64(hf), hfo, dtype, "h_final")
 
 
+@pytest.mark.parametrize("K,chunk,N", [(16, 16, 32), (40, 16, 64), (13, 4, 32)])
+def test_scan_position_split_is_bit_identical(K, chunk, N):
+    """A batch with few heads runs four waves per head, each taking every
+    fourth position; 64 requests of 16 heads run one wave per head.  The same
+    requests must get the same bits either way (y and h_final)."""
+    C, H, P, ng = 64, 16, 64, 1
+    g = np.random.default_rng(7000 + K + N)
+    enc = lambda a: wl.f32_to_bf16_bits(a.astype(np.float32))
+    x = enc(g.standard_normal((C, K, H, P)))
+    B = enc(g.standard_normal((C, K, ng, N)))
+    Cm = enc(g.standard_normal((C, K, ng, N)))
+    delta = np.logaddexp(0, g.standard_normal((C, K, H)) - 4.0).astype(np.float32)
+    A = (-np.exp(g.uniform(0, 1, H))).astype(np.float32)
+    h0 = g.standard_normal((C, H, P, N)).astype(np.float32)
+    D = g.standard_normal(H).astype(np.float32)
+
+    def run(c):
+        return ops.ssd_scan(to_dev(x[:c], "bf16"), to_dev(delta[:c], "bf16"), to_dev(A, "bf16"),
+                            to_dev(B[:c], "bf16"), to_dev(Cm[:c], "bf16"), chunk=chunk, h0=to_dev(h0[:c], "bf16"),
+                            Dskip=to_dev(D, "bf16"), want_final=True)
+    y_all, hf_all = run(C)     # C * H = 1024: one wave per head
+    y_few, hf_few = run(5)     # C * H = 80: four waves per head
+    torch.cuda.synchronize()
+    assert torch.equal(y_few, y_all[:5]) and torch.equal(hf_few, hf_all[:5])
+    yo, hfo = oracle.ssd_recurrence(oracle.decode(x[:5], "bf16"), delta[:5], A, oracle.decode(B[:5], "bf16"),
+                                    oracle.decode(Cm[:5], "bf16"), h0=h0[:5], Dskip=D)
+    assert_close(to_host64(y_few), yo, "bf16", "y")
+    assert_close(to_host64(hf_few), hfo, "bf16", "h_final")
+
+
 # ----------------------------------------------------------------------------
 # projection
 # ----------------------------------------------------------------------------
