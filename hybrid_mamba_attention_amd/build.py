@@ -18,11 +18,12 @@ SOURCES = ["api.hip", "attention.hip", "ssd.hip", "init_state.hip", "gemm.hip", 
 ARCH = "gfx950"
 # Per-file code generation flags.  attention.hip: matrix-core results stay in
 # ordinary VGPRs (its accumulators are rescaled by VALU every few stages, and
-# AGPR-resident accumulators would be copied out and back each time), and no
-# NaN semantics are honoured -- NaN-poisoned cache slots are never fed to
-# arithmetic (they are masked by selects or zero-filled first).
+# AGPR-resident accumulators would be copied out and back each time).  NaN
+# semantics stay on everywhere: dropping them (-fno-honor-nans) changed the
+# attention's time by under 0.3% at every measured shape, and would make its
+# correctness rest on no NaN-poisoned cache slot ever reaching arithmetic.
 FILE_FLAGS = {
-    "attention.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 
