@@ -5,9 +5,14 @@
 // along K (weights in the [out, in] convention), which is exactly the operand
 // layout of the bf16 matrix cores: a lane's eight contraction-adjacent
 // elements are one 16-byte row piece.
-//   * Workgroup: 4 waves in a 2 x 2 arrangement over a (64*WM) x (64*WN)
-//     output tile; each wave owns WM x WN tiles of 32 x 32
-//     (v_mfma_f32_32x32x16_bf16, fp32 accumulation in registers).
+//   * Workgroup: NWR x 2 waves over a (32*WM*NWR) x (64*WN) output tile;
+//     each wave owns WM x WN tiles of 32 x 32 (v_mfma_f32_32x32x16_bf16, fp32
+//     accumulation in registers).  64 x 128 tiles: 4 waves (one per SIMD).
+//     128 x 128 tiles: 8 waves of 32 x 64 outputs, two per SIMD, so one
+//     wave's MFMAs run while the other waits on LDS, its loads or the
+//     barrier; at 2048 rows that took the 2048 x 2048 x 4096 part of the
+//     Mamba-2 input projection from 56 to 45 us and the block from 132 to
+//     118 us against 4 waves of 64 x 64 (a 4-stage load ring on top: 122 us).
 //   * K advances 64 at a time.  Every thread issues 16-byte loads of A and B
 //     row pieces for the stage PF ahead into a register ring; a stage is then
 //     written to one of two LDS buffers, one barrier, and the waves run their
@@ -55,10 +60,13 @@ __device__ __forceinline__ OutT* scatter_col(const KvScatter& s, int n) {
 // bf16 GEMM on matrix cores
 // ---------------------------------------------------------------------------
 
-template <int WM, int WN, typename OutT, int PF>
-__global__ __launch_bounds__(256) void k_gemm_tn(GemmArgs g) {
-  constexpr int BM = 64 * WM, BN = 64 * WN;
-  constexpr int LA = BM / 32, LB = BN / 32;        // 16-byte loads per thread per stage
+template <int WM, int WN, typename OutT, int PF, int NWR = 2>
+__global__ __launch_bounds__(128 * NWR) void k_gemm_tn(GemmArgs g) {
+  constexpr int NT = 128 * NWR;                    // threads
+  constexpr int RPP = NT / 8;                      // rows one load pass covers
+  constexpr int BM = 32 * WM * NWR, BN = 64 * WN;
+  static_assert(BM % RPP == 0 && BN % RPP == 0, "whole load passes");
+  constexpr int LA = BM / RPP, LB = BN / RPP;      // 16-byte loads per thread per stage
   constexpr int TA = BM * 128, TB = BN * 128;      // bytes of one LDS tile
   static_assert(PF >= 2 && PF % 2 == 0, "even prefetch depth keeps the LDS buffer parity static");
   __shared__ __align__(16) unsigned char lds[2 * (TA + TB)];
@@ -73,20 +81,20 @@ __global__ __launch_bounds__(256) void k_gemm_tn(GemmArgs g) {
   const int k_hi = min(g.K, k_lo + g.kchunk);
   const int nst = (k_hi - k_lo + 63) >> 6;
 
-  // loader: thread -> 16-byte piece lc of rows lr + 32*i
+  // loader: thread -> 16-byte piece lc of rows lr + RPP*i
   const int lc = tid & 7, lr = tid >> 3;
   const bf16_t* __restrict__ A = static_cast<const bf16_t*>(g.a);
   const bf16_t* __restrict__ B = static_cast<const bf16_t*>(g.b);
   const bf16_t* pa[LA];
   const bf16_t* pb[LB];
 #pragma unroll
-  for (int i = 0; i < LA; ++i) pa[i] = A + size_t(min(m0 + lr + 32 * i, g.M - 1)) * g.lda;
+  for (int i = 0; i < LA; ++i) pa[i] = A + size_t(min(m0 + lr + RPP * i, g.M - 1)) * g.lda;
 #pragma unroll
-  for (int i = 0; i < LB; ++i) pb[i] = B + size_t(min(n0 + lr + 32 * i, g.N - 1)) * g.ldb;
+  for (int i = 0; i < LB; ++i) pb[i] = B + size_t(min(n0 + lr + RPP * i, g.N - 1)) * g.ldb;
   uint32_t wpos[LA > LB ? LA : LB];
 #pragma unroll
   for (int i = 0; i < (LA > LB ? LA : LB); ++i) {
-    const int r = lr + 32 * i;
+    const int r = lr + RPP * i;
     wpos[i] = r * 128 + ((lc ^ ((r >> 1) & 7)) << 4);
   }
 
@@ -347,10 +355,10 @@ __global__ __launch_bounds__(256) void k_splitk_sum(GemmArgs g) {
 // steady loop then waits at vmcnt(24)) measured no faster than two.
 constexpr int kGemmPf = 2;
 
-// bf16 tile shapes (WM, WN): cfg 0 = 64 x 128, 1 = 128 x 128, 3 = 64 x 64,
-// 4 = 128 x 256, 5 = 256 x 128; cfg 2 is the fp32 kernel.
+// bf16 tile shapes: cfg 0 = 64 x 128 (4 waves), 1 = 128 x 128 (8 waves);
+// cfg 2 is the fp32 kernel (64 x 64).
 static void cfg_tile(int cfg, int& bm, int& bn) {
-  static const int t[6][2] = {{64, 128}, {128, 128}, {64, 64}, {64, 64}, {128, 256}, {256, 128}};
+  static const int t[3][2] = {{64, 128}, {128, 128}, {64, 64}};
   bm = t[cfg][0];
   bn = t[cfg][1];
 }
@@ -414,10 +422,7 @@ static hipError_t launch_gemm_part(hipStream_t st, GemmArgs g, const GemmPart& p
   const dim3 grid(p.tiles, p.splits);
   switch (p.cfg) {
     case 0: hipLaunchKernelGGL((k_gemm_tn<1, 2, OutT, kGemmPf>), grid, dim3(256), 0, st, g); break;
-    case 1: hipLaunchKernelGGL((k_gemm_tn<2, 2, OutT, kGemmPf>), grid, dim3(256), 0, st, g); break;
-    case 3: hipLaunchKernelGGL((k_gemm_tn<1, 1, OutT, kGemmPf>), grid, dim3(256), 0, st, g); break;
-    case 4: hipLaunchKernelGGL((k_gemm_tn<2, 4, OutT, kGemmPf>), grid, dim3(256), 0, st, g); break;
-    case 5: hipLaunchKernelGGL((k_gemm_tn<4, 2, OutT, kGemmPf>), grid, dim3(256), 0, st, g); break;
+    case 1: hipLaunchKernelGGL((k_gemm_tn<1, 2, OutT, kGemmPf, 4>), grid, dim3(512), 0, st, g); break;
     default: hipLaunchKernelGGL((k_gemm_tn_f32<OutT>), grid, dim3(256), 0, st, g); break;
   }
   if (p.splits > 1) {
