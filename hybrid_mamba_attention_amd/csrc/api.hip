@@ -114,6 +114,12 @@ AttnPlanShape plan_shape(int dtype, int C, int K, int Hq, int Hkv, int D, int64_
     // two heads per workgroup when the batch at its bound gives ranges of
     // 128+ slabs
     p.head_pair = hp_ok && tmax * p.gran >= 128 * std::min(w_max, tmax);
+    // The device makes W = min(w_max, max(1, floor(T / min_gran))) ranges and
+    // T <= tmax (contexts are clamped to max_ctx), so no more can ever be
+    // needed: a small batch's grid then holds no workgroups without a range
+    // (C = 1 at 8192 tokens: 257 instead of 513, whose idle half still took
+    // dispatch slots and ran the range scan).
+    w_max = std::min<int64_t>(w_max, std::max<int64_t>(1, tmax / p.min_gran));
   }
   w_max = std::max<int64_t>(1, std::min(w_max, tmax));   // a range holds at least one granule
   p.w_max = int(std::min<int64_t>(w_max, 0x7fffffff));

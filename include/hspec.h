@@ -165,7 +165,9 @@ int hspec_ssd_scan(void* stream, int dtype, int C, int K, int H, int P, int ng, 
  * takes its range's slabs request by request; a request inside one range is
  * finished there, a request spanning several ranges (its pieces) is merged
  * by log-sum-exp.  w_max, a bound the host derives from C, max_ctx, K, Hkv
- * and the page size, sizes the grid and the workspace.  The workspace
+ * and the page size, sizes the grid and the workspace: automatically
+ * min(512/Hkv, max(1, floor(C*Gmax / ceil(16/g)))), Gmax the granules of a
+ * max_ctx request; with kv_split_pages, ceil(C*Gmax / R).  The workspace
  * starts with the int32 plan the kernels derive from ctx_lens:
  *         [0] W  [1] g  [2] C  [3] w_max
  *         [4, 4+C) S_b    [4+C, 4+2C) range of request b's first granule
