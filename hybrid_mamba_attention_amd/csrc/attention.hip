@@ -373,9 +373,16 @@ __global__ __launch_bounds__(64 * NW, (RT == 2 && sizeof(T) == 2) ? 2 : 1) void 
   static_assert(HP == 1 || HP == 2, "one or two kv heads per workgroup");
   constexpr int NT = 64 * NW;
   constexpr int DS = D / 32, DPL = D / 16, EPC = Gm::EPC, CPR = Gm::CPR;
-  constexpr int RPP = (NT / CPR) < 16 ? (NT / CPR) : 16;  // page rows one load round covers
+  constexpr int TPR = NT / CPR;                          // loader thread rows
+  // Page split: with 32 thread rows (8 waves on 256-byte rows, or 4 on
+  // 128-byte rows) rows 0-15 load the stage's first page and rows 16-31 its
+  // second, one 16-byte piece per tensor each, so every thread loads and the
+  // hot path applies.  Otherwise a round of thread rows covers RPP rows of
+  // each page.
+  constexpr bool PS = TPR == 32;
+  constexpr int RPP = PS ? 16 : (TPR < 16 ? TPR : 16);   // page rows one load round covers
   constexpr int RND = 16 / RPP;                          // load rounds per page
-  constexpr int NLD = 2 * RND;                           // 16-byte loads per tensor per stage
+  constexpr int NLD = PS ? 1 : 2 * RND;                  // 16-byte loads per tensor per stage
   constexpr int TILE_B = Gm::TILE * 16;
   static_assert(PF % 2 == 0, "even prefetch depth keeps the LDS buffer parity static");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -433,19 +440,26 @@ __global__ __launch_bounds__(64 * NW, (RT == 2 && sizeof(T) == 2) ? 2 : 1) void 
   const int last_phys = a.num_pages - 1;
   const size_t blk_page_b = size_t(16) * Hkv * D * sizeof(T);
 
-  // ---- loader geometry: thread -> (page row trow + q*RPP, 16-byte chunk tchunk)
+  // ---- loader geometry: thread -> (page row trw + q*RPP, 16-byte chunk tchunk)
+  // of both pages, or with the page split of page tpage only
   const int tchunk = threadIdx.x % CPR;
   const int trow = threadIdx.x / CPR;
-  const bool lactive = trow < RPP;
+  const int tpage = PS ? __builtin_amdgcn_readfirstlane(trow >> 4) : 0;  // wave-uniform
+  const int trw = PS ? trow & 15 : trow;
+  const bool lactive = PS ? trow < 32 : trow < RPP;
   const uint32_t ts_b = uint32_t(a.token_stride * int64_t(sizeof(T)));
   const uint32_t bts_b = uint32_t(Hkv * D * sizeof(T));
   uint32_t coff[RND], wpos[NLD];
 #pragma unroll
   for (int qq = 0; qq < RND; ++qq) {
-    const uint32_t slot = trow + qq * RPP;
+    const uint32_t slot = trw + qq * RPP;
     coff[qq] = slot * ts_b + tchunk * 16;
+    if constexpr (PS) {
+      wpos[0] = Gm::pos(tpage * 16 + slot, tchunk) * 16;
+    } else {
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) wpos[tt * RND + qq] = Gm::pos(tt * 16 + slot, tchunk) * 16;
+      for (int tt = 0; tt < 2; ++tt) wpos[tt * RND + qq] = Gm::pos(tt * 16 + slot, tchunk) * 16;
+    }
   }
 
 
@@ -563,7 +577,7 @@ __global__ __launch_bounds__(64 * NW, (RT == 2 && sizeof(T) == 2) ? 2 : 1) void 
     // Two full context pages (stage st < nhot): page numbers from the window,
     // unpredicated loads off scalar page bases (entries clamped into the pool:
     // never a stray read).
-    constexpr bool kHot = RPP * CPR == NT;
+    constexpr bool kHot = PS || RPP * CPR == NT;
     auto issue_hot = [&](int st, uint4 (&stk)[NLD], uint4 (&stv)[NLD]) __attribute__((always_inline)) {
       // slabs 2st and 2st+1 of the split: window entries o0, o1 (the same page
       // unless pages are 16 tokens; an even o0 keeps both in one lane half)
@@ -573,16 +587,22 @@ __global__ __launch_bounds__(64 * NW, (RT == 2 && sizeof(T) == 2) ? 2 : 1) void 
       const int ph1 = min(max(__builtin_amdgcn_readlane(v, o1 & 63), 0), last_phys);
       const int64_t off0 = int64_t(ph0) * page_b + int64_t(q0 & smask) * slab_b;
       const int64_t off1 = int64_t(ph1) * page_b + int64_t((q0 + 1) & smask) * slab_b;
-      const char* k0 = kcj + off0;
-      const char* v0 = vcj + off0;
-      const char* k1 = kcj + off1;
-      const char* v1 = vcj + off1;
+      if constexpr (PS) {
+        const int64_t off = tpage ? off1 : off0;
+        stk[0] = ld_stream(kcj + off + coff[0]);
+        stv[0] = ld_stream(vcj + off + coff[0]);
+      } else {
+        const char* k0 = kcj + off0;
+        const char* v0 = vcj + off0;
+        const char* k1 = kcj + off1;
+        const char* v1 = vcj + off1;
 #pragma unroll
-      for (int qq = 0; qq < RND; ++qq) {
-        stk[qq] = ld_stream(k0 + coff[qq]);
-        stv[qq] = ld_stream(v0 + coff[qq]);
-        stk[RND + qq] = ld_stream(k1 + coff[qq]);
-        stv[RND + qq] = ld_stream(v1 + coff[qq]);
+        for (int qq = 0; qq < RND; ++qq) {
+          stk[qq] = ld_stream(k0 + coff[qq]);
+          stv[qq] = ld_stream(v0 + coff[qq]);
+          stk[RND + qq] = ld_stream(k1 + coff[qq]);
+          stv[RND + qq] = ld_stream(v1 + coff[qq]);
+        }
       }
     };
     auto issue = [&](int st, uint4 (&stk)[NLD], uint4 (&stv)[NLD], int (&nv)[2]) __attribute__((always_inline)) {
@@ -597,31 +617,48 @@ __global__ __launch_bounds__(64 * NW, (RT == 2 && sizeof(T) == 2) ? 2 : 1) void 
       // stage is on the unmasked fast path exactly when both words equal 16
       nv[0] = p0.n | (p0.cb << 8);
       nv[1] = p1.n | (p1.cb << 8);
-      // (each page spelled out: selecting between the two by reference would
-      // keep the staging registers from being promoted out of memory)
-#pragma unroll
-      for (int qq = 0; qq < RND; ++qq) {
-        const int slot = trow + qq * RPP;
-        const uint32_t off = p0.blk ? uint32_t(slot) * bts_b + tchunk * 16 : coff[qq];
+      if constexpr (PS) {
+        // this thread's page, field by field (wave-uniform selects)
+        const bool second = tpage != 0;
+        const char* pk = second ? p1.k : p0.k;
+        const char* pv = second ? p1.v : p0.v;
+        const int pn = second ? p1.n : p0.n;
+        const bool pblk = second ? p1.blk : p0.blk;
+        const uint32_t off = pblk ? uint32_t(trw) * bts_b + tchunk * 16 : coff[0];
         uint4 kx = make_uint4(0, 0, 0, 0), vx = make_uint4(0, 0, 0, 0);  // absent tokens: V must be 0, not NaN
-        if (lactive && slot < p0.n) {
-          kx = *reinterpret_cast<const uint4*>(p0.k + off);
-          vx = *reinterpret_cast<const uint4*>(p0.v + off);
+        if (lactive && trw < pn) {
+          kx = *reinterpret_cast<const uint4*>(pk + off);
+          vx = *reinterpret_cast<const uint4*>(pv + off);
         }
-        stk[qq] = kx;
-        stv[qq] = vx;
-      }
+        stk[0] = kx;
+        stv[0] = vx;
+      } else {
+        // (each page spelled out: selecting between the two by reference would
+        // keep the staging registers from being promoted out of memory)
 #pragma unroll
-      for (int qq = 0; qq < RND; ++qq) {
-        const int slot = trow + qq * RPP;
-        const uint32_t off = p1.blk ? uint32_t(slot) * bts_b + tchunk * 16 : coff[qq];
-        uint4 kx = make_uint4(0, 0, 0, 0), vx = make_uint4(0, 0, 0, 0);
-        if (lactive && slot < p1.n) {
-          kx = *reinterpret_cast<const uint4*>(p1.k + off);
-          vx = *reinterpret_cast<const uint4*>(p1.v + off);
+        for (int qq = 0; qq < RND; ++qq) {
+          const int slot = trow + qq * RPP;
+          const uint32_t off = p0.blk ? uint32_t(slot) * bts_b + tchunk * 16 : coff[qq];
+          uint4 kx = make_uint4(0, 0, 0, 0), vx = make_uint4(0, 0, 0, 0);  // absent tokens: V must be 0, not NaN
+          if (lactive && slot < p0.n) {
+            kx = *reinterpret_cast<const uint4*>(p0.k + off);
+            vx = *reinterpret_cast<const uint4*>(p0.v + off);
+          }
+          stk[qq] = kx;
+          stv[qq] = vx;
         }
-        stk[RND + qq] = kx;
-        stv[RND + qq] = vx;
+#pragma unroll
+        for (int qq = 0; qq < RND; ++qq) {
+          const int slot = trow + qq * RPP;
+          const uint32_t off = p1.blk ? uint32_t(slot) * bts_b + tchunk * 16 : coff[qq];
+          uint4 kx = make_uint4(0, 0, 0, 0), vx = make_uint4(0, 0, 0, 0);
+          if (lactive && slot < p1.n) {
+            kx = *reinterpret_cast<const uint4*>(p1.k + off);
+            vx = *reinterpret_cast<const uint4*>(p1.v + off);
+          }
+          stk[RND + qq] = kx;
+          stv[RND + qq] = vx;
+        }
       }
     };
     auto commit = [&](int buf, const uint4 (&stk)[NLD], const uint4 (&stv)[NLD]) __attribute__((always_inline)) {
