@@ -71,7 +71,7 @@ int check_ssd(int dtype, int C, int K, int H, int P, int ng, int N, int chunk, c
 // from ctx_lens; include/hspec.h documents it).  The host knows only bounds:
 // w_max, the most ranges the plan can use, sizes the grid and the workspace.
 struct AttnPlanShape {
-  int w_max, gran, range_gran, min_gran, nbk, head_pair;
+  int w_max, gran, range_gran, min_gran, seg, nbk, head_pair;
   size_t plan_bytes, part_o_off, part_ml_off, total;
 };
 
@@ -84,6 +84,14 @@ struct AttnPlanShape {
 // request of a uniform batch in two: C = 32 and 64 at 8192 tokens took 12%
 // and 9% longer.)
 constexpr int kTargetUnits = 512;
+// A request's fixed cost in an automatic range, in slabs of streaming: its
+// query rows and page-table window, the first stages' round trip, the partial
+// last page and block slabs on the general path, the output store.  A
+// timestamp probe of every workgroup (workload 2: C = 32, 512-4096 tokens)
+// measured ~6 us per extra request in a range against ~1 us per granule of
+// two slabs, and the cost model put the slowest range of that batch at
+// 45 us with 12 slabs against 53 us with none.
+constexpr int kSegSlabs = 12;
 
 // log2(page_size / 16) for a supported page size, else -1
 int page_shift(int page_size) {
@@ -102,6 +110,9 @@ AttnPlanShape plan_shape(int dtype, int C, int K, int Hq, int Hkv, int D, int64_
   // granules of a max_ctx request, and of the batch at most
   const int64_t gmax = ((int64_t(max_ctx) + 15) / 16 + p.nbk + p.gran - 1) / p.gran;
   const int64_t tmax = int64_t(C) * gmax;
+  // automatic ranges charge each request kSegSlabs slabs' worth of fixed cost
+  p.seg = kv_split_pages > 0 ? 0 : (kSegSlabs + p.gran - 1) / p.gran;
+  const int64_t tunits = int64_t(C) * (gmax + p.seg);   // the batch's units at its bound
   const bool hp_ok = head_pair_fits((Hq / Hkv) * K, Hkv, head_stride, dtype, D);
   int64_t w_max;
   if (kv_split_pages > 0) {
@@ -119,7 +130,7 @@ AttnPlanShape plan_shape(int dtype, int C, int K, int Hq, int Hkv, int D, int64_
     // needed: a small batch's grid then holds no workgroups without a range
     // (C = 1 at 8192 tokens: 257 instead of 513, whose idle half still took
     // dispatch slots and ran the range scan).
-    w_max = std::min<int64_t>(w_max, std::max<int64_t>(1, tmax / p.min_gran));
+    w_max = std::min<int64_t>(w_max, std::max<int64_t>(1, tunits / p.min_gran));
   }
   w_max = std::max<int64_t>(1, std::min(w_max, tmax));   // a range holds at least one granule
   p.w_max = int(std::min<int64_t>(w_max, 0x7fffffff));
@@ -167,7 +178,8 @@ int check_attn(int dtype, int C, int K, int Hq, int Hkv, int D, const void* q, c
   // slabs per granule) and launch w_max workgroups per kv head group, + 1
   const int spp = page_size / 16, gran = std::max(2, spp);
   const int64_t gmax = ((int64_t(max_ctx) + 15) / 16 + (K + 15) / 16 + gran - 1) / gran;
-  if (int64_t(C) * gmax * gran >= 0x7fffffff) return HSPEC_ERR_UNSUPPORTED;
+  const int64_t seg = (kSegSlabs + gran - 1) / gran;
+  if (int64_t(C) * (gmax + seg) * gran >= 0x7fffffff) return HSPEC_ERR_UNSUPPORTED;
   const AttnPlanShape p = plan_shape(dtype, C, K, Hq, Hkv, D, hs, max_ctx, kv_split_pages, page_size);
   if (int64_t(p.w_max) * Hkv >= 0x7fffffff) return HSPEC_ERR_UNSUPPORTED;
   return HSPEC_OK;
@@ -199,6 +211,7 @@ int attn_args(AttnArgs& a, int dtype, int C, int K, int Hq, int Hkv, int D, cons
   a.gran = p.gran;
   a.range_gran = p.range_gran;
   a.min_gran = p.min_gran;
+  a.seg = p.seg;
   a.nbk = p.nbk;
   a.head_pair = p.head_pair;
   a.block_causal = block_causal;

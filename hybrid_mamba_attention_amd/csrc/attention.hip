@@ -11,11 +11,13 @@
 // Work plan (a0).  Each request's keys are its context, in slabs of 16
 // tokens, followed by its K block keys (nbk slabs), counted in granules of
 // `gran` slabs (max(2, slabs per page), from the request's start, so a
-// granule boundary starts a page and an even slab).  The batch's granules,
+// granule boundary starts a page and an even slab).  Automatic ranges also
+// charge each request `seg` units of fixed cost placed before its keys (the
+// segment's prologue, general-path tail and store); the batch's units,
 // request after request, are cut into W nearly equal ranges (B_w =
 // floor(w * T / W)); a workgroup takes its range's slabs request by request
 // (segments).  Long and short requests thus cost the same wall time: ragged
-// batches keep every workgroup busy for the same number of slabs.  Every
+// batches keep every workgroup busy for about the same time.  Every
 // workgroup derives the plan from ctx_lens itself (a block scan over the
 // requests); a segment that is a whole request writes its normalised output,
 // one that is a piece of a longer request writes fp32 (m, l, O) to slot
@@ -120,9 +122,10 @@ __device__ __forceinline__ int block_incl_scan(int v, int* lds, int* total) {
   return x + before;
 }
 
-// The batch's total granules T (every thread; lds as block_incl_scan).  g0
-// receives this thread's request granules of the first chunk (requests
-// 0 .. NT-1), which a second pass over a batch of C <= NT then reuses.
+// The batch's total units T = sum (seg + G_b) (every thread; lds as
+// block_incl_scan).  g0 receives this thread's request granules G_b of the
+// first chunk (requests 0 .. NT-1), which a second pass over a batch of
+// C <= NT then reuses.
 template <int NT>
 __device__ __forceinline__ int batch_granules(const AttnArgs& a, int* lds, int* g0) {
   int part = 0;
@@ -131,7 +134,7 @@ __device__ __forceinline__ int batch_granules(const AttnArgs& a, int* lds, int* 
     const int b = base + int(threadIdx.x);
     const int gb = b < a.C ? req_granules(a, ctx_of(a, b)) : 0;
     if (base == 0) *g0 = gb;
-    part += gb;
+    part += b < a.C ? gb + a.seg : 0;
   }
   int T;
   block_incl_scan<NT>(part, lds, &T);
@@ -139,8 +142,8 @@ __device__ __forceinline__ int batch_granules(const AttnArgs& a, int* lds, int* 
 }
 
 // Written by the grid's last workgroup, which does nothing else: W, the
-// request starts S_b, each request's first range and piece count, and the
-// range bounds B_0 .. B_W (-1 past W up to the capacity).
+// units S_b where the requests' keys start, each request's first range and
+// piece count, and the range bounds B_0 .. B_W (-1 past W up to the capacity).
 template <int NT>
 __device__ void write_plan(const AttnArgs& a, int* lds) {
   const int tid = threadIdx.x, C = a.C;
@@ -153,9 +156,9 @@ __device__ void write_plan(const AttnArgs& a, int* lds) {
     const int b = base + tid;
     const int gb = base == 0 ? g0 : (b < C ? req_granules(a, ctx_of(a, b)) : 0);
     int tot;
-    const int incl = carry + block_incl_scan<NT>(gb, lds, &tot);
+    const int incl = carry + block_incl_scan<NT>(b < C ? gb + a.seg : 0, lds, &tot);
     if (b < C) {
-      const int S = incl - gb;
+      const int S = incl - gb;   // the fixed cost comes first
       const int wf = range_of(a, S, T, W), wl = range_of(a, incl - 1, T, W);
       plan[4 + b] = S;
       plan[4 + C + b] = wf;
@@ -184,9 +187,9 @@ __device__ __forceinline__ int wave_incl_scan(int x) {
   return x;
 }
 
-// Where range w starts: the request b holding its first granule B0, that
-// request's first granule S and its context length (uniform over the
-// workgroup; b = -1 when w >= W).
+// Where range w starts: the request b whose units (fixed cost, then keys)
+// hold the range's first unit B0, the unit S where that request's keys start
+// and its context length (uniform over the workgroup; b = -1 when w >= W).
 struct RangeStart {
   int W, T, B0, B1, b, S, ctx;
 };
@@ -200,7 +203,8 @@ __device__ RangeStart find_range(const AttnArgs& a, int w, int* lds) {
     const int lane = tid & 63;
     const int ctx = lane < C ? ctx_of(a, lane) : 0;
     const int gb = lane < C ? req_granules(a, ctx) : 0;
-    const int incl = wave_incl_scan(gb);
+    const int gv = lane < C ? gb + a.seg : 0;
+    const int incl = wave_incl_scan(gv);
     r.T = __builtin_amdgcn_readlane(incl, 63);
     r.W = range_count(a, r.T);
     r.b = -1;
@@ -209,7 +213,7 @@ __device__ RangeStart find_range(const AttnArgs& a, int w, int* lds) {
     if (w >= r.W) return r;
     r.B0 = range_bound(a, w, r.T, r.W);
     r.B1 = range_bound(a, w + 1, r.T, r.W);
-    const uint64_t hit = __ballot(lane < C && incl - gb <= r.B0 && r.B0 < incl);
+    const uint64_t hit = __ballot(lane < C && incl - gv <= r.B0 && r.B0 < incl);
     if (hit == 0) return r;   // cannot happen: B0 < T lies in some request
     const int fb = __ffsll(static_cast<long long>(hit)) - 1;   // exactly one lane
     r.b = fb;
@@ -232,9 +236,10 @@ __device__ RangeStart find_range(const AttnArgs& a, int w, int* lds) {
   for (int base = 0; base < C; base += NT) {
     const int b = base + tid;
     const int gb = base == 0 ? g0 : (b < C ? req_granules(a, ctx_of(a, b)) : 0);
+    const int gv = b < C ? gb + a.seg : 0;
     int tot;
-    const int incl = carry + block_incl_scan<NT>(gb, lds, &tot);  // (its barriers order found[0] = -1)
-    if (b < C && incl - gb <= r.B0 && r.B0 < incl) {   // exactly one thread of the batch
+    const int incl = carry + block_incl_scan<NT>(gv, lds, &tot);  // (its barriers order found[0] = -1)
+    if (b < C && incl - gv <= r.B0 && r.B0 < incl) {   // exactly one thread of the batch
       found[0] = b;
       found[1] = incl - gb;
     }
@@ -899,7 +904,7 @@ __global__ __launch_bounds__(64 * NW, (RT == 2 && sizeof(T) == 2) ? 2 : 1) void 
       }
     }
 
-    S += Gb;
+    S += Gb + a.seg;   // the next request's keys start after its fixed cost
     ++b;
     if (S < rs.B1) ctx_next = ctx_of(a, b);
   }

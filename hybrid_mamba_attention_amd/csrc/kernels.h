@@ -34,6 +34,7 @@ struct AttnArgs {
   int gran;
   int range_gran;                 // 0 = automatic
   int min_gran;
+  int seg;                        // a request's fixed cost in units (automatic ranges; else 0)
   int nbk;
   int head_pair;                  // 1: two kv heads per workgroup when the shape allows (long ranges)
   int block_causal;               // 1: block query t sees block keys s <= t only

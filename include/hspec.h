@@ -155,22 +155,24 @@ int hspec_ssd_scan(void* stream, int dtype, int C, int K, int H, int P, int ng, 
  *       at least the queried size.
  * Work plan.  Request b's keys are its ceil(ctx_b/16) context slabs of 16
  * tokens followed by its ceil(K/16) block slabs, counted in granules of
- * g = max(2, P/16) slabs from the request's start (G_b granules).  The
- * batch's T = sum G_b granules, request after request (request b from
- * granule S_b), are cut into W ranges [B_w, B_{w+1}): automatically W =
- * min(w_max, max(1, floor(T / ceil(16/g)))) nearly equal ranges, B_w =
- * floor(w*T/W);
+ * g = max(2, P/16) slabs from the request's start (G_b granules).
+ * Automatic ranges charge each request a fixed cost of s = ceil(12/g)
+ * units placed before its keys (s = 0 with kv_split_pages), so request b
+ * spans s + G_b units, request after request, and its keys start at unit
+ * S_b; the batch's T = sum (s + G_b) units are cut into W ranges
+ * [B_w, B_{w+1}): automatically W = min(w_max, max(1, floor(T /
+ * ceil(16/g)))) ranges of nearly equal cost, B_w = floor(w*T/W);
  * with kv_split_pages, ranges of R = ceil(kv_split_pages*(P/16)/g)
  * granules, B_w = min(w*R, T).  One workgroup per (range, kv head group)
  * takes its range's slabs request by request; a request inside one range is
  * finished there, a request spanning several ranges (its pieces) is merged
  * by log-sum-exp.  w_max, a bound the host derives from C, max_ctx, K, Hkv
  * and the page size, sizes the grid and the workspace: automatically
- * min(512/Hkv, max(1, floor(C*Gmax / ceil(16/g)))), Gmax the granules of a
- * max_ctx request; with kv_split_pages, ceil(C*Gmax / R).  The workspace
+ * min(512/Hkv, max(1, floor(C*(s + Gmax) / ceil(16/g)))), Gmax the granules
+ * of a max_ctx request; with kv_split_pages, ceil(C*Gmax / R).  The workspace
  * starts with the int32 plan the kernels derive from ctx_lens:
  *         [0] W  [1] g  [2] C  [3] w_max
- *         [4, 4+C) S_b    [4+C, 4+2C) range of request b's first granule
+ *         [4, 4+C) S_b    [4+C, 4+2C) range of request b's first key granule
  *         [4+2C, 4+3C) ranges request b spans (its pieces)
  *         [4+3C, 4+3C+w_max+1) B_0 .. B_W (B_W = T), then -1
  *       followed, when w_max > 1, by fp32 partials of two slots per range.

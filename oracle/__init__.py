@@ -28,7 +28,7 @@ from .init_state import init_state
 from .ssd import ssd_recurrence, ssd_chunked
 from .attention import (PoisonedRead, gather_context, block_attention,
                         block_attention_ranges, split_partials, merge_partials, key_index)
-from .plan import (range_plan, plan_len, range_count, request_granules, request_pieces,
+from .plan import (range_plan, plan_len, range_count, request_granules, request_pieces, segment_granules,
                    granule_slabs)
 from .layer import draft_layer
 from .mamba_block import (mamba_block, causal_conv, gated_rmsnorm, silu, softplus,
@@ -39,7 +39,7 @@ from .stack import stack_forward, rmsnorm
 __all__ = [
     "decode", "BF16", "F32", "init_state", "ssd_recurrence", "ssd_chunked",
     "PoisonedRead", "gather_context", "block_attention", "block_attention_ranges",
-    "split_partials", "merge_partials", "key_index", "range_plan", "plan_len", "range_count",
+    "split_partials", "merge_partials", "key_index", "range_plan", "plan_len", "range_count", "segment_granules",
     "request_granules", "request_pieces", "granule_slabs",
     "draft_layer", "mamba_block", "causal_conv", "gated_rmsnorm", "silu", "softplus",
     "in_proj_sizes", "kv_project", "kv_inject", "extra_kv_bytes_per_token", "stack_forward",

@@ -14,17 +14,27 @@ that long and short requests cost the same wall time:
     starts a page and an even slab.  Request b holds G_b = ceil(L_b / g)
     granules; the batch holds T = sum_b G_b, request b starting at granule
     S_b = sum_{b' < b} G_b' of the concatenation.
-  * The concatenation is cut into W ranges, range w holding granules
+  * Automatic ranges also charge every request a fixed cost of sigma =
+    ceil(12 / g) virtual granules (12 slabs' worth) placed before its keys:
+    the work a request costs its range however short it is (its query rows
+    and page-table window, the first stages' round trip, the partial last
+    page and the block's own slabs on the general path, the output store).
+    Request b then spans V_b = sigma + G_b units of the concatenation and its
+    keys start at unit S_b = sum_{b' < b} V_b' + sigma; T = sum_b V_b.  Fixed
+    ranges take sigma = 0 (V_b = G_b, S_b the plain prefix sum).
+  * The concatenation is cut into W ranges, range w holding units
     [B_w, B_{w+1}):
       - automatic (range_pages = 0): W = min(w_max, max(1, floor(T / r_min))),
-        r_min = ceil(16 / g) granules (every range holds >= 16 slabs when the
-        batch has them), and B_w = floor(w * T / W): nearly equal ranges;
+        r_min = ceil(16 / g) granules (every range holds >= 16 slabs' worth
+        when the batch has them), and B_w = floor(w * T / W): ranges of
+        nearly equal cost;
       - fixed (range_pages > 0): ranges of exactly R = max(1,
         ceil(range_pages * (P/16) / g)) granules, the last one shorter:
         W = ceil(T / R), B_w = min(w * R, T).
-    In both cases W <= T, so no range is empty.
-  * Request b's pieces are the ranges it overlaps: w_first_b (the range
-    holding granule S_b) through the range holding granule S_b + G_b - 1.
+    In both cases W <= T, so no range is empty (a range may still hold only
+    the fixed cost of a request, and then no keys).
+  * Request b's pieces are the ranges its keys overlap: w_first_b (the range
+    holding unit S_b) through the range holding unit S_b + G_b - 1.
     A request inside one range (one piece) is finished by that range; the
     pieces of a longer request are merged by log-sum-exp (E5).
   * A piece's partial result goes to slot 2*w + k of its range w: k = 0 for
@@ -37,7 +47,7 @@ The plan is one int32 array, laid out as the library writes it at the start
 of its attention workspace (so the two can be compared bit for bit):
 
     [0] W     [1] g     [2] C     [3] w_max
-    [4 : 4+C]            S_b        (first granule of request b)
+    [4 : 4+C]            S_b        (unit of request b's first key granule)
     [4+C : 4+2C]         w_first_b  (range holding request b's first granule)
     [4+2C : 4+3C]        pieces_b   (ranges request b overlaps)
     [4+3C : 4+3C+w_max+1]  B_w for w = 0..W (B_W = T), then -1 up to the capacity
@@ -48,6 +58,7 @@ and workspace by it.
 import numpy as np
 
 SLAB = 16
+SEG_SLABS = 12   # a request's fixed cost in automatic ranges, in slabs
 
 
 def granule_slabs(page_size: int) -> int:
@@ -66,6 +77,11 @@ def request_granules(ctx_lens, K: int, page_size: int = 16) -> np.ndarray:
     g = granule_slabs(page_size)
     L = (ctx + SLAB - 1) // SLAB + (K + SLAB - 1) // SLAB
     return (L + g - 1) // g
+
+
+def segment_granules(page_size: int = 16, range_pages: int = 0) -> int:
+    """sigma: a request's fixed cost in units (0 for fixed ranges)."""
+    return 0 if range_pages else -(-SEG_SLABS // granule_slabs(page_size))
 
 
 def range_count(T: int, *, w_max: int, page_size: int = 16, range_pages: int = 0) -> int:
@@ -92,7 +108,8 @@ def range_plan(ctx_lens, *, K: int, w_max: int, page_size: int = 16, range_pages
     C = len(G)
     if C < 1:
         raise ValueError("at least one request")
-    T = int(G.sum())
+    sigma = segment_granules(page_size, range_pages)
+    T = int((G + sigma).sum())
     W = range_count(T, w_max=w_max, page_size=page_size, range_pages=range_pages)
     assert 1 <= W <= T
     if range_pages == 0:
@@ -100,7 +117,7 @@ def range_plan(ctx_lens, *, K: int, w_max: int, page_size: int = 16, range_pages
     else:
         R = max(1, -(-(range_pages * (page_size // SLAB)) // granule_slabs(page_size)))
         B = [min(w * R, T) for w in range(W + 1)]
-    S = np.concatenate([[0], np.cumsum(G)[:-1]])
+    S = np.cumsum(G + sigma) - G   # each request's keys start after its fixed cost
     w_first = np.zeros(C, np.int64)
     pieces = np.zeros(C, np.int64)
     for b in range(C):

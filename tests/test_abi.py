@@ -116,8 +116,8 @@ def test_attention_workspace_query():
     granules of 2 slabs; the batch at most 128 granules."""
     code, n = _attn(split=32)                           # 32 pages = 16 granules per range: 8 ranges
     assert code == OK and n == _ws_expect(4, 8, 64)
-    code0, n0 = _attn(split=0)                          # automatic: at most floor(128 / 8) = 16 ranges
-    assert code0 == OK and n0 == _ws_expect(4, 16, 64)
+    code0, n0 = _attn(split=0)                          # automatic: at most floor(4 * (32 + 6) / 8) = 19 ranges
+    assert code0 == OK and n0 == _ws_expect(4, 19, 64)
     code1, n1 = _attn(split=1000)                       # one range for the whole batch: no partials
     assert code1 == OK and n1 == _ws_expect(4, 1, 64)
     # a real (non-NULL) workspace that is too small is refused before any launch

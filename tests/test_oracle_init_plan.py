@@ -79,7 +79,8 @@ def test_plan_invariants(page, w_max, range_pages):
         f = oracle.plan.unpack(plan, C)
         W, T, g, B = f["W"], f["T"], f["g"], f["B"]
         G = oracle.request_granules(ctx, K, page)
-        assert g == max(2, page // 16) and T == G.sum() and 1 <= W <= min(w_max, T)
+        sigma = oracle.segment_granules(page, range_pages)
+        assert g == max(2, page // 16) and T == (G + sigma).sum() and 1 <= W <= min(w_max, T)
         assert B[0] == 0 and B[-1] == T and (np.diff(B) >= 1).all()
         if range_pages == 0:
             assert np.diff(B).max() - np.diff(B).min() <= 1
