@@ -212,15 +212,17 @@ def test_hnd_pool_layout_is_bit_identical():
     assert_attn_close(to_host64(oh), oracle_attn(case), "bf16", "HND")
 
 
+@pytest.mark.parametrize("hq", [32, 64], ids=["64-rows", "128-rows"])
 @pytest.mark.parametrize("page", [16, 64])
 @pytest.mark.parametrize("causal", [False, True], ids=["mask-free", "block-causal"])
-def test_head_pair_workgroups_match_single_heads(causal, page):
+def test_head_pair_workgroups_match_single_heads(causal, page, hq):
     """Splits of at least 2048 tokens over NHD pools (adjacent kv heads) take
     two heads per workgroup; the HND layout of the same pools keeps one head
     per workgroup.  Same bits, and the oracle within tolerance (ragged
     contexts, one split and 2048-token splits with a merge, the block keys,
-    16- and 64-token pages)."""
-    case = make_attn_case(960, [2100, 4000, 2048, 3000], 16, 32, 8, 128, "bf16", page=page)
+    16- and 64-token pages; 64 query rows per kv head, one row tile per wave,
+    and 128, two row tiles per wave)."""
+    case = make_attn_case(960, [2100, 4000, 2048, 3000], 16, hq, 8, 128, "bf16", page=page)
     for split in (10 ** 6, 2048 // page):
         on, _, _ = run_attn(case, split=split, layout="NHD", causal=causal)
         oh, _, _ = run_attn(case, split=split, layout="HND", causal=causal)
