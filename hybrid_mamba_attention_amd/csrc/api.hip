@@ -92,6 +92,15 @@ constexpr int kTargetUnits = 512;
 // two slabs, and the cost model put the slowest range of that batch at
 // 45 us with 12 slabs against 53 us with none.
 constexpr int kSegSlabs = 12;
+// Ranges (at the batch's bound) of at least this many slabs take two kv heads
+// per workgroup when the pools and rows allow it.  Flushed medians of the
+// attention call on one box, one head per workgroup -> head pair, 8192-token
+// contexts: C = 4 44.4 -> 41.7 us and C = 8 65.4 -> 61.7 (ranges of 32 and 64
+// slabs), the C = 32 ragged batch (~126) 74.5 -> 70.4; but C = 1 24.0 -> 27.0
+// and C = 2 33.2 -> 33.7 (8 and 16 slabs at the bound; one request at 2048
+// tokens: 19.7 -> 23.1), where the halved workgroup count leaves CUs idle or
+// each workgroup only a few stages.
+constexpr int kPairSlabs = 32;
 
 // log2(page_size / 16) for a supported page size, else -1
 int page_shift(int page_size) {
@@ -118,13 +127,13 @@ AttnPlanShape plan_shape(int dtype, int C, int K, int Hq, int Hkv, int D, int64_
   if (kv_split_pages > 0) {
     p.range_gran = int(std::max<int64_t>(1, (int64_t(kv_split_pages) * spp + p.gran - 1) / p.gran));
     w_max = (tmax + p.range_gran - 1) / p.range_gran;
-    p.head_pair = hp_ok && int64_t(p.range_gran) * p.gran >= 128;
+    p.head_pair = hp_ok && int64_t(p.range_gran) * p.gran >= kPairSlabs;
   } else {
     p.range_gran = 0;
     w_max = std::max<int64_t>(1, kTargetUnits / Hkv);
     // two heads per workgroup when the batch at its bound gives ranges of
-    // 128+ slabs
-    p.head_pair = hp_ok && tmax * p.gran >= 128 * std::min(w_max, tmax);
+    // kPairSlabs slabs or more
+    p.head_pair = hp_ok && tmax * p.gran >= kPairSlabs * std::min(w_max, tmax);
     // The device makes W = min(w_max, max(1, floor(T / min_gran))) ranges and
     // T <= tmax (contexts are clamped to max_ctx), so no more can ever be
     // needed: a small batch's grid then holds no workgroups without a range

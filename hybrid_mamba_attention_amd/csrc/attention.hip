@@ -947,14 +947,13 @@ static hipError_t launch_attn_d(hipStream_t st, const AttnArgs& a) {
   if (a.rows <= 16) return launch_attn_cfg<T, D, 1, 1>(st, a);
   if (a.rows <= 32) return launch_attn_cfg<T, D, 1, 2>(st, a);
   // Two adjacent kv heads per workgroup (bf16, D = 128, 33..128 rows per
-  // head, ranges of about 128 slabs or more, as the host planned): each stage
-  // row is then one 512-byte piece of the token's K (V) instead of two
-  // 256-byte pieces read by two workgroups, which a read probe of the pattern
-  // measures at 7.1-7.2 TB/s against 6.6 TB/s (C = 128: 687 -> 651 us; with
-  // two row tiles per wave, 128 rows per head, the 64-head ragged batch went
-  // from 315 to 296 us: its odd heads' 256-byte pieces, 256 bytes into each
-  // 1 KB of the row, had streamed 15-25% slower).  With short ranges (small
-  // C) halving the workgroup count costs more than the pieces gain.
+  // head, adjacent heads in the pools): each stage row is then one 512-byte
+  // piece of the token's K (V) instead of two 256-byte pieces read by two
+  // workgroups, which a read probe of the pattern measures at 7.1-7.2 TB/s
+  // against 6.6 TB/s (C = 128: 687 -> 651 us; with two row tiles per wave,
+  // 128 rows per head, the 64-head ragged batch went from 315 to 296 us: its
+  // odd heads' 256-byte pieces, 256 bytes into each 1 KB of the row, had
+  // streamed 15-25% slower).
   if constexpr (std::is_same<T, bf16_t>::value && D == 128) {
     if (a.head_pair && head_pair_fits(a.rows, a.Hkv, a.head_stride, 1, D))
       return a.rows <= 64 ? launch_attn_cfg<T, D, 1, 8, 2>(st, a) : launch_attn_cfg<T, D, 2, 8, 2>(st, a);

@@ -216,9 +216,8 @@ def test_hnd_pool_layout_is_bit_identical():
 @pytest.mark.parametrize("page", [16, 64])
 @pytest.mark.parametrize("causal", [False, True], ids=["mask-free", "block-causal"])
 def test_head_pair_workgroups_match_single_heads(causal, page, hq):
-    """Splits of at least 2048 tokens over NHD pools (adjacent kv heads) take
-    two heads per workgroup; the HND layout of the same pools keeps one head
-    per workgroup.  Same bits, and the oracle within tolerance (ragged
+    """NHD pools (adjacent kv heads) take two heads per workgroup; the HND
+    layout of the same pools keeps one head per workgroup.  Same bits, and the oracle within tolerance (ragged
     contexts, one split and 2048-token splits with a merge, the block keys,
     16- and 64-token pages; 64 query rows per kv head, one row tile per wave,
     and 128, two row tiles per wave)."""
