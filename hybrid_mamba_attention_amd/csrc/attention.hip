@@ -698,17 +698,71 @@ __global__ __launch_bounds__(64 * NW, (RT == 2 && sizeof(T) == 2) ? 2 : 1) void 
             }
           }
         }
-      float p[RT][8];
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+      // Scores of row tile rt.  With two row tiles every tile's scores come
+      // first: the K operands die before the softmax, and the second tile's
+      // matrix work runs under the first tile's softmax instead of after its
+      // max and rescale (the 128-row ragged batch: 298.5 -> 291.7 us).  With
+      // one tile they stay next to its softmax (computed first, the head pair
+      // at C = 128 took 648.7 against 646.8 us, nine runs each).
+      f32x4 sacc[RT][2];
+      auto scores = [&](int rt) __attribute__((always_inline)) {
+        sacc[rt][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+        sacc[rt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ds = 0; ds < DS; ++ds)
 #pragma unroll
-          for (int tt = 0; tt < 2; ++tt) sacc[tt] = mma8(kop[tt][ds], qv[rt][ds], sacc[tt]);
+          for (int tt = 0; tt < 2; ++tt) sacc[rt][tt] = mma8(kop[tt][ds], qv[rt][ds], sacc[rt][tt]);
+      };
+      constexpr bool kScoresFirst = RT > 1;
+      if constexpr (kScoresFirst) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) scores(rt);
+      }
+      // V operands: lane reads 8 token rows x D/16 values and transposes them
+      // in registers.  They do not depend on the softmax, so in the bf16
+      // one-head one-tile forms they are read beside the score MFMAs, their
+      // LDS latency and permutes then overlapping the matrix work (C = 2 at
+      // 8192 tokens: 33.5 -> 32.6 us; one request at 2048 tokens: 19.8 ->
+      // 19.2).  The two-tile forms, at their register bound, spill more that
+      // way and lose the gain (the 128-row ragged batch: 292 -> 299 us); the
+      // head pair measured no better (C = 128: 648.2 against 647.3 us, nine
+      // runs each); fp32 operands are twice the registers.  Those read them
+      // after the softmax, in the order of the code below.
+      constexpr bool kVEarly = sizeof(T) == 2 && RT == 1 && HP == 1;
+      auto read_v = [&](VRow<T, DPL> (&vr)[8]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const unsigned char* base = tv + (e >> 2) * 16 * CPR * 16;
+          if constexpr (sizeof(T) == 2 && DPL == 8) {
+            vr[e].v = *reinterpret_cast<const uint4*>(base + vpos[e & 3][0]);
+          } else if constexpr (sizeof(T) == 2) {
+            vr[e].v = *reinterpret_cast<const uint2*>(base + vpos[e & 3][0]);
+          } else {
+#pragma unroll
+            for (int h = 0; h < DPL / 4; ++h) {
+              const uint4 x = *reinterpret_cast<const uint4*>(base + vpos[e & 3][h]);
+              vr[e].v[4 * h + 0] = __uint_as_float(x.x);
+              vr[e].v[4 * h + 1] = __uint_as_float(x.y);
+              vr[e].v[4 * h + 2] = __uint_as_float(x.z);
+              vr[e].v[4 * h + 3] = __uint_as_float(x.w);
+            }
+          }
+        }
+      };
+      Vec8<T> vte[kVEarly ? DPL : 1];
+      if constexpr (kVEarly) {
+        VRow<T, DPL> vr[8];
+        read_v(vr);
+#pragma unroll
+        for (int cc = 0; cc < DPL; ++cc) vtrans<DPL>(vte[cc], vr, cc);
+      }
+      float p[RT][8];
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        if constexpr (!kScoresFirst) scores(rt);
         float sv[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) sv[e] = sacc[e >> 2][e & 3];
+        for (int e = 0; e < 8; ++e) sv[e] = sacc[rt][e >> 2][e & 3];
         if (partial) {
           // token 4*lg + (e&3) of page e>>2 is kept when it is one of the page's
           // valid tokens and, on a block-causal block page with index cb-1, its
@@ -742,29 +796,18 @@ __global__ __launch_bounds__(64 * NW, (RT == 2 && sizeof(T) == 2) ? 2 : 1) void 
         acc.l[rt] += ((p[rt][0] + p[rt][1]) + (p[rt][2] + p[rt][3])) +
                      ((p[rt][4] + p[rt][5]) + (p[rt][6] + p[rt][7]));
       }
-      // O^T += V^T . P^T: lane reads 8 token rows x D/16 values, transposes in registers
+      // O^T += V^T . P^T
       VRow<T, DPL> vr[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const unsigned char* base = tv + (e >> 2) * 16 * CPR * 16;
-        if constexpr (sizeof(T) == 2 && DPL == 8) {
-          vr[e].v = *reinterpret_cast<const uint4*>(base + vpos[e & 3][0]);
-        } else if constexpr (sizeof(T) == 2) {
-          vr[e].v = *reinterpret_cast<const uint2*>(base + vpos[e & 3][0]);
-        } else {
-#pragma unroll
-          for (int h = 0; h < DPL / 4; ++h) {
-            const uint4 x = *reinterpret_cast<const uint4*>(base + vpos[e & 3][h]);
-            vr[e].v[4 * h + 0] = __uint_as_float(x.x);
-            vr[e].v[4 * h + 1] = __uint_as_float(x.y);
-            vr[e].v[4 * h + 2] = __uint_as_float(x.z);
-            vr[e].v[4 * h + 3] = __uint_as_float(x.w);
-          }
-        }
-      }
+      if constexpr (!kVEarly) read_v(vr);
       Vec8<T> vt[DPL];
 #pragma unroll
-      for (int cc = 0; cc < DPL; ++cc) vtrans<DPL>(vt[cc], vr, cc);
+      for (int cc = 0; cc < DPL; ++cc) {
+        if constexpr (kVEarly) {
+          vt[cc] = vte[cc];
+        } else {
+          vtrans<DPL>(vt[cc], vr, cc);
+        }
+      }
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
         Vec8<T> pv;
