@@ -230,19 +230,21 @@ def test_head_pair_workgroups_match_single_heads(causal, page, hq):
 
 
 @pytest.mark.parametrize("page", [16, 32, 64])
-def test_contexts_across_page_table_windows(page):
+@pytest.mark.parametrize("hq", [32, 64], ids=["64-rows", "128-rows"])
+def test_contexts_across_page_table_windows(page, hq):
     """One split per request over contexts that span the kernel's 128-page
     windows of the page table: a window starting at the last stage of full
     pages (fetched during the loop over full pages, made current by the stages
     after it) or right after them, and two window crossings.  NHD pools (two
     heads per workgroup) and HND pools (one head) agree bit for bit, and both
-    match the oracle."""
-    flush(f"[attn windows page {page}]")
+    match the oracle; 64 and 128 query rows per kv head (one and two row
+    tiles per wave)."""
+    flush(f"[attn windows page {page} hq {hq}]")
     w = 64 * (page // 16)                 # stages (two 16-token slabs each) per window
     ctx = [16 * (2 * w + 2) + 5,          # full-page stages end one past the first window start
            16 * (2 * w) + 2,              # they end right before it
            16 * (4 * w + 2) + 9]          # two window crossings
-    case = make_attn_case(970 + page, ctx, 16, 32, 8, 128, "bf16", page=page)
+    case = make_attn_case(970 + page, ctx, 16, hq, 8, 128, "bf16", page=page)
     want = oracle_attn(case)
     on, _, _ = run_attn(case, split=10 ** 6, layout="NHD")
     oh, _, _ = run_attn(case, split=10 ** 6, layout="HND")
