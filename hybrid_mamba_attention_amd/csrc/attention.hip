@@ -30,7 +30,7 @@
 //   * The G*K query rows of kv head j (row r -> block position r / G, head
 //     j*G + r % G) are split over NW/HP waves, RT tiles of 16 rows each, and
 //     held in registers as matrix-core operands for a whole segment.  With
-//     HP = 2 (NHD pools, ranges of 2048+ tokens) a stage row is the 2D-wide
+//     HP = 2 (NHD pools, ranges of 32+ slabs) a stage row is the 2D-wide
 //     piece of both heads, 512 bytes for bf16 D = 128, and each half of the
 //     waves computes on its own head's columns.
 //   * A segment's slabs stream through LDS 32 tokens (two slabs) at a time:
