@@ -92,6 +92,13 @@ constexpr int kTargetUnits = 512;
 // two slabs, and the cost model put the slowest range of that batch at
 // 45 us with 12 slabs against 53 us with none.
 constexpr int kSegSlabs = 12;
+// The same with more than 64 query rows per kv head (two row tiles per wave):
+// a segment's query rows, output store and general-path stages are twice the
+// work.  Attention on the 64-head ragged batch (128 rows per kv head),
+// flushed medians over six runs: 12 slabs 292.9 us, 18 288.5, 24 287.8,
+// 32 290.7.
+constexpr int kSegSlabsTwoTiles = 24;
+int seg_slabs(int rows) { return rows > 64 ? kSegSlabsTwoTiles : kSegSlabs; }
 // Ranges (at the batch's bound) of at least this many slabs take two kv heads
 // per workgroup when the pools and rows allow it.  Flushed medians of the
 // attention call on one box, one head per workgroup -> head pair, 8192-token
@@ -119,8 +126,9 @@ AttnPlanShape plan_shape(int dtype, int C, int K, int Hq, int Hkv, int D, int64_
   // granules of a max_ctx request, and of the batch at most
   const int64_t gmax = ((int64_t(max_ctx) + 15) / 16 + p.nbk + p.gran - 1) / p.gran;
   const int64_t tmax = int64_t(C) * gmax;
-  // automatic ranges charge each request kSegSlabs slabs' worth of fixed cost
-  p.seg = kv_split_pages > 0 ? 0 : (kSegSlabs + p.gran - 1) / p.gran;
+  // automatic ranges charge each request seg_slabs(rows) slabs' worth of fixed
+  // cost
+  p.seg = kv_split_pages > 0 ? 0 : (seg_slabs((Hq / Hkv) * K) + p.gran - 1) / p.gran;
   const int64_t tunits = int64_t(C) * (gmax + p.seg);   // the batch's units at its bound
   const bool hp_ok = head_pair_fits((Hq / Hkv) * K, Hkv, head_stride, dtype, D);
   int64_t w_max;
@@ -187,7 +195,7 @@ int check_attn(int dtype, int C, int K, int Hq, int Hkv, int D, const void* q, c
   // slabs per granule) and launch w_max workgroups per kv head group, + 1
   const int spp = page_size / 16, gran = std::max(2, spp);
   const int64_t gmax = ((int64_t(max_ctx) + 15) / 16 + (K + 15) / 16 + gran - 1) / gran;
-  const int64_t seg = (kSegSlabs + gran - 1) / gran;
+  const int64_t seg = (seg_slabs((Hq / Hkv) * K) + gran - 1) / gran;
   if (int64_t(C) * (gmax + seg) * gran >= 0x7fffffff) return HSPEC_ERR_UNSUPPORTED;
   const AttnPlanShape p = plan_shape(dtype, C, K, Hq, Hkv, D, hs, max_ctx, kv_split_pages, page_size);
   if (int64_t(p.w_max) * Hkv >= 0x7fffffff) return HSPEC_ERR_UNSUPPORTED;

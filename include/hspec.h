@@ -157,7 +157,8 @@ int hspec_ssd_scan(void* stream, int dtype, int C, int K, int H, int P, int ng, 
  * tokens followed by its ceil(K/16) block slabs, counted in granules of
  * g = max(2, P/16) slabs from the request's start (G_b granules).
  * Automatic ranges charge each request a fixed cost of s = ceil(12/g)
- * units placed before its keys (s = 0 with kv_split_pages), so request b
+ * units, ceil(24/g) with more than 64 query rows per kv head ((Hq/Hkv)*K),
+ * placed before its keys (s = 0 with kv_split_pages), so request b
  * spans s + G_b units, request after request, and its keys start at unit
  * S_b; the batch's T = sum (s + G_b) units are cut into W ranges
  * [B_w, B_{w+1}): automatically W = min(w_max, max(1, floor(T /

@@ -163,7 +163,7 @@ def block_attention_ranges(q, k_blk, v_blk, k_cache, v_cache, page_table, ctx_le
     G = Hq // Hkv
     sc = _scale(D, scale)
     P = k_cache.shape[1]
-    plan = range_plan(ctx_lens, K=K, w_max=w_max, page_size=P, range_pages=range_pages)
+    plan = range_plan(ctx_lens, K=K, w_max=w_max, page_size=P, range_pages=range_pages, rows=G * K)
     out = np.zeros((C, K, Hq, D))
     reqs = range(C) if requests is None else requests
     for b in reqs:

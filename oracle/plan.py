@@ -19,6 +19,8 @@ that long and short requests cost the same wall time:
     the work a request costs its range however short it is (its query rows
     and page-table window, the first stages' round trip, the partial last
     page and the block's own slabs on the general path, the output store).
+    With more than 64 query rows per kv head (rows = (Hq / Hkv) * K) that
+    work is twice as large and the charge is ceil(24 / g).
     Request b then spans V_b = sigma + G_b units of the concatenation and its
     keys start at unit S_b = sum_{b' < b} V_b' + sigma; T = sum_b V_b.  Fixed
     ranges take sigma = 0 (V_b = G_b, S_b the plain prefix sum).
@@ -59,6 +61,7 @@ import numpy as np
 
 SLAB = 16
 SEG_SLABS = 12   # a request's fixed cost in automatic ranges, in slabs
+SEG_SLABS_TWO_TILES = 24   # the same with more than 64 query rows per kv head
 
 
 def granule_slabs(page_size: int) -> int:
@@ -79,9 +82,13 @@ def request_granules(ctx_lens, K: int, page_size: int = 16) -> np.ndarray:
     return (L + g - 1) // g
 
 
-def segment_granules(page_size: int = 16, range_pages: int = 0) -> int:
-    """sigma: a request's fixed cost in units (0 for fixed ranges)."""
-    return 0 if range_pages else -(-SEG_SLABS // granule_slabs(page_size))
+def segment_granules(page_size: int = 16, range_pages: int = 0, rows: int = 64) -> int:
+    """sigma: a request's fixed cost in units (0 for fixed ranges); rows =
+    query rows per kv head, (Hq / Hkv) * K."""
+    if range_pages:
+        return 0
+    slabs = SEG_SLABS_TWO_TILES if rows > 64 else SEG_SLABS
+    return -(-slabs // granule_slabs(page_size))
 
 
 def range_count(T: int, *, w_max: int, page_size: int = 16, range_pages: int = 0) -> int:
@@ -102,13 +109,15 @@ def plan_len(C: int, w_max: int) -> int:
     return 4 + 3 * int(C) + int(w_max) + 1
 
 
-def range_plan(ctx_lens, *, K: int, w_max: int, page_size: int = 16, range_pages: int = 0) -> np.ndarray:
-    """The int32 plan laid out as in the module docstring."""
+def range_plan(ctx_lens, *, K: int, w_max: int, page_size: int = 16, range_pages: int = 0,
+               rows: int = 64) -> np.ndarray:
+    """The int32 plan laid out as in the module docstring (rows = query rows
+    per kv head, which sets the fixed cost of automatic ranges)."""
     G = request_granules(ctx_lens, K, page_size)
     C = len(G)
     if C < 1:
         raise ValueError("at least one request")
-    sigma = segment_granules(page_size, range_pages)
+    sigma = segment_granules(page_size, range_pages, rows)
     T = int((G + sigma).sum())
     W = range_count(T, w_max=w_max, page_size=page_size, range_pages=range_pages)
     assert 1 <= W <= T

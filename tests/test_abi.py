@@ -120,6 +120,10 @@ def test_attention_workspace_query():
     assert code0 == OK and n0 == _ws_expect(4, 19, 64)
     code1, n1 = _attn(split=1000)                       # one range for the whole batch: no partials
     assert code1 == OK and n1 == _ws_expect(4, 1, 64)
+    # 128 query rows per kv head: a charge of ceil(24/2) = 12 units per request,
+    # at most floor(4 * (32 + 12) / 8) = 22 ranges
+    code2, n2 = _attn(split=0, Hq=64)
+    assert code2 == OK and n2 == _ws_expect(4, 22, 128)
     # a real (non-NULL) workspace that is too small is refused before any launch
     assert _attn(ws=FAKE, nbytes=n - 1, split=32)[0] == WORKSPACE
 

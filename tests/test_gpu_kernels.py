@@ -104,8 +104,13 @@ def test_attention_shapes(name, ctx, K, Hq, Hkv, D, dtype):
     case = make_attn_case(sum(ctx) + K, ctx, K, Hq, Hkv, D, dtype)
     want = oracle_attn(case)
     for split in (0, 1, 3):
-        o, _, _ = run_attn(case, split=split)
+        o, ws, _ = run_attn(case, split=split)
         assert_attn_close(to_host64(o), want, dtype, f"{name} split={split}")
+        # the device's work plan, bit for bit (automatic ranges charge by rows)
+        plan = ops.plan_of(ws, len(ctx)).cpu().numpy()
+        want_plan = oracle.range_plan(case["ctx_lens"], K=K, w_max=int(plan[3]), page_size=PAGE,
+                                      range_pages=split, rows=(Hq // Hkv) * K)
+        assert np.array_equal(plan, want_plan), f"{name} split={split}: work plan"
 
 
 CAUSAL_CASES = [
@@ -189,7 +194,7 @@ def test_split_invariance_and_repeatability():
         assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)), f"split={split} not repeatable"
         assert_attn_close(to_host64(o1), want, "bf16", f"split={split}")
         plan = ops.plan_of(ws, len(case["ctx_lens"])).cpu().numpy()
-        want_plan = oracle.range_plan(case["ctx_lens"], K=16, w_max=int(plan[3]), range_pages=split)
+        want_plan = oracle.range_plan(case["ctx_lens"], K=16, w_max=int(plan[3]), range_pages=split, rows=64)
         assert np.array_equal(plan, want_plan), split
 
 

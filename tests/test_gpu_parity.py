@@ -40,7 +40,7 @@ def _check_layer(idx, sample_requests=None):
     # the int32 work plan at the head of the workspace, bit for bit (the
     # capacity w_max is the host's sizing bound, read from the plan)
     plan = layer.plan().cpu().numpy()
-    want = oracle.range_plan(inp.ctx_lens, K=w.K, w_max=int(plan[3]))
+    want = oracle.range_plan(inp.ctx_lens, K=w.K, w_max=int(plan[3]), rows=(w.Hq // w.Hkv) * w.K)
     assert np.array_equal(plan, want), "work plan differs from the oracle planner"
     flush(f"[parity] workload {idx}: ok")
 

@@ -45,7 +45,7 @@ def test_plan_hand(golden_dir):
     g = json.load(open(os.path.join(golden_dir, "plan_hand.json")))
     for case in g["cases"]:
         plan = oracle.range_plan(case["ctx"], K=case["K"], w_max=case["w_max"], page_size=case["page"],
-                                 range_pages=case["range_pages"])
+                                 range_pages=case["range_pages"], rows=case.get("rows", 64))
         assert plan.dtype == np.int32
         head = case["plan_head"]
         assert plan[:len(head)].tolist() == head
@@ -58,11 +58,21 @@ def test_plan_hand(golden_dir):
             assert [list(p) for p in oracle.request_pieces(plan, C, b, L)] == want
 
 
-CASES = [(16, 64, 0), (16, 7, 0), (16, 64, 3), (32, 64, 0), (64, 16, 5), (256, 64, 0), (16, 3, 0)]
+CASES = [(16, 64, 0, 64), (16, 7, 0, 64), (16, 64, 3, 64), (32, 64, 0, 64), (64, 16, 5, 64), (256, 64, 0, 64),
+         (16, 3, 0, 64), (16, 64, 0, 128), (64, 16, 0, 256), (16, 64, 3, 128)]
 
 
-@pytest.mark.parametrize("page,w_max,range_pages", CASES)
-def test_plan_invariants(page, w_max, range_pages):
+def test_segment_charge():
+    """The fixed cost of automatic ranges: ceil(12 / g) units, ceil(24 / g)
+    above 64 query rows per kv head, none for fixed ranges."""
+    assert [oracle.segment_granules(p, 0, 64) for p in (16, 32, 64, 128, 256)] == [6, 6, 3, 2, 1]
+    assert [oracle.segment_granules(p, 0, 128) for p in (16, 32, 64, 128, 256)] == [12, 12, 6, 3, 2]
+    assert oracle.segment_granules(16, 0, 65) == 12 and oracle.segment_granules(16, 0, 8) == 6
+    assert oracle.segment_granules(16, 4, 128) == 0
+
+
+@pytest.mark.parametrize("page,w_max,range_pages,rows", CASES)
+def test_plan_invariants(page, w_max, range_pages, rows):
     """Every slab of every request lies in exactly one of its pieces, in
     order; each range's segments tile it; slots of partial pieces are unique;
     automatic ranges differ in size by at most one granule."""
@@ -72,14 +82,14 @@ def test_plan_invariants(page, w_max, range_pages):
         K = int(rng.integers(1, 65))
         ctx = rng.integers(0, 3000, size=C) * (rng.random(C) < 0.9)
         try:
-            plan = oracle.range_plan(ctx, K=K, w_max=w_max, page_size=page, range_pages=range_pages)
+            plan = oracle.range_plan(ctx, K=K, w_max=w_max, page_size=page, range_pages=range_pages, rows=rows)
         except ValueError:
             assert range_pages > 0   # fixed ranges beyond the capacity are refused
             continue
         f = oracle.plan.unpack(plan, C)
         W, T, g, B = f["W"], f["T"], f["g"], f["B"]
         G = oracle.request_granules(ctx, K, page)
-        sigma = oracle.segment_granules(page, range_pages)
+        sigma = oracle.segment_granules(page, range_pages, rows)
         assert g == max(2, page // 16) and T == (G + sigma).sum() and 1 <= W <= min(w_max, T)
         assert B[0] == 0 and B[-1] == T and (np.diff(B) >= 1).all()
         if range_pages == 0:
