@@ -257,6 +257,30 @@ def test_contexts_across_page_table_windows(page, hq):
     assert_attn_close(to_host64(on), want, "bf16", f"windows page {page}")
 
 
+@pytest.mark.parametrize("causal", [False, True], ids=["mask-free", "block-causal"])
+def test_ranges_without_keys(causal):
+    """128 query rows per kv head charge each request 24 slabs (12 units of
+    2-slab granules), more than the 8-unit shortest range: with short
+    requests some ranges hold only charges and no keys (ranges 0, 2, 5 and
+    10 of this batch, by the oracle's plan).  Their workgroups do nothing;
+    the output matches the oracle, NHD and HND pools agree bit for bit, and
+    the device's plan equals the oracle's."""
+    ctx = [0, 1, 5, 16, 17, 0, 3, 40]
+    want_plan = oracle.range_plan(ctx, K=16, w_max=64, rows=128)
+    f = oracle.plan.unpack(want_plan, len(ctx))
+    G = oracle.request_granules(np.array(ctx), 16, PAGE)
+    keys = [(int(f["S"][b]), int(f["S"][b] + G[b])) for b in range(len(ctx))]
+    empty = [w for w in range(f["W"]) if not any(lo < f["B"][w + 1] and hi > f["B"][w] for lo, hi in keys)]
+    assert empty == [0, 2, 5, 10]
+    case = make_attn_case(980 + causal, ctx, 16, 64, 8, 128, "bf16")
+    on, ws, _ = run_attn(case, split=0, layout="NHD", causal=causal)
+    oh, _, _ = run_attn(case, split=0, layout="HND", causal=causal)
+    assert torch.equal(on.view(torch.int16), oh.view(torch.int16))
+    assert_attn_close(to_host64(on), oracle_attn(case, causal=causal), "bf16", f"empty ranges causal={causal}")
+    plan = ops.plan_of(ws, len(ctx)).cpu().numpy()
+    assert np.array_equal(plan, oracle.range_plan(ctx, K=16, w_max=int(plan[3]), rows=128))
+
+
 def test_kv_pool_untouched_and_output_bounded():
     case = make_attn_case(13, [400, 3], 16, 32, 8, 128, "bf16")
     dt = case["dtype"]
