@@ -156,7 +156,7 @@ AttnPlanShape plan_shape(int dtype, int C, int K, int Hq, int Hkv, int D, int64_
   p.part_o_off = p.plan_bytes;
   size_t po = 0, pml = 0;
   if (p.w_max > 1) {  // only then can a request span several ranges
-    po = align256(2 * size_t(p.w_max) * Hkv * rows * D * 4);
+    po = align256(2 * size_t(p.w_max) * Hkv * rows * D * (dtype == 1 ? 2 : 4));   // activation dtype
     pml = align256(2 * size_t(p.w_max) * Hkv * rows * 2 * 4);
   }
   p.part_ml_off = p.part_o_off + po;
@@ -222,7 +222,7 @@ int attn_args(AttnArgs& a, int dtype, int C, int K, int Hq, int Hkv, int D, cons
   a.out = out;
   unsigned char* base = static_cast<unsigned char*>(ws);
   a.plan = reinterpret_cast<int32_t*>(base);
-  a.part_o = reinterpret_cast<float*>(base + p.part_o_off);
+  a.part_o = base + p.part_o_off;
   a.part_ml = reinterpret_cast<float*>(base + p.part_ml_off);
   a.w_max = p.w_max;
   a.gran = p.gran;

@@ -897,53 +897,53 @@ __global__ __launch_bounds__(64 * NW, (RT == 2 && sizeof(T) == 2) ? 2 : 1) void 
       });
     }
 
-    // store: lane holds row li of each tile and d = dch(4*lg + r)*DPL + cc
+    // store: lane holds row li of each tile and d = dch(4*lg + r)*DPL + cc.
+    // A whole request writes its normalised output; a piece writes its own
+    // normalised partial O / l in the activation dtype (half the bytes of
+    // fp32 for the attention to write and the merge to read) and its fp32
+    // (m, l), which weight it in the merge.  A piece whose keys the block-causal
+    // mask hides from a row has l = 0 and stores zeros.
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
       const float lsum = group4_sum(acc.l[rt]);
       const int row = (wt + rt) * 16 + li;
       if (row >= rows || nstage == 0) continue;
+      T* o;
+      float inv;
       if (whole) {
         const int t = row / G, gg = row % G;
-        T* o = static_cast<T*>(a.out) + ((size_t(b) * K + t) * a.Hq + j * G + gg) * D;
-        const float inv = 1.f / lsum;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          T* dst = o + dch(4 * lg + r) * DPL;
-          if constexpr (sizeof(T) == 2) {
-            if constexpr (DPL == 8) {
-              uint4 pk;
-              pk.x = pack_bf16x2(acc.o[rt][0][r] * inv, acc.o[rt][1][r] * inv);
-              pk.y = pack_bf16x2(acc.o[rt][2][r] * inv, acc.o[rt][3][r] * inv);
-              pk.z = pack_bf16x2(acc.o[rt][4][r] * inv, acc.o[rt][5][r] * inv);
-              pk.w = pack_bf16x2(acc.o[rt][6][r] * inv, acc.o[rt][7][r] * inv);
-              *reinterpret_cast<uint4*>(dst) = pk;
-            } else {
-              uint2 pk;
-              pk.x = pack_bf16x2(acc.o[rt][0][r] * inv, acc.o[rt][1][r] * inv);
-              pk.y = pack_bf16x2(acc.o[rt][2][r] * inv, acc.o[rt][3][r] * inv);
-              *reinterpret_cast<uint2*>(dst) = pk;
-            }
-          } else {
-#pragma unroll
-            for (int cc = 0; cc < DPL; cc += 4)
-              *reinterpret_cast<float4*>(reinterpret_cast<float*>(dst) + cc) =
-                  make_float4(acc.o[rt][cc][r] * inv, acc.o[rt][cc + 1][r] * inv,
-                              acc.o[rt][cc + 2][r] * inv, acc.o[rt][cc + 3][r] * inv);
-          }
-        }
+        o = static_cast<T*>(a.out) + ((size_t(b) * K + t) * a.Hq + j * G + gg) * D;
+        inv = 1.f / lsum;
       } else {
         const size_t prow = (size_t(pslot) * Hkv + j) * rows + row;
-        float* po = a.part_o + prow * D;
+        o = static_cast<T*>(a.part_o) + prow * D;
+        inv = lsum > 0.f ? 1.f / lsum : 0.f;
+        if (lg == 0) *reinterpret_cast<float2*>(a.part_ml + prow * 2) = make_float2(acc.m2[rt], lsum);
+      }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float* dst = po + dch(4 * lg + r) * DPL;
+      for (int r = 0; r < 4; ++r) {
+        T* dst = o + dch(4 * lg + r) * DPL;
+        if constexpr (sizeof(T) == 2) {
+          if constexpr (DPL == 8) {
+            uint4 pk;
+            pk.x = pack_bf16x2(acc.o[rt][0][r] * inv, acc.o[rt][1][r] * inv);
+            pk.y = pack_bf16x2(acc.o[rt][2][r] * inv, acc.o[rt][3][r] * inv);
+            pk.z = pack_bf16x2(acc.o[rt][4][r] * inv, acc.o[rt][5][r] * inv);
+            pk.w = pack_bf16x2(acc.o[rt][6][r] * inv, acc.o[rt][7][r] * inv);
+            *reinterpret_cast<uint4*>(dst) = pk;
+          } else {
+            uint2 pk;
+            pk.x = pack_bf16x2(acc.o[rt][0][r] * inv, acc.o[rt][1][r] * inv);
+            pk.y = pack_bf16x2(acc.o[rt][2][r] * inv, acc.o[rt][3][r] * inv);
+            *reinterpret_cast<uint2*>(dst) = pk;
+          }
+        } else {
 #pragma unroll
           for (int cc = 0; cc < DPL; cc += 4)
-            *reinterpret_cast<float4*>(dst + cc) =
-                make_float4(acc.o[rt][cc][r], acc.o[rt][cc + 1][r], acc.o[rt][cc + 2][r], acc.o[rt][cc + 3][r]);
+            *reinterpret_cast<float4*>(reinterpret_cast<float*>(dst) + cc) =
+                make_float4(acc.o[rt][cc][r] * inv, acc.o[rt][cc + 1][r] * inv,
+                            acc.o[rt][cc + 2][r] * inv, acc.o[rt][cc + 3][r] * inv);
         }
-        if (lg == 0) *reinterpret_cast<float2*>(a.part_ml + prow * 2) = make_float2(acc.m2[rt], lsum);
       }
     }
 

@@ -23,7 +23,8 @@ struct AttnArgs {
   float scale_log2;               // softmax scale * log2(e)
   void* out;
   int32_t* plan;                  // workspace head: the work plan (written by the last block)
-  float* part_o;                  // [2 * w_max, Hkv, rows, D]: piece of range w's segment k at slot 2w + k
+  void* part_o;                   // [2 * w_max, Hkv, rows, D], activation dtype: piece of range
+                                  // w's segment k at slot 2w + k, normalised by its own l
   float* part_ml;                 // [2 * w_max, Hkv, rows, 2]
   // Work plan: each request's keys are its context slabs (16 tokens) then
   // nbk block slabs, counted in granules of `gran` slabs; the batch's

@@ -51,7 +51,13 @@ __device__ __forceinline__ void attn_merge_block(const AttnArgs& a, int bx, int 
       for (int u = 0; u < UU; ++u) {
         const size_t pr = prow(min(s0 + LPO * u, ns - 1));
         ml[u] = *reinterpret_cast<const float2*>(a.part_ml + pr * 2);
-        v[u] = reinterpret_cast<const float4*>(a.part_o + pr * D)[d4];
+        if constexpr (sizeof(T) == 2) {   // four bf16 of the piece's normalised output
+          const uint2 x = reinterpret_cast<const uint2*>(static_cast<const T*>(a.part_o) + pr * D)[d4];
+          v[u] = make_float4(__uint_as_float(x.x << 16), __uint_as_float(x.x & 0xffff0000u),
+                             __uint_as_float(x.y << 16), __uint_as_float(x.y & 0xffff0000u));
+        } else {
+          v[u] = reinterpret_cast<const float4*>(static_cast<const float*>(a.part_o) + pr * D)[d4];
+        }
       }
       // A piece's maximum is -inf when the block-causal mask hides all its
       // keys from this row (a piece of block keys only); such a piece weighs
@@ -66,9 +72,10 @@ __device__ __forceinline__ void attn_merge_block(const AttnArgs& a, int bx, int 
       Ls *= sc;
 #pragma unroll
       for (int u = 0; u < UU; ++u) {
-        const float f = (s0 + LPO * u < ns && ml[u].x != -INFINITY) ? fast_exp2(ml[u].x - mr) : 0.f;
+        // a piece weighs l e^(m - M): its output is stored divided by its l
+        const float f = (s0 + LPO * u < ns && ml[u].x != -INFINITY) ? fast_exp2(ml[u].x - mr) * ml[u].y : 0.f;
         acc.x += f * v[u].x; acc.y += f * v[u].y; acc.z += f * v[u].z; acc.w += f * v[u].w;
-        Ls += f * ml[u].y;
+        Ls += f;
       }
       M = mr;
     }

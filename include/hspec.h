@@ -144,8 +144,10 @@ int hspec_ssd_scan(void* stream, int dtype, int C, int K, int H, int P, int ng, 
  *                max_pages >= ceil(max_ctx/P)
  *   kv_split_pages  0 = automatic work ranges (below); otherwise ranges of
  *                this many pages of P tokens each (the last one shorter).
- *                Results do not depend on it beyond fp32 rounding, and are
- *                bitwise repeatable for a fixed value
+ *                Results do not depend on it beyond rounding (fp32
+ *                accumulation, and each piece's output rounded to the
+ *                activation dtype before the merge), and are bitwise
+ *                repeatable for a fixed value
  *   scale        softmax scale; 0.f means 1/sqrt(D)
  *   out          act [C, K, Hq, D]
  *   workspace / workspace_bytes:
@@ -176,7 +178,9 @@ int hspec_ssd_scan(void* stream, int dtype, int C, int K, int H, int P, int ng, 
  *         [4, 4+C) S_b    [4+C, 4+2C) range of request b's first key granule
  *         [4+2C, 4+3C) ranges request b spans (its pieces)
  *         [4+3C, 4+3C+w_max+1) B_0 .. B_W (B_W = T), then -1
- *       followed, when w_max > 1, by fp32 partials of two slots per range.
+ *       followed, when w_max > 1, by the partials of two slots per range:
+ *       each piece's output divided by its own softmax sum, in the activation
+ *       dtype, and its fp32 (max, sum).
  * Limits: D in {64, 128}; 1 <= K <= 64; Hq % Hkv == 0; (Hq/Hkv)*K <= 256;
  * token_stride times the element size <= 2^27 bytes; the batch's keys at
  * their bound, C * g * ceil((ceil(max_ctx/16) + ceil(K/16)) / g) slabs,

@@ -101,17 +101,20 @@ def test_attention_validation(kw, code):
     assert _attn(**kw)[0] == code
 
 
-def _ws_expect(C, w_max, rows, Hkv=8, D=128):
+def _ws_expect(C, w_max, rows, Hkv=8, D=128, esize=2):
+    """Plan, then the pieces' outputs in the activation dtype (esize bytes) and
+    their fp32 (m, l)."""
     up = lambda x: -(-x // 256) * 256
     plan = up((4 + 3 * C + w_max + 1) * 4)
     if w_max == 1:
         return plan
-    return plan + up(2 * w_max * Hkv * rows * D * 4) + up(2 * w_max * Hkv * rows * 2 * 4)
+    return plan + up(2 * w_max * Hkv * rows * D * esize) + up(2 * w_max * Hkv * rows * 2 * 4)
 
 
 def test_attention_workspace_query():
     """The workspace holds the int32 plan (4 + 3C + w_max + 1 entries) and,
-    when a request can span ranges, fp32 partials for two slots per range.
+    when a request can span ranges, partials for two slots per range (bf16
+    outputs, fp32 (m, l)).
     C = 4, K = 16, max_ctx = 1000: a request's keys are 63 + 1 slabs, 32
     granules of 2 slabs; the batch at most 128 granules."""
     code, n = _attn(split=32)                           # 32 pages = 16 granules per range: 8 ranges

@@ -51,7 +51,7 @@ def test_noalloc_matches_the_workspace_entry_point_twice():
 
 
 def test_noalloc_refuses_more_than_the_scratch():
-    """One-page ranges of 8192-token contexts need ~0.5 GB of partial slots."""
+    """One-page ranges of 8192-token contexts need ~0.28 GB of partial slots."""
     w = replace(wl.sweep_workload(4), name="noalloc-too-big", seed=9003)
     inp = wl.make_inputs(w, parts=("attn", "mamba"))
     layer = layer_from_inputs(inp, kv_split_pages=1)
