@@ -42,7 +42,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", type=int, default=3)
+    p.add_argument("--workload", type=int, default=DEFAULT_WORKLOAD)
     p.add_argument("--kv-split-pages", type=int, default=0)
     p.add_argument("--no-sweep", action="store_true")
     p.add_argument("--no-cpu", action="store_true")
@@ -491,6 +491,7 @@ SIMDS = 256 * 4          # MI355X: 256 CUs x 4 SIMDs
 XCDS = 8                 # GRBM_GUI_ACTIVE is reported summed over the 8 XCDs' instances
 KERNEL_KEYS = ("k_block_attn", "k_attn_merge", "k_init_wide", "k_init_state", "k_ssd_scan", "k_scan_merge",
                "k_gemm_tn", "k_splitk_sum", "k_gate_norm", "__amd_rocclr_copyBuffer")
+DEFAULT_WORKLOAD = 3   # the C = 128, 8192-token batch the headline line measures
 _BENCH = "python3 bench.py --steps {steps} --warmup {warmup} --no-sweep --no-cpu --no-variants --no-stack --no-configs"
 # The passes the profiles/ summaries come from, each a run of its own, from the
 # repository root on one MI355X with TMPDIR=/tmp (counters are never combined
@@ -510,6 +511,13 @@ PROFILE_PASSES = {
           "--output-format csv -d gpurun_out/prof_sq -o run -- "
           + _BENCH.format(steps=3, warmup=1) + " --no-block --no-inject --no-probe",
 }
+
+
+def profile_passes(workload_idx):
+    """The passes of PROFILE_PASSES for a workload (the default one needs no flag)."""
+    if workload_idx == DEFAULT_WORKLOAD:
+        return dict(PROFILE_PASSES)
+    return {k: v + f" --workload {workload_idx}" for k, v in PROFILE_PASSES.items()}
 
 
 def _rocprof_csv(d, what):
@@ -560,13 +568,13 @@ def _write(path, text, written):
     written.append(path)
 
 
-def _stats_md(d, w, written):
+def _stats_md(d, w, written, passes):
     """Kernel-time table of a --kernel-trace --stats run."""
     rows = _rocprof_csv(d, "kernel_stats")
     if not rows:
         return
     lines = [f"# Kernel time summary: drafter layer and Mamba-2 block, workload {w.name}", "",
-             "Command (from the repository root, on one MI355X; TMPDIR=/tmp):", "", "    " + PROFILE_PASSES["trace"], "",
+             "Command (from the repository root, on one MI355X; TMPDIR=/tmp):", "", "    " + passes["trace"], "",
              "The run times 10 drafter-layer calls and 10 calls of each of its entry points alone, then the "
              "Mamba-2 block (hspec_mamba_block) and the drafter-side KV-injection contrast at C = 4 ... 128, each "
              "call after a 2 GiB read that evicts L2 and the Infinity Cache (the at::native reduce_kernel rows); "
@@ -590,6 +598,7 @@ def summarize_profiles(dirs, workload_idx):
     import numpy as np
     from hybrid_mamba_attention_amd import workloads as wl
     w = wl.WORKLOADS[workload_idx]
+    passes = profile_passes(workload_idx)
     inp = wl.make_inputs(w, parts=())
     alg = {"k_block_attn": attention_bytes(w, inp.ctx_lens), "k_init_wide": init_bytes(w),
            "k_ssd_scan": ssd_bytes(w)}
@@ -601,7 +610,7 @@ def summarize_profiles(dirs, workload_idx):
             k = _short(r["Kernel_Name"])
             if k:
                 trace.setdefault(k, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
-        _stats_md(d, w, written)
+        _stats_md(d, w, written, passes)
 
     def find(counter):
         for d, t in tables.items():
@@ -625,7 +634,7 @@ def summarize_profiles(dirs, workload_idx):
         write_factor = copy_bytes / (calib(wt, "WRITE_SIZE") * 1024)
         rec = dict(workload=w.name, source_hash=kernel_source_hash(), fetch_factor=fetch_factor,
                    write_factor=write_factor, kernels={},
-                   fetch_command=PROFILE_PASSES["fetch"], write_command=PROFILE_PASSES["write"])
+                   fetch_command=passes["fetch"], write_command=passes["write"])
         for k in ("k_block_attn", "k_init_wide", "k_ssd_scan"):
             g = main_grid(ft, k)
             if g is None:
@@ -643,7 +652,7 @@ def summarize_profiles(dirs, workload_idx):
         written.append(path)
         lines = [f"# HBM traffic per launch: workload {w.name}", "",
                  "Two counter passes, each in a run of its own (from the repository root, on one MI355X; TMPDIR=/tmp):",
-                 "", "    " + PROFILE_PASSES["fetch"], "    " + PROFILE_PASSES["write"], "",
+                 "", "    " + passes["fetch"], "    " + passes["write"], "",
                  "Calibration: the same runs launch a plain 1 GiB device copy (__amd_rocclr_copyBuffer). "
                  f"It reads {calib(ft, 'FETCH_SIZE'):.1f} KiB by FETCH_SIZE and writes {calib(wt, 'WRITE_SIZE'):.1f} KiB "
                  f"by WRITE_SIZE per dispatch, so bytes = FETCH_SIZE x 1024 x {fetch_factor:.4f} and "
@@ -654,14 +663,14 @@ def summarize_profiles(dirs, workload_idx):
             lines.append(f"| `{k}` | {v['fetch_kib']:.1f} | {v['write_kib']:.1f} | {v['hbm_bytes']:.4e} | "
                          f"{v['algorithmic_bytes']:.4e} | {v['ratio']:.3f} |")
         if "k_block_attn_avg_us_kernel_trace" in rec:
-            lines += ["", f"Average k_block_attn duration in the kernel-trace run ({PROFILE_PASSES['trace'].split(' -d ')[0]} ...): "
+            lines += ["", f"Average k_block_attn duration in the kernel-trace run ({passes['trace'].split(' -d ')[0]} ...): "
                       f"{rec['k_block_attn_avg_us_kernel_trace']:.1f} us."]
         lines += ["", f"Attention sources hash (bench.py kernel_source_hash): {rec['source_hash']}."]
         _write(os.path.join(PROFILE_DIR, f"k_block_attn_{w.name}_traffic.md"), "\n".join(lines) + "\n", written)
     md_, mt = find("SQ_INSTS_VALU_MFMA_MOPS_BF16")
     if mt:
         rec = dict(workload=w.name, source_hash=mfma_source_hash(), simds=SIMDS, xcds=XCDS,
-                   command=PROFILE_PASSES["mfma"], kernels={})
+                   command=passes["mfma"], kernels={})
         for (k, g), cs in sorted(mt.items()):
             if k == "__amd_rocclr_copyBuffer" or "SQ_VALU_MFMA_BUSY_CYCLES" not in cs:
                 continue
@@ -678,7 +687,7 @@ def summarize_profiles(dirs, workload_idx):
         json.dump(rec, open(path, "w"), indent=1)
         written.append(path)
         lines = [f"# Matrix-core utilisation per kernel: workload {w.name}", "",
-                 "Command (from the repository root, on one MI355X; TMPDIR=/tmp):", "", "    " + PROFILE_PASSES["mfma"], "",
+                 "Command (from the repository root, on one MI355X; TMPDIR=/tmp):", "", "    " + passes["mfma"], "",
                  "Per dispatch, averaged per kernel and grid (threads). `MFMA busy` = SQ_VALU_MFMA_BUSY_CYCLES "
                  f"/ (GRBM_GUI_ACTIVE of one XCD x {SIMDS} SIMDs): the csv gives GRBM_GUI_ACTIVE summed over the "
                  f"{XCDS} XCDs, 8 x 2.4 GHz x the kernel's time.  `counted TFLOP/s` = SQ_INSTS_VALU_MFMA_MOPS_BF16 "
@@ -693,7 +702,7 @@ def summarize_profiles(dirs, workload_idx):
     sd, st = find("SQ_WAIT_INST_ANY")
     if st:
         lines = [f"# Where the waves spend their cycles: workload {w.name}", "",
-                 "Command (from the repository root, on one MI355X; TMPDIR=/tmp):", "", "    " + PROFILE_PASSES["sq"], "",
+                 "Command (from the repository root, on one MI355X; TMPDIR=/tmp):", "", "    " + passes["sq"], "",
                  "Per dispatch of each kernel's benchmarked launch, chip sums averaged over the dispatches, as "
                  "shares of SQ_WAVE_CYCLES (the cycles its waves were resident).  `MFMA busy` as in the "
                  "matrix-core table; `VALU / SIMD-cycle` = SQ_INSTS_VALU / (GRBM_GUI_ACTIVE of one XCD x SIMDs).", "",
