@@ -214,21 +214,30 @@ struct WideCfg {
 // step j are built, before its MFMAs.  At 128 rows a wave's 16 MFMAs would
 // otherwise hold the next loads back by ~500 cycles every step (C = 128:
 // 60-63 -> 57.5 us); at 32 and 64 rows issuing after the MFMAs is faster.
-template <int MT, int PF, bool EARLY>
+//
+// KS = false (wide states, enough column blocks to fill the chip twice): a
+// workgroup covers 256 columns, one 64-column quarter per wave, and every
+// wave takes both 32-row k-steps of each 64-row step (NKK = 2).  The u slice
+// a workgroup stages then serves twice the W columns, halving the u bytes
+// read per W byte, and the k-halves' sum through LDS goes away.
+template <int MT, int PF, bool EARLY, bool KS = true>
 __global__ __launch_bounds__(256) void k_init_wide(InitArgs a) {
   using Cfg = WideCfg<MT>;
   static_assert(PF >= 2, "the u slice of step j+1 must already be in flight");
-  __shared__ __align__(16) char lds[Cfg::LDS];
+  constexpr int NKK = KS ? 1 : 2;        // 32-row k-steps of a 64-row step per wave
+  constexpr int BW = KS ? 128 : 256;     // columns per workgroup
+  constexpr int LDSB = KS ? Cfg::LDS : 2 * Cfg::TILE;
+  __shared__ __align__(16) char lds[LDSB];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int c = lane & 31, g = lane >> 5;
-  const int cg = wave & 1, kh = wave >> 1;
+  const int cg = KS ? (wave & 1) : wave, kh = KS ? (wave >> 1) : 0;
   const int C = a.C, d = a.d, S = a.S;
-  // 1-D grid of (S/128) column blocks x MB row blocks.  When the column
+  // 1-D grid of (S/BW) column blocks x MB row blocks.  When the column
   // blocks split evenly over the 8 XCDs, the row blocks of one column block
   // are dispatched back to back on one XCD (blocks L and L+8 share an XCD),
   // so they run together and all but the first read their W from that L2.
   const int MB = (C + Cfg::ROWS - 1) / Cfg::ROWS;
-  const int nb = S >> 7, L = blockIdx.x;
+  const int nb = S / BW, L = blockIdx.x;
   int cb, mb;
   if ((nb & 7) == 0) {
     cb = (L / (8 * MB)) * 8 + (L & 7);
@@ -238,7 +247,7 @@ __global__ __launch_bounds__(256) void k_init_wide(InitArgs a) {
     mb = L % MB;
   }
   const int m0 = mb * Cfg::ROWS;
-  const int n0 = cb * 128 + cg * 64;
+  const int n0 = cb * BW + cg * 64;
   const int ns = d >> 6;
   const bf16_t* __restrict__ u = static_cast<const bf16_t*>(a.u);
   const char* __restrict__ wk = static_cast<const char*>(a.w) + (size_t(kh) * 32 * S + n0) * 2;
@@ -270,56 +279,70 @@ __global__ __launch_bounds__(256) void k_init_wide(InitArgs a) {
     usrc[t] = u + size_t(min(m0 + row, C - 1)) * d + 8 * (slot ^ ((row >> 1) & 7));
     udst[t] = uint32_t(q) * 16;
   }
-  // A operand of m-tile m, k-half h: row 32m + c, logical segment kh*4 + 2h + g
-  uint32_t aoff[MT][2];
+  // A operand of m-tile m, 32-row k-step kk, k-half h: row 32m + c, logical
+  // segment k*4 + 2h + g of the slice, k = kh with the k split, kk without
+  uint32_t aoff[MT][NKK][2];
 #pragma unroll
   for (int m = 0; m < MT; ++m)
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
-      aoff[m][h] = uint32_t(m * 32 + c) * 128 + uint32_t(((kh * 4 + 2 * h + g) ^ ((c >> 1) & 7)) << 4);
+    for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        aoff[m][kk][h] = uint32_t(m * 32 + c) * 128 +
+                         uint32_t((((KS ? kh : kk) * 4 + 2 * h + g) ^ ((c >> 1) & 7)) << 4);
 
-  uint32_t ring[PF][16];  // k-step rows 8g+e (e < 8) and 16+8g+e (e >= 8), columns 2c, 2c+1
+  // per 32-row k-step kk: rows 8g+e (e < 8) and 16+8g+e (e >= 8) at 16kk + e, columns 2c, 2c+1
+  uint32_t ring[PF][16 * NKK];
   u32x4 uring[PF][Cfg::NU];
-  auto issue = [&](int j, uint32_t (&w)[16], u32x4 (&ud)[Cfg::NU]) __attribute__((always_inline)) {
+  auto issue = [&](int j, uint32_t (&w)[16 * NKK], u32x4 (&ud)[Cfg::NU]) __attribute__((always_inline)) {
     const int jj = min(j, ns - 1);  // past the end: re-read the last step, never used
     const char* base = wk + size_t(jj) * step_b;
 #pragma unroll
     for (int t = 0; t < Cfg::NU; ++t) ud[t] = *reinterpret_cast<const u32x4*>(usrc[t] + 64 * jj);
     // W is read exactly once per call: nontemporal loads
 #pragma unroll
-    for (int e = 0; e < 8; ++e) w[e] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(base + roff[e]));
+    for (int kk = 0; kk < NKK; ++kk) {
+      const char* kb = base + size_t(kk) * 2 * half_b;  // rows 32kk.. of the step
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-      w[8 + e] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(base + half_b + roff[e]));
+      for (int e = 0; e < 8; ++e)
+        w[16 * kk + e] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(kb + roff[e]));
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        w[16 * kk + 8 + e] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(kb + half_b + roff[e]));
+    }
   };
   auto put_u = [&](int buf, const u32x4 (&ud)[Cfg::NU]) __attribute__((always_inline)) {
 #pragma unroll
     for (int t = 0; t < Cfg::NU; ++t) *reinterpret_cast<u32x4*>(lds + buf * Cfg::TILE + udst[t]) = ud[t];
   };
-  auto bops = [&](const uint32_t (&w)[16], Vec8<bf16_t> (&bop)[2][2]) __attribute__((always_inline)) {
-    // B operand (k-half h, n-tile t): element e = W[16h + 8g + e][n0 + 2c + t]
+  auto bops = [&](const uint32_t (&w)[16 * NKK], Vec8<bf16_t> (&bop)[NKK][2][2]) __attribute__((always_inline)) {
+    // B operand (k-step kk, k-half h, n-tile t): element e = W[32kk + 16h + 8g + e][n0 + 2c + t]
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+    for (int kk = 0; kk < NKK; ++kk)
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const uint32_t sel = t ? 0x07060302u : 0x05040100u;
-        const uint32_t* r = w + 8 * h;
-        bop[h][t].v.x = __builtin_amdgcn_perm(r[1], r[0], sel);
-        bop[h][t].v.y = __builtin_amdgcn_perm(r[3], r[2], sel);
-        bop[h][t].v.z = __builtin_amdgcn_perm(r[5], r[4], sel);
-        bop[h][t].v.w = __builtin_amdgcn_perm(r[7], r[6], sel);
-      }
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const uint32_t sel = t ? 0x07060302u : 0x05040100u;
+          const uint32_t* r = w + 16 * kk + 8 * h;
+          bop[kk][h][t].v.x = __builtin_amdgcn_perm(r[1], r[0], sel);
+          bop[kk][h][t].v.y = __builtin_amdgcn_perm(r[3], r[2], sel);
+          bop[kk][h][t].v.z = __builtin_amdgcn_perm(r[5], r[4], sel);
+          bop[kk][h][t].v.w = __builtin_amdgcn_perm(r[7], r[6], sel);
+        }
   };
-  auto mmas = [&](int buf, const Vec8<bf16_t> (&bop)[2][2]) __attribute__((always_inline)) {
+  auto mmas = [&](int buf, const Vec8<bf16_t> (&bop)[NKK][2][2]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int m = 0; m < MT; ++m)
+    for (int kk = 0; kk < NKK; ++kk)
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        Vec8<bf16_t> ap;
-        ap.v = *reinterpret_cast<const uint4*>(lds + buf * Cfg::TILE + aoff[m][h]);
+      for (int m = 0; m < MT; ++m)
 #pragma unroll
-        for (int t = 0; t < 2; ++t) acc[m][t] = mma32(ap, bop[h][t], acc[m][t]);
-      }
+        for (int h = 0; h < 2; ++h) {
+          Vec8<bf16_t> ap;
+          ap.v = *reinterpret_cast<const uint4*>(lds + buf * Cfg::TILE + aoff[m][kk][h]);
+#pragma unroll
+          for (int t = 0; t < 2; ++t) acc[m][t] = mma32(ap, bop[kk][h][t], acc[m][t]);
+        }
   };
   static_for<0, PF>([&](auto P) __attribute__((always_inline)) {
     issue(decltype(P)::value, ring[decltype(P)::value], uring[decltype(P)::value]);
@@ -330,7 +353,7 @@ __global__ __launch_bounds__(256) void k_init_wide(InitArgs a) {
   auto step = [&](int j, auto P) __attribute__((always_inline)) {
     constexpr int p = decltype(P)::value;
     __syncthreads();
-    Vec8<bf16_t> bop[2][2];
+    Vec8<bf16_t> bop[NKK][2][2];
     bops(ring[p], bop);
     if constexpr (EARLY) {
       issue(j + PF, ring[p], uring[p]);
@@ -350,6 +373,18 @@ __global__ __launch_bounds__(256) void k_init_wide(InitArgs a) {
     if (j < ns) step(j, P);  // block-uniform; only the last few steps
   });
 
+  if constexpr (!KS) {
+    // no k split: every wave holds final values
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int row = m0 + m * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
+        if (row < C)
+          *reinterpret_cast<float2*>(a.h0 + size_t(row) * S + n0 + 2 * c) = make_float2(acc[m][0][i], acc[m][1][i]);
+      }
+    return;
+  }
   // k-half 1 hands its partial tile to k-half 0 through LDS
   __syncthreads();
   float* red = reinterpret_cast<float*>(lds) + cg * (MT * 2 * 16 * 64);
@@ -384,6 +419,14 @@ static hipError_t launch_cfg(hipStream_t st, const InitArgs& a) {
 template <int MT, int PF>
 static hipError_t launch_wide(hipStream_t st, const InitArgs& a) {
   const int mb = (a.C + 32 * MT - 1) / (32 * MT);
+  // 256-column blocks without the k split when they still give every CU two
+  // workgroups (up to 64 rows, where two of them fit a CU at once)
+  if constexpr (MT <= 2) {
+    if (a.S % 256 == 0 && int64_t(a.S / 256) * mb >= 512) {
+      hipLaunchKernelGGL((k_init_wide<MT, PF, (MT >= 4), false>), dim3((a.S / 256) * mb), dim3(256), 0, st, a);
+      return hipGetLastError();
+    }
+  }
   hipLaunchKernelGGL((k_init_wide<MT, PF, (MT >= 4)>), dim3((a.S / 128) * mb), dim3(256), 0, st, a);
   return hipGetLastError();
 }

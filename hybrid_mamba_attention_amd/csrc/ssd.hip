@@ -39,6 +39,16 @@ template <int NMAX, int QM> struct SsdLds {
   static constexpr int oWave = oCB + QM * QM;         // per wave: lam, w, dt, pad [QM]; M[QM][QM]
   static constexpr int WAVE = 4 * QM + QM * QM;
   static constexpr int floats = oWave + 4 * WAVE;
+  // Before the first chunk each row block of 64 state rows (one per wave, or
+  // one shared by the four waves of a head) is staged here, rows padded to
+  // LDH floats: a lane reading its own row, 16 lanes per pass, then hits 16
+  // distinct bank quads.  It aliases the arrays above and is only used with
+  // 16-byte state rows and states of up to 64.  `total` is the most any
+  // layout needs (four blocks).
+  static constexpr int LDH = NMAX + 4;
+  static constexpr int stage(int blocks) { return NMAX <= 64 ? blocks * 64 * LDH : 0; }
+  static constexpr int with_stage(int blocks) { return floats > stage(blocks) ? floats : stage(blocks); }
+  static constexpr int total = with_stage(4);
 };
 
 // the smallest chunk capacity that holds a chunk
@@ -74,13 +84,15 @@ __host__ __device__ inline int ssd_heads_per_block(int H, int ng, int P) {
 // with one wave per head.
 // The scan of workgroup `bid` (a device function so that the drafter layer's
 // combined scan + merge launch runs the same code).
-template <typename T, int NMAX, int QM, bool V4, bool CONV, int TS = 1>
+// STG: stage the initial state through LDS where it can (see STAGE_H0).
+template <typename T, int NMAX, int QM, bool V4, bool CONV, int TS = 1, bool STG = true>
 __device__ __forceinline__ void ssd_scan_block(const SsdArgs& a, int bid) {
   using L = SsdLds<NMAX, QM>;
   constexpr int Q = QM, LDB = L::LDB;
   constexpr int E = Q * NMAX / 256;  // B and Cm entries staged per thread
   static_assert(Q * NMAX % 256 == 0 && Q <= 64, "whole staging rounds; one lane per chunk position");
-  __shared__ __align__(16) float lds[L::floats];
+  constexpr bool STAGE_H0 = STG && V4 && NMAX <= 64;
+  __shared__ __align__(16) float lds[STAGE_H0 ? L::with_stage(4 / TS) : L::floats];
   const int H = a.H, P = a.P, N = a.N, K = a.K, QC = a.chunk;
   static_assert(TS == 1 || TS == 4, "one wave per head row block, or four per head");
   static_assert(TS == 1 || V4, "the column-split h_final store is the 16-byte one");
@@ -118,7 +130,26 @@ __device__ __forceinline__ void ssd_scan_block(const SsdArgs& a, int bid) {
   float Hs[NMAX];
 #pragma unroll
   for (int k = 0; k < NMAX; ++k) Hs[k] = 0.f;
-  if (a.h0) {
+  // STAGE_H0: the wave's rows [r0, r0 + nr) of the head's state are one
+  // contiguous block of nr * N floats, read as 1 KB-contiguous wave loads
+  // (each lane's own 128-byte row as 16-byte pieces would make every load
+  // touch 64 cache lines) and moved into the lanes' rows through LDS once the
+  // first chunk's loads are in flight.  The block is loaded by the GT
+  // threads that share it (the wave, or with TS = 4 the head's four waves),
+  // piece j of group thread gi being floats 4 * (gi + GT * j) .. + 3; until
+  // the staging Hs[4j .. 4j + 3] holds it.
+  constexpr int GT = 64 * TS, PPT = NMAX / 4 / TS;  // PPT: pieces per thread
+  const int gi = TS == 1 ? lane : tid;
+  const int r0 = (hw % RB) * 64, nr = min(64, P - r0);
+  if (STAGE_H0 && a.h0) {
+    const float* blk = a.h0 + ((size_t(b) * H + h) * P + r0) * N;
+    const int lastf = nr * N - 4;  // N % 4 == 0: every piece lies in one row
+#pragma unroll
+    for (int j = 0; j < PPT; ++j) {
+      const float4 v = *reinterpret_cast<const float4*>(blk + min(4 * (gi + GT * j), lastf));
+      Hs[4 * j] = v.x; Hs[4 * j + 1] = v.y; Hs[4 * j + 2] = v.z; Hs[4 * j + 3] = v.w;
+    }
+  } else if (a.h0) {
     const float* hrow = a.h0 + ((size_t(b) * H + h) * P + pc) * N;
     if constexpr (V4) {  // N % 4 == 0: 16-byte loads
 #pragma unroll
@@ -192,6 +223,27 @@ __device__ __forceinline__ void ssd_scan_block(const SsdArgs& a, int bid) {
       dv = a.delta[(size_t(b) * K + min(c0 + lane, K - 1)) * H + h];
     }
     if (!hmasked) {
+      if (STAGE_H0 && a.h0) {
+        // piece j starts at float f of the block: row f / N, columns f % N
+        // .. + 3 (pieces past the block repeat its last one)
+        float* st = lds + (TS == 1 ? wave : 0) * 64 * L::LDH;
+        const int lastf = nr * N - 4;
+#pragma unroll
+        for (int j = 0; j < PPT; ++j) {
+          const int f = min(4 * (gi + GT * j), lastf);
+          const int r = N == NMAX ? f / NMAX : f / N, cc = f - r * N;
+          *reinterpret_cast<float4*>(st + r * L::LDH + cc) =
+              make_float4(Hs[4 * j], Hs[4 * j + 1], Hs[4 * j + 2], Hs[4 * j + 3]);
+        }
+        __syncthreads();
+        // rows past nr and columns past N hold stale values: the selects below drop them
+#pragma unroll
+        for (int k = 0; k < NMAX; k += 4) {
+          const float4 v = *reinterpret_cast<const float4*>(st + lane * L::LDH + k);
+          Hs[k] = v.x; Hs[k + 1] = v.y; Hs[k + 2] = v.z; Hs[k + 3] = v.w;
+        }
+        __syncthreads();  // the chunk arrays below alias the staging
+      }
 #pragma unroll
       for (int k = 0; k < NMAX; ++k) Hs[k] = (own && k < N) ? Hs[k] : 0.f;
       hmasked = true;
@@ -381,11 +433,15 @@ __global__ __launch_bounds__(256) void k_ssd_scan(SsdArgs a) {
 // partials (grid (C * Hkv) x slabs, flattened request-major).  The two
 // are independent: the scan needs the projected state, the merge the
 // attention's partials, both written by earlier launches on the stream.
+// The merge's many short workgroups take the scan's LDS too, so the state is
+// staged through LDS only where that does not enlarge it (TS = 4: one block
+// per workgroup): with four blocks (36 KB) the uncut batch of 128 requests
+// gained 1.3 us of scan and lost as much to the merge's occupancy.
 template <int NMAX, int LPO, int U, int TS>
 __global__ __launch_bounds__(256) void k_scan_merge(SsdArgs s, AttnArgs m, int n_scan) {
   const int bid = blockIdx.x;
   if (bid < n_scan) {
-    ssd_scan_block<bf16_t, NMAX, 16, true, false, TS>(s, bid);
+    ssd_scan_block<bf16_t, NMAX, 16, true, false, TS, (TS > 1)>(s, bid);
   } else {
     const int r = bid - n_scan, ch = m.C * m.Hkv;
     attn_merge_block<bf16_t, 128, LPO, U>(m, r % ch, r / ch);
@@ -397,15 +453,15 @@ size_t ssd_lds_bytes(int P, int N, int Q) {
   const int qm = ssd_chunk_cap(Q);
   auto by_n = [&](auto QC) -> size_t {
     constexpr int QM = decltype(QC)::value;
-    if (N <= 16) return SsdLds<16, QM>::floats * sizeof(float);
-    if (N <= 32) return SsdLds<32, QM>::floats * sizeof(float);
-    if (N <= 64) return SsdLds<64, QM>::floats * sizeof(float);
-    return SsdLds<128, QM>::floats * sizeof(float);
+    if (N <= 16) return SsdLds<16, QM>::total * sizeof(float);
+    if (N <= 32) return SsdLds<32, QM>::total * sizeof(float);
+    if (N <= 64) return SsdLds<64, QM>::total * sizeof(float);
+    return SsdLds<128, QM>::total * sizeof(float);
   };
   if (qm == 16) return by_n(std::integral_constant<int, 16>{});
   // chunks of 32 and 64 run with a state capacity of 64
-  if (qm == 32) return SsdLds<64, 32>::floats * sizeof(float);
-  return SsdLds<64, 64>::floats * sizeof(float);
+  if (qm == 32) return SsdLds<64, 32>::total * sizeof(float);
+  return SsdLds<64, 64>::total * sizeof(float);
 }
 
 // Four waves per head (TS = 4) when the batch has too few heads for the

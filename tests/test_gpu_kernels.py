@@ -409,6 +409,11 @@ def test_scan_position_split_is_bit_identical(K, chunk, N):
     (1, 256, 4096, "bf16"), (5, 512, 8192, "bf16"), (17, 256, 4096, "bf16"), (33, 4096, 2048, "bf16"),
     (64, 1024, 4096, "bf16"), (65, 256, 4096, "bf16"), (130, 256, 8192, "bf16"), (256, 128, 1024, "bf16"),
     (3, 256, 640, "bf16"), (200, 192, 1152, "bf16"), (97, 320, 1024, "bf16"),
+    # its 256-column form without the k split (>= 512 column blocks of up to 64
+    # rows): 32- and 64-row blocks, block counts with and without a multiple
+    # of 8, one step (below the prefetch depth) and several
+    (1, 128, 131072, "bf16"), (40, 64, 131072, "bf16"), (64, 192, 131072, "bf16"),
+    (17, 64, 131328, "bf16"), (64, 128, 131328, "bf16"),
     # general kernel: fp32, or d % 64 == 32, or S % 128 == 64
     (1, 256, 4096, "f32"), (100, 512, 4096, "f32"), (7, 96, 4096, "bf16"), (40, 256, 4160, "bf16"),
     (129, 160, 1088, "bf16"),
