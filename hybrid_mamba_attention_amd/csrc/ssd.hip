@@ -465,12 +465,14 @@ size_t ssd_lds_bytes(int P, int N, int Q) {
 }
 
 // Four waves per head (TS = 4) when the batch has too few heads for the
-// four-heads form to give every CU a workgroup: at C = 1 (16 heads) that form
+// four-heads form to give every SIMD two waves: at C = 1 (16 heads) that form
 // runs 16 waves on the whole chip, each a serial chain over its chunk's
 // positions.  States of 17..64 (the model shapes), plain inputs, N % 4 == 0.
+// Up to 1024 heads (one wave per SIMD in the four-heads form) it is faster
+// (1024 heads: 10.0 against 10.9 us), at 2048 slower (17.2 against 15.7).
 static bool ssd_split_positions(const SsdArgs& a) {
   return !a.zx && a.P <= 64 && a.N > 16 && a.N <= 64 && a.N % 4 == 0 && a.chunk <= 16 &&
-         int64_t(a.C) * a.H < 1024;
+         int64_t(a.C) * a.H <= 1024;
 }
 
 template <typename T, int NMAX>
