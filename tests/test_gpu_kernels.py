@@ -328,6 +328,9 @@ SSD_CASES = [
     # two row blocks per head with the largest state; partial row block
     (2, 16, 2, 128, 1, 128, 16, "bf16", True, False),
     (2, 16, 4, 100, 1, 24, 16, "bf16", False, False),
+    # four waves per head sharing one staged state block of fewer than 64
+    # rows, with a state narrower than its capacity
+    (2, 16, 4, 48, 1, 24, 16, "bf16", True, False),
     # N not a multiple of 4 (scalar state-row loads); heads per group not a
     # multiple of 4 (2- and 1-head workgroups)
     (2, 11, 6, 64, 1, 7, 4, "f32", True, False),
@@ -371,9 +374,9 @@ def test_ssd_scan(C, K, H, P, ng, N, chunk, dtype, dskip, zero_state):
 @pytest.mark.parametrize("K,chunk,N", [(16, 16, 32), (40, 16, 64), (13, 4, 32)])
 def test_scan_position_split_is_bit_identical(K, chunk, N):
     """A batch with few heads runs four waves per head, each taking every
-    fourth position; 64 requests of 16 heads run one wave per head.  The same
+    fourth position; 65 requests of 16 heads run one wave per head.  The same
     requests must get the same bits either way (y and h_final)."""
-    C, H, P, ng = 64, 16, 64, 1
+    C, H, P, ng = 65, 16, 64, 1
     g = np.random.default_rng(7000 + K + N)
     enc = lambda a: wl.f32_to_bf16_bits(a.astype(np.float32))
     x = enc(g.standard_normal((C, K, H, P)))
@@ -388,7 +391,7 @@ def test_scan_position_split_is_bit_identical(K, chunk, N):
         return ops.ssd_scan(to_dev(x[:c], "bf16"), to_dev(delta[:c], "bf16"), to_dev(A, "bf16"),
                             to_dev(B[:c], "bf16"), to_dev(Cm[:c], "bf16"), chunk=chunk, h0=to_dev(h0[:c], "bf16"),
                             Dskip=to_dev(D, "bf16"), want_final=True)
-    y_all, hf_all = run(C)     # C * H = 1024: one wave per head
+    y_all, hf_all = run(C)     # C * H = 1040: one wave per head
     y_few, hf_few = run(5)     # C * H = 80: four waves per head
     torch.cuda.synchronize()
     assert torch.equal(y_few, y_all[:5]) and torch.equal(hf_few, hf_all[:5])
