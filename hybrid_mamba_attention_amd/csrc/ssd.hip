@@ -424,8 +424,11 @@ __device__ __forceinline__ void ssd_scan_block(const SsdArgs& a, int bid) {
   }
 }
 
+// Chunks of up to 16 with states of up to 64 are held to two waves per SIMD
+// (256 registers): the convolution-fused form at N = 64 took 257 unbounded,
+// which halved its occupancy and ran a 2048-head batch in two rounds.
 template <typename T, int NMAX, int QM, bool V4, bool CONV, int TS = 1>
-__global__ __launch_bounds__(256) void k_ssd_scan(SsdArgs a) {
+__global__ __launch_bounds__(256, (QM == 16 && NMAX <= 64) ? 2 : 1) void k_ssd_scan(SsdArgs a) {
   ssd_scan_block<T, NMAX, QM, V4, CONV, TS>(a, blockIdx.x);
 }
 
