@@ -383,30 +383,30 @@ __global__ __launch_bounds__(256) void k_init_wide(InitArgs a) {
         if (row < C)
           *reinterpret_cast<float2*>(a.h0 + size_t(row) * S + n0 + 2 * c) = make_float2(acc[m][0][i], acc[m][1][i]);
       }
-    return;
-  }
-  // k-half 1 hands its partial tile to k-half 0 through LDS
-  __syncthreads();
-  float* red = reinterpret_cast<float*>(lds) + cg * (MT * 2 * 16 * 64);
-  if (kh == 1) {
+  } else {
+    // k-half 1 hands its partial tile to k-half 0 through LDS
+    __syncthreads();
+    float* red = reinterpret_cast<float*>(lds) + cg * (MT * 2 * 16 * 64);
+    if (kh == 1) {
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) red[((m * 2 + t) * 16 + i) * 64 + lane] = acc[m][t][i];
+    }
+    __syncthreads();
+    if (kh == 1) return;
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) red[((m * 2 + t) * 16 + i) * 64 + lane] = acc[m][t][i];
+      for (int i = 0; i < 16; ++i) {
+        const float v0 = acc[m][0][i] + red[((m * 2 + 0) * 16 + i) * 64 + lane];
+        const float v1 = acc[m][1][i] + red[((m * 2 + 1) * 16 + i) * 64 + lane];
+        const int row = m0 + m * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
+        if (row < C) *reinterpret_cast<float2*>(a.h0 + size_t(row) * S + n0 + 2 * c) = make_float2(v0, v1);
+      }
   }
-  __syncthreads();
-  if (kh == 1) return;
-#pragma unroll
-  for (int m = 0; m < MT; ++m)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float v0 = acc[m][0][i] + red[((m * 2 + 0) * 16 + i) * 64 + lane];
-      const float v1 = acc[m][1][i] + red[((m * 2 + 1) * 16 + i) * 64 + lane];
-      const int row = m0 + m * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
-      if (row < C) *reinterpret_cast<float2*>(a.h0 + size_t(row) * S + n0 + 2 * c) = make_float2(v0, v1);
-    }
 }
 
 template <typename T, int MT, int NCL, int PF>
